@@ -1,0 +1,162 @@
+"""CPU oracle for the block-scaled FP8 GEMM (numpy front end over ``dgo.cpp``).
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The HIP library never
+imports, links or calls it, and it imports nothing from the HIP library.
+
+The arithmetic lives in ``dgo.cpp``; its header states what each function
+computes and which passage of the pages it follows:
+
+* ``e4m3_decode`` / ``e4m3_encode``: OCP E4M3FN codec (the pages: "4 exponent
+  bits, 3 mantissa bits"; input type torch.float8_e4m3fn, DeepGEMM实战 §4.2).
+* ``quantize_blocks``: per g x g block, scale = amax/448 (FP32), codes =
+  E4M3_RNE_SAT(x / scale) (DeepGEMM实战 §2.2, §4.4, §5.2).
+* ``gemm_ref``: ref[i,j] = sum_kb sa[i/g,kb]*sb[j/g,kb] * P[i,j,kb] with the
+  exact FP64 segment partials P (DeepGEMM实战 §2.2, §3.2, §3.3, §4.2).
+
+Parity status: every function above is pinned by the CPU tests
+(``tests/test_oracle_*.py``) against torch's float8 cast, brute force, exact
+rational arithmetic, numpy's float64 matmul, closed forms and invariants.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dgo.cpp")
+_LIB = os.path.join(_HERE, "libdgo.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``dgo.cpp`` into ``libdgo.so`` with plain g++ (no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+               "-shared", "-pthread", _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    i64 = ctypes.c_int64
+    lib.dgo_e4m3_decode.restype = ctypes.c_double
+    lib.dgo_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.dgo_e4m3_encode.restype = ctypes.c_uint8
+    lib.dgo_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.dgo_e4m3_decode_n.restype = None
+    lib.dgo_e4m3_decode_n.argtypes = [u8p, i64, f64p]
+    lib.dgo_e4m3_encode_n.restype = None
+    lib.dgo_e4m3_encode_n.argtypes = [f32p, i64, u8p]
+    lib.dgo_quantize_blocks.restype = ctypes.c_int
+    lib.dgo_quantize_blocks.argtypes = [f32p, i64, i64, ctypes.c_int, u8p, f32p, ctypes.c_int]
+    lib.dgo_segment_partials.restype = None
+    lib.dgo_segment_partials.argtypes = [u8p, u8p, i64, ctypes.c_int, f64p]
+    lib.dgo_gemm_ref.restype = ctypes.c_int
+    lib.dgo_gemm_ref.argtypes = [u8p, u8p, f32p, f32p, i64, i64, i64, ctypes.c_int,
+                                 i64p, i64, i64p, i64, f64p, ctypes.c_int]
+    lib.dgo_hardware_threads.restype = ctypes.c_int
+    lib.dgo_hardware_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(arr: np.ndarray, ctype):
+    return arr.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: all hardware threads, at most 16."""
+    return max(1, min(16, _load().dgo_hardware_threads()))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3FN codes (uint8, any shape) -> float64 values (NaN for 0x7F/0xFF)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().dgo_e4m3_decode_n(_ptr(c, ctypes.c_uint8), c.size, _ptr(out, ctypes.c_double))
+    return out
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """float32 values (any shape) -> E4M3FN codes, RNE, saturating at +-448."""
+    v = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().dgo_e4m3_encode_n(_ptr(v, ctypes.c_float), v.size, _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def quantize_blocks(x, g: int, nthreads: int | None = None):
+    """x [rows, cols] float32 -> (codes uint8 [rows, cols], scales float32 [ceil(rows/g), cols/g])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    if cols % g:
+        raise ValueError("cols must be a multiple of g")
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty(((rows + g - 1) // g, cols // g), dtype=np.float32)
+    rc = _load().dgo_quantize_blocks(_ptr(x, ctypes.c_float), rows, cols, g, _ptr(q, ctypes.c_uint8),
+                                     _ptr(s, ctypes.c_float), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("dgo_quantize_blocks rejected its arguments")
+    return q, s
+
+
+def segment_partials(a_row, b_row, g: int) -> np.ndarray:
+    """Exact FP64 segment partials P[kb] for one output element."""
+    a_row = np.ascontiguousarray(a_row, dtype=np.uint8)
+    b_row = np.ascontiguousarray(b_row, dtype=np.uint8)
+    K = a_row.size
+    P = np.empty(K // g, dtype=np.float64)
+    _load().dgo_segment_partials(_ptr(a_row, ctypes.c_uint8), _ptr(b_row, ctypes.c_uint8), K, g,
+                                 _ptr(P, ctypes.c_double))
+    return P
+
+
+def gemm_ref(a8, b8, sa, sb, g: int, rows=None, cols=None, nthreads: int | None = None) -> np.ndarray:
+    """FP64 reference of C = A*B^T with block scales, on rows x cols of the output.
+
+    a8 [M,K] uint8, b8 [N,K] uint8, sa [ceil(M/g), K/g] float32, sb [ceil(N/g), K/g] float32.
+    rows / cols: optional index arrays; the result has shape [len(rows), len(cols)].
+    """
+    a8 = np.ascontiguousarray(a8, dtype=np.uint8)
+    b8 = np.ascontiguousarray(b8, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sb = np.ascontiguousarray(sb, dtype=np.float32)
+    M, K = a8.shape
+    N, K2 = b8.shape
+    if K2 != K or K % g:
+        raise ValueError("bad K")
+    if sa.shape != ((M + g - 1) // g, K // g) or sb.shape != ((N + g - 1) // g, K // g):
+        raise ValueError("bad scale shapes")
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    c = None if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    nr = M if r is None else r.size
+    nc = N if c is None else c.size
+    out = np.empty((nr, nc), dtype=np.float64)
+    rc = _load().dgo_gemm_ref(
+        _ptr(a8, ctypes.c_uint8), _ptr(b8, ctypes.c_uint8), _ptr(sa, ctypes.c_float),
+        _ptr(sb, ctypes.c_float), M, N, K, g,
+        None if r is None else _ptr(r, ctypes.c_int64), nr,
+        None if c is None else _ptr(c, ctypes.c_int64), nc,
+        _ptr(out, ctypes.c_double), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("dgo_gemm_ref rejected its arguments")
+    return out
+

@@ -1,0 +1,209 @@
+// dgo: plain CPU oracle for the block-scaled FP8 GEMM.
+//
+// TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call
+// this file: only the tests, the package smoke check and the benchmark's
+// CPU-baseline leg use it. It shares no code, header, table or constant with
+// the HIP library; the two meet only in the tests, through the seeded inputs.
+//
+// What it computes, and from which passage of the pages:
+//
+//  * E4M3 decode/encode. The pages give the format only as "4 exponent bits,
+//    3 mantissa bits" (DeepGEMM-style template article, §3.4; DeepGEMM in
+//    practice / DeepGEMM实战, §2.2) and name torch.float8_e4m3fn as the input
+//    type (DeepGEMM实战, §4.2). The reading taken is the OCP E4M3FN format that
+//    type implements: bias 7, exponent field 0 holds subnormals m/8 * 2^-6,
+//    largest finite value 0x7E = 448, codes 0x7F/0xFF are NaN, no infinity.
+//
+//  * Block quantisation, the step that feeds the GEMM (DeepGEMM实战 §2.2: one
+//    factor per 128x128 block maps the block into FP8 range when quantising;
+//    §4.4: quantisation happens outside the GEMM and must use the GEMM's
+//    granularity; §5.2: divide when quantising, multiply when dequantising).
+//    Per g x g block: amax over the elements present (edge blocks are
+//    partial), scale = amax / 448 in FP32 (1.0 for an all-zero block), and
+//    each element becomes E4M3(x / scale), an FP32 divide followed by
+//    round-to-nearest-even with saturation to +-448.
+//
+//  * The GEMM, C = A * B^T in the NT layout (DeepGEMM实战 §3.3, §4.2): A is
+//    [M,K], B is [N,K], both K-contiguous. Each g-wide K segment kb is summed
+//    on its own (§3.2: segments accumulated separately, then added) and then
+//    restored with the product of its two block scales (§2.2):
+//        P[i,j,kb] = sum_{k in kb} dec(A[i,k]) * dec(B[j,k])
+//        ref[i,j]  = sum_kb (sa[i/g,kb] * sb[j/g,kb]) * P[i,j,kb]   (kb ascending)
+//    in FP64. Every E4M3 value is an integer multiple of 2^-9 below 2^9, so a
+//    product is a multiple of 2^-18 below 2^18 and a sum of up to 2^14 of
+//    them stays below 2^53 units: P is exact in FP64 in any order. The only
+//    roundings are the scale multiply and the segment sum.
+//
+// Scale tensors are row-major FP32: sa is [ceil(M/g)][K/g], sb is
+// [ceil(N/g)][K/g]. K must be a multiple of g.
+//
+// Build: g++ -O2 -std=c++17 -ffp-contract=off -fPIC -shared -pthread.
+// No fast-math: the arithmetic above must be IEEE single/double as written.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace {
+
+// One worker per slice of [0, n). Plain std::thread fan-out.
+template <typename F>
+void parallel_for(int64_t n, int nthreads, F body) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > n) nthreads = (int)(n > 0 ? n : 1);
+  if (nthreads == 1) {
+    body(0, n);
+    return;
+  }
+  std::vector<std::thread> pool;
+  int64_t per = (n + nthreads - 1) / nthreads;
+  for (int t = 0; t < nthreads; ++t) {
+    int64_t lo = t * per, hi = lo + per < n ? lo + per : n;
+    if (lo >= hi) break;
+    pool.emplace_back(body, lo, hi);
+  }
+  for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+// OCP E4M3FN decode of one code, straight from the bit fields.
+double dgo_e4m3_decode(uint8_t code) {
+  const int s = code >> 7;
+  const int e = (code >> 3) & 0xF;
+  const int m = code & 0x7;
+  if (e == 0xF && m == 0x7) return std::nan("");
+  double mag;
+  if (e == 0)
+    mag = std::ldexp((double)m / 8.0, -6);             // subnormal: m/8 * 2^(1-7)
+  else
+    mag = std::ldexp(1.0 + (double)m / 8.0, e - 7);    // normal: (1+m/8) * 2^(e-7)
+  return s ? -mag : mag;
+}
+
+// FP32 -> E4M3FN: round to nearest, ties to even, saturate to +-448.
+// Never produces NaN (finite input assumed).
+uint8_t dgo_e4m3_encode(float y) {
+  const uint8_t sign = std::signbit(y) ? 0x80 : 0x00;
+  const double v = std::fabs((double)y);
+  if (v >= 448.0) return sign | 0x7E;
+  if (v < std::ldexp(1.0, -6)) {
+    // Subnormal range, spacing 2^-9. Scaling by 512 is exact; nearbyint rounds
+    // half to even in the default rounding mode. n == 8 is code 0x08 = 2^-6,
+    // the smallest normal, so the code is n itself.
+    const double n = std::nearbyint(v * 512.0);
+    return sign | (uint8_t)n;
+  }
+  int e2;
+  std::frexp(v, &e2);            // v = f * 2^e2, f in [0.5, 1)
+  int E = e2 - 1;                // v in [2^E, 2^(E+1)), -6 <= E <= 8
+  double n = std::nearbyint(std::ldexp(v, 3 - E));  // mantissa steps: n in [8, 16]
+  if (n == 16.0) {               // rounded up into the next binade
+    n = 8.0;
+    E += 1;
+  }
+  return sign | (uint8_t)(((E + 7) << 3) | ((int)n - 8));
+}
+
+// Decode an array of codes (convenience for the Python side).
+void dgo_e4m3_decode_n(const uint8_t* codes, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = dgo_e4m3_decode(codes[i]);
+}
+
+void dgo_e4m3_encode_n(const float* y, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = dgo_e4m3_encode(y[i]);
+}
+
+// Block quantiser. x is [rows][cols] FP32 row-major; q receives [rows][cols]
+// E4M3 codes; scales receives [ceil(rows/g)][cols/g] FP32.
+// Returns 0, or -1 on bad arguments.
+int dgo_quantize_blocks(const float* x, int64_t rows, int64_t cols, int g, uint8_t* q,
+                        float* scales, int nthreads) {
+  if (!x || !q || !scales || rows <= 0 || cols <= 0 || g <= 0 || cols % g != 0) return -1;
+  const int64_t nrb = (rows + g - 1) / g, ncb = cols / g;
+  parallel_for(nrb, nthreads, [&](int64_t lo, int64_t hi) {
+    for (int64_t rb = lo; rb < hi; ++rb) {
+      const int64_t r0 = rb * g, r1 = (r0 + g < rows) ? r0 + g : rows;
+      for (int64_t cb = 0; cb < ncb; ++cb) {
+        const int64_t c0 = cb * g, c1 = c0 + g;
+        float amax = 0.0f;
+        for (int64_t r = r0; r < r1; ++r)
+          for (int64_t c = c0; c < c1; ++c) {
+            const float a = std::fabs(x[r * cols + c]);
+            if (a > amax) amax = a;
+          }
+        const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scales[rb * ncb + cb] = scale;
+        for (int64_t r = r0; r < r1; ++r)
+          for (int64_t c = c0; c < c1; ++c) q[r * cols + c] = dgo_e4m3_encode(x[r * cols + c] / scale);
+      }
+    }
+  });
+  return 0;
+}
+
+// Segment partials P[kb] = sum_{k in segment kb} dec(a_row[k]) * dec(b_row[k])
+// for one output element (a_row = A[i,:], b_row = B[j,:]), FP64.
+void dgo_segment_partials(const uint8_t* a_row, const uint8_t* b_row, int64_t K, int g, double* P) {
+  double tab[256];
+  for (int c = 0; c < 256; ++c) tab[c] = dgo_e4m3_decode((uint8_t)c);
+  for (int64_t kb = 0; kb < K / g; ++kb) {
+    double p = 0.0;
+    for (int64_t k = kb * g; k < kb * g + g; ++k) p += tab[a_row[k]] * tab[b_row[k]];
+    P[kb] = p;
+  }
+}
+
+// Reference GEMM in FP64 on a subset of the output.
+//   rows: nrows row indices into [0,M) (NULL = all M rows, nrows ignored)
+//   cols: ncols column indices into [0,N) (NULL = all N columns)
+//   out : [nrows][ncols] FP64, out[r][c] = ref[rows[r], cols[c]]
+// Returns 0, or -1 on bad arguments.
+int dgo_gemm_ref(const uint8_t* a, const uint8_t* b, const float* sa, const float* sb, int64_t M,
+                 int64_t N, int64_t K, int g, const int64_t* rows, int64_t nrows, const int64_t* cols,
+                 int64_t ncols, double* out, int nthreads) {
+  if (!a || !b || !sa || !sb || !out || M <= 0 || N <= 0 || K <= 0 || g <= 0 || K % g != 0) return -1;
+  if (!rows) nrows = M;
+  if (!cols) ncols = N;
+  for (int64_t r = 0; rows && r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= M) return -1;
+  for (int64_t c = 0; cols && c < ncols; ++c)
+    if (cols[c] < 0 || cols[c] >= N) return -1;
+
+  double tab[256];
+  for (int c = 0; c < 256; ++c) tab[c] = dgo_e4m3_decode((uint8_t)c);
+  const int64_t nkb = K / g;
+
+  parallel_for(nrows, nthreads, [&](int64_t lo, int64_t hi) {
+    for (int64_t r = lo; r < hi; ++r) {
+      const int64_t i = rows ? rows[r] : r;
+      const uint8_t* arow = a + i * K;
+      const float* sarow = sa + (i / g) * nkb;
+      for (int64_t c = 0; c < ncols; ++c) {
+        const int64_t j = cols ? cols[c] : c;
+        const uint8_t* brow = b + j * K;
+        const float* sbrow = sb + (j / g) * nkb;
+        double ref = 0.0;
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+          double p = 0.0;  // exact: see the header
+          for (int64_t k = kb * g; k < kb * g + g; ++k) p += tab[arow[k]] * tab[brow[k]];
+          const double s = (double)sarow[kb] * (double)sbrow[kb];  // exact (24 x 24 bits)
+          ref += s * p;
+        }
+        out[r * ncols + c] = ref;
+      }
+    }
+  });
+  return 0;
+}
+
+int dgo_hardware_threads(void) {
+  unsigned n = std::thread::hardware_concurrency();
+  return n ? (int)n : 1;
+}
+
+}  // extern "C"
