@@ -1,0 +1,141 @@
+"""Block-scaled FP8 GEMM for AMD MI355X (gfx950): Python binding of libdg.so.
+
+Argument marshalling only. Every step of the GEMM runs in the HIP kernels of
+``libdg.so`` (C ABI in ``include/dg.h``); this module checks tensor dtypes,
+shapes and devices, passes raw device pointers and the current HIP stream, and
+turns status codes into exceptions. There is no fallback: if the library is
+missing or fails to load, importing this package raises.
+
+The operation (DeepGEMM实战 §2.2, §3.2, §4.2):
+  out[i,j] = bf16( sum_kb sa[i/g,kb] * sb[j/g,kb] * sum_{k in kb} A[i,k] * B[j,k] )
+with A [M,K], B [N,K] in E4M3FN (NT layout), FP32 scales per g x g block and
+FP32 accumulation within and across K segments.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime libdg.so binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+
+DG_OK = 0
+DG_EINVAL = -1
+DG_EALIGN = -2
+DG_EUNSUPPORTED = -3
+DG_ELAUNCH = -4
+
+
+class dg_tile_info(ctypes.Structure):
+    _fields_ = [("kernel_id", ctypes.c_int), ("bm", ctypes.c_int), ("bn", ctypes.c_int),
+                ("bk", ctypes.c_int), ("stages", ctypes.c_int), ("waves", ctypes.c_int),
+                ("ksplit", ctypes.c_int), ("grid", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libdg.so is not built (run fp8_block_scaled_scales_amd.build.build()); "
+                          "there is no non-HIP fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.dg_gemm_fp8_nt.restype = ctypes.c_int
+    lib.dg_gemm_fp8_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    lib.dg_query_tile.restype = ctypes.c_int
+    lib.dg_query_tile.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(dg_tile_info)]
+    lib.dg_strerror.restype = ctypes.c_char_p
+    lib.dg_strerror.argtypes = [ctypes.c_int]
+    lib.dg_version.restype = ctypes.c_int
+    lib.dg_version.argtypes = []
+    return lib
+
+
+_lib = _load()
+lib = _lib  # raw ctypes handle, for tests that exercise the C ABI directly
+
+
+class DGError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s: %s (status %d)" % (where, dg_strerror(code), code))
+        self.code = code
+
+
+class DGArgumentError(DGError, ValueError):
+    pass
+
+
+def _raise(code: int, where: str):
+    if code in (DG_EINVAL, DG_EALIGN):
+        raise DGArgumentError(code, where)
+    raise DGError(code, where)
+
+
+def dg_strerror(code: int) -> str:
+    return _lib.dg_strerror(int(code)).decode()
+
+
+def dg_version() -> int:
+    return _lib.dg_version()
+
+
+def dg_query_tile(M: int, N: int, K: int, gran: int = 128) -> dict:
+    info = dg_tile_info()
+    rc = _lib.dg_query_tile(M, N, K, gran, ctypes.byref(info))
+    if rc != DG_OK:
+        _raise(rc, "dg_query_tile")
+    return {name: getattr(info, name) for name, _ in dg_tile_info._fields_}
+
+
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _check(t, name, dtypes, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype not in dtypes:
+        raise ValueError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def dg_gemm_fp8_nt(a, b, sa, sb, out=None, gran: int = 128, stream=None):
+    """out[M,N] (bf16) = A[M,K] * B[N,K]^T with gran x gran FP32 block scales.
+
+    a: [M,K] float8_e4m3fn (or uint8 holding E4M3FN codes), b: [N,K] likewise,
+    sa: [ceil(M/gran), K/gran] float32, sb: [ceil(N/gran), K/gran] float32,
+    out: optional preallocated [M,N] bfloat16 (allocated when None).
+    Enqueued on ``stream`` (a torch.cuda.Stream; default: the current stream).
+    """
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    M, K = a.shape
+    N = b.shape[0]
+    dev = a.device
+    if dev.type != "cuda":
+        raise ValueError("a must be a GPU tensor")
+    if gran not in (64, 128) or K % gran:
+        raise ValueError("gran must be 64 or 128 and divide K")
+    _check(a, "a", _FP8, (M, K), dev)
+    _check(b, "b", _FP8, (N, K), dev)
+    _check(sa, "sa", (torch.float32,), ((M + gran - 1) // gran, K // gran), dev)
+    _check(sb, "sb", (torch.float32,), ((N + gran - 1) // gran, K // gran), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", (torch.bfloat16,), (M, N), dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = _lib.dg_gemm_fp8_nt(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
+                                 M, N, K, gran, s.cuda_stream)
+    if rc != DG_OK:
+        _raise(rc, "dg_gemm_fp8_nt")
+    return out
+
+
+__all__ = ["dg_gemm_fp8_nt", "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError",
+           "DG_OK", "DG_EINVAL", "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH", "LIB_PATH"]

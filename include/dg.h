@@ -1,0 +1,122 @@
+/*
+ * dg.h - C ABI of the block-scaled FP8 GEMM library for AMD MI355X (gfx950).
+ *
+ * The operation (DeepGEMM in practice / DeepGEMM实战: §2.2 one FP32 scale
+ * factor per 128x128 block of each input, restored while the products are
+ * accumulated; §3.2 FP32 accumulation, each K segment summed on its own and
+ * the segments then added; §3.3 and §4.2 the NT layout, A [M,K] and B [N,K]
+ * in FP8, preallocated BF16 output):
+ *
+ *   out[i,j] = bf16( sum_kb  sa[i/g, kb] * sb[j/g, kb] * P[i,j,kb] )
+ *   P[i,j,kb] = sum_{k = kb*g}^{kb*g+g-1} A[i,k] * B[j,k]
+ *
+ * with A, B decoded from OCP E4M3FN codes, P accumulated in FP32 over exactly
+ * one g-wide K segment, the promotion acc = fma(P, sa*sb, acc) done in FP32
+ * once per segment, and the FP32 result rounded to BF16 (nearest even).
+ * Summation order inside a segment is unspecified; results are deterministic
+ * for a given (M, N, K, g) and device.
+ *
+ * All pointers are device pointers (memory the caller allocated, e.g. PyTorch
+ * tensors). The library keeps no pointer after a call returns and allocates
+ * nothing per call. Calls are asynchronous on `stream` (a hipStream_t; NULL is
+ * the default stream); faults during execution surface at the caller's next
+ * synchronisation. No call prints unless the environment sets DG_LOG=1, and
+ * no call exits or throws.
+ *
+ * Thread safety: calls may come from several host threads. The one-time
+ * per-device check (architecture must be gfx950) runs under std::call_once.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define DG_OK 0
+#define DG_EINVAL (-1)       /* bad argument; nothing was launched (recoverable) */
+#define DG_EALIGN (-2)       /* misaligned pointer; nothing was launched */
+#define DG_EUNSUPPORTED (-3) /* device is not gfx950, or an unsupported option */
+#define DG_ELAUNCH (-4)      /* a HIP call failed; dg_strerror() gives its text */
+
+#define DG_VERSION 100 /* 1.0.0 */
+
+/* Largest accepted dimension; keeps every in-tile byte offset in 32 bits. */
+#define DG_MAX_DIM (1LL << 24)
+
+/*
+ * dg_gemm_fp8_nt - C[M,N] = A[M,K] * B[N,K]^T with g x g block scales.
+ *
+ *   a    E4M3FN codes, [M,K] row-major (K contiguous, lda = K). 16-byte aligned.
+ *   b    E4M3FN codes, [N,K] row-major (K contiguous, ldb = K). 16-byte aligned.
+ *   sa   FP32 scales of A, [ceil(M/g)][K/g] row-major. 4-byte aligned.
+ *   sb   FP32 scales of B, [ceil(N/g)][K/g] row-major. 4-byte aligned.
+ *   out  BF16 result, [M,N] row-major (ldc = N), fully overwritten. 2-byte
+ *        aligned; must not overlap the inputs.
+ *   M, N, K  > 0 and <= DG_MAX_DIM; K a multiple of gran.
+ *   gran block granularity g: 64 or 128 (the pages' 64x64 and 128x128
+ *        choices, DeepGEMM实战 §3.1).
+ *   stream hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Rows of A beyond M and rows of B beyond N are never read, and nothing
+ * outside out[0..M-1][0..N-1] is written (ragged M and N are supported).
+ * Returns DG_OK, DG_EINVAL (null pointer, bad dims, K % g != 0, bad g),
+ * DG_EALIGN, DG_EUNSUPPORTED (not gfx950) or DG_ELAUNCH. Argument errors are
+ * reported before any HIP call.
+ */
+int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* sb, void* out,
+                   int64_t M, int64_t N, int64_t K, int gran, void* stream);
+
+/* The tile-table entry a call with these sizes would use. */
+typedef struct dg_tile_info {
+  int kernel_id; /* index in the precompiled table */
+  int bm, bn;    /* workgroup output tile */
+  int bk;        /* K bytes staged per pipeline step */
+  int stages;    /* LDS ring depth */
+  int waves;     /* waves per workgroup */
+  int ksplit;    /* waves splitting K inside a workgroup (1 = none) */
+  int64_t grid;  /* workgroups launched */
+} dg_tile_info;
+
+/*
+ * dg_query_tile - fill *info with the tile-table entry dg_gemm_fp8_nt would
+ * launch for (M, N, K, gran). Pure host logic, no HIP call. Returns DG_OK or
+ * DG_EINVAL for arguments dg_gemm_fp8_nt would reject.
+ */
+int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info);
+
+/*
+ * dg_quantize_e4m3_blocks - block quantisation FP32 -> E4M3FN, the step that
+ * produces the GEMM's operands (DeepGEMM实战 §4.4: quantisation sits outside
+ * the GEMM, activations are quantised online, and the granularity must match
+ * the GEMM's; §2.2: one factor per block maps it into FP8 range; §5.2:
+ * quantise by dividing).
+ *
+ *   x       FP32 [rows][cols] row-major, 16-byte aligned.
+ *   q       E4M3FN codes out, [rows][cols] row-major, 4-byte aligned.
+ *   scales  FP32 out, [ceil(rows/gran)][cols/gran] row-major, 4-byte aligned.
+ *   rows, cols > 0 and <= DG_MAX_DIM; cols a multiple of gran; gran 64 or 128.
+ *
+ * Per gran x gran block (rows past the end make edge blocks partial):
+ * amax = max |x| over present elements, scale = amax / 448 in FP32 (1.0 for
+ * an all-zero block), q = E4M3(x / scale) with an FP32 divide and
+ * round-to-nearest-even. Inputs must be finite. Same status codes and
+ * asynchrony as dg_gemm_fp8_nt.
+ */
+int dg_quantize_e4m3_blocks(const float* x, int64_t rows, int64_t cols, int gran, void* q, float* scales,
+                            void* stream);
+
+/* Text for a status code (for DG_ELAUNCH: the last HIP error on this thread). */
+const char* dg_strerror(int code);
+
+/* DG_VERSION of the loaded library. */
+int dg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

@@ -1,0 +1,91 @@
+"""The C ABI on the CPU: the library loads, exports every function include/dg.h
+declares, and rejects bad arguments with the documented status codes before it
+makes any HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+@pytest.fixture(scope="module")
+def dg():
+    import fp8_block_scaled_scales_amd as dg
+
+    return dg
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_api():
+    names = _declared_functions()
+    for f in ("dg_gemm_fp8_nt", "dg_query_tile", "dg_strerror", "dg_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(dg):
+    lib = ctypes.CDLL(dg.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_codes_match_header(dg):
+    text = open(HEADER).read()
+    for name in ("DG_OK", "DG_EINVAL", "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH"):
+        m = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
+        assert m and int(m.group(1)) == getattr(dg, name), name
+    assert dg.dg_version() == int(re.search(r"#define DG_VERSION (\d+)", text).group(1))
+
+
+# Fake but aligned, non-null device addresses: the checks below must fail
+# before anything dereferences them or calls into HIP.
+A, B, SA, SB, OUT = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+
+
+def _call(dg, a=A, b=B, sa=SA, sb=SB, out=OUT, M=256, N=256, K=256, g=128):
+    return dg.lib.dg_gemm_fp8_nt(a, b, sa, sb, out, M, N, K, g, None)
+
+
+@pytest.mark.parametrize("kw", [dict(a=0), dict(b=0), dict(sa=0), dict(sb=0), dict(out=0),
+                                dict(M=0), dict(N=0), dict(K=0), dict(M=-5), dict(K=-128),
+                                dict(K=192), dict(K=100, g=64), dict(g=96), dict(g=256), dict(g=0),
+                                dict(M=(1 << 24) + 1), dict(K=1 << 25)])
+def test_einval(dg, kw):
+    assert _call(dg, **kw) == dg.DG_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(a=A + 8), dict(b=B + 4), dict(sa=SA + 2), dict(sb=SB + 1), dict(out=OUT + 1)])
+def test_ealign(dg, kw):
+    assert _call(dg, **kw) == dg.DG_EALIGN
+
+
+def test_strerror(dg):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(dg.dg_strerror(code), str) and dg.dg_strerror(code)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(256, 256, 256, 128), (64, 4096, 7168, 128), (4096, 7168, 2048, 128),
+                                     (8192, 8192, 8192, 128), (2000, 4000, 16384, 64), (1, 1, 64, 64)])
+def test_query_tile(dg, M, N, K, g):
+    t = dg.dg_query_tile(M, N, K, g)
+    assert t["bm"] > 0 and t["bn"] > 0 and t["bk"] == 128
+    tiles = -(-M // t["bm"]) * -(-N // t["bn"])
+    assert t["grid"] == tiles * t["ksplit"] or t["grid"] == tiles
+    with pytest.raises(ValueError):
+        dg.dg_query_tile(M, N, K + 1, g)
+
+
+def test_python_binding_rejects_bad_tensors(dg):
+    import torch
+
+    a = torch.zeros((4, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        dg.dg_gemm_fp8_nt(a, a, torch.ones(1, 1), torch.ones(1, 1))  # CPU tensors

@@ -1,0 +1,185 @@
+"""Parity of the HIP GEMM (through the C ABI) with the CPU oracle.
+
+Bar (elementwise): |gpu - ref| <= 1e-2*|ref| + 1e-2*rms(ref), the output being
+BF16 and the FP32 summation order free. Closed forms whose FP32 accumulation is
+exact must match bf16(ref) bit for bit, and so must the scale invariants.
+The five workloads run at full size; where the oracle cannot afford the whole
+output, sampled rows x columns (always including the first and last 8 of each)
+are compared.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _common, _golden
+from tests._gpu import gemm, say, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _assert_parity(got, ref, label):
+    ok, rms = _common.within_tolerance(got, ref)
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        detail = ", ".join("(%d,%d) got %.6g ref %.6g" % (i, j, got[i, j], ref[i, j]) for i, j in idx)
+        raise AssertionError("%s: %d of %d outside tolerance (rms %.4g): %s" % (label, int((~ok).sum()), ok.size, rms, detail))
+    bf_ref = _common.bf16_bits_to_f64(_common.f32_to_bf16_bits(ref.astype(np.float32)))
+    ulp = np.abs(bf_ref) * 2.0 ** -8 + 1e-30
+    within1 = float(np.mean(np.abs(got - bf_ref) <= ulp))
+    say("%s: max|err|/rms = %.3g, within 1 bf16 ulp of bf16(ref): %.4f" % (label, np.max(np.abs(got - ref)) / rms, within1))
+    return within1
+
+
+def test_worked_example_bitwise():
+    w = _golden.worked_gemm()
+    say("worked example 2x2x128 g=64")
+    got, _ = gemm(w["a8"], w["sa"], w["b8"], w["sb"], w["g"])
+    assert np.array_equal(got, w["bf16"])
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+def test_workload_parity(c):
+    w, a8, sa, b8, sb = workload(c)
+    M, N, g = w["M"], w["N"], w["g"]
+    say("workload %d %s" % (c, w["name"]))
+    got, _ = gemm(a8, sa, b8, sb, g)
+    assert np.all(np.isfinite(got))
+    if c in (1, 2):
+        ref = oracle.gemm_ref(a8, b8, sa, sb, g)
+        within1 = _assert_parity(got, ref, "workload %d (full)" % c)
+    else:
+        rows = _common.sample_indices(M, 120, seed=c)
+        cols = _common.sample_indices(N, 120, seed=100 + c)
+        ref = oracle.gemm_ref(a8, b8, sa, sb, g, rows, cols)
+        within1 = _assert_parity(got[np.ix_(rows, cols)], ref, "workload %d (sampled)" % c)
+    assert within1 > 0.95
+
+
+RAGGED = [
+    (1, 1, 64, 64), (1, 17, 128, 128), (15, 16, 128, 64), (17, 15, 192, 64), (63, 65, 256, 128),
+    (64, 64, 448, 64), (65, 127, 384, 128), (127, 129, 896, 128), (129, 1, 128, 64), (200, 136, 256, 128),
+    (1021, 1023, 128, 128), (1023, 1025, 448, 64), (1025, 1021, 256, 128), (2000, 130, 640, 64),
+    (130, 2000, 512, 128), (257, 255, 128, 64),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g", RAGGED)
+def test_ragged_sweep(M, N, K, g):
+    x = synth.normal(7000 + M, (M, K))
+    y = synth.normal(8000 + N, (N, K), sigma=0.02)
+    a8, sa = oracle.quantize_blocks(x, g)
+    b8, sb = oracle.quantize_blocks(y, g)
+    say("ragged M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    got, _ = gemm(a8, sa, b8, sb, g)
+    ref = oracle.gemm_ref(a8, b8, sa, sb, g)
+    _assert_parity(got, ref, "ragged %dx%dx%d g=%d" % (M, N, K, g))
+
+
+def _pow2_scales(nrb, nkb, f):
+    return np.array([[2.0 ** f(r, k) for k in range(nkb)] for r in range(nrb)], dtype=np.float32)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(300, 260, 512, 128), (200, 330, 640, 64), (64, 4096, 1024, 128)])
+def test_closed_form_all_ones_bitwise(M, N, K, g):
+    a8 = np.full((M, K), 0x38, np.uint8)
+    b8 = np.full((N, K), 0x38, np.uint8)
+    sa = _pow2_scales(-(-M // g), K // g, lambda mb, kb: (mb - kb) % 7 - 3)
+    sb = _pow2_scales(-(-N // g), K // g, lambda nb, kb: (2 * nb + kb) % 3)
+    say("all-ones M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    got, bits = gemm(a8, sa, b8, sb, g)
+    ref = oracle.gemm_ref(a8, b8, sa, sb, g)
+    assert np.array_equal(bits, _common.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+def test_closed_form_identity_bitwise():
+    M = K = 512
+    N, g = 300, 128
+    rng = np.random.default_rng(21)
+    a8 = np.zeros((M, K), np.uint8)
+    a8[np.arange(M), np.arange(K)] = 0x38
+    b8 = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    b8[(b8 & 0x7F) == 0x7F] = 0x00
+    sa = _pow2_scales(M // g, K // g, lambda mb, kb: (mb * 3 + kb) % 5 - 2)
+    sb = _pow2_scales(-(-N // g), K // g, lambda nb, kb: (nb + 2 * kb) % 4 - 1)
+    say("identity M=K=512 N=300")
+    got, bits = gemm(a8, sa, b8, sb, g)
+    ref = oracle.gemm_ref(a8, b8, sa, sb, g)
+    assert np.array_equal(bits, _common.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+def test_scale_invariants_bitwise():
+    w, a8, sa, b8, sb = workload(3)
+    g = w["g"]
+    say("invariants on workload 3")
+    _, base = gemm(a8, sa, b8, sb, g)
+    _, doubled = gemm(a8, (sa * np.float32(2)), b8, sb, g)
+    # 2x every sa: every FP32 step scales exactly, and so does BF16 rounding
+    assert np.array_equal(doubled.astype(np.uint32), np.where(base & 0x7FFF, base + 0x80, base).astype(np.uint32))
+    mb, kb = 5, 3
+    sa2 = sa.copy()
+    sa2[mb, kb] *= 2
+    _, one = gemm(a8, sa2, b8, sb, g)
+    rows = np.arange(w["M"]) // g == mb
+    assert np.array_equal(one[~rows], base[~rows])
+    assert not np.array_equal(one[rows], base[rows])
+
+
+def test_determinism_repeated_calls():
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+    from tests._gpu import device_inputs
+
+    w, a8, sa, b8, sb = workload(5)
+    ta, tsa, tb, tsb = device_inputs(a8, sa, b8, sb)
+    say("determinism x20 on workload 5")
+    first = dg.dg_gemm_fp8_nt(ta, tb, tsa, tsb, gran=w["g"]).clone()
+    for _ in range(19):
+        again = dg.dg_gemm_fp8_nt(ta, tb, tsa, tsb, gran=w["g"])
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K,g", [(65, 130, 256, 64), (1023, 1025, 128, 128), (200, 4000, 512, 64)])
+def test_canary_bands_untouched(M, N, K, g):
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+    from tests._gpu import device_inputs
+
+    x = synth.normal(31, (M, K))
+    y = synth.normal(32, (N, K), sigma=0.02)
+    a8, sa = oracle.quantize_blocks(x, g)
+    b8, sb = oracle.quantize_blocks(y, g)
+    ta, tsa, tb, tsb = device_inputs(a8, sa, b8, sb)
+    pad = 8 * N + 4096
+    buf = torch.full((M * N + pad,), -12345.0, dtype=torch.bfloat16, device="cuda:0")
+    out = buf[: M * N].view(M, N)
+    say("canary M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    dg.dg_gemm_fp8_nt(ta, tb, tsa, tsb, out=out, gran=g)
+    torch.cuda.synchronize()
+    assert torch.all(buf[M * N:] == -12345.0)
+    ref = oracle.gemm_ref(a8, b8, sa, sb, g)
+    _assert_parity(out.float().cpu().numpy().astype(np.float64), ref, "canary case")
+
+
+def test_non_default_stream_and_unaligned_out():
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+    from tests._gpu import device_inputs
+
+    M, N, K, g = 96, 100, 256, 64
+    a8, sa = oracle.quantize_blocks(synth.normal(41, (M, K)), g)
+    b8, sb = oracle.quantize_blocks(synth.normal(42, (N, K), sigma=0.02), g)
+    ta, tsa, tb, tsb = device_inputs(a8, sa, b8, sb)
+    buf = torch.zeros(M * N + 1, dtype=torch.bfloat16, device="cuda:0")
+    out = buf[1:].view(M, N)  # 2-byte aligned only: the scalar store path
+    s = torch.cuda.Stream()
+    say("side stream + unaligned out")
+    with torch.cuda.stream(s):
+        dg.dg_gemm_fp8_nt(ta, tb, tsa, tsb, out=out, gran=g)
+    s.synchronize()
+    ref = oracle.gemm_ref(a8, b8, sa, sb, g)
+    _assert_parity(out.float().cpu().numpy().astype(np.float64), ref, "side stream")
