@@ -1,0 +1,247 @@
+"""Throughput of the block-scaled FP8 GEMM (NT, E4M3, FP32 g x g block scales,
+BF16 out) on one MI355X, printed as one JSON line.
+
+A step is one call of dg_gemm_fp8_nt over one input set: the whole method
+(tile schedule, HBM->LDS staging, scale fetch, FP8 MFMA partials, per-segment
+FP32 promotion, BF16 epilogue) runs inside that one kernel launch.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Inputs: FP32 matrices drawn from the seeded generators in ``synth`` (the
+workload's shapes and value distributions), copied to the GPU and block
+quantised there by the library's own quantiser (dg_quantize_e4m3_blocks), so
+every byte the GEMM reads is resident in HBM before the timed region. Input
+sets are cloned so that consecutive steps rotate over enough distinct
+buffers (> 2x the 256 MB Infinity Cache) that the operands come from HBM,
+not from the last-level cache.
+
+Timing: W untimed warm-up steps, then K steps between two HIP events on the
+stream the GEMM is launched on, bracketed by torch.cuda.synchronize().
+value = 2*M*N*K / (time per step) in TFLOP/s.
+
+roofline: the GEMM kernel is the only kernel of a step. Its average launch
+duration is the timed region / K. achieved = algorithmic FLOPs (MFMA-bound
+shapes) or algorithmic bytes (HBM-bound shapes) per launch / that duration,
+against MI355X's published dense FP8 MFMA peak (5.0 PFLOP/s) or HBM
+bandwidth (8 TB/s). Algorithmic bytes = M*K + N*K (FP8 operands, once) +
+4*(ceil(M/g) + ceil(N/g))*K/g (FP32 scales) + 2*M*N (BF16 out).
+
+cpu_baseline: the CPU oracle (plain FP64, test infrastructure) timed on the
+host's cores over a bounded sample of the same workload: whole output rows,
+as many as fit in about 10 s, or the whole output repeated for that long.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402  (seeded inputs only; no GEMM arithmetic)
+
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published)
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E (published)
+MALL_BYTES = 256 << 20    # Infinity Cache
+DEFAULT_WORKLOAD = 2      # small-M decode shape, M=64 N=4096 K=7168, g=128
+
+# HBM traffic of the GEMM kernel per launch, from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (each scaled by the copy-kernel calibration factor), keyed by
+# workload and tagged with the hash of the kernel source the counters were
+# taken on. A different hash means the kernel changed since: traffic is null.
+TRAFFIC = {}
+
+
+def _kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in ("gemm_fp8_nt.hip", "gemm_fp8_nt.h", "dg_host.hip"):
+        with open(os.path.join(ROOT, "fp8_block_scaled_scales_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_by_name(key: str) -> int:
+    for c, w in synth.WORKLOADS.items():
+        if key in (str(c), w["name"]):
+            return c
+    raise SystemExit("unknown workload %r; choose one of %s" % (
+        key, ", ".join("%d=%s" % (c, w["name"]) for c, w in synth.WORKLOADS.items())))
+
+
+def algorithmic(w) -> tuple[float, float]:
+    M, N, K, g = w["M"], w["N"], w["K"], w["g"]
+    flops = 2.0 * M * N * K
+    nbytes = M * K + N * K + 4 * (math.ceil(M / g) + math.ceil(N / g)) * (K // g) + 2 * M * N
+    return flops, float(nbytes)
+
+
+def bound_of(w) -> str:
+    flops, nbytes = algorithmic(w)
+    # machine balance 5.0e15 / 8e12 = 625 FLOP/B
+    return "hbm" if flops / nbytes < PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+
+
+def make_inputs(c: int, dev):
+    """Quantised GPU inputs of workload c: (a8, sa, b8, sb)."""
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    w = synth.WORKLOADS[c]
+    g = w["g"]
+    xa = torch.from_numpy(synth.make_a(c)).to(dev)
+    a8, sa = dg.dg_quantize_e4m3_blocks(xa, gran=g)
+    del xa
+    xb = torch.from_numpy(synth.make_b(c)).to(dev)
+    b8, sb = dg.dg_quantize_e4m3_blocks(xb, gran=g)
+    del xb
+    torch.cuda.synchronize(dev)
+    return a8, sa, b8, sb
+
+
+def gpu_leg(c: int, steps: int, warmup: int, sets: int | None):
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    w = synth.WORKLOADS[c]
+    M, N, K, g = w["M"], w["N"], w["K"], w["g"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    a8, sa, b8, sb = make_inputs(c, dev)
+    set_bytes = a8.numel() + b8.numel() + 4 * (sa.numel() + sb.numel()) + 2 * M * N
+    if sets is None:
+        sets = max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes) + 1))
+    bufs = [(a8, sa, b8, sb, torch.empty((M, N), dtype=torch.bfloat16, device=dev))]
+    for _ in range(sets - 1):
+        bufs.append((a8.clone(), sa.clone(), b8.clone(), sb.clone(),
+                     torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    stream = torch.cuda.current_stream(dev)
+    print("bench: workload %d %s, %d input sets of %.1f MB, tile %s" % (
+        c, w["name"], sets, set_bytes / 1e6, dg.dg_query_tile(M, N, K, g)), file=sys.stderr, flush=True)
+
+    for i in range(warmup):
+        x = bufs[i % sets]
+        dg.dg_gemm_fp8_nt(x[0], x[2], x[1], x[3], out=x[4], gran=g, stream=stream)
+    torch.cuda.synchronize(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        x = bufs[i % sets]
+        dg.dg_gemm_fp8_nt(x[0], x[2], x[1], x[3], out=x[4], gran=g, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = start.elapsed_time(end) / steps
+    finite = bool(torch.isfinite(bufs[(steps - 1) % sets][4].float()).all().item())
+    return ms, sets, finite
+
+
+def cpu_leg(c: int, budget_s: float = 10.0):
+    """The oracle on a bounded sample of workload c, in TFLOP/s (FP64 on the host)."""
+    import numpy as np
+
+    import oracle
+
+    w = synth.WORKLOADS[c]
+    M, N, K, g = w["M"], w["N"], w["K"], w["g"]
+    threads = oracle.default_threads()
+    a8, sa = oracle.quantize_blocks(synth.make_a(c), g)
+    b8, sb = oracle.quantize_blocks(synth.make_b(c), g)
+    # probe: one row per thread
+    probe = np.arange(min(M, threads), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.gemm_ref(a8, b8, sa, sb, g, rows=probe)
+    per_row = (time.perf_counter() - t0) / probe.size
+    rows = int(budget_s / max(per_row, 1e-9))
+    rows = max(threads, (rows // threads) * threads)
+    if rows < M:
+        sel = np.linspace(0, M - 1, rows).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.gemm_ref(a8, b8, sa, sb, g, rows=sel)
+        dt = time.perf_counter() - t0
+        done = 2.0 * rows * N * K
+        sample = "%d of %d output rows (evenly spaced) x all %d columns, K=%d" % (rows, M, N, K)
+    else:
+        reps, dt, done = 0, 0.0, 0.0
+        t0 = time.perf_counter()
+        while dt < budget_s:
+            oracle.gemm_ref(a8, b8, sa, sb, g)
+            reps += 1
+            dt = time.perf_counter() - t0
+        done = 2.0 * M * N * K * reps
+        sample = "the whole %dx%d output, %d times, K=%d" % (M, N, reps, K)
+    return {"value": done / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample + " (FP64, %.1f s)" % dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=str(DEFAULT_WORKLOAD),
+                    help="workload number or name (default: the small-M decode shape)")
+    ap.add_argument("--sets", type=int, default=None, help="input sets rotated over (default: defeat the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU only: the GEMM runs whole on a single MI355X and "
+                         "nothing here launches or coordinates more than one (asked for --gpus %d)\n" % args.gpus)
+        raise SystemExit(2)
+    if args.steps < 1 or args.warmup < 0:
+        raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+
+    c = workload_by_name(args.workload)
+    w = synth.WORKLOADS[c]
+    flops, nbytes = algorithmic(w)
+    ms, sets, finite = gpu_leg(c, args.steps, args.warmup, args.sets)
+    if not finite:
+        raise SystemExit("GEMM output holds non-finite values")
+    sec = ms * 1e-3
+    tflops = flops / sec / 1e12
+    bound = bound_of(w)
+    if bound == "mfma":
+        achieved, peak, unit = tflops, PEAK_FP8_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
+    tr = TRAFFIC.get(w["name"])
+    traffic = tr["bytes"] if tr and tr["src"] == _kernel_source_hash() else None
+
+    cpu = None if args.no_cpu_baseline else cpu_leg(c)
+
+    line = {
+        "metric": "FP8 block-scaled GEMM TFLOPS and % of MI355X dense FP8 peak (1 GPU)",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "M": w["M"], "N": w["N"], "K": w["K"], "gran": w["g"],
+                   "layout": "NT", "out": "bf16", "input_sets": sets,
+                   "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
+                   "alg_GBps": round(nbytes / sec / 1e9, 1)},
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

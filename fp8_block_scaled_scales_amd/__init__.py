@@ -45,6 +45,8 @@ def _load():
     lib.dg_gemm_fp8_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.dg_query_tile.restype = ctypes.c_int
     lib.dg_query_tile.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(dg_tile_info)]
+    lib.dg_quantize_e4m3_blocks.restype = ctypes.c_int
+    lib.dg_quantize_e4m3_blocks.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp]
     lib.dg_strerror.restype = ctypes.c_char_p
     lib.dg_strerror.argtypes = [ctypes.c_int]
     lib.dg_version.restype = ctypes.c_int
@@ -137,5 +139,37 @@ def dg_gemm_fp8_nt(a, b, sa, sb, out=None, gran: int = 128, stream=None):
     return out
 
 
-__all__ = ["dg_gemm_fp8_nt", "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError",
+def dg_quantize_e4m3_blocks(x, gran: int = 128, q=None, scales=None, stream=None):
+    """Block-quantise x [rows, cols] float32 on the GPU -> (q uint8 [rows, cols], scales float32).
+
+    Per gran x gran block: scale = amax / 448 (1.0 for an all-zero block) and
+    q = E4M3FN(x / scale), round to nearest even. ``scales`` has shape
+    [ceil(rows/gran), cols/gran]. The codes come back as uint8 holding E4M3FN
+    bytes (``q.view(torch.float8_e4m3fn)`` reinterprets them).
+    """
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor")
+    rows, cols = x.shape
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    if gran not in (64, 128) or cols % gran:
+        raise ValueError("gran must be 64 or 128 and divide cols")
+    _check(x, "x", (torch.float32,), (rows, cols), dev)
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(((rows + gran - 1) // gran, cols // gran), dtype=torch.float32, device=dev)
+    _check(q, "q", _FP8, (rows, cols), dev)
+    _check(scales, "scales", (torch.float32,), ((rows + gran - 1) // gran, cols // gran), dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = _lib.dg_quantize_e4m3_blocks(x.data_ptr(), rows, cols, gran, q.data_ptr(), scales.data_ptr(),
+                                          s.cuda_stream)
+    if rc != DG_OK:
+        _raise(rc, "dg_quantize_e4m3_blocks")
+    return q, scales
+
+
+__all__ = ["dg_gemm_fp8_nt", "dg_quantize_e4m3_blocks", "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError",
            "DG_OK", "DG_EINVAL", "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH", "LIB_PATH"]
