@@ -15,9 +15,13 @@ sets are cloned so that consecutive steps rotate over enough distinct
 buffers (> 2x the 256 MB Infinity Cache) that the operands come from HBM,
 not from the last-level cache.
 
-Timing: W untimed warm-up steps, then K steps between two HIP events on the
-stream the GEMM is launched on, bracketed by torch.cuda.synchronize().
-value = 2*M*N*K / (time per step) in TFLOP/s.
+Timing: W untimed warm-up steps (eager calls), then K steps between two HIP
+events on the stream the GEMM is launched on, bracketed by
+torch.cuda.synchronize(). The K steps are replays of a HIP graph that
+captures L consecutive launches (L the largest divisor of K up to 100; the
+graph is replayed once untimed first, and its outputs are checked bit for bit
+against the eager calls'), so the host's per-call cost does not sit between
+kernels of a few microseconds. value = 2*M*N*K / (time per step) in TFLOP/s.
 
 roofline: the GEMM kernel is the only kernel of a step. Its average launch
 duration is the timed region / K. achieved = algorithmic FLOPs (MFMA-bound
@@ -128,21 +132,48 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None):
     print("bench: workload %d %s, %d input sets of %.1f MB, tile %s" % (
         c, w["name"], sets, set_bytes / 1e6, dg.dg_query_tile(M, N, K, g)), file=sys.stderr, flush=True)
 
-    for i in range(warmup):
+    def launch(i, st):
         x = bufs[i % sets]
-        dg.dg_gemm_fp8_nt(x[0], x[2], x[1], x[3], out=x[4], gran=g, stream=stream)
+        dg.dg_gemm_fp8_nt(x[0], x[2], x[1], x[3], out=x[4], gran=g, stream=st)
+
+    # Warm-up, eager: also allocates the library's split-K workspace and runs
+    # its one-time device check, neither of which may happen under capture.
+    for i in range(max(1, warmup)):
+        launch(i, stream)
     torch.cuda.synchronize(dev)
+    eager = bufs[0][4].clone()  # every set holds the same inputs, so every output must match it
+
+    # The timed steps are replays of a captured graph of L launches (L divides
+    # K), so the host's per-call cost does not starve the GPU between these
+    # few-microsecond kernels. The graph holds kernel launches only.
+    L = max(d for d in range(1, min(steps, 100) + 1) if steps % d == 0)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(L):
+                launch(i, cap)
+    torch.cuda.synchronize(dev)
+    for x in bufs:
+        x[4].zero_()  # so the check below sees what the replay wrote
+    graph.replay()  # untimed: uploads the graph; replays run on the current stream
+    torch.cuda.synchronize(dev)
+    assert torch.cuda.current_stream(dev) == stream
+    for i in range(min(sets, L)):
+        if not torch.equal(bufs[i][4].view(torch.int16), eager.view(torch.int16)):
+            raise SystemExit("graph replay output differs from the eager call's")
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
     start.record(stream)
-    for i in range(steps):
-        x = bufs[i % sets]
-        dg.dg_gemm_fp8_nt(x[0], x[2], x[1], x[3], out=x[4], gran=g, stream=stream)
+    for _ in range(steps // L):
+        graph.replay()
     end.record(stream)
     torch.cuda.synchronize(dev)
     ms = start.elapsed_time(end) / steps
     finite = bool(torch.isfinite(bufs[(steps - 1) % sets][4].float()).all().item())
-    return ms, sets, finite
+    return ms, sets, finite, L
 
 
 def cpu_leg(c: int, budget_s: float = 10.0):
@@ -204,7 +235,7 @@ def main():
     c = workload_by_name(args.workload)
     w = synth.WORKLOADS[c]
     flops, nbytes = algorithmic(w)
-    ms, sets, finite = gpu_leg(c, args.steps, args.warmup, args.sets)
+    ms, sets, finite, glen = gpu_leg(c, args.steps, args.warmup, args.sets)
     if not finite:
         raise SystemExit("GEMM output holds non-finite values")
     sec = ms * 1e-3
@@ -234,6 +265,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w["name"], "M": w["M"], "N": w["N"], "K": w["K"], "gran": w["g"],
                    "layout": "NT", "out": "bf16", "input_sets": sets,
+                   "launch": "hipGraph of %d launches, replayed %d times" % (glen, args.steps // glen),
                    "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
                    "alg_GBps": round(nbytes / sec / 1e9, 1)},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,

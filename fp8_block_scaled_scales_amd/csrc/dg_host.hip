@@ -10,6 +10,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -22,6 +23,15 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_status[kMaxDevices];  // DG_OK or DG_EUNSUPPORTED, set once per device
+
+// Split-K workspace, allocated once per device on first need and kept until
+// the process ends: FP32 partial tiles plus one arrival counter per tile
+// (zeroed once here; the kernel returns each counter to zero).
+constexpr int64_t kWsFloats = 8ll << 20;  // 32 MB of partial tiles
+constexpr int64_t kWsCounters = 1 << 16;
+std::once_flag g_ws_once[kMaxDevices];
+float* g_ws[kMaxDevices];
+uint32_t* g_counters[kMaxDevices];
 
 thread_local hipError_t t_last_hip = hipSuccess;
 thread_local char t_msg[256];
@@ -52,26 +62,62 @@ int validate(int64_t M, int64_t N, int64_t K, int gran) {
   return DG_OK;
 }
 
-const dg::KernelEntry* select(int64_t M, int64_t N, int64_t K, int gran) {
-  (void)M;
-  (void)N;
-  (void)K;
+const dg::KernelEntry* find(int cls, int gran) {
   for (int i = 0; i < dg::kTableSize; ++i)
-    if (dg::kTable[i].gran == gran) return &dg::kTable[i];
+    if (dg::kTable[i].gran == gran && dg::kTable[i].cls == cls) return &dg::kTable[i];
   return nullptr;
 }
 
+struct Plan {
+  const dg::KernelEntry* e;
+  int ksplit;
+  int64_t tiles;
+};
+
+// Tile-table choice (pure host arithmetic, no HIP call).
+// Small M streams B: few output tiles exist, so the K range of each 64x64 tile
+// is split over several workgroups until about one workgroup per CU (256)
+// runs, keeping at least 4 pipeline steps per split. Everything else takes
+// the large-tile kernel over the whole K.
+Plan plan(int64_t M, int64_t N, int64_t K, int gran) {
+  Plan p{nullptr, 1, 0};
+  const int64_t nsteps = (K + 127) / 128;
+  if (M <= 128) {
+    p.e = find(dg::kClassSplitK, gran);
+    p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
+    int64_t ks = (256 + p.tiles / 2) / p.tiles;
+    ks = std::min<int64_t>(ks, nsteps / 4);
+    while (ks > 1 && (p.tiles * ks * p.e->bm * p.e->bn > kWsFloats || p.tiles > kWsCounters)) --ks;
+    p.ksplit = (int)std::max<int64_t>(ks, 1);
+  } else {
+    p.e = find(dg::kClassTiled, gran);
+    p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
+  }
+  return p;
+}
+
+void alloc_workspace(int dev) {
+  if (hipMalloc(&g_ws[dev], kWsFloats * sizeof(float)) != hipSuccess) {
+    g_ws[dev] = nullptr;
+    return;
+  }
+  if (hipMalloc(&g_counters[dev], kWsCounters * sizeof(uint32_t)) != hipSuccess ||
+      hipMemset(g_counters[dev], 0, kWsCounters * sizeof(uint32_t)) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(g_ws[dev]);
+    g_ws[dev] = nullptr;
+    g_counters[dev] = nullptr;
+  }
+}
+
 // One-time per-device check; returns DG_OK, DG_EUNSUPPORTED or DG_ELAUNCH.
-int device_ready() {
+int device_ready(int* dev_out = nullptr) {
   int dev = 0;
   if ((t_last_hip = hipGetDevice(&dev)) != hipSuccess) return DG_ELAUNCH;
   if (dev < 0 || dev >= kMaxDevices) return DG_EUNSUPPORTED;
   std::call_once(g_dev_once[dev], check_device, dev);
+  if (dev_out) *dev_out = dev;
   return g_dev_status[dev];
-}
-
-int64_t grid_of(const dg::KernelEntry* e, int64_t M, int64_t N) {
-  return ((M + e->bm - 1) / e->bm) * ((N + e->bn - 1) / e->bn);
 }
 
 }  // namespace
@@ -97,16 +143,16 @@ int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info)
   if (!info) return DG_EINVAL;
   const int rc = validate(M, N, K, gran);
   if (rc != DG_OK) return rc;
-  const dg::KernelEntry* e = select(M, N, K, gran);
-  if (!e || grid_of(e, M, N) > 0x7fffffff) return DG_EINVAL;
-  info->kernel_id = e->id;
-  info->bm = e->bm;
-  info->bn = e->bn;
+  const Plan p = plan(M, N, K, gran);
+  if (!p.e || p.tiles * p.ksplit > 0x7fffffff) return DG_EINVAL;
+  info->kernel_id = p.e->id;
+  info->bm = p.e->bm;
+  info->bn = p.e->bn;
   info->bk = 128;
-  info->stages = e->stages;
-  info->waves = e->waves;
-  info->ksplit = e->ksplit;
-  info->grid = grid_of(e, M, N);
+  info->stages = p.e->stages;
+  info->waves = p.e->waves;
+  info->ksplit = p.ksplit;
+  info->grid = p.tiles * p.ksplit;
   return DG_OK;
 }
 
@@ -118,11 +164,17 @@ int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* s
   if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)sa & 3) || ((uintptr_t)sb & 3) ||
       ((uintptr_t)out & 1))
     return DG_EALIGN;
-  const dg::KernelEntry* e = select(M, N, K, gran);
-  if (!e || grid_of(e, M, N) > 0x7fffffff) return DG_EINVAL;
+  Plan pl = plan(M, N, K, gran);
+  if (!pl.e || pl.tiles * pl.ksplit > 0x7fffffff) return DG_EINVAL;
 
-  rc = device_ready();
+  int dev = 0;
+  rc = device_ready(&dev);
   if (rc != DG_OK) return rc;
+  if (pl.ksplit > 1) {
+    std::call_once(g_ws_once[dev], alloc_workspace, dev);
+    if (!g_ws[dev]) pl.ksplit = 1;  // no workspace: the same kernel over the whole K
+  }
+  const dg::KernelEntry* e = pl.e;
 
   dg::GemmArgs p;
   p.a = static_cast<const uint8_t*>(a);
@@ -135,10 +187,15 @@ int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* s
   p.K = K;
   p.gran = gran;
   p.vec_store = (((uintptr_t)out & 15) == 0 && N % 8 == 0) ? 1 : 0;
+  p.ksplit = pl.ksplit;
+  p.ws = pl.ksplit > 1 ? g_ws[dev] : nullptr;
+  p.counters = pl.ksplit > 1 ? g_counters[dev] : nullptr;
   if (log_enabled())
-    std::fprintf(stderr, "dg_gemm_fp8_nt M=%lld N=%lld K=%lld g=%d -> kernel %d (%dx%d, %d stages, %d waves) grid %lld\n",
+    std::fprintf(stderr,
+                 "dg_gemm_fp8_nt M=%lld N=%lld K=%lld g=%d -> kernel %d (%dx%d, %d stages, %d waves) "
+                 "ksplit %d grid %lld\n",
                  (long long)M, (long long)N, (long long)K, gran, e->id, e->bm, e->bn, e->stages, e->waves,
-                 (long long)grid_of(e, M, N));
+                 pl.ksplit, (long long)(pl.tiles * pl.ksplit));
   t_last_hip = e->launch(p, static_cast<hipStream_t>(stream));
   return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
 }

@@ -15,16 +15,23 @@ struct GemmArgs {
   int64_t M, N, K;
   int gran;
   int vec_store;  // out is 16-byte aligned and N % 8 == 0: full-row chunks use 16-byte stores
+  int ksplit;     // workgroups per output tile along K (1 = no split)
+  float* ws;      // split-K partial tiles, tiles * ksplit * bm * bn floats (ksplit > 1)
+  uint32_t* counters;  // split-K arrival counters, one per tile, zero between calls
 };
 
 typedef hipError_t (*Launcher)(const GemmArgs&, hipStream_t);
 
+// Kernel classes of the tile table: large tiles over the whole K, or small
+// tiles whose K range is split over several workgroups (small M).
+enum TileClass { kClassTiled = 0, kClassSplitK = 1 };
+
 struct KernelEntry {
   int id;
+  int cls;
   int bm, bn;
   int stages;
   int waves;
-  int ksplit;
   int gran;
   Launcher launch;
 };

@@ -39,6 +39,7 @@ namespace dg {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -48,21 +49,21 @@ constexpr int BK = 128;  // K bytes per pipeline step (row pitch of a staged sla
 #define DG_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // Raw buffer (stride 0): any 16-byte access at offset >= bytes reads as zero.
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Workgroup id -> (tile row, tile col).
+// Workgroup id -> (split, tile row, tile col).
 // The dispatcher hands workgroup i to XCD i % 8. Renumber so that each XCD
-// owns a contiguous run of the logical order, then walk that order as a
-// grouped raster: GROUP_M tile rows advance together along N.
+// owns a contiguous run of the logical order. The logical order runs over the
+// K splits slowest, then walks the tiles of one split as a grouped raster:
+// GROUP_M tile rows advance together along N, so the tiles resident on one XCD
+// share A row panels and B column panels of the same K range.
 template <int GROUP_M>
-__device__ __forceinline__ void map_tile(int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ void map_tile(int tiles_m, int tiles_n, int& ks, int& tm, int& tn) {
   const int nwg = gridDim.x;
   int pid = blockIdx.x;
   const int xcd = pid & 7, local = pid >> 3, q = nwg >> 3, r = nwg & 7;
   pid = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+  const int tiles = tiles_m * tiles_n;
+  ks = pid / tiles;
+  pid -= ks * tiles;
   const int group = GROUP_M * tiles_n;
   const int gid = pid / group;
   const int first = gid * GROUP_M;
@@ -72,24 +73,46 @@ __device__ __forceinline__ void map_tile(int tiles_m, int tiles_n, int& tm, int&
   tn = in / gsz;
 }
 
+// Buffer descriptor as four SGPRs: base, stride 0 (raw buffer), range in
+// bytes, and the same config word as above.
+__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return (v4i){(int)(uint32_t)p, (int)(uint32_t)(p >> 32) & 0xFFFF, (int)bytes, 0x00020000};
+}
+
+// One 16-byte-per-lane HBM->LDS copy: lane L's 16 bytes land at LDS byte
+// lds_addr + 16*L. Written as inline assembly so that the compiler's wait
+// insertion, which cannot tell the ring slots apart, does not wait for every
+// slot before each LDS read; the kernel waits for these loads itself
+// (wait_steps), in issue order, before the barrier that publishes a slot.
+__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
 // Copy a [ROWS x 128-byte] slab starting at column byte k0 of the rows the
 // descriptor covers into LDS. One instruction per wave moves 8 rows (64 lanes
 // x 16 B, written lane-contiguously from the wave-uniform LDS address). Lane
 // L writes physical chunk L%8 of row L/8, so it fetches logical chunk
 // (L%8) ^ (row%8): the XOR swizzle is applied on the global-address side.
 template <int ROWS, int NWAVES>
-__device__ __forceinline__ void stage_slab(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, uint32_t K,
-                                           uint32_t k0, int wave, int lane) {
+__device__ __forceinline__ void stage_slab(v4i rsrc, uint8_t* lds, uint32_t K, uint32_t k0, int wave, int lane) {
   constexpr int GROUPS = ROWS / 8;
   static_assert(GROUPS % NWAVES == 0, "slab rows must split evenly over the waves");
   const uint32_t r_in = lane >> 3;
   const uint32_t chunk = (uint32_t)(lane & 7) ^ r_in;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
 #pragma unroll
   for (int i = 0; i < GROUPS / NWAVES; ++i) {
     const int grp = i * NWAVES + wave;
     const uint32_t row = grp * 8 + r_in;
     const uint32_t voff = row * K + k0 + chunk * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + grp * 1024), 16, voff, 0, 0, 0);
+    lds_dma16(rsrc, __builtin_amdgcn_readfirstlane(lds_base + grp * 1024), voff);
   }
 }
 
@@ -110,11 +133,31 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);  // v_cvt_pk_bf16_f32: nearest even
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M>
+// Wait until at most `steps` later pipeline steps' loads (LOADS each) are
+// still in flight for this wave; steps is 0 .. MAXS.
+template <int LOADS, int MAXS>
+__device__ __forceinline__ void wait_steps(int steps) {
+  if constexpr (MAXS == 0) {
+    DG_WAIT_VMCNT(0);
+  } else {
+    if (steps >= MAXS) {
+      DG_WAIT_VMCNT(LOADS * MAXS);
+    } else {
+      wait_steps<LOADS, MAXS - 1>(steps);
+    }
+  }
+}
+
+// Split-K: ksplit workgroups share one output tile, each covering a contiguous
+// range of 128-byte K steps. Each writes its FP32 partial tile to ws; the
+// last to arrive (per-tile arrival counter) adds the partials in split order
+// (so the result does not depend on which arrives last), resets the counter
+// and writes the BF16 tile. ksplit == 1 skips all of this.
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ b, const float* __restrict__ sa,
     const float* __restrict__ sb, uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
-    int tiles_n, int vec_store) {
+    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, uint32_t* __restrict__ counters) {
   constexpr int NWAVES = WM * WN;
   constexpr int NT = 64 * NWAVES;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
@@ -127,7 +170,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 sub-tiles");
   static_assert(G % 32 == 0 && BK % G == 0, "granularity must cover whole sub-tiles and steps");
   static_assert(BM * LDC * 2 <= STAGES * STAGE_BYTES, "epilogue tile must fit in the ring");
-  static_assert(LOADS < 64, "vmcnt range");
+  static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
@@ -135,15 +178,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  int tmi, tni;
-  map_tile<GROUP_M>(tiles_m, tiles_n, tmi, tni);
+  int ks, tmi, tni;
+  map_tile<GROUP_M>(tiles_m, tiles_n, ks, tmi, tni);
   const int m0 = tmi * BM, n0 = tni * BN;
   const uint32_t uK = (uint32_t)K;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * uK);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
+  const v4i ra = rsrc_words(a + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * uK);
+  const v4i rb = rsrc_words(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
 
-  const int nkb = K / G;                 // K segments
-  const int nsteps = (K + BK - 1) / BK;  // pipeline steps
+  const int nkb = K / G;                       // K segments
+  const int nsteps_all = (K + BK - 1) / BK;    // pipeline steps over the whole K
+  const int st0 = (int)((int64_t)ks * nsteps_all / ksplit);
+  const int nsteps = (int)((int64_t)(ks + 1) * nsteps_all / ksplit) - st0;  // this split's steps
 
   // Scale rows of this wave's sub-tiles. A sub-tile lies inside one g-block
   // (g >= 32, sub-tiles aligned to 32); sub-tiles past the edge clamp to the
@@ -166,8 +211,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
   for (int s = 0; s < STAGES - 1; ++s) {
     if (s < nsteps) {
       uint8_t* slot = smem + s * STAGE_BYTES;
-      stage_slab<BM, NWAVES>(ra, slot, uK, s * BK, wave, lane);
-      stage_slab<BN, NWAVES>(rb, slot + A_BYTES, uK, s * BK, wave, lane);
+      stage_slab<BM, NWAVES>(ra, slot, uK, (st0 + s) * BK, wave, lane);
+      stage_slab<BN, NWAVES>(rb, slot + A_BYTES, uK, (st0 + s) * BK, wave, lane);
     }
   }
 
@@ -177,25 +222,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
 
   for (int s = 0; s < nsteps; ++s) {
     // Step s landed once only the later steps' loads are outstanding.
-    if (STAGES == 3 && s + 1 < nsteps) {
-      DG_WAIT_VMCNT(LOADS);
-    } else {
-      DG_WAIT_VMCNT(0);
-    }
+    wait_steps<LOADS, STAGES - 2>(min(STAGES - 2, nsteps - 1 - s));
     __syncthreads();  // step s visible to all waves; slot (s-1)%STAGES free
 
     if (s + STAGES - 1 < nsteps) {
       const int sn = s + STAGES - 1;
       uint8_t* slot = smem + (sn % STAGES) * STAGE_BYTES;
-      stage_slab<BM, NWAVES>(ra, slot, uK, sn * BK, wave, lane);
-      stage_slab<BN, NWAVES>(rb, slot + A_BYTES, uK, sn * BK, wave, lane);
+      stage_slab<BM, NWAVES>(ra, slot, uK, (st0 + sn) * BK, wave, lane);
+      stage_slab<BN, NWAVES>(rb, slot + A_BYTES, uK, (st0 + sn) * BK, wave, lane);
     }
 
     const uint8_t* As = smem + (s % STAGES) * STAGE_BYTES;
     const uint8_t* Bs = As + A_BYTES;
 #pragma unroll
     for (int seg = 0; seg < SEGS; ++seg) {
-      const int kb = s * SEGS + seg;
+      const int kb = (st0 + s) * SEGS + seg;
       if (kb >= nkb) break;  // K % 128 == 64 with g = 64: the last step holds one segment
       v8i af[TM][KSTEPS], bfr[TN][KSTEPS];
 #pragma unroll
@@ -225,6 +266,87 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     }
   }
 
+  if (SPLIT && ksplit > 1) {
+    // Partial tile layout: [wave][i][j][v][lane] floats, so each store and
+    // load below moves 256 contiguous bytes per wave.
+    //
+    // Publication without cache-wide write-back or invalidate: the partials
+    // are written and read with device-scope atomic stores and loads, which
+    // go to the point of coherence shared by all XCDs (the per-XCD L2s are
+    // not coherent with each other). The stores are waited for before the
+    // workgroup arrives at the tile's counter, and the last arrival's loads
+    // are issued only after its arrival returned, so it reads every split's
+    // finished partial.
+    const int tile = tmi * tiles_n + tni;
+    float* const base = ws + (int64_t)tile * ksplit * (BM * BN);
+    float* const mine = base + (int64_t)ks * (BM * BN) + wave * (TM * TN * 16 * 64);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          __hip_atomic_store(mine + ((i * TN + j) * 16 + v) * 64 + lane, acc[i][j][v], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores have completed
+    __syncthreads();
+    __shared__ int last;
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(ksplit - 1);
+    __syncthreads();
+    if (!last) return;
+    // Sum in split order 0, 1, ..., ksplit-1 (this split's own partial from
+    // registers): the same additions whichever split arrived last. The
+    // other splits' partials are fetched four splits at a time, all loads of
+    // a batch in flight together, so the fetch costs one memory round trip
+    // per four splits.
+    float tot[TM][TN][16];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tot[i][j][v] = 0.0f;
+    const float* const part0 = base + wave * (TM * TN * 16 * 64) + lane;
+    for (int sp0 = 0; sp0 < ksplit; sp0 += 4) {
+      float got[4][TM][TN][16];
+#pragma unroll
+      for (int bsp = 0; bsp < 4; ++bsp) {
+        // splits past the end and this split's own slot read slot 0 (never
+        // summed or replaced below), keeping every address in the workspace
+        const int sp = sp0 + bsp;
+        const float* const part = part0 + (int64_t)((sp < ksplit && sp != ks) ? sp : 0) * (BM * BN);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              got[bsp][i][j][v] = __hip_atomic_load(part + ((i * TN + j) * 16 + v) * 64, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int bsp = 0; bsp < 4; ++bsp) {
+        const int sp = sp0 + bsp;
+        if (sp < ksplit) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) tot[i][j][v] += sp == ks ? acc[i][j][v] : got[bsp][i][j][v];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = tot[i][j][v];
+  }
+
   // Epilogue: BF16 tile through LDS, then 16-byte row-contiguous stores.
   __syncthreads();
   uint16_t* cs = reinterpret_cast<uint16_t*>(smem);
@@ -250,27 +372,34 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     if (vec_store && gc + 8 <= N) {
       *reinterpret_cast<v4i*>(dst) = val;
     } else {
-      const uint16_t* e = reinterpret_cast<const uint16_t*>(&val);
-      for (int t = 0; t < 8 && gc + t < N; ++t) dst[t] = e[t];
+      for (int t = 0; t < 8 && gc + t < N; ++t) dst[t] = (uint16_t)((uint32_t)val[t >> 1] >> (16 * (t & 1)));
     }
   }
+  // The reducer returns the tile's arrival counter to zero for the next call.
+  // It is issued last: a device-coherent store ahead of the output stores
+  // holds them up.
+  if (SPLIT && ksplit > 1 && threadIdx.x == 0)
+    __hip_atomic_store(&counters[tmi * tiles_n + tni], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- launch table -------------------------------------------------------------
 
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M>
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT>
 static hipError_t launch_tiled(const GemmArgs& p, hipStream_t stream) {
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M>), dim3(tiles_m * tiles_n),
+  if (!SPLIT && p.ksplit != 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT>), dim3(tiles_m * tiles_n * p.ksplit),
                      dim3(64 * WM * WN), 0, stream, p.a, p.b, p.sa, p.sb, p.out, (int)p.M, (int)p.N,
-                     (int)p.K, tiles_m, tiles_n, p.vec_store);
+                     (int)p.K, tiles_m, tiles_n, p.vec_store, p.ksplit, p.ws, p.counters);
   return hipGetLastError();
 }
 
 KernelEntry kTable[] = {
-    // id, bm, bn, stages, waves, ksplit, gran, launcher
-    {0, 128, 128, 2, 4, 1, 128, &launch_tiled<128, 128, 2, 2, 2, 128, 4>},
-    {1, 128, 128, 2, 4, 1, 64, &launch_tiled<128, 128, 2, 2, 2, 64, 4>},
+    // id, class, bm, bn, stages, waves, gran, launcher
+    {0, kClassTiled, 128, 128, 2, 4, 128, &launch_tiled<128, 128, 2, 2, 2, 128, 4, false>},
+    {1, kClassTiled, 128, 128, 2, 4, 64, &launch_tiled<128, 128, 2, 2, 2, 64, 4, false>},
+    {2, kClassSplitK, 64, 64, 8, 4, 128, &launch_tiled<64, 64, 2, 2, 8, 128, 4, true>},
+    {3, kClassSplitK, 64, 64, 8, 4, 64, &launch_tiled<64, 64, 2, 2, 8, 64, 4, true>},
 };
 const int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 

@@ -141,7 +141,8 @@ def test_determinism_repeated_calls():
         assert torch.equal(again.view(torch.int16), first.view(torch.int16))
 
 
-@pytest.mark.parametrize("M,N,K,g", [(65, 130, 256, 64), (1023, 1025, 128, 128), (200, 4000, 512, 64)])
+@pytest.mark.parametrize("M,N,K,g", [(65, 130, 256, 64), (1023, 1025, 128, 128), (200, 4000, 512, 64),
+                                     (100, 520, 2048, 128)])
 def test_canary_bands_untouched(M, N, K, g):
     import torch
 
@@ -183,3 +184,69 @@ def test_non_default_stream_and_unaligned_out():
     s.synchronize()
     ref = oracle.gemm_ref(a8, b8, sa, sb, g)
     _assert_parity(out.float().cpu().numpy().astype(np.float64), ref, "side stream")
+
+
+# Small M takes the split-K class: several workgroups per 64x64 tile, each
+# over a range of K steps, partials added in split order by the last to
+# arrive. Shapes chosen so the split count is > 1 (see dg_query_tile).
+SPLITK = [
+    (1, 4096, 7168, 128), (64, 1000, 4096, 64), (100, 520, 2048, 128), (33, 700, 64 * 37, 64),
+    (128, 512, 8192, 128), (7, 64, 16384, 64), (96, 4100, 1024, 128),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g", SPLITK)
+def test_splitk_parity(M, N, K, g):
+    import fp8_block_scaled_scales_amd as dg
+
+    tile = dg.dg_query_tile(M, N, K, g)
+    assert tile["ksplit"] > 1, tile
+    x = synth.normal(5000 + M, (M, K))
+    y = synth.normal(6000 + N, (N, K), sigma=0.02)
+    a8, sa = oracle.quantize_blocks(x, g)
+    b8, sb = oracle.quantize_blocks(y, g)
+    say("split-K M=%d N=%d K=%d g=%d ksplit=%d" % (M, N, K, g, tile["ksplit"]))
+    got, bits = gemm(a8, sa, b8, sb, g)
+    ref = oracle.gemm_ref(a8, b8, sa, sb, g)
+    _assert_parity(got, ref, "split-K %dx%dx%d g=%d" % (M, N, K, g))
+    # a second call must see the arrival counters back at zero
+    got2, bits2 = gemm(a8, sa, b8, sb, g)
+    assert np.array_equal(bits, bits2)
+
+
+def test_splitk_all_ones_bitwise():
+    M, N, K, g = 64, 384, 4096, 128
+    a8 = np.full((M, K), 0x38, np.uint8)
+    b8 = np.full((N, K), 0x38, np.uint8)
+    sa = _pow2_scales(-(-M // g), K // g, lambda mb, kb: (mb - kb) % 7 - 3)
+    sb = _pow2_scales(-(-N // g), K // g, lambda nb, kb: (2 * nb + kb) % 3)
+    say("split-K all-ones")
+    got, bits = gemm(a8, sa, b8, sb, g)
+    ref = oracle.gemm_ref(a8, b8, sa, sb, g)
+    assert np.array_equal(bits, _common.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+def test_splitk_determinism_and_interleaving():
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+    from tests._gpu import device_inputs
+
+    # decode workload, repeated, interleaved with a different split-K shape
+    w, a8, sa, b8, sb = workload(2)
+    ta, tsa, tb, tsb = device_inputs(a8, sa, b8, sb)
+    x = synth.normal(77, (8, 2048))
+    y = synth.normal(78, (300, 2048), sigma=0.02)
+    c8, sc = oracle.quantize_blocks(x, 128)
+    d8, sd = oracle.quantize_blocks(y, 128)
+    tc, tsc, td, tsd = device_inputs(c8, sc, d8, sd)
+    say("split-K determinism x20 on workload 2, interleaved")
+    first = dg.dg_gemm_fp8_nt(ta, tb, tsa, tsb, gran=128).clone()
+    other = dg.dg_gemm_fp8_nt(tc, td, tsc, tsd, gran=128).clone()
+    for _ in range(19):
+        again = dg.dg_gemm_fp8_nt(ta, tb, tsa, tsb, gran=128)
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+        o2 = dg.dg_gemm_fp8_nt(tc, td, tsc, tsd, gran=128)
+        assert torch.equal(o2.view(torch.int16), other.view(torch.int16))
+    ref = oracle.gemm_ref(c8, d8, sc, sd, 128)
+    _assert_parity(other.float().cpu().numpy().astype(np.float64), ref, "interleaved small case")
