@@ -77,8 +77,9 @@ struct Plan {
 // Tile-table choice (pure host arithmetic, no HIP call).
 // Small M streams B: few output tiles exist, so the K range of each 64x64 tile
 // is split over several workgroups until about one workgroup per CU (256)
-// runs, keeping at least 4 pipeline steps per split. Everything else takes
-// the large-tile kernel over the whole K.
+// runs, keeping at least 4 pipeline steps per split. Large M and N take
+// 256x256 tiles when they give at least 3/4 of a tile per CU; the rest takes
+// 128x128 tiles over the whole K.
 Plan plan(int64_t M, int64_t N, int64_t K, int gran) {
   Plan p{nullptr, 1, 0};
   const int64_t nsteps = (K + 127) / 128;
@@ -89,10 +90,12 @@ Plan plan(int64_t M, int64_t N, int64_t K, int gran) {
     ks = std::min<int64_t>(ks, nsteps / 4);
     while (ks > 1 && (p.tiles * ks * p.e->bm * p.e->bn > kWsFloats || p.tiles > kWsCounters)) --ks;
     p.ksplit = (int)std::max<int64_t>(ks, 1);
-  } else {
-    p.e = find(dg::kClassTiled, gran);
-    p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
+    return p;
   }
+  const dg::KernelEntry* big = find(dg::kClassBig, gran);
+  const int64_t big_tiles = ((M + big->bm - 1) / big->bm) * ((N + big->bn - 1) / big->bn);
+  p.e = big_tiles >= 192 ? big : find(dg::kClassTiled, gran);
+  p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
   return p;
 }
 

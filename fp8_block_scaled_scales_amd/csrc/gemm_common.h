@@ -1,0 +1,94 @@
+// Device helpers shared by the gfx950 GEMM kernels: vector types, the
+// explicit memory-counter wait, the XCD-aware tile order, raw buffer
+// descriptors and the HBM->LDS copy of a staged slab.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// vmcnt(n) with expcnt and lgkmcnt left at their maxima (gfx9 encoding).
+#define DG_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
+
+// Workgroup id -> (split, tile row, tile col).
+// The dispatcher hands workgroup i to XCD i % 8. Renumber so that each XCD
+// owns a contiguous run of the logical order. The logical order runs over the
+// K splits slowest, then walks the tiles of one split as a grouped raster:
+// GROUP_M tile rows advance together along N, so the tiles resident on one XCD
+// share A row panels and B column panels of the same K range.
+template <int GROUP_M>
+__device__ __forceinline__ void map_tile(int tiles_m, int tiles_n, int& ks, int& tm, int& tn) {
+  const int nwg = gridDim.x;
+  int pid = blockIdx.x;
+  const int xcd = pid & 7, local = pid >> 3, q = nwg >> 3, r = nwg & 7;
+  pid = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+  const int tiles = tiles_m * tiles_n;
+  ks = pid / tiles;
+  pid -= ks * tiles;
+  const int group = GROUP_M * tiles_n;
+  const int gid = pid / group;
+  const int first = gid * GROUP_M;
+  const int gsz = min(tiles_m - first, GROUP_M);
+  const int in = pid - gid * group;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+// Buffer descriptor as four SGPRs: base, stride 0 (raw buffer), range in
+// bytes, and the same config word as above.
+__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return (v4i){(int)(uint32_t)p, (int)(uint32_t)(p >> 32) & 0xFFFF, (int)bytes, 0x00020000};
+}
+
+// One 16-byte-per-lane HBM->LDS copy: lane L's 16 bytes land at LDS byte
+// lds_addr + 16*L. Written as inline assembly so that the compiler's wait
+// insertion, which cannot tell the ring slots apart, does not wait for every
+// slot before each LDS read; the kernel waits for these loads itself
+// (wait_steps), in issue order, before the barrier that publishes a slot.
+__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// Copy a [ROWS x 128-byte] slab starting at column byte k0 of the rows the
+// descriptor covers into LDS. One instruction per wave moves 8 rows (64 lanes
+// x 16 B, written lane-contiguously from the wave-uniform LDS address). Lane
+// L writes physical chunk L%8 of row L/8, so it fetches logical chunk
+// (L%8) ^ ((row >> SW) % 8): the XOR swizzle is applied on the global-address
+// side. SW = 0 makes 8 consecutive rows conflict free, SW = 1 makes 16
+// consecutive rows (two rows fill the 64 four-byte banks) conflict free.
+template <int ROWS, int NWAVES, int SW = 0>
+__device__ __forceinline__ void stage_slab(v4i rsrc, uint8_t* lds, uint32_t K, uint32_t k0, int wave, int lane) {
+  constexpr int GROUPS = ROWS / 8;
+  static_assert(GROUPS % NWAVES == 0, "slab rows must split evenly over the waves");
+  const uint32_t r_in = lane >> 3;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+#pragma unroll
+  for (int i = 0; i < GROUPS / NWAVES; ++i) {
+    const int grp = i * NWAVES + wave;
+    const uint32_t row = grp * 8 + r_in;
+    const uint32_t chunk = (uint32_t)(lane & 7) ^ ((row >> SW) & 7);
+    const uint32_t voff = row * K + k0 + chunk * 16;
+    lds_dma16(rsrc, __builtin_amdgcn_readfirstlane(lds_base + grp * 1024), voff);
+  }
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);  // v_cvt_pk_bf16_f32: nearest even
+}
+
+}  // namespace dg

@@ -22,9 +22,10 @@ struct GemmArgs {
 
 typedef hipError_t (*Launcher)(const GemmArgs&, hipStream_t);
 
-// Kernel classes of the tile table: large tiles over the whole K, or small
-// tiles whose K range is split over several workgroups (small M).
-enum TileClass { kClassTiled = 0, kClassSplitK = 1 };
+// Kernel classes of the tile table: 128x128 tiles over the whole K, small
+// tiles whose K range is split over several workgroups (small M), and
+// 256x256 tiles over the whole K (large M and N).
+enum TileClass { kClassTiled = 0, kClassSplitK = 1, kClassBig = 2 };
 
 struct KernelEntry {
   int id;
@@ -35,6 +36,9 @@ struct KernelEntry {
   int gran;
   Launcher launch;
 };
+
+hipError_t launch_big_g128(const GemmArgs& p, hipStream_t stream);
+hipError_t launch_big_g64(const GemmArgs& p, hipStream_t stream);
 
 extern KernelEntry kTable[];
 extern const int kTableSize;
