@@ -59,14 +59,16 @@ DEFAULT_WORKLOAD = 2      # small-M decode shape, M=64 N=4096 K=7168, g=128
 # WRITE_SIZE (each scaled by the copy-kernel calibration factor), keyed by
 # workload and tagged with the hash of the kernel source the counters were
 # taken on. A different hash means the kernel changed since: traffic is null.
-TRAFFIC = {}
+TRAFFIC = {
+    "decode_m64_n4096_k7168": {"src": "75673187149077a6", "bytes": 38370594},
+}
 
 
 def _kernel_source_hash() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in ("gemm_fp8_nt.hip", "gemm_fp8_nt.h", "dg_host.hip"):
+    for name in ("gemm_fp8_nt.hip", "gemm_fp8_nt.h", "gemm_common.h", "gemm_fp8_nt_big.hip", "dg_host.hip"):
         with open(os.path.join(ROOT, "fp8_block_scaled_scales_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -223,7 +225,23 @@ def main():
                     help="workload number or name (default: the small-M decode shape)")
     ap.add_argument("--sets", type=int, default=None, help="input sets rotated over (default: defeat the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes three times (calibrates the HBM "
+                         "byte counters of a profiler run) and exit")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+
+        n = args.copy_probe << 20
+        x = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "repeats": 3}), flush=True)
+        return
 
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU only: the GEMM runs whole on a single MI355X and "

@@ -54,37 +54,50 @@ __device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
 // insertion, which cannot tell the ring slots apart, does not wait for every
 // slot before each LDS read; the kernel waits for these loads itself
 // (wait_steps), in issue order, before the barrier that publishes a slot.
-__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds_addr, uint32_t voff) {
+// The buffer offset is voff (per lane) + soff (wave-uniform).
+__device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff = 0) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
       :
-      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
       : "memory", "m0");
 }
 
-// Copy a [ROWS x 128-byte] slab starting at column byte k0 of the rows the
-// descriptor covers into LDS. One instruction per wave moves 8 rows (64 lanes
-// x 16 B, written lane-contiguously from the wave-uniform LDS address). Lane
-// L writes physical chunk L%8 of row L/8, so it fetches logical chunk
-// (L%8) ^ ((row >> SW) % 8): the XOR swizzle is applied on the global-address
-// side. SW = 0 makes 8 consecutive rows conflict free, SW = 1 makes 16
-// consecutive rows (two rows fill the 64 four-byte banks) conflict free.
+// One instruction of a slab copy: rows 8*grp .. 8*grp+7 of a [rows x 128-byte]
+// slab starting at column byte k0 of the rows the descriptor covers, into
+// LDS at lds + 1024*grp (64 lanes x 16 B, written lane-contiguously from the
+// wave-uniform LDS address). Lane L writes physical chunk L%8 of row L/8, so
+// it fetches logical chunk (L%8) ^ ((row >> SW) % 8): the XOR swizzle is
+// applied on the global-address side. SW = 0 makes 8 consecutive rows
+// conflict free, SW = 1 makes 16 consecutive rows conflict free.
+// The wave-uniform part of the offset (row group and K position) goes in the
+// instruction's scalar offset, so a wave's copies share one or two per-lane
+// offset registers.
+//
+// valid = false turns the copy into one that moves no data: the scalar offset
+// is put past any descriptor range (offsets at or past the range read zero).
+template <int SW>
+__device__ __forceinline__ void stage_group(v4i rsrc, uint8_t* lds, uint32_t K, uint32_t k0, int grp, int lane,
+                                            bool valid = true) {
+  static_assert(SW == 0 || SW == 1, "swizzle");
+  const uint32_t r_in = (uint32_t)lane >> 3;
+  // (row >> SW) & 7 with row = 8*grp + r_in
+  const uint32_t key = SW == 0 ? r_in : ((((uint32_t)grp & 1) << 2) + (r_in >> 1)) & 7;
+  const uint32_t chunk = ((uint32_t)lane & 7) ^ key;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  lds_dma16(rsrc, __builtin_amdgcn_readfirstlane(lds_base + grp * 1024), r_in * K + chunk * 16,
+            __builtin_amdgcn_readfirstlane(valid ? (uint32_t)grp * 8 * K + k0 : 0x80000000u));
+}
+
+// The whole slab of ROWS rows, split evenly over the workgroup's waves.
 template <int ROWS, int NWAVES, int SW = 0>
 __device__ __forceinline__ void stage_slab(v4i rsrc, uint8_t* lds, uint32_t K, uint32_t k0, int wave, int lane) {
   constexpr int GROUPS = ROWS / 8;
   static_assert(GROUPS % NWAVES == 0, "slab rows must split evenly over the waves");
-  const uint32_t r_in = lane >> 3;
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
 #pragma unroll
-  for (int i = 0; i < GROUPS / NWAVES; ++i) {
-    const int grp = i * NWAVES + wave;
-    const uint32_t row = grp * 8 + r_in;
-    const uint32_t chunk = (uint32_t)(lane & 7) ^ ((row >> SW) & 7);
-    const uint32_t voff = row * K + k0 + chunk * 16;
-    lds_dma16(rsrc, __builtin_amdgcn_readfirstlane(lds_base + grp * 1024), voff);
-  }
+  for (int i = 0; i < GROUPS / NWAVES; ++i) stage_group<SW>(rsrc, lds, K, k0, i * NWAVES + wave, lane);
 }
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
