@@ -68,7 +68,7 @@ def _kernel_source_hash() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in ("gemm_fp8_nt.hip", "gemm_fp8_nt.h", "gemm_common.h", "gemm_fp8_nt_big.hip", "dg_host.hip"):
+    for name in ("gemm_fp8_nt.hip", "gemm_fp8_nt.h", "gemm_common.h", "gemm_fp8_nt_big.hip", "gemm_fp8_nt_stream.hip", "dg_host.hip"):
         with open(os.path.join(ROOT, "fp8_block_scaled_scales_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

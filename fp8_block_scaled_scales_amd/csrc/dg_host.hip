@@ -75,21 +75,54 @@ struct Plan {
 };
 
 // Tile-table choice (pure host arithmetic, no HIP call).
-// Small M streams B: few output tiles exist, so the K range of each 64x64 tile
-// is split over several workgroups until about one workgroup per CU (256)
-// runs, keeping at least 4 pipeline steps per split. Large M and N take
+// Small M streams B. When 32x32 tiles give at least 3/4 of a workgroup per CU,
+// each takes the whole K and its waves split K inside the workgroup. With
+// fewer tiles, the K range of each 64x64 tile is split over several
+// workgroups until about one workgroup per CU (256) runs, keeping at least 4
+// pipeline steps per split. Large M and N take
 // 256x256 tiles when they give at least 3/4 of a tile per CU; the rest takes
 // 128x128 tiles over the whole K.
+// DG_FORCE_TILE=<kernel id> overrides the choice when that entry has the
+// call's granularity (tuning and benchmarking only).
+int forced_tile() {
+  static const int id = [] {
+    const char* e = std::getenv("DG_FORCE_TILE");
+    return e ? std::atoi(e) : -1;
+  }();
+  return id;
+}
+
+int64_t splits_for(const dg::KernelEntry* e, int64_t tiles, int64_t nsteps) {
+  int64_t ks = (256 + tiles / 2) / tiles;
+  ks = std::min<int64_t>(ks, nsteps / 4);
+  while (ks > 1 && (tiles * ks * e->bm * e->bn > kWsFloats || tiles > kWsCounters)) --ks;
+  return std::max<int64_t>(ks, 1);
+}
+
 Plan plan(int64_t M, int64_t N, int64_t K, int gran) {
   Plan p{nullptr, 1, 0};
   const int64_t nsteps = (K + 127) / 128;
+  const int force = forced_tile();
+  if (force >= 0) {
+    for (int i = 0; i < dg::kTableSize; ++i)
+      if (dg::kTable[i].id == force && dg::kTable[i].gran == gran) p.e = &dg::kTable[i];
+    if (p.e) {
+      p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
+      if (p.e->cls == dg::kClassSplitK) p.ksplit = (int)splits_for(p.e, p.tiles, nsteps);
+      return p;
+    }
+  }
   if (M <= 128) {
+    const dg::KernelEntry* st = find(dg::kClassStream, gran);
+    const int64_t st_tiles = ((M + st->bm - 1) / st->bm) * ((N + st->bn - 1) / st->bn);
+    if (st_tiles >= 192) {
+      p.e = st;
+      p.tiles = st_tiles;
+      return p;
+    }
     p.e = find(dg::kClassSplitK, gran);
     p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
-    int64_t ks = (256 + p.tiles / 2) / p.tiles;
-    ks = std::min<int64_t>(ks, nsteps / 4);
-    while (ks > 1 && (p.tiles * ks * p.e->bm * p.e->bn > kWsFloats || p.tiles > kWsCounters)) --ks;
-    p.ksplit = (int)std::max<int64_t>(ks, 1);
+    p.ksplit = (int)splits_for(p.e, p.tiles, nsteps);
     return p;
   }
   const dg::KernelEntry* big = find(dg::kClassBig, gran);

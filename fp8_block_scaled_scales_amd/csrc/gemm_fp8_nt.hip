@@ -187,27 +187,34 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
   }
 
   if (SPLIT && ksplit > 1) {
-    // Partial tile layout: [wave][i][j][v][lane] floats, so each store and
-    // load below moves 256 contiguous bytes per wave.
+    // Partial tile layout: [split][wave][i][j][quarter][lane] of float4 within
+    // the tile's slice of ws, so each store and load below moves 1 KB
+    // contiguous per wave.
     //
     // Publication without cache-wide write-back or invalidate: the partials
-    // are written and read with device-scope atomic stores and loads, which
-    // go to the point of coherence shared by all XCDs (the per-XCD L2s are
-    // not coherent with each other). The stores are waited for before the
-    // workgroup arrives at the tile's counter, and the last arrival's loads
-    // are issued only after its arrival returned, so it reads every split's
-    // finished partial.
+    // are written and read with device-scope (sc1) buffer stores and loads,
+    // which go to the point of coherence shared by all XCDs (the per-XCD L2s
+    // are not coherent with each other). The stores are waited for before
+    // the workgroup arrives at the tile's counter, and the last arrival's
+    // loads are issued only after its arrival returned, so it reads every
+    // split's finished partial.
+    constexpr int CPOL_SC1 = 16;  // device-scope coherence bit of the buffer instructions
+    constexpr int TILE_F = BM * BN, WAVE_F = TM * TN * 16 * 64;
     const int tile = tmi * tiles_n + tni;
-    float* const base = ws + (int64_t)tile * ksplit * (BM * BN);
-    float* const mine = base + (int64_t)ks * (BM * BN) + wave * (TM * TN * 16 * 64);
+    const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
+        ws + (int64_t)tile * ksplit * TILE_F, (short)0, ksplit * TILE_F * 4, 0x00020000);
+    const uint32_t lane_off = (uint32_t)(wave * WAVE_F + lane * 4) * 4;  // bytes
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          __hip_atomic_store(mine + ((i * TN + j) * 16 + v) * 64 + lane, acc[i][j][v], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        for (int c = 0; c < 4; ++c) {
+          const v4f v = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rws,
+                                                 lane_off + (uint32_t)(((i * TN + j) * 4 + c) * 256 * 4),
+                                                 (uint32_t)ks * TILE_F * 4, CPOL_SC1);
+        }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores have completed
     __syncthreads();
     __shared__ int last;
@@ -217,34 +224,33 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     __syncthreads();
     if (!last) return;
     // Sum in split order 0, 1, ..., ksplit-1 (this split's own partial from
-    // registers): the same additions whichever split arrived last. The
-    // other splits' partials are fetched four splits at a time, all loads of
-    // a batch in flight together, so the fetch costs one memory round trip
-    // per four splits.
-    float tot[TM][TN][16];
+    // registers): the same additions whichever split arrived last. The other
+    // splits' partials are fetched four splits at a time, all loads of a
+    // batch in flight together.
+    v4f tot[TM][TN][4];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) tot[i][j][v] = 0.0f;
-    const float* const part0 = base + wave * (TM * TN * 16 * 64) + lane;
+        for (int c = 0; c < 4; ++c) tot[i][j][c] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
     for (int sp0 = 0; sp0 < ksplit; sp0 += 4) {
-      float got[4][TM][TN][16];
+      v4f got[4][TM][TN][4];
 #pragma unroll
       for (int bsp = 0; bsp < 4; ++bsp) {
-        // splits past the end and this split's own slot read slot 0 (never
-        // summed or replaced below), keeping every address in the workspace
+        // splits past the end and this split's own slot read nothing (an
+        // offset past the range reads zero) and are not added
         const int sp = sp0 + bsp;
-        const float* const part = part0 + (int64_t)((sp < ksplit && sp != ks) ? sp : 0) * (BM * BN);
+        const uint32_t soff = (sp < ksplit && sp != ks) ? (uint32_t)sp * TILE_F * 4 : 0x80000000u;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-              got[bsp][i][j][v] = __hip_atomic_load(part + ((i * TN + j) * 16 + v) * 64, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
+            for (int c = 0; c < 4; ++c)
+              got[bsp][i][j][c] = __builtin_bit_cast(
+                  v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                           rws, lane_off + (uint32_t)(((i * TN + j) * 4 + c) * 256 * 4), soff, CPOL_SC1));
       }
 #pragma unroll
       for (int bsp = 0; bsp < 4; ++bsp) {
@@ -255,7 +261,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-              for (int v = 0; v < 16; ++v) tot[i][j][v] += sp == ks ? acc[i][j][v] : got[bsp][i][j][v];
+              for (int c = 0; c < 4; ++c)
+                tot[i][j][c] += sp == ks ? (v4f){acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
+                                                 acc[i][j][4 * c + 3]}
+                                         : got[bsp][i][j][c];
         }
       }
     }
@@ -264,7 +273,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = tot[i][j][v];
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * c + e] = tot[i][j][c][e];
   }
 
   // Epilogue: BF16 tile through LDS, then 16-byte row-contiguous stores.
@@ -322,6 +333,8 @@ KernelEntry kTable[] = {
     {3, kClassSplitK, 64, 64, 8, 4, 64, &launch_tiled<64, 64, 2, 2, 8, 64, 4, true>},
     {4, kClassBig, 256, 256, 2, 8, 128, &launch_big_g128},
     {5, kClassBig, 256, 256, 2, 8, 64, &launch_big_g64},
+    {6, kClassStream, 32, 32, 4, 4, 128, &launch_stream_g128},
+    {7, kClassStream, 32, 32, 4, 4, 64, &launch_stream_g64},
 };
 const int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 

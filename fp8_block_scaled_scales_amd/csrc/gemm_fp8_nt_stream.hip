@@ -1,0 +1,183 @@
+// Small-M block-scaled FP8 GEMM for gfx950 that streams B once, without a
+// reduction across workgroups.
+//
+// Same operation as the other kernels (DeepGEMM实战 §2.2: FP32 scale per g x g
+// block, restored during accumulation; §3.2: FP32 accumulation per K segment,
+// the segments then added; §3.3/§4.2: NT layout, A [M,K], B [N,K], BF16 out).
+//
+// With M this small the GEMM is a stream of B from HBM, and the way to reach
+// HBM speed is to spread B over every CU with many bytes in flight
+// (DeepGEMM实战 §5.3 names too little parallelism as the problem of small
+// shapes). One workgroup owns a 32 x 32 output tile over the whole K (M = 64,
+// N = 4096 gives 256 workgroups). Its four waves split the K steps (wave w
+// takes steps w, w+4, ...), each with a private ring of four LDS slots fed by
+// HBM->LDS copies: a wave waits only for its own copies, so the main loop has
+// no barrier (A, which stays in L2, and B, which streams from HBM, have
+// rings of different depths). Each wave accumulates the whole 32 x 32 tile over its steps
+// (one 32x32x64 MFMA per 64-wide K segment, promoted by sa*sb into an FP32
+// accumulator); at the end the four partial tiles are added through LDS in
+// wave order, so results do not depend on timing, and written as BF16.
+//
+// Per CU this reads 32 rows of A and 32 rows of B over the whole K (458 KB for
+// K = 7168); A comes from L2 after its first touch, so HBM sees B once.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.h"
+#include "gemm_fp8_nt.h"
+
+namespace dg {
+
+namespace stream {
+
+constexpr int BM = 32, BN = 32, BK = 128;
+constexpr int NW = 4;
+// Per wave: A slabs (L2 hits after their first touch) are copied two steps
+// ahead into a 3-slot ring, B slabs (streamed from HBM, whose loaded latency
+// is several microseconds) six steps ahead into a 7-slot ring. 40 KB per
+// wave, the whole 160 KB LDS for four waves.
+constexpr int A_SLOTS = 3, B_SLOTS = 7, A_AHEAD = A_SLOTS - 1, B_AHEAD = B_SLOTS - 1;
+constexpr int A_SLAB = BM * BK, B_SLAB = BN * BK;  // 4 KB each per step
+constexpr int WAVE_LDS = A_SLOTS * A_SLAB + B_SLOTS * B_SLAB;
+constexpr int A_LOADS = BM / 8, B_LOADS = BN / 8;  // copy instructions per step and operand (one wave)
+// Issue order per iteration t: A(t + A_AHEAD), then B(t + B_AHEAD). Waiting for
+// A(t) (the later-issued of A(t), B(t)) leaves in flight what followed it:
+// B(t + B_AHEAD - 1), then A(t + A_AHEAD) .. the copies of A_AHEAD - 1 more
+// iterations.
+constexpr int WAIT_AFTER_A = (A_AHEAD - 1) * (A_LOADS + B_LOADS) + B_LOADS;
+static_assert(NW * WAVE_LDS <= 160 * 1024, "LDS");
+static_assert(A_AHEAD * (A_LOADS + B_LOADS) + (B_AHEAD - A_AHEAD) * B_LOADS < 64, "vmcnt range");
+
+__device__ __forceinline__ v8i frag(const uint8_t* slab, int row, int c0) {
+  const int sw = (row >> 1) & 7;
+  const v4i lo = *reinterpret_cast<const v4i*>(slab + row * BK + ((c0 ^ sw) << 4));
+  const v4i hi = *reinterpret_cast<const v4i*>(slab + row * BK + (((c0 + 1) ^ sw) << 4));
+  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+template <int G>
+__global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __restrict__ a,
+                                                              const uint8_t* __restrict__ b,
+                                                              const float* __restrict__ sa,
+                                                              const float* __restrict__ sb,
+                                                              uint16_t* __restrict__ out, int M, int N, int K,
+                                                              int tiles_m, int tiles_n) {
+  static_assert(G == 64 || G == 128, "granularity");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NW * WAVE_LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int ks, tmi, tni;
+  map_tile<2>(tiles_m, tiles_n, ks, tmi, tni);
+  const int m0 = tmi * BM, n0 = tni * BN;
+  const uint32_t uK = (uint32_t)K;
+  const v4i ra = rsrc_words(a + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * uK);
+  const v4i rb = rsrc_words(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
+
+  const int nkb = K / G;
+  const int nsteps = (K + BK - 1) / BK;
+  // 32 rows starting at a multiple of 32 lie in one g-block (g >= 64).
+  const float* const sa_row = sa + (int64_t)(m0 / G) * nkb;
+  const float* const sb_row = sb + (int64_t)(n0 / G) * nkb;
+
+  uint8_t* const a_ring = smem + wave * WAVE_LDS;
+  uint8_t* const b_ring = a_ring + A_SLOTS * A_SLAB;
+  // This wave's step t is global step wave + NW*t. Steps past the end issue
+  // copies of nothing, so every wait below counts exactly.
+  auto issue_a = [&](int t) {
+    const int st = wave + NW * t;
+#pragma unroll
+    for (int g = 0; g < BM / 8; ++g)
+      stage_group<1>(ra, a_ring + (t % A_SLOTS) * A_SLAB, uK, (uint32_t)st * BK, g, lane, st < nsteps);
+  };
+  auto issue_b = [&](int t) {
+    const int st = wave + NW * t;
+#pragma unroll
+    for (int g = 0; g < BN / 8; ++g)
+      stage_group<1>(rb, b_ring + (t % B_SLOTS) * B_SLAB, uK, (uint32_t)st * BK, g, lane, st < nsteps);
+  };
+
+  v16f acc = {};
+  const int my_steps = nsteps > wave ? (nsteps - wave + NW - 1) / NW : 0;
+  // Prologue in the steady-state order: B(0) .. B(B_AHEAD - A_AHEAD - 1), then
+  // for j = 0 .. A_AHEAD-1 the pair A(j), B(B_AHEAD - A_AHEAD + j).
+#pragma unroll
+  for (int t = 0; t < B_AHEAD - A_AHEAD; ++t) issue_b(t);
+#pragma unroll
+  for (int j = 0; j < A_AHEAD; ++j) {
+    issue_a(j);
+    issue_b(B_AHEAD - A_AHEAD + j);
+  }
+
+  const int r32 = lane & 31, h2 = lane >> 5;
+  for (int t = 0; t < my_steps; ++t) {
+    DG_WAIT_VMCNT(WAIT_AFTER_A);  // A(t) and the earlier-issued B(t) have landed
+    const int st = wave + NW * t;
+    const uint8_t* As = a_ring + (t % A_SLOTS) * A_SLAB;
+    const uint8_t* Bs = b_ring + (t % B_SLOTS) * B_SLAB;
+#pragma unroll
+    for (int h = 0; h < BK / 64; ++h) {
+      const int kb = G == 128 ? st : 2 * st + h;
+      if (G == 64 && kb >= nkb) break;  // K % 128 == 64: the last step holds one segment
+      const int c0 = 4 * h + 2 * h2;
+      const v8i af = frag(As, r32, c0);
+      const v8i bf = frag(Bs, r32, c0);
+      if (G == 128) {
+        if (h == 0) {
+          // the segment is the whole step: chain both halves, then promote once
+          const v8i af1 = frag(As, r32, c0 + 4);
+          const v8i bf1 = frag(Bs, r32, c0 + 4);
+          v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, (v16f){}, 0, 0, 0, 0, 0, 0);
+          p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af1, bf1, p, 0, 0, 0, 0, 0, 0);
+          const float sc = sa_row[kb] * sb_row[kb];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[v] = __builtin_fmaf(p[v], sc, acc[v]);
+        }
+      } else {
+        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, (v16f){}, 0, 0, 0, 0, 0, 0);
+        const float sc = sa_row[kb] * sb_row[kb];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] = __builtin_fmaf(p[v], sc, acc[v]);
+      }
+    }
+    // Refill the slots of step t-1, read by this wave only and done with one
+    // iteration ago.
+    issue_a(t + A_AHEAD);
+    issue_b(t + B_AHEAD);
+  }
+  DG_WAIT_VMCNT(0);  // copies of nothing issued past this wave's last step
+
+  // Add the four waves' partial tiles in wave order, through LDS.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);  // [NW][16][64]
+#pragma unroll
+  for (int v = 0; v < 16; ++v) red[(wave * 16 + v) * 64 + lane] = acc[v];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float tsum = red[v * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) tsum += red[(w * 16 + v) * 64 + lane];
+    const int row = m0 + 8 * (v >> 2) + 4 * h2 + (v & 3);
+    const int col = n0 + r32;
+    if (row < M && col < N) out[(int64_t)row * N + col] = bf16_bits(tsum);
+  }
+}
+
+template <int G>
+hipError_t launch(const GemmArgs& p, hipStream_t stream) {
+  if (p.ksplit != 1) return hipErrorInvalidValue;
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_fp8_nt_stream<G>), dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream, p.a, p.b, p.sa,
+                     p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace stream
+
+hipError_t launch_stream_g128(const GemmArgs& p, hipStream_t s) { return stream::launch<128>(p, s); }
+hipError_t launch_stream_g64(const GemmArgs& p, hipStream_t s) { return stream::launch<64>(p, s); }
+
+}  // namespace dg

@@ -191,7 +191,7 @@ def test_non_default_stream_and_unaligned_out():
 # arrive. Shapes chosen so the split count is > 1 (see dg_query_tile).
 SPLITK = [
     (1, 4096, 7168, 128), (64, 1000, 4096, 64), (100, 520, 2048, 128), (33, 700, 64 * 37, 64),
-    (128, 512, 8192, 128), (7, 64, 16384, 64), (96, 4100, 1024, 128),
+    (128, 512, 8192, 128), (7, 64, 16384, 64), (96, 2000, 1024, 128),
 ]
 
 
@@ -291,3 +291,39 @@ def test_big_tile_all_ones_bitwise(g):
     cols = np.unique(np.concatenate([np.arange(0, N, 41), [N - 1]]))
     ref = oracle.gemm_ref(a8, b8, sa, sb, g, rows, cols)
     assert np.array_equal(bits[np.ix_(rows, cols)], _common.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+# Small M with many 32x32 tiles takes the streaming class (kernel ids 6, 7):
+# whole K per workgroup, waves splitting K, partials added in wave order.
+STREAM = [(64, 6150, 1920, 128), (1, 8192, 1024, 128), (33, 8000, 64 * 37, 64), (128, 7168, 2048, 64),
+          (100, 3000, 896, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,g", STREAM)
+def test_stream_parity(M, N, K, g):
+    import fp8_block_scaled_scales_amd as dg
+
+    tile = dg.dg_query_tile(M, N, K, g)
+    assert tile["bm"] == 32 and tile["bn"] == 32, tile
+    x = synth.normal(4000 + M, (M, K))
+    y = synth.normal(4500 + N, (N, K), sigma=0.02)
+    a8, sa = oracle.quantize_blocks(x, g)
+    b8, sb = oracle.quantize_blocks(y, g)
+    say("stream M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    got, bits = gemm(a8, sa, b8, sb, g)
+    ref = oracle.gemm_ref(a8, b8, sa, sb, g)
+    _assert_parity(got, ref, "stream %dx%dx%d g=%d" % (M, N, K, g))
+    _, bits2 = gemm(a8, sa, b8, sb, g)
+    assert np.array_equal(bits, bits2)
+
+
+def test_stream_all_ones_bitwise():
+    M, N, K, g = 64, 6000, 2048, 128
+    a8 = np.full((M, K), 0x38, np.uint8)
+    b8 = np.full((N, K), 0x38, np.uint8)
+    sa = _pow2_scales(-(-M // g), K // g, lambda mb, kb: (mb - kb) % 7 - 3)
+    sb = _pow2_scales(-(-N // g), K // g, lambda nb, kb: (2 * nb + kb) % 3)
+    say("stream all-ones")
+    got, bits = gemm(a8, sa, b8, sb, g)
+    ref = oracle.gemm_ref(a8, b8, sa, sb, g)
+    assert np.array_equal(bits, _common.f32_to_bf16_bits(ref.astype(np.float32)))
