@@ -125,9 +125,25 @@ Plan plan(int64_t M, int64_t N, int64_t K, int gran) {
     p.ksplit = (int)splits_for(p.e, p.tiles, nsteps);
     return p;
   }
-  const dg::KernelEntry* big = find(dg::kClassBig, gran);
-  const int64_t big_tiles = ((M + big->bm - 1) / big->bm) * ((N + big->bn - 1) / big->bn);
-  p.e = big_tiles >= 192 ? big : find(dg::kClassTiled, gran);
+  // 256-row tiles: the width whose tile count fills the 256 CUs best, weighed
+  // by the width's own speed per CU (narrower tiles stage more bytes per
+  // FLOP); too few tiles of any width fall back to 128 x 128.
+  const dg::KernelEntry* big = nullptr;
+  double best = 0.0;
+  int64_t big_tiles = 0;
+  for (int i = 0; i < dg::kTableSize; ++i) {
+    const dg::KernelEntry* e = &dg::kTable[i];
+    if (e->cls != dg::kClassBig || e->gran != gran) continue;
+    const int64_t t = ((M + e->bm - 1) / e->bm) * ((N + e->bn - 1) / e->bn);
+    const double fill = (double)t / (double)(256 * ((t + 255) / 256));
+    const double per_cu = e->bn == 256 ? 1.0 : e->bn == 224 ? 0.97 : 0.8;
+    if (fill * per_cu > best) {
+      best = fill * per_cu;
+      big = e;
+      big_tiles = t;
+    }
+  }
+  p.e = big && big_tiles >= 192 ? big : find(dg::kClassTiled, gran);
   p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
   return p;
 }

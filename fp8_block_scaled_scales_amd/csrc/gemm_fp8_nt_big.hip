@@ -1,4 +1,5 @@
-// Large-tile block-scaled FP8 GEMM for gfx950: 256 x 256 output tiles.
+// Large-tile block-scaled FP8 GEMM for gfx950: 256 x BN output tiles,
+// BN = 256, 224 or 128.
 //
 // Same operation as the other kernels (DeepGEMM实战 §2.2: one FP32 scale per
 // g x g block of each operand, restored while the products are accumulated,
@@ -6,26 +7,36 @@
 // K segment summed on its own and the segments then added; §3.3/§4.2: NT
 // layout, A [M,K] and B [N,K] K-contiguous, BF16 out).
 //
-// Why this shape. On MI355X a CU's L2->LDS intake is about 50 bytes per clock
-// and its FP8 matrix rate 8192 FLOP per clock, so a tile must do at least
-// ~170 FLOPs per staged byte to keep the matrix cores fed: 2*BM*BN/(BM+BN) is
-// 128 for 128x128 and 256 for 256x256. A 256x256x128 step stages 64 KB and
+// Why this shape. On MI355X a CU's L2->LDS intake is about 50-70 bytes per
+// clock and its FP8 matrix rate 8192 FLOP per clock, so a tile must do at
+// least ~170 FLOPs per staged byte to keep the matrix cores fed: 2*BM*BN/(BM+BN)
+// is 128 for 128x128 and 256 for 256x256. A 256x256x128 step stages 64 KB and
 // does 16.8 MFLOP (2048 clocks at peak); two ring slots fill 128 KB of the
-// 160 KB LDS.
+// 160 KB LDS. The narrower tiles exist for tile counts: 256x224 splits a
+// 7168-wide N into 32 tiles, and 256x128 gives a 2000 x 4000 output 256 tiles,
+// one per CU, where 256x256 would leave half the chip idle.
 //
-// Workgroup: 8 waves (two per SIMD), laid out 2 (M) x 4 (N), each owning a
-// 128 x 64 sub-tile with its FP32 accumulator in 128 VGPRs. Per 128-byte K
+// Workgroup: 8 waves (two per SIMD), laid out WM x WN, each owning a
+// WTM x WTN sub-tile with its FP32 accumulator in registers. Per 128-byte K
 // step:
 //   * g = 128: the step is one K segment. Each 16 x 16 output block is one
 //     v_mfma_f32_16x16x128_f8f6f4 from a zero accumulator (the whole segment
 //     in one instruction), promoted with acc = fma(partial, sa*sb, acc);
 //   * g = 64: the step holds two segments. Each 32 x 32 output block per
 //     segment is one v_mfma_f32_32x32x64_f8f6f4 from zero, promoted the same
-//     way; the wave's 128 rows span two row blocks of scales.
+//     way; a 128-row wave tile spans two row blocks of scales.
+// Instruction order inside a step is fixed by hand (schedule barriers): the
+// MFMAs go out back to back and each promotion runs a few MFMAs behind its
+// own, so the matrix core never waits for the FMA of the block it just
+// produced; A fragments are read from LDS one row block ahead.
+// The next step's copies are issued by waves 0-3 at the start of the step and
+// by waves 4-7 a quarter of the way in: the memory pipeline takes one 1 KB
+// copy per ~14 clocks and a wave stalls until its copy is taken, so this way
+// one wave per SIMD is always free to issue MFMAs.
 // The tiles' LDS slabs use the SW = 1 swizzle: the 16 (or 32) rows a fragment
 // read touches together hit distinct banks.
 //
-// Epilogue: the BF16 tile goes through LDS in two 128-row halves so every
+// Epilogue: the BF16 tile goes through LDS in two 128-row passes so every
 // lane stores 16 contiguous bytes, masked at the M and N edges.
 //
 // MFMA layouts used. 16x16x128: lane l supplies row (A) or column (B) l%16
@@ -45,13 +56,8 @@ namespace dg {
 
 namespace big {
 
-constexpr int BM = 256, BN = 256, BK = 128, STAGES = 2;
-constexpr int WM = 2, WN = 4, NW = WM * WN, NT = 64 * NW;
-constexpr int WTM = BM / WM, WTN = BN / WN;  // 128 x 64 wave tile
-constexpr int A_BYTES = BM * BK, STAGE_BYTES = (BM + BN) * BK;
-constexpr int LOADS = (BM / 8 + BN / 8) / NW;  // HBM->LDS instructions per wave per step
-constexpr int LDC = BN + 8;                    // bf16 pitch of the epilogue half-tile
-static_assert(WTM * LDC * 2 <= STAGES * STAGE_BYTES, "epilogue half-tile must fit in the ring");
+constexpr int BM = 256, BK = 128, NW = 8, NT = 64 * NW;
+constexpr int A_BYTES = BM * BK;
 
 // 32 K bytes (logical 16-byte chunks c0, c0+1) of staged row `row` under the
 // SW = 1 swizzle.
@@ -70,33 +76,43 @@ __device__ __forceinline__ v16f mfma32(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, (v16f){}, 0, 0, 0, 0, 0, 0);
 }
 
-// Accumulator: 128 FP32 per lane either way.
-template <int G>
+template <int G, int WTM, int WTN>
 struct Acc;
-template <>
-struct Acc<128> {
-  v4f t[WTM / 16][WTN / 16];  // 8 x 4 blocks of 16 x 16
+template <int WTM, int WTN>
+struct Acc<128, WTM, WTN> {
+  v4f t[WTM / 16][WTN / 16];
 };
-template <>
-struct Acc<64> {
-  v16f t[WTM / 32][WTN / 32];  // 4 x 2 blocks of 32 x 32
+template <int WTM, int WTN>
+struct Acc<64, WTM, WTN> {
+  v16f t[WTM / 32][WTN / 32];
 };
 
-template <int G, int GROUP_M>
+template <int G, int BN, int WM, int GROUP_M>
 __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
                                                       const float* __restrict__ sa, const float* __restrict__ sb,
                                                       uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
                                                       int tiles_n, int vec_store) {
   static_assert(G == 64 || G == 128, "granularity");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+  constexpr int WN = NW / WM;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int STAGE = A_BYTES + BN * BK;
+  constexpr int LDC = BN + 8;  // bf16 pitch of an epilogue pass
+  static_assert(WTM == 64 || WTM == 128, "a wave's rows lie in one 128-row scale block");
+  static_assert(WTN % 16 == 0 && WTN <= 128, "a wave's columns touch at most two 128-column scale blocks");
+  static_assert(G == 128 || WTN == 64, "g = 64: one 64-column scale block per wave");
+  static_assert(BN % 8 == 0 && BN / 8 <= 4 * NW, "B copies: at most four row groups per wave");
+  static_assert(128 * LDC * 2 <= 2 * STAGE, "an epilogue pass must fit in the ring");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  const int grp = wave >> 2;  // copy-issue group: one wave per SIMD in each
 
   int ks, tmi, tni;
   map_tile<GROUP_M>(tiles_m, tiles_n, ks, tmi, tni);
   const int m0 = tmi * BM, n0 = tni * BN;
+
   const uint32_t uK = (uint32_t)K;
   const v4i ra = rsrc_words(a + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * uK);
   const v4i rb = rsrc_words(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
@@ -104,14 +120,20 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   const int nkb = K / G;
   const int nsteps = (K + BK - 1) / BK;
 
-  // Scale rows of this wave. Rows of a block past the edge clamp to the last
-  // block row (their data is zero).
+  // Scale rows of this wave. Blocks past the edge clamp to the last block
+  // (their data is zero). g = 128: one A block; the wave's columns may cross
+  // into a second B block after jsplit 16-column blocks. g = 64: A blocks of
+  // rows wr0 and wr0 + 64, one B block.
   const int wr0 = m0 + wm * WTM, wc0 = n0 + wn * WTN;
-  const float* const sa0 = sa + (int64_t)min(wr0 / G, (M - 1) / G) * nkb;
-  const float* const sa1 = sa + (int64_t)min((wr0 + 64) / G, (M - 1) / G) * nkb;  // g = 64: second row block
-  const float* const sbr = sb + (int64_t)min(wc0 / G, (N - 1) / G) * nkb;
+  const int lastm = (M - 1) / G, lastn = (N - 1) / G;
+  const float* const sa0 = sa + (int64_t)min(wr0 / G, lastm) * nkb;
+  const float* const sa1 = sa + (int64_t)min((wr0 + 64) / G, lastm) * nkb;
+  const int bn0 = wc0 / G;
+  const float* const sb0 = sb + (int64_t)min(bn0, lastn) * nkb;
+  const float* const sb1 = sb + (int64_t)min(bn0 + 1, lastn) * nkb;
+  const int jsplit = ((bn0 + 1) * G - wc0) / 16;  // g = 128: column blocks in the first B block
 
-  Acc<G> acc;
+  Acc<G, WTM, WTN> acc;
   if constexpr (G == 128) {
 #pragma unroll
     for (int i = 0; i < WTM / 16; ++i)
@@ -124,70 +146,111 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       for (int j = 0; j < WTN / 32; ++j) acc.t[i][j] = (v16f){};
   }
 
-  stage_slab<BM, NW, 1>(ra, smem, uK, 0, wave, lane);
-  stage_slab<BN, NW, 1>(rb, smem + A_BYTES, uK, 0, wave, lane);
+  // This wave's share of a step's copies: A row groups 8i + wave (i < 4) and
+  // B row groups 8i + wave below BN / 8, into the slot of step t.
+  auto issue_step = [&](int t) {
+    uint8_t* slot = smem + (t & 1) * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage_group<1>(ra, slot, uK, (uint32_t)t * BK, i * NW + wave, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i * NW + wave < BN / 8) stage_group<1>(rb, slot + A_BYTES, uK, (uint32_t)t * BK, i * NW + wave, lane);
+  };
+
+  issue_step(0);
 
   for (int s = 0; s < nsteps; ++s) {
     DG_WAIT_VMCNT(0);  // this wave's part of step s has landed
     __syncthreads();   // all of step s visible; the other slot is free
-    if (s + 1 < nsteps) {
-      uint8_t* slot = smem + ((s + 1) & 1) * STAGE_BYTES;
-      stage_slab<BM, NW, 1>(ra, slot, uK, (s + 1) * BK, wave, lane);
-      stage_slab<BN, NW, 1>(rb, slot + A_BYTES, uK, (s + 1) * BK, wave, lane);
-    }
-    const uint8_t* As = smem + (s & 1) * STAGE_BYTES + wm * WTM * BK;
-    const uint8_t* Bs = smem + (s & 1) * STAGE_BYTES + A_BYTES + wn * WTN * BK;
+    auto issue_next = [&](int who) {
+      if (s + 1 < nsteps && grp == who) issue_step(s + 1);
+    };
+    const uint8_t* As = smem + (s & 1) * STAGE + wm * WTM * BK;
+    const uint8_t* Bs = smem + (s & 1) * STAGE + A_BYTES + wn * WTN * BK;
 
     if constexpr (G == 128) {
+      // Slots t = (row block i, column block j). Slot t issues MFMA t and the
+      // promotion of slot t - LAG, whose result has had LAG MFMAs' time to
+      // land. Left alone, the scheduler puts each FMA right behind its own
+      // MFMA and waits out the MFMA latency.
+      constexpr int LAG = 3;
+      constexpr int NJ = WTN / 16, SLOTS = (WTM / 16) * NJ, DSLOT = SLOTS / 4;
       const int r16 = lane & 15, q = lane >> 4;
-      const float sc = sa0[s] * sbr[s];
-      v8i bf[WTN / 16];
+      const float a_s = sa0[s];
+      const float sc0 = a_s * sb0[s], sc1 = a_s * sb1[s];
+      v8i bf[NJ];
 #pragma unroll
-      for (int j = 0; j < WTN / 16; ++j) bf[j] = frag(Bs, j * 16 + r16, 2 * q);
+      for (int j = 0; j < NJ; ++j) bf[j] = frag(Bs, j * 16 + r16, 2 * q);
+      v8i a_cur = frag(As, r16, 2 * q), a_nxt = a_cur;
+      v4f pr[LAG + 1];
 #pragma unroll
-      for (int i = 0; i < WTM / 16; ++i) {
-        const v8i af = frag(As, i * 16 + r16, 2 * q);
-#pragma unroll
-        for (int j = 0; j < WTN / 16; ++j) {
-          const v4f p = mfma16(af, bf[j]);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc.t[i][j][v] = __builtin_fmaf(p[v], sc, acc.t[i][j][v]);
+      for (int t = 0; t < SLOTS + LAG; ++t) {
+        const int i = t / NJ, j = t % NJ;
+        if (t == 0) issue_next(0);
+        if (t == DSLOT) issue_next(1);
+        if (t < SLOTS) {
+          if (j == 0 && i + 1 < WTM / 16) a_nxt = frag(As, (i + 1) * 16 + r16, 2 * q);
+          pr[t % (LAG + 1)] = mfma16(a_cur, bf[j]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (t >= LAG) {
+          const int u = t - LAG, ui = u / NJ, uj = u % NJ;
+          const float sc = uj < jsplit ? sc0 : sc1;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], sc, acc.t[ui][uj][v]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (t < SLOTS && j == NJ - 1) a_cur = a_nxt;
       }
     } else {
+      // The same schedule over the 32 x 32 blocks of each segment; waves 4-7
+      // issue their copies at the second segment.
+      constexpr int LAG = 2;
+      constexpr int NJ = WTN / 32, SLOTS = (WTM / 32) * NJ;
       const int r32 = lane & 31, h2 = lane >> 5;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int kb = 2 * s + h;
+        issue_next(h);
         if (kb < nkb) {  // K % 128 == 64: the last step holds one segment
-          const float sbv = sbr[kb];
-          const float sc0 = sa0[kb] * sbv, sc1 = sa1[kb] * sbv;
-          v8i bf[WTN / 32];
+          const float sbv = sb0[kb];
+          const float f0 = sa0[kb] * sbv, f1 = sa1[kb] * sbv;
+          v8i bf[NJ];
 #pragma unroll
-          for (int j = 0; j < WTN / 32; ++j) bf[j] = frag(Bs, j * 32 + r32, 4 * h + 2 * h2);
+          for (int j = 0; j < NJ; ++j) bf[j] = frag(Bs, j * 32 + r32, 4 * h + 2 * h2);
+          v8i a_cur = frag(As, r32, 4 * h + 2 * h2), a_nxt = a_cur;
+          v16f pr[LAG + 1];
 #pragma unroll
-          for (int i = 0; i < WTM / 32; ++i) {
-            const v8i af = frag(As, i * 32 + r32, 4 * h + 2 * h2);
-            const float sc = i < 2 ? sc0 : sc1;
-#pragma unroll
-            for (int j = 0; j < WTN / 32; ++j) {
-              const v16f p = mfma32(af, bf[j]);
-#pragma unroll
-              for (int v = 0; v < 16; ++v) acc.t[i][j][v] = __builtin_fmaf(p[v], sc, acc.t[i][j][v]);
+          for (int t = 0; t < SLOTS + LAG; ++t) {
+            const int i = t / NJ, j = t % NJ;
+            if (t < SLOTS) {
+              if (j == 0 && i + 1 < WTM / 32) a_nxt = frag(As, (i + 1) * 32 + r32, 4 * h + 2 * h2);
+              pr[t % (LAG + 1)] = mfma32(a_cur, bf[j]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            if (t >= LAG) {
+              const int u = t - LAG, ui = u / NJ, uj = u % NJ;
+              const float f = ui < 2 ? f0 : f1;  // rows 64.. of a 128-row wave tile use the next A block
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], f, acc.t[ui][uj][v]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (t < SLOTS && j == NJ - 1) a_cur = a_nxt;
           }
         }
       }
     }
   }
+  DG_WAIT_VMCNT(0);
 
-  // Epilogue, two halves of 128 rows: the waves of wave-row `half` write
-  // their BF16 sub-tiles to LDS, then all threads store the half.
+  // Epilogue, two passes of 128 rows: the waves whose rows lie in the pass
+  // write their BF16 sub-tiles to LDS, then all threads store the pass.
   uint16_t* cs = reinterpret_cast<uint16_t*>(smem);
+  const int prow = wm * WTM % 128;  // first row of this wave inside its pass
 #pragma unroll
-  for (int half = 0; half < WM; ++half) {
+  for (int pass = 0; pass < 2; ++pass) {
     __syncthreads();
-    if (wm == half) {
+    if (wm * WTM / 128 == pass) {
       if constexpr (G == 128) {
         const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
@@ -196,7 +259,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
           for (int j = 0; j < WTN / 16; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              cs[(i * 16 + 4 * q + v) * LDC + wn * WTN + j * 16 + r16] = bf16_bits(acc.t[i][j][v]);
+              cs[(prow + i * 16 + 4 * q + v) * LDC + wn * WTN + j * 16 + r16] = bf16_bits(acc.t[i][j][v]);
       } else {
         const int r32 = lane & 31, h2 = lane >> 5;
 #pragma unroll
@@ -205,17 +268,18 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
           for (int j = 0; j < WTN / 32; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              cs[(i * 32 + 8 * (v >> 2) + 4 * h2 + (v & 3)) * LDC + wn * WTN + j * 32 + r32] =
+              cs[(prow + i * 32 + 8 * (v >> 2) + 4 * h2 + (v & 3)) * LDC + wn * WTN + j * 32 + r32] =
                   bf16_bits(acc.t[i][j][v]);
       }
     }
     __syncthreads();
-    constexpr int CHUNKS = WTM * BN / 8;
+    constexpr int CHUNKS = 128 * BN / 8;
+    static_assert(CHUNKS % NT == 0, "epilogue chunks split evenly over the threads");
 #pragma unroll
     for (int it = 0; it < CHUNKS / NT; ++it) {
       const int idx = it * NT + threadIdx.x;
       const int r = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
-      const int gr = m0 + half * WTM + r, gc = n0 + c;
+      const int gr = m0 + pass * 128 + r, gc = n0 + c;
       if (gr >= M || gc >= N) continue;
       const v4i val = *reinterpret_cast<const v4i*>(cs + r * LDC + c);
       uint16_t* dst = out + (int64_t)gr * N + gc;
@@ -228,18 +292,21 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   }
 }
 
-template <int G, int GROUP_M>
+template <int G, int BN, int WM>
 hipError_t launch(const GemmArgs& p, hipStream_t stream) {
   if (p.ksplit != 1) return hipErrorInvalidValue;
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_big<G, GROUP_M>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, p.a, p.b, p.sa, p.sb,
-                     p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store);
+  hipLaunchKernelGGL((gemm_fp8_nt_big<G, BN, WM, 4>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, p.a, p.b, p.sa,
+                     p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store);
   return hipGetLastError();
 }
 
 }  // namespace big
 
-hipError_t launch_big_g128(const GemmArgs& p, hipStream_t s) { return big::launch<128, 4>(p, s); }
-hipError_t launch_big_g64(const GemmArgs& p, hipStream_t s) { return big::launch<64, 4>(p, s); }
+hipError_t launch_big_g128(const GemmArgs& p, hipStream_t s) { return big::launch<128, 256, 2>(p, s); }
+hipError_t launch_big_g64(const GemmArgs& p, hipStream_t s) { return big::launch<64, 256, 2>(p, s); }
+hipError_t launch_big224_g128(const GemmArgs& p, hipStream_t s) { return big::launch<128, 224, 4>(p, s); }
+hipError_t launch_big128_g128(const GemmArgs& p, hipStream_t s) { return big::launch<128, 128, 4>(p, s); }
+hipError_t launch_big128_g64(const GemmArgs& p, hipStream_t s) { return big::launch<64, 128, 4>(p, s); }
 
 }  // namespace dg

@@ -89,3 +89,18 @@ def test_python_binding_rejects_bad_tensors(dg):
     a = torch.zeros((4, 128), dtype=torch.uint8)
     with pytest.raises(ValueError):
         dg.dg_gemm_fp8_nt(a, a, torch.ones(1, 1), torch.ones(1, 1))  # CPU tensors
+
+
+# Host-side tile choice for the five workloads and the 256-row widths: the
+# width whose tile count fills the 256 CUs best, weighed by per-CU speed.
+@pytest.mark.parametrize("M,N,K,g,cls", [
+    (256, 256, 256, 128, (128, 128, 1)),      # too few tiles for 256-row tiles
+    (64, 4096, 7168, 128, (32, 32, 1)),       # small M, 256 streaming tiles
+    (64, 512, 7168, 128, (64, 64, 14)),       # small M, few tiles: split-K
+    (4096, 7168, 2048, 128, (256, 224, 1)),   # 512 tiles of 256x224 vs 448 of 256x256
+    (8192, 8192, 8192, 128, (256, 256, 1)),   # 1024 tiles of 256x256
+    (2000, 4000, 16384, 64, (256, 128, 1)),   # 256 tiles of 256x128 vs 128 of 256x256
+])
+def test_query_tile_choice(dg, M, N, K, g, cls):
+    t = dg.dg_query_tile(M, N, K, g)
+    assert (t["bm"], t["bn"], t["ksplit"]) == cls, t

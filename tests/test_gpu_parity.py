@@ -252,40 +252,48 @@ def test_splitk_determinism_and_interleaving():
     _assert_parity(other.float().cpu().numpy().astype(np.float64), ref, "interleaved small case")
 
 
-# Large M and N take the 256x256-tile class (kernel ids 4 and 5). Ragged
-# edges at both granularities, and K % 128 == 64 at g = 64 (a half step).
-BIG = [(3583, 3585, 512, 128), (3600, 4000, 320, 64), (4096, 3328, 1024, 128), (3841, 4100, 704, 64)]
+# Large M and N take the 256-row-tile class (kernel ids 4, 5: 256 columns;
+# 8: 224 columns; 9, 10: 128 columns), the width chosen by tile count.
+# Ragged edges at both granularities, K % 128 == 64 at g = 64 (a half step),
+# and 224-wide tiles whose waves straddle two 128-column scale blocks.
+BIG = [(3583, 3585, 512, 128, 224), (4096, 3328, 1024, 128, 224), (4000, 4000, 256, 128, 256),
+       (2000, 4000, 1024, 128, 128), (3600, 4000, 320, 64, 256), (3841, 4100, 704, 64, 128),
+       (2000, 4000, 1088, 64, 128)]
 
 
-@pytest.mark.parametrize("M,N,K,g", BIG)
-def test_big_tile_parity(M, N, K, g):
+@pytest.mark.parametrize("M,N,K,g,bn", BIG)
+def test_big_tile_parity(M, N, K, g, bn):
     import fp8_block_scaled_scales_amd as dg
 
     tile = dg.dg_query_tile(M, N, K, g)
-    assert tile["bm"] == 256 and tile["bn"] == 256, tile
+    assert tile["bm"] == 256 and tile["bn"] == bn, tile
     x = synth.normal(9000 + M, (M, K))
     y = synth.normal(9500 + N, (N, K), sigma=0.02)
     a8, sa = oracle.quantize_blocks(x, g)
     b8, sb = oracle.quantize_blocks(y, g)
-    say("big tile M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    say("big tile M=%d N=%d K=%d g=%d bn=%d" % (M, N, K, g, bn))
     got, _ = gemm(a8, sa, b8, sb, g)
     rows = _common.sample_indices(M, 200, seed=M)
     cols = _common.sample_indices(N, 200, seed=N)
-    # every 256-row and 256-column tile edge, too
+    # every tile edge, too
     rows = np.unique(np.concatenate([rows, np.arange(255, M, 256), np.arange(0, M, 256)]))
-    cols = np.unique(np.concatenate([cols, np.arange(255, N, 256), np.arange(0, N, 256)]))
+    cols = np.unique(np.concatenate([cols, np.arange(bn - 1, N, bn), np.arange(0, N, bn)]))
     ref = oracle.gemm_ref(a8, b8, sa, sb, g, rows, cols)
-    _assert_parity(got[np.ix_(rows, cols)], ref, "big %dx%dx%d g=%d" % (M, N, K, g))
+    _assert_parity(got[np.ix_(rows, cols)], ref, "big %dx%dx%d g=%d bn=%d" % (M, N, K, g, bn))
 
 
-@pytest.mark.parametrize("g", [128, 64])
-def test_big_tile_all_ones_bitwise(g):
-    M, N, K = 3600, 3500, 1024
+@pytest.mark.parametrize("M,N,K,g,bn", [(3600, 3500, 1024, 128, 224), (3600, 3500, 1024, 64, 256),
+                                        (4000, 4000, 512, 128, 256), (2000, 4000, 1024, 128, 128),
+                                        (2000, 4000, 1024, 64, 128)])
+def test_big_tile_all_ones_bitwise(M, N, K, g, bn):
+    import fp8_block_scaled_scales_amd as dg
+
+    assert dg.dg_query_tile(M, N, K, g)["bn"] == bn
     a8 = np.full((M, K), 0x38, np.uint8)
     b8 = np.full((N, K), 0x38, np.uint8)
     sa = _pow2_scales(-(-M // g), K // g, lambda mb, kb: (mb - kb) % 7 - 3)
     sb = _pow2_scales(-(-N // g), K // g, lambda nb, kb: (2 * nb + kb) % 3)
-    say("big all-ones g=%d" % g)
+    say("big all-ones %dx%dx%d g=%d bn=%d" % (M, N, K, g, bn))
     _, bits = gemm(a8, sa, b8, sb, g)
     rows = np.unique(np.concatenate([np.arange(0, M, 37), [M - 1]]))
     cols = np.unique(np.concatenate([np.arange(0, N, 41), [N - 1]]))
