@@ -13,6 +13,10 @@ computes and which passage of the pages it follows:
   E4M3_RNE_SAT(x / scale) (DeepGEMM实战 §2.2, §4.4, §5.2).
 * ``gemm_ref``: ref[i,j] = sum_kb sa[i/g,kb]*sb[j/g,kb] * P[i,j,kb] with the
   exact FP64 segment partials P (DeepGEMM实战 §2.2, §3.2, §3.3, §4.2).
+* ``e5m2_decode`` / ``e5m2_encode``, ``quantize_blocks_fmt``, ``gemm_ref_fmt``:
+  the same with E5M2 operands (DeepGEMM实战 §2.2 names E4M3 and E5M2 as the
+  input formats; OCP E5M2 as torch.float8_e5m2 implements it), and any block
+  granularity g (§3.1: 64, 128 and 256).
 
 Parity status: every function above is pinned by the CPU tests
 (``tests/test_oracle_*.py``) against torch's float8 cast, brute force, exact
@@ -72,6 +76,19 @@ def _load():
     lib.dgo_gemm_ref.restype = ctypes.c_int
     lib.dgo_gemm_ref.argtypes = [u8p, u8p, f32p, f32p, i64, i64, i64, ctypes.c_int,
                                  i64p, i64, i64p, i64, f64p, ctypes.c_int]
+    lib.dgo_e5m2_decode.restype = ctypes.c_double
+    lib.dgo_e5m2_decode.argtypes = [ctypes.c_uint8]
+    lib.dgo_e5m2_encode.restype = ctypes.c_uint8
+    lib.dgo_e5m2_encode.argtypes = [ctypes.c_float]
+    lib.dgo_e5m2_decode_n.restype = None
+    lib.dgo_e5m2_decode_n.argtypes = [u8p, i64, f64p]
+    lib.dgo_e5m2_encode_n.restype = None
+    lib.dgo_e5m2_encode_n.argtypes = [f32p, i64, u8p]
+    lib.dgo_quantize_blocks_fmt.restype = ctypes.c_int
+    lib.dgo_quantize_blocks_fmt.argtypes = [f32p, i64, i64, ctypes.c_int, ctypes.c_int, u8p, f32p, ctypes.c_int]
+    lib.dgo_gemm_ref_fmt.restype = ctypes.c_int
+    lib.dgo_gemm_ref_fmt.argtypes = [u8p, u8p, f32p, f32p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, i64p, i64, i64p, i64, f64p, ctypes.c_int]
     lib.dgo_hardware_threads.restype = ctypes.c_int
     lib.dgo_hardware_threads.argtypes = []
     _lib = lib
@@ -160,3 +177,67 @@ def gemm_ref(a8, b8, sa, sb, g: int, rows=None, cols=None, nthreads: int | None 
         raise ValueError("dgo_gemm_ref rejected its arguments")
     return out
 
+
+
+# Operand formats: 0 = E4M3FN, 1 = E5M2.
+E4M3, E5M2 = 0, 1
+
+
+def e5m2_decode(codes) -> np.ndarray:
+    """E5M2 codes (uint8, any shape) -> float64 values (+-inf for 0x7C/0xFC, NaN above)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().dgo_e5m2_decode_n(_ptr(c, ctypes.c_uint8), c.size, _ptr(out, ctypes.c_double))
+    return out
+
+
+def e5m2_encode(y) -> np.ndarray:
+    """float32 values (any shape) -> E5M2 codes, RNE, saturating at +-57344."""
+    v = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().dgo_e5m2_encode_n(_ptr(v, ctypes.c_float), v.size, _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def quantize_blocks_fmt(x, g: int, fmt: int, nthreads: int | None = None):
+    """quantize_blocks for either format: scale = amax / (448 or 57344)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    if cols % g:
+        raise ValueError("cols must be a multiple of g")
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty(((rows + g - 1) // g, cols // g), dtype=np.float32)
+    rc = _load().dgo_quantize_blocks_fmt(_ptr(x, ctypes.c_float), rows, cols, g, fmt, _ptr(q, ctypes.c_uint8),
+                                         _ptr(s, ctypes.c_float), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("dgo_quantize_blocks_fmt rejected its arguments")
+    return q, s
+
+
+def gemm_ref_fmt(a8, b8, sa, sb, g: int, fmt_a: int, fmt_b: int, rows=None, cols=None,
+                 nthreads: int | None = None) -> np.ndarray:
+    """gemm_ref with the operands' formats given (0 = E4M3, 1 = E5M2)."""
+    a8 = np.ascontiguousarray(a8, dtype=np.uint8)
+    b8 = np.ascontiguousarray(b8, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sb = np.ascontiguousarray(sb, dtype=np.float32)
+    M, K = a8.shape
+    N, K2 = b8.shape
+    if K2 != K or K % g:
+        raise ValueError("bad K")
+    if sa.shape != ((M + g - 1) // g, K // g) or sb.shape != ((N + g - 1) // g, K // g):
+        raise ValueError("bad scale shapes")
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    c = None if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    nr = M if r is None else r.size
+    nc = N if c is None else c.size
+    out = np.empty((nr, nc), dtype=np.float64)
+    rc = _load().dgo_gemm_ref_fmt(
+        _ptr(a8, ctypes.c_uint8), _ptr(b8, ctypes.c_uint8), _ptr(sa, ctypes.c_float),
+        _ptr(sb, ctypes.c_float), M, N, K, g, fmt_a, fmt_b,
+        None if r is None else _ptr(r, ctypes.c_int64), nr,
+        None if c is None else _ptr(c, ctypes.c_int64), nc,
+        _ptr(out, ctypes.c_double), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("dgo_gemm_ref_fmt rejected its arguments")
+    return out

@@ -34,6 +34,17 @@
 //    them stays below 2^53 units: P is exact in FP64 in any order. The only
 //    roundings are the scale multiply and the segment sum.
 //
+//  * E5M2 and mixed formats, g = 256 (the variants the pages name beside the
+//    default: DeepGEMM实战 §2.2 lists E4M3 and E5M2 as the two FP8 formats,
+//    §3.1 discusses other scale granularities). E5M2 is read as the OCP E5M2
+//    format torch.float8_e5m2 implements: bias 15, exponent field 0 holds
+//    subnormals m/4 * 2^-14, largest finite value 0x7B = 57344, exponent
+//    field 31 is infinity (m = 0) or NaN. Quantisation to E5M2 follows the
+//    same block rule with 57344 in place of 448. With an E5M2 operand a
+//    segment partial is no longer exact in FP64 in general (products span
+//    more than 53 bits); its relative error stays below K * 2^-53 of the sum
+//    of the products' magnitudes, far inside the GEMM tolerance.
+//
 // Scale tensors are row-major FP32: sa is [ceil(M/g)][K/g], sb is
 // [ceil(N/g)][K/g]. K must be a multiple of g.
 //
@@ -107,6 +118,56 @@ uint8_t dgo_e4m3_encode(float y) {
     E += 1;
   }
   return sign | (uint8_t)(((E + 7) << 3) | ((int)n - 8));
+}
+
+// OCP E5M2 decode of one code, straight from the bit fields.
+double dgo_e5m2_decode(uint8_t code) {
+  const int s = code >> 7;
+  const int e = (code >> 2) & 0x1F;
+  const int m = code & 0x3;
+  double mag;
+  if (e == 0x1F)
+    mag = m == 0 ? INFINITY : std::nan("");
+  else if (e == 0)
+    mag = std::ldexp((double)m / 4.0, -14);            // subnormal: m/4 * 2^(1-15)
+  else
+    mag = std::ldexp(1.0 + (double)m / 4.0, e - 15);   // normal: (1+m/4) * 2^(e-15)
+  return s ? -mag : mag;
+}
+
+// FP32 -> E5M2: round to nearest, ties to even, saturate to +-57344.
+// Never produces infinity or NaN (finite input assumed).
+uint8_t dgo_e5m2_encode(float y) {
+  const uint8_t sign = std::signbit(y) ? 0x80 : 0x00;
+  const double v = std::fabs((double)y);
+  if (v >= 57344.0) return sign | 0x7B;
+  if (v < std::ldexp(1.0, -14)) {
+    // Subnormal range, spacing 2^-16; n == 4 is code 0x04 = 2^-14, the
+    // smallest normal, so the code is n itself.
+    const double n = std::nearbyint(v * 65536.0);
+    return sign | (uint8_t)n;
+  }
+  int e2;
+  std::frexp(v, &e2);
+  int E = e2 - 1;                                     // v in [2^E, 2^(E+1)), -14 <= E <= 15
+  double n = std::nearbyint(std::ldexp(v, 2 - E));    // mantissa steps: n in [4, 8]
+  if (n == 8.0) {
+    n = 4.0;
+    E += 1;
+  }
+  return sign | (uint8_t)(((E + 15) << 2) | ((int)n - 4));
+}
+
+// Format codes shared with the Python side: 0 = E4M3FN, 1 = E5M2.
+static double decode_fmt(int fmt, uint8_t code) { return fmt == 1 ? dgo_e5m2_decode(code) : dgo_e4m3_decode(code); }
+static uint8_t encode_fmt(int fmt, float y) { return fmt == 1 ? dgo_e5m2_encode(y) : dgo_e4m3_encode(y); }
+
+void dgo_e5m2_decode_n(const uint8_t* codes, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = dgo_e5m2_decode(codes[i]);
+}
+
+void dgo_e5m2_encode_n(const float* y, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = dgo_e5m2_encode(y[i]);
 }
 
 // Decode an array of codes (convenience for the Python side).
@@ -192,6 +253,78 @@ int dgo_gemm_ref(const uint8_t* a, const uint8_t* b, const float* sa, const floa
           double p = 0.0;  // exact: see the header
           for (int64_t k = kb * g; k < kb * g + g; ++k) p += tab[arow[k]] * tab[brow[k]];
           const double s = (double)sarow[kb] * (double)sbrow[kb];  // exact (24 x 24 bits)
+          ref += s * p;
+        }
+        out[r * ncols + c] = ref;
+      }
+    }
+  });
+  return 0;
+}
+
+// Block quantiser for either format: as dgo_quantize_blocks with the
+// format's largest finite value (448 for E4M3, 57344 for E5M2) in the scale.
+int dgo_quantize_blocks_fmt(const float* x, int64_t rows, int64_t cols, int g, int fmt, uint8_t* q,
+                            float* scales, int nthreads) {
+  if (!x || !q || !scales || rows <= 0 || cols <= 0 || g <= 0 || cols % g != 0 || (fmt != 0 && fmt != 1)) return -1;
+  const float fmax = fmt == 1 ? 57344.0f : 448.0f;
+  const int64_t nrb = (rows + g - 1) / g, ncb = cols / g;
+  parallel_for(nrb, nthreads, [&](int64_t lo, int64_t hi) {
+    for (int64_t rb = lo; rb < hi; ++rb) {
+      const int64_t r0 = rb * g, r1 = (r0 + g < rows) ? r0 + g : rows;
+      for (int64_t cb = 0; cb < ncb; ++cb) {
+        const int64_t c0 = cb * g, c1 = c0 + g;
+        float amax = 0.0f;
+        for (int64_t r = r0; r < r1; ++r)
+          for (int64_t c = c0; c < c1; ++c) {
+            const float a = std::fabs(x[r * cols + c]);
+            if (a > amax) amax = a;
+          }
+        const float scale = amax > 0.0f ? amax / fmax : 1.0f;
+        scales[rb * ncb + cb] = scale;
+        for (int64_t r = r0; r < r1; ++r)
+          for (int64_t c = c0; c < c1; ++c) q[r * cols + c] = encode_fmt(fmt, x[r * cols + c] / scale);
+      }
+    }
+  });
+  return 0;
+}
+
+// Reference GEMM with the operands' formats given (fmt_a, fmt_b: 0 = E4M3,
+// 1 = E5M2); otherwise exactly dgo_gemm_ref.
+int dgo_gemm_ref_fmt(const uint8_t* a, const uint8_t* b, const float* sa, const float* sb, int64_t M,
+                     int64_t N, int64_t K, int g, int fmt_a, int fmt_b, const int64_t* rows, int64_t nrows,
+                     const int64_t* cols, int64_t ncols, double* out, int nthreads) {
+  if (!a || !b || !sa || !sb || !out || M <= 0 || N <= 0 || K <= 0 || g <= 0 || K % g != 0) return -1;
+  if ((fmt_a != 0 && fmt_a != 1) || (fmt_b != 0 && fmt_b != 1)) return -1;
+  if (!rows) nrows = M;
+  if (!cols) ncols = N;
+  for (int64_t r = 0; rows && r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= M) return -1;
+  for (int64_t c = 0; cols && c < ncols; ++c)
+    if (cols[c] < 0 || cols[c] >= N) return -1;
+
+  double ta[256], tb[256];
+  for (int c = 0; c < 256; ++c) {
+    ta[c] = decode_fmt(fmt_a, (uint8_t)c);
+    tb[c] = decode_fmt(fmt_b, (uint8_t)c);
+  }
+  const int64_t nkb = K / g;
+
+  parallel_for(nrows, nthreads, [&](int64_t lo, int64_t hi) {
+    for (int64_t r = lo; r < hi; ++r) {
+      const int64_t i = rows ? rows[r] : r;
+      const uint8_t* arow = a + i * K;
+      const float* sarow = sa + (i / g) * nkb;
+      for (int64_t c = 0; c < ncols; ++c) {
+        const int64_t j = cols ? cols[c] : c;
+        const uint8_t* brow = b + j * K;
+        const float* sbrow = sb + (j / g) * nkb;
+        double ref = 0.0;
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+          double p = 0.0;
+          for (int64_t k = kb * g; k < kb * g + g; ++k) p += ta[arow[k]] * tb[brow[k]];
+          const double s = (double)sarow[kb] * (double)sbrow[kb];
           ref += s * p;
         }
         out[r * ncols + c] = ref;
