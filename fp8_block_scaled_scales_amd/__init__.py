@@ -8,8 +8,8 @@ missing or fails to load, importing this package raises.
 
 The operation (DeepGEMM实战 §2.2, §3.2, §4.2):
   out[i,j] = bf16( sum_kb sa[i/g,kb] * sb[j/g,kb] * sum_{k in kb} A[i,k] * B[j,k] )
-with A [M,K], B [N,K] in E4M3FN (NT layout), FP32 scales per g x g block and
-FP32 accumulation within and across K segments.
+with A [M,K], B [N,K] in E4M3FN or E5M2 (NT layout), FP32 scales per g x g
+block (g = 64, 128 or 256) and FP32 accumulation within and across K segments.
 """
 
 from __future__ import annotations
@@ -27,6 +27,8 @@ DG_EINVAL = -1
 DG_EALIGN = -2
 DG_EUNSUPPORTED = -3
 DG_ELAUNCH = -4
+DG_FMT_E4M3 = 0
+DG_FMT_E5M2 = 1
 
 
 class dg_tile_info(ctypes.Structure):
@@ -45,8 +47,13 @@ def _load():
     lib.dg_gemm_fp8_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     lib.dg_query_tile.restype = ctypes.c_int
     lib.dg_query_tile.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(dg_tile_info)]
+    lib.dg_gemm_fp8_nt_fmt.restype = ctypes.c_int
+    lib.dg_gemm_fp8_nt_fmt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       vp]
     lib.dg_quantize_e4m3_blocks.restype = ctypes.c_int
     lib.dg_quantize_e4m3_blocks.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp]
+    lib.dg_quantize_fp8_blocks.restype = ctypes.c_int
+    lib.dg_quantize_fp8_blocks.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.dg_strerror.restype = ctypes.c_char_p
     lib.dg_strerror.argtypes = [ctypes.c_int]
     lib.dg_version.restype = ctypes.c_int
@@ -91,6 +98,8 @@ def dg_query_tile(M: int, N: int, K: int, gran: int = 128) -> dict:
 
 
 _FP8 = (torch.float8_e4m3fn, torch.uint8)
+_FP8_OF = {DG_FMT_E4M3: (torch.float8_e4m3fn, torch.uint8), DG_FMT_E5M2: (torch.float8_e5m2, torch.uint8)}
+_GRANS = (64, 128, 256)
 
 
 def _check(t, name, dtypes, shape, device):
@@ -106,14 +115,7 @@ def _check(t, name, dtypes, shape, device):
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
 
 
-def dg_gemm_fp8_nt(a, b, sa, sb, out=None, gran: int = 128, stream=None):
-    """out[M,N] (bf16) = A[M,K] * B[N,K]^T with gran x gran FP32 block scales.
-
-    a: [M,K] float8_e4m3fn (or uint8 holding E4M3FN codes), b: [N,K] likewise,
-    sa: [ceil(M/gran), K/gran] float32, sb: [ceil(N/gran), K/gran] float32,
-    out: optional preallocated [M,N] bfloat16 (allocated when None).
-    Enqueued on ``stream`` (a torch.cuda.Stream; default: the current stream).
-    """
+def _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, where):
     if a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D")
     M, K = a.shape
@@ -121,10 +123,12 @@ def dg_gemm_fp8_nt(a, b, sa, sb, out=None, gran: int = 128, stream=None):
     dev = a.device
     if dev.type != "cuda":
         raise ValueError("a must be a GPU tensor")
-    if gran not in (64, 128) or K % gran:
-        raise ValueError("gran must be 64 or 128 and divide K")
-    _check(a, "a", _FP8, (M, K), dev)
-    _check(b, "b", _FP8, (N, K), dev)
+    if gran not in _GRANS or K % gran:
+        raise ValueError("gran must be 64, 128 or 256 and divide K")
+    if fmt_a not in _FP8_OF or fmt_b not in _FP8_OF:
+        raise ValueError("formats must be DG_FMT_E4M3 or DG_FMT_E5M2")
+    _check(a, "a", _FP8_OF[fmt_a], (M, K), dev)
+    _check(b, "b", _FP8_OF[fmt_b], (N, K), dev)
     _check(sa, "sa", (torch.float32,), ((M + gran - 1) // gran, K // gran), dev)
     _check(sb, "sb", (torch.float32,), ((N + gran - 1) // gran, K // gran), dev)
     if out is None:
@@ -132,44 +136,86 @@ def dg_gemm_fp8_nt(a, b, sa, sb, out=None, gran: int = 128, stream=None):
     _check(out, "out", (torch.bfloat16,), (M, N), dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
-        rc = _lib.dg_gemm_fp8_nt(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
-                                 M, N, K, gran, s.cuda_stream)
+        if fmt_a == DG_FMT_E4M3 and fmt_b == DG_FMT_E4M3 and where == "dg_gemm_fp8_nt":
+            rc = _lib.dg_gemm_fp8_nt(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
+                                     M, N, K, gran, s.cuda_stream)
+        else:
+            rc = _lib.dg_gemm_fp8_nt_fmt(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
+                                         M, N, K, gran, fmt_a, fmt_b, s.cuda_stream)
     if rc != DG_OK:
-        _raise(rc, "dg_gemm_fp8_nt")
+        _raise(rc, where)
     return out
 
 
-def dg_quantize_e4m3_blocks(x, gran: int = 128, q=None, scales=None, stream=None):
-    """Block-quantise x [rows, cols] float32 on the GPU -> (q uint8 [rows, cols], scales float32).
+def dg_gemm_fp8_nt(a, b, sa, sb, out=None, gran: int = 128, stream=None):
+    """out[M,N] (bf16) = A[M,K] * B[N,K]^T with gran x gran FP32 block scales.
 
-    Per gran x gran block: scale = amax / 448 (1.0 for an all-zero block) and
-    q = E4M3FN(x / scale), round to nearest even. ``scales`` has shape
-    [ceil(rows/gran), cols/gran]. The codes come back as uint8 holding E4M3FN
-    bytes (``q.view(torch.float8_e4m3fn)`` reinterprets them).
+    a: [M,K] float8_e4m3fn (or uint8 holding E4M3FN codes), b: [N,K] likewise,
+    sa: [ceil(M/gran), K/gran] float32, sb: [ceil(N/gran), K/gran] float32,
+    gran 64, 128 or 256, out: optional preallocated [M,N] bfloat16 (allocated
+    when None). Enqueued on ``stream`` (a torch.cuda.Stream; default: the
+    current stream).
     """
+    return _gemm(a, b, sa, sb, out, gran, DG_FMT_E4M3, DG_FMT_E4M3, stream, "dg_gemm_fp8_nt")
+
+
+def dg_gemm_fp8_nt_fmt(a, b, sa, sb, out=None, gran: int = 128, fmt_a: int = DG_FMT_E4M3,
+                       fmt_b: int = DG_FMT_E4M3, stream=None):
+    """dg_gemm_fp8_nt with each operand's FP8 format given (DG_FMT_E4M3 / DG_FMT_E5M2).
+
+    An E5M2 operand is float8_e5m2 (or uint8 holding E5M2 codes).
+    """
+    return _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, "dg_gemm_fp8_nt_fmt")
+
+
+def _quantize(x, gran, fmt, q, scales, stream, where):
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be a 2-D tensor")
     rows, cols = x.shape
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("x must be a GPU tensor")
-    if gran not in (64, 128) or cols % gran:
-        raise ValueError("gran must be 64 or 128 and divide cols")
+    if gran not in _GRANS or cols % gran:
+        raise ValueError("gran must be 64, 128 or 256 and divide cols")
+    if fmt not in _FP8_OF:
+        raise ValueError("fmt must be DG_FMT_E4M3 or DG_FMT_E5M2")
     _check(x, "x", (torch.float32,), (rows, cols), dev)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
     if scales is None:
         scales = torch.empty(((rows + gran - 1) // gran, cols // gran), dtype=torch.float32, device=dev)
-    _check(q, "q", _FP8, (rows, cols), dev)
+    _check(q, "q", _FP8_OF[fmt], (rows, cols), dev)
     _check(scales, "scales", (torch.float32,), ((rows + gran - 1) // gran, cols // gran), dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
-        rc = _lib.dg_quantize_e4m3_blocks(x.data_ptr(), rows, cols, gran, q.data_ptr(), scales.data_ptr(),
-                                          s.cuda_stream)
+        if fmt == DG_FMT_E4M3 and where == "dg_quantize_e4m3_blocks":
+            rc = _lib.dg_quantize_e4m3_blocks(x.data_ptr(), rows, cols, gran, q.data_ptr(), scales.data_ptr(),
+                                              s.cuda_stream)
+        else:
+            rc = _lib.dg_quantize_fp8_blocks(x.data_ptr(), rows, cols, gran, fmt, q.data_ptr(), scales.data_ptr(),
+                                             s.cuda_stream)
     if rc != DG_OK:
-        _raise(rc, "dg_quantize_e4m3_blocks")
+        _raise(rc, where)
     return q, scales
 
 
-__all__ = ["dg_gemm_fp8_nt", "dg_quantize_e4m3_blocks", "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError",
-           "DG_OK", "DG_EINVAL", "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH", "LIB_PATH"]
+def dg_quantize_e4m3_blocks(x, gran: int = 128, q=None, scales=None, stream=None):
+    """Block-quantise x [rows, cols] float32 on the GPU -> (q uint8 [rows, cols], scales float32).
+
+    Per gran x gran block (gran 64, 128 or 256): scale = amax / 448 (1.0 for
+    an all-zero block) and q = E4M3FN(x / scale), round to nearest even.
+    ``scales`` has shape [ceil(rows/gran), cols/gran]. The codes come back as
+    uint8 holding E4M3FN bytes (``q.view(torch.float8_e4m3fn)`` reinterprets
+    them).
+    """
+    return _quantize(x, gran, DG_FMT_E4M3, q, scales, stream, "dg_quantize_e4m3_blocks")
+
+
+def dg_quantize_fp8_blocks(x, gran: int = 128, fmt: int = DG_FMT_E4M3, q=None, scales=None, stream=None):
+    """dg_quantize_e4m3_blocks for either format; E5M2 uses scale = amax / 57344."""
+    return _quantize(x, gran, fmt, q, scales, stream, "dg_quantize_fp8_blocks")
+
+
+__all__ = ["dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "dg_quantize_e4m3_blocks", "dg_quantize_fp8_blocks",
+           "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError", "DG_OK", "DG_EINVAL",
+           "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH", "DG_FMT_E4M3", "DG_FMT_E5M2", "LIB_PATH"]

@@ -16,7 +16,7 @@
 
 #include "../../include/dg.h"
 #include "gemm_fp8_nt.h"
-#include "quant_e4m3.h"
+#include "quant_fp8.h"
 
 namespace {
 
@@ -57,10 +57,14 @@ void check_device(int dev) {
 int validate(int64_t M, int64_t N, int64_t K, int gran) {
   if (M <= 0 || N <= 0 || K <= 0) return DG_EINVAL;
   if (M > DG_MAX_DIM || N > DG_MAX_DIM || K > DG_MAX_DIM) return DG_EINVAL;
-  if (gran != 64 && gran != 128) return DG_EINVAL;
+  if (gran != 64 && gran != 128 && gran != 256) return DG_EINVAL;
   if (K % gran != 0) return DG_EINVAL;
   return DG_OK;
 }
+
+// K segment the kernels contract before each promotion: g itself for 64 and
+// 128; g = 256 runs the 128 kernels with one scale factor per two segments.
+int kernel_gran(int gran) { return gran > 128 ? 128 : gran; }
 
 const dg::KernelEntry* find(int cls, int gran) {
   for (int i = 0; i < dg::kTableSize; ++i)
@@ -99,8 +103,9 @@ int64_t splits_for(const dg::KernelEntry* e, int64_t tiles, int64_t nsteps) {
   return std::max<int64_t>(ks, 1);
 }
 
-Plan plan(int64_t M, int64_t N, int64_t K, int gran) {
+Plan plan(int64_t M, int64_t N, int64_t K, int sgran) {
   Plan p{nullptr, 1, 0};
+  const int gran = kernel_gran(sgran);
   const int64_t nsteps = (K + 127) / 128;
   const int force = forced_tile();
   if (force >= 0) {
@@ -174,6 +179,82 @@ int device_ready(int* dev_out = nullptr) {
 
 }  // namespace
 
+namespace {
+
+int gemm(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M, int64_t N, int64_t K,
+         int gran, int fmt_a, int fmt_b, void* stream) {
+  if (!a || !b || !sa || !sb || !out) return DG_EINVAL;
+  if ((fmt_a != DG_FMT_E4M3 && fmt_a != DG_FMT_E5M2) || (fmt_b != DG_FMT_E4M3 && fmt_b != DG_FMT_E5M2))
+    return DG_EINVAL;
+  int rc = validate(M, N, K, gran);
+  if (rc != DG_OK) return rc;
+  if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)sa & 3) || ((uintptr_t)sb & 3) ||
+      ((uintptr_t)out & 1))
+    return DG_EALIGN;
+  Plan pl = plan(M, N, K, gran);
+  if (!pl.e || pl.tiles * pl.ksplit > 0x7fffffff) return DG_EINVAL;
+
+  int dev = 0;
+  rc = device_ready(&dev);
+  if (rc != DG_OK) return rc;
+  if (pl.ksplit > 1) {
+    std::call_once(g_ws_once[dev], alloc_workspace, dev);
+    if (!g_ws[dev]) pl.ksplit = 1;  // no workspace: the same kernel over the whole K
+  }
+  const dg::KernelEntry* e = pl.e;
+
+  dg::GemmArgs p;
+  p.a = static_cast<const uint8_t*>(a);
+  p.b = static_cast<const uint8_t*>(b);
+  p.sa = sa;
+  p.sb = sb;
+  p.out = static_cast<uint16_t*>(out);
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.gran = kernel_gran(gran);
+  p.sshift = gran == 256 ? 1 : 0;
+  p.fmt = (fmt_a == DG_FMT_E5M2 ? 1 : 0) | (fmt_b == DG_FMT_E5M2 ? 2 : 0);
+  p.vec_store = (((uintptr_t)out & 15) == 0 && N % 8 == 0) ? 1 : 0;
+  p.ksplit = pl.ksplit;
+  p.ws = pl.ksplit > 1 ? g_ws[dev] : nullptr;
+  p.counters = pl.ksplit > 1 ? g_counters[dev] : nullptr;
+  if (log_enabled())
+    std::fprintf(stderr,
+                 "dg_gemm_fp8_nt M=%lld N=%lld K=%lld g=%d fmt=%d,%d -> kernel %d (%dx%d, %d stages, %d waves) "
+                 "ksplit %d grid %lld\n",
+                 (long long)M, (long long)N, (long long)K, gran, fmt_a, fmt_b, e->id, e->bm, e->bn, e->stages,
+                 e->waves, pl.ksplit, (long long)(pl.tiles * pl.ksplit));
+  t_last_hip = e->launch(p, static_cast<hipStream_t>(stream));
+  return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
+}
+
+int quantize(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q, float* scales, void* stream) {
+  if (!x || !q || !scales) return DG_EINVAL;
+  if (fmt != DG_FMT_E4M3 && fmt != DG_FMT_E5M2) return DG_EINVAL;
+  if (rows <= 0 || cols <= 0 || rows > DG_MAX_DIM || cols > DG_MAX_DIM) return DG_EINVAL;
+  if ((gran != 64 && gran != 128 && gran != 256) || cols % gran != 0) return DG_EINVAL;
+  if (((rows + gran - 1) / gran) * (cols / gran) > 0x7fffffff) return DG_EINVAL;
+  if (((uintptr_t)x & 15) || ((uintptr_t)q & 3) || ((uintptr_t)scales & 3)) return DG_EALIGN;
+  const int rc = device_ready();
+  if (rc != DG_OK) return rc;
+  dg::QuantArgs p;
+  p.x = x;
+  p.q = static_cast<uint8_t*>(q);
+  p.scales = scales;
+  p.rows = rows;
+  p.cols = cols;
+  p.gran = gran;
+  p.fmt = fmt;
+  if (log_enabled())
+    std::fprintf(stderr, "dg_quantize_fp8_blocks rows=%lld cols=%lld g=%d fmt=%d\n", (long long)rows,
+                 (long long)cols, gran, fmt);
+  t_last_hip = dg::launch_quant(p, static_cast<hipStream_t>(stream));
+  return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
+}
+
+}  // namespace
+
 extern "C" {
 
 int dg_version(void) { return DG_VERSION; }
@@ -181,7 +262,9 @@ int dg_version(void) { return DG_VERSION; }
 const char* dg_strerror(int code) {
   switch (code) {
     case DG_OK: return "success";
-    case DG_EINVAL: return "invalid argument (null pointer, bad dimension, K not a multiple of gran, or gran not 64/128)";
+    case DG_EINVAL:
+      return "invalid argument (null pointer, bad dimension, K not a multiple of gran, gran not 64/128/256, "
+             "or a format code other than DG_FMT_E4M3/DG_FMT_E5M2)";
     case DG_EALIGN: return "misaligned pointer (a, b need 16 bytes; sa, sb 4 bytes; out 2 bytes)";
     case DG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
     case DG_ELAUNCH:
@@ -210,68 +293,22 @@ int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info)
 
 int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
                    int64_t N, int64_t K, int gran, void* stream) {
-  if (!a || !b || !sa || !sb || !out) return DG_EINVAL;
-  int rc = validate(M, N, K, gran);
-  if (rc != DG_OK) return rc;
-  if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)sa & 3) || ((uintptr_t)sb & 3) ||
-      ((uintptr_t)out & 1))
-    return DG_EALIGN;
-  Plan pl = plan(M, N, K, gran);
-  if (!pl.e || pl.tiles * pl.ksplit > 0x7fffffff) return DG_EINVAL;
+  return gemm(a, b, sa, sb, out, M, N, K, gran, DG_FMT_E4M3, DG_FMT_E4M3, stream);
+}
 
-  int dev = 0;
-  rc = device_ready(&dev);
-  if (rc != DG_OK) return rc;
-  if (pl.ksplit > 1) {
-    std::call_once(g_ws_once[dev], alloc_workspace, dev);
-    if (!g_ws[dev]) pl.ksplit = 1;  // no workspace: the same kernel over the whole K
-  }
-  const dg::KernelEntry* e = pl.e;
+int dg_gemm_fp8_nt_fmt(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
+                       int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, void* stream) {
+  return gemm(a, b, sa, sb, out, M, N, K, gran, fmt_a, fmt_b, stream);
+}
 
-  dg::GemmArgs p;
-  p.a = static_cast<const uint8_t*>(a);
-  p.b = static_cast<const uint8_t*>(b);
-  p.sa = sa;
-  p.sb = sb;
-  p.out = static_cast<uint16_t*>(out);
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.gran = gran;
-  p.vec_store = (((uintptr_t)out & 15) == 0 && N % 8 == 0) ? 1 : 0;
-  p.ksplit = pl.ksplit;
-  p.ws = pl.ksplit > 1 ? g_ws[dev] : nullptr;
-  p.counters = pl.ksplit > 1 ? g_counters[dev] : nullptr;
-  if (log_enabled())
-    std::fprintf(stderr,
-                 "dg_gemm_fp8_nt M=%lld N=%lld K=%lld g=%d -> kernel %d (%dx%d, %d stages, %d waves) "
-                 "ksplit %d grid %lld\n",
-                 (long long)M, (long long)N, (long long)K, gran, e->id, e->bm, e->bn, e->stages, e->waves,
-                 pl.ksplit, (long long)(pl.tiles * pl.ksplit));
-  t_last_hip = e->launch(p, static_cast<hipStream_t>(stream));
-  return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
+int dg_quantize_fp8_blocks(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q, float* scales,
+                           void* stream) {
+  return quantize(x, rows, cols, gran, fmt, q, scales, stream);
 }
 
 int dg_quantize_e4m3_blocks(const float* x, int64_t rows, int64_t cols, int gran, void* q, float* scales,
                             void* stream) {
-  if (!x || !q || !scales) return DG_EINVAL;
-  if (rows <= 0 || cols <= 0 || rows > DG_MAX_DIM || cols > DG_MAX_DIM) return DG_EINVAL;
-  if ((gran != 64 && gran != 128) || cols % gran != 0) return DG_EINVAL;
-  if (((rows + gran - 1) / gran) * (cols / gran) > 0x7fffffff) return DG_EINVAL;
-  if (((uintptr_t)x & 15) || ((uintptr_t)q & 3) || ((uintptr_t)scales & 3)) return DG_EALIGN;
-  const int rc = device_ready();
-  if (rc != DG_OK) return rc;
-  dg::QuantArgs p;
-  p.x = x;
-  p.q = static_cast<uint8_t*>(q);
-  p.scales = scales;
-  p.rows = rows;
-  p.cols = cols;
-  p.gran = gran;
-  if (log_enabled())
-    std::fprintf(stderr, "dg_quantize_e4m3_blocks rows=%lld cols=%lld g=%d\n", (long long)rows, (long long)cols, gran);
-  t_last_hip = dg::launch_quant_e4m3(p, static_cast<hipStream_t>(stream));
-  return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
+  return quantize(x, rows, cols, gran, DG_FMT_E4M3, q, scales, stream);
 }
 
 }  // extern "C"

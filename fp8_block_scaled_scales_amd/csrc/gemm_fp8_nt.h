@@ -13,7 +13,9 @@ struct GemmArgs {
   const float* sb;
   uint16_t* out;
   int64_t M, N, K;
-  int gran;
+  int gran;       // K segment of the kernel (64 or 128)
+  int sshift;     // scale blocks are (gran << sshift) square: 1 for g = 256 on the gran-128 kernels
+  int fmt;        // bit 0: A is E5M2 (else E4M3); bit 1: B is E5M2
   int vec_store;  // out is 16-byte aligned and N % 8 == 0: full-row chunks use 16-byte stores
   int ksplit;     // workgroups per output tile along K (1 = no split)
   float* ws;      // split-K partial tiles, tiles * ksplit * bm * bn floats (ksplit > 1)

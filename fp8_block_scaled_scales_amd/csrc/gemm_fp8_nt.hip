@@ -48,9 +48,11 @@ __device__ __forceinline__ v8i frag32(const uint8_t* slab, int row, int c0) {
   return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
+// FMT bit 0: A is E5M2 (else E4M3), bit 1: B is E5M2 -- the instruction's
+// operand-format fields (0 = E4M3, 1 = E5M2); no block-exponent scaling.
+template <int FMT>
 __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
-  // E4M3 x E4M3 (format code 0 for both operands), no block-exponent scaling.
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT & 1, FMT >> 1, 0, 0, 0, 0);
 }
 
 // Wait until at most `steps` later pipeline steps' loads (LOADS each) are
@@ -73,11 +75,15 @@ __device__ __forceinline__ void wait_steps(int steps) {
 // last to arrive (per-tile arrival counter) adds the partials in split order
 // (so the result does not depend on which arrives last), resets the counter
 // and writes the BF16 tile. ksplit == 1 skips all of this.
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT>
+//
+// G is the K segment contracted before each promotion; the scale blocks are
+// sg x sg with sg = G << sshift (g = 256 runs G = 128 with one factor per two
+// segments).
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ b, const float* __restrict__ sa,
     const float* __restrict__ sb, uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
-    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, uint32_t* __restrict__ counters) {
+    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, uint32_t* __restrict__ counters, int sshift) {
   constexpr int NWAVES = WM * WN;
   constexpr int NT = 64 * NWAVES;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
@@ -113,12 +119,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
   // Scale rows of this wave's sub-tiles. A sub-tile lies inside one g-block
   // (g >= 32, sub-tiles aligned to 32); sub-tiles past the edge clamp to the
   // last block row so the index stays inside the scale tensor.
+  const int sg = G << sshift, nks = K / sg;  // scale blocks
   const float* sa_row[TM];
   const float* sb_row[TN];
 #pragma unroll
-  for (int t = 0; t < TM; ++t) sa_row[t] = sa + (int64_t)min((m0 + wm * WTM + t * 32) / G, (M - 1) / G) * nkb;
+  for (int t = 0; t < TM; ++t) sa_row[t] = sa + (int64_t)min((m0 + wm * WTM + t * 32) / sg, (M - 1) / sg) * nks;
 #pragma unroll
-  for (int t = 0; t < TN; ++t) sb_row[t] = sb + (int64_t)min((n0 + wn * WTN + t * 32) / G, (N - 1) / G) * nkb;
+  for (int t = 0; t < TN; ++t) sb_row[t] = sb + (int64_t)min((n0 + wn * WTN + t * 32) / sg, (N - 1) / sg) * nks;
 
   v16f acc[TM][TN];
 #pragma unroll
@@ -169,15 +176,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
       }
       float sbv[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) sbv[j] = sb_row[j][kb];
+      for (int j = 0; j < TN; ++j) sbv[j] = sb_row[j][kb >> sshift];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const float sav = sa_row[i][kb];
+        const float sav = sa_row[i][kb >> sshift];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          v16f p = mfma_fp8(af[i][0], bfr[j][0], (v16f){});
+          v16f p = mfma_fp8<FMT>(af[i][0], bfr[j][0], (v16f){});
 #pragma unroll
-          for (int ks = 1; ks < KSTEPS; ++ks) p = mfma_fp8(af[i][ks], bfr[j][ks], p);
+          for (int ks = 1; ks < KSTEPS; ++ks) p = mfma_fp8<FMT>(af[i][ks], bfr[j][ks], p);
           const float sc = sav * sbv[j];
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc, acc[i][j][v]);
@@ -315,14 +322,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
 
 // ---- launch table -------------------------------------------------------------
 
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT>
+static hipError_t launch_tiled_fmt(const GemmArgs& p, hipStream_t stream) {
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT>),
+                     dim3(tiles_m * tiles_n * p.ksplit), dim3(64 * WM * WN), 0, stream, p.a, p.b, p.sa, p.sb, p.out,
+                     (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.ksplit, p.ws, p.counters,
+                     p.sshift);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT>
 static hipError_t launch_tiled(const GemmArgs& p, hipStream_t stream) {
-  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  if (!SPLIT && p.ksplit != 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT>), dim3(tiles_m * tiles_n * p.ksplit),
-                     dim3(64 * WM * WN), 0, stream, p.a, p.b, p.sa, p.sb, p.out, (int)p.M, (int)p.N,
-                     (int)p.K, tiles_m, tiles_n, p.vec_store, p.ksplit, p.ws, p.counters);
-  return hipGetLastError();
+  if ((!SPLIT && p.ksplit != 1) || p.sshift < 0 || p.sshift > 1) return hipErrorInvalidValue;
+  switch (p.fmt) {
+    case 0: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 0>(p, stream);
+    case 1: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 1>(p, stream);
+    case 2: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 2>(p, stream);
+    case 3: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 3>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 KernelEntry kTable[] = {

@@ -68,12 +68,16 @@ __device__ __forceinline__ v8i frag(const uint8_t* slab, int row, int c0) {
   return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
+// FMT bit 0: A is E5M2 (else E4M3), bit 1: B is E5M2; the instructions'
+// operand-format fields (0 = E4M3, 1 = E5M2), no block-exponent scaling.
+template <int FMT>
 __device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, (v4f){}, 0, 0, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, (v4f){}, FMT & 1, FMT >> 1, 0, 0, 0, 0);
 }
 
+template <int FMT>
 __device__ __forceinline__ v16f mfma32(const v8i& a, const v8i& b) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, (v16f){}, 0, 0, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, (v16f){}, FMT & 1, FMT >> 1, 0, 0, 0, 0);
 }
 
 template <int G, int WTM, int WTN>
@@ -87,11 +91,14 @@ struct Acc<64, WTM, WTN> {
   v16f t[WTM / 32][WTN / 32];
 };
 
-template <int G, int BN, int WM, int GROUP_M>
+// G is the K segment the matrix cores contract before each promotion (64 or
+// 128). The scale blocks are sg x sg with sg = G << sshift: for g = 256 the
+// G = 128 kernel promotes every 128 K with its 256-block's factor.
+template <int G, int BN, int WM, int GROUP_M, int FMT>
 __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
                                                       const float* __restrict__ sa, const float* __restrict__ sb,
                                                       uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
-                                                      int tiles_n, int vec_store) {
+                                                      int tiles_n, int vec_store, int sshift) {
   static_assert(G == 64 || G == 128, "granularity");
   constexpr int WN = NW / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -117,21 +124,22 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   const v4i ra = rsrc_words(a + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * uK);
   const v4i rb = rsrc_words(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
 
-  const int nkb = K / G;
+  const int nkb = K / G;  // K segments
+  const int sg = G << sshift, nks = K / sg;  // scale blocks
   const int nsteps = (K + BK - 1) / BK;
 
   // Scale rows of this wave. Blocks past the edge clamp to the last block
-  // (their data is zero). g = 128: one A block; the wave's columns may cross
+  // (their data is zero). g >= 128: one A block; the wave's columns may cross
   // into a second B block after jsplit 16-column blocks. g = 64: A blocks of
   // rows wr0 and wr0 + 64, one B block.
   const int wr0 = m0 + wm * WTM, wc0 = n0 + wn * WTN;
-  const int lastm = (M - 1) / G, lastn = (N - 1) / G;
-  const float* const sa0 = sa + (int64_t)min(wr0 / G, lastm) * nkb;
-  const float* const sa1 = sa + (int64_t)min((wr0 + 64) / G, lastm) * nkb;
-  const int bn0 = wc0 / G;
-  const float* const sb0 = sb + (int64_t)min(bn0, lastn) * nkb;
-  const float* const sb1 = sb + (int64_t)min(bn0 + 1, lastn) * nkb;
-  const int jsplit = ((bn0 + 1) * G - wc0) / 16;  // g = 128: column blocks in the first B block
+  const int lastm = (M - 1) / sg, lastn = (N - 1) / sg;
+  const float* const sa0 = sa + (int64_t)min(wr0 / sg, lastm) * nks;
+  const float* const sa1 = sa + (int64_t)min((wr0 + 64) / sg, lastm) * nks;
+  const int bn0 = wc0 / sg;
+  const float* const sb0 = sb + (int64_t)min(bn0, lastn) * nks;
+  const float* const sb1 = sb + (int64_t)min(bn0 + 1, lastn) * nks;
+  const int jsplit = ((bn0 + 1) * sg - wc0) / 16;  // g >= 128: column blocks in the first B block
 
   Acc<G, WTM, WTN> acc;
   if constexpr (G == 128) {
@@ -176,8 +184,9 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       constexpr int LAG = 3;
       constexpr int NJ = WTN / 16, SLOTS = (WTM / 16) * NJ, DSLOT = SLOTS / 4;
       const int r16 = lane & 15, q = lane >> 4;
-      const float a_s = sa0[s];
-      const float sc0 = a_s * sb0[s], sc1 = a_s * sb1[s];
+      const int ksc = s >> sshift;
+      const float a_s = sa0[ksc];
+      const float sc0 = a_s * sb0[ksc], sc1 = a_s * sb1[ksc];
       v8i bf[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bf[j] = frag(Bs, j * 16 + r16, 2 * q);
@@ -190,7 +199,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
         if (t == DSLOT) issue_next(1);
         if (t < SLOTS) {
           if (j == 0 && i + 1 < WTM / 16) a_nxt = frag(As, (i + 1) * 16 + r16, 2 * q);
-          pr[t % (LAG + 1)] = mfma16(a_cur, bf[j]);
+          pr[t % (LAG + 1)] = mfma16<FMT>(a_cur, bf[j]);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (t >= LAG) {
@@ -225,7 +234,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
             const int i = t / NJ, j = t % NJ;
             if (t < SLOTS) {
               if (j == 0 && i + 1 < WTM / 32) a_nxt = frag(As, (i + 1) * 32 + r32, 4 * h + 2 * h2);
-              pr[t % (LAG + 1)] = mfma32(a_cur, bf[j]);
+              pr[t % (LAG + 1)] = mfma32<FMT>(a_cur, bf[j]);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (t >= LAG) {
@@ -292,13 +301,24 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   }
 }
 
+template <int G, int BN, int WM, int FMT>
+hipError_t launch_fmt(const GemmArgs& p, hipStream_t stream) {
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_fp8_nt_big<G, BN, WM, 4, FMT>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, p.a, p.b,
+                     p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.sshift);
+  return hipGetLastError();
+}
+
 template <int G, int BN, int WM>
 hipError_t launch(const GemmArgs& p, hipStream_t stream) {
-  if (p.ksplit != 1) return hipErrorInvalidValue;
-  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_big<G, BN, WM, 4>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, p.a, p.b, p.sa,
-                     p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store);
-  return hipGetLastError();
+  if (p.ksplit != 1 || p.sshift < 0 || p.sshift > 1) return hipErrorInvalidValue;
+  switch (p.fmt) {
+    case 0: return launch_fmt<G, BN, WM, 0>(p, stream);
+    case 1: return launch_fmt<G, BN, WM, 1>(p, stream);
+    case 2: return launch_fmt<G, BN, WM, 2>(p, stream);
+    case 3: return launch_fmt<G, BN, WM, 3>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace big

@@ -56,13 +56,16 @@ __device__ __forceinline__ v8i frag(const uint8_t* slab, int row, int c0) {
   return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-template <int G>
+// G: K segment contracted before each promotion; scale blocks sg = G << sshift
+// (g = 256 runs the G = 128 kernel with one factor per two segments). FMT bit
+// 0: A is E5M2 (else E4M3), bit 1: B is E5M2.
+template <int G, int FMT>
 __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __restrict__ a,
                                                               const uint8_t* __restrict__ b,
                                                               const float* __restrict__ sa,
                                                               const float* __restrict__ sb,
                                                               uint16_t* __restrict__ out, int M, int N, int K,
-                                                              int tiles_m, int tiles_n) {
+                                                              int tiles_m, int tiles_n, int sshift) {
   static_assert(G == 64 || G == 128, "granularity");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NW * WAVE_LDS];
 
@@ -76,10 +79,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
   const v4i rb = rsrc_words(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
 
   const int nkb = K / G;
+  const int sg = G << sshift, nks = K / sg;
   const int nsteps = (K + BK - 1) / BK;
   // 32 rows starting at a multiple of 32 lie in one g-block (g >= 64).
-  const float* const sa_row = sa + (int64_t)(m0 / G) * nkb;
-  const float* const sb_row = sb + (int64_t)(n0 / G) * nkb;
+  const float* const sa_row = sa + (int64_t)(m0 / sg) * nks;
+  const float* const sb_row = sb + (int64_t)(n0 / sg) * nks;
 
   uint8_t* const a_ring = smem + wave * WAVE_LDS;
   uint8_t* const b_ring = a_ring + A_SLOTS * A_SLAB;
@@ -128,14 +132,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
           // the segment is the whole step: chain both halves, then promote once
           const v8i af1 = frag(As, r32, c0 + 4);
           const v8i bf1 = frag(Bs, r32, c0 + 4);
-          v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, (v16f){}, 0, 0, 0, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af1, bf1, p, 0, 0, 0, 0, 0, 0);
-          const float sc = sa_row[kb] * sb_row[kb];
+          v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, (v16f){}, FMT & 1, FMT >> 1, 0, 0, 0, 0);
+          p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af1, bf1, p, FMT & 1, FMT >> 1, 0, 0, 0, 0);
+          const float sc = sa_row[kb >> sshift] * sb_row[kb >> sshift];
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[v] = __builtin_fmaf(p[v], sc, acc[v]);
         }
       } else {
-        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, (v16f){}, 0, 0, 0, 0, 0, 0);
+        const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, (v16f){}, FMT & 1, FMT >> 1, 0, 0, 0, 0);
         const float sc = sa_row[kb] * sb_row[kb];
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[v] = __builtin_fmaf(p[v], sc, acc[v]);
@@ -166,13 +170,24 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
   }
 }
 
+template <int G, int FMT>
+hipError_t launch_fmt(const GemmArgs& p, hipStream_t stream) {
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_fp8_nt_stream<G, FMT>), dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream, p.a, p.b,
+                     p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.sshift);
+  return hipGetLastError();
+}
+
 template <int G>
 hipError_t launch(const GemmArgs& p, hipStream_t stream) {
-  if (p.ksplit != 1) return hipErrorInvalidValue;
-  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_stream<G>), dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream, p.a, p.b, p.sa,
-                     p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n);
-  return hipGetLastError();
+  if (p.ksplit != 1 || p.sshift < 0 || p.sshift > 1) return hipErrorInvalidValue;
+  switch (p.fmt) {
+    case 0: return launch_fmt<G, 0>(p, stream);
+    case 1: return launch_fmt<G, 1>(p, stream);
+    case 2: return launch_fmt<G, 2>(p, stream);
+    case 3: return launch_fmt<G, 3>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace stream

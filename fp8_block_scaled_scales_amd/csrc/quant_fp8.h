@@ -11,9 +11,10 @@ struct QuantArgs {
   uint8_t* q;
   float* scales;
   int64_t rows, cols;
-  int gran;
+  int gran;  // 64, 128 or 256
+  int fmt;   // 0 = E4M3FN, 1 = E5M2
 };
 
-hipError_t launch_quant_e4m3(const QuantArgs& p, hipStream_t stream);
+hipError_t launch_quant(const QuantArgs& p, hipStream_t stream);
 
 }  // namespace dg

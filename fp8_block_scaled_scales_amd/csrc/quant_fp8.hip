@@ -1,0 +1,111 @@
+// Block quantiser FP32 -> FP8 (E4M3FN or E5M2) with one FP32 scale per g x g
+// block, g = 64, 128 or 256, for gfx950. It produces the GEMM's inputs: the
+// pages place quantisation outside the GEMM, say that activations must be
+// quantised online and that the granularity must equal the GEMM's
+// (DeepGEMM实战 §4.4), that one factor per block maps the block into FP8 range
+// (§2.2) by dividing (§5.2), and name E4M3 and E5M2 as the formats (§2.2).
+//
+// Per block: amax = max |x| over the elements present (edge blocks past the
+// last row are partial), scale = amax / fmax (FP32, correctly rounded; 1.0
+// for an all-zero block; fmax = 448 for E4M3, 57344 for E5M2), code =
+// FP8(x / scale) with a correctly rounded FP32 divide and the hardware's
+// round-to-nearest-even conversion. Because |x / scale| <= fmax up to one
+// rounding, which still rounds to fmax, no value can overflow the format.
+//
+// One workgroup per block, 256 threads (1024 for g = 256). The block (64 KB
+// for g = 128) stays in registers between the amax pass and the encode pass,
+// so x is read from HBM once: the kernel is bound by HBM bandwidth (4 bytes
+// in, 1 byte out per element).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "quant_fp8.h"
+
+namespace dg {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int G, int FMT>
+__global__ __launch_bounds__(G == 256 ? 1024 : 256) void quant_fp8_blocks(const float* __restrict__ x,
+                                                                          uint8_t* __restrict__ q,
+                                                                          float* __restrict__ scales, int rows,
+                                                                          int cols) {
+  constexpr int NT = G == 256 ? 1024 : 256;
+  constexpr float FMAX = FMT == 1 ? 57344.0f : 448.0f;
+  constexpr int ROW_V4 = G / 4;              // float4 per block row
+  constexpr int ROWS_PER_PASS = NT / ROW_V4;  // block rows covered by one pass
+  constexpr int PASSES = G / ROWS_PER_PASS;
+  __shared__ float red[NT / 64];
+
+  const int ncb = cols / G;
+  const int rb = blockIdx.x / ncb, cb = blockIdx.x % ncb;
+  const int t = threadIdx.x;
+  const int rsub = t / ROW_V4, c4 = t % ROW_V4;
+  const int col = cb * G + c4 * 4;
+
+  v4f v[PASSES];
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int r = rb * G + p * ROWS_PER_PASS + rsub;
+    if (r < rows) {
+      v[p] = *reinterpret_cast<const v4f*>(x + (int64_t)r * cols + col);
+    } else {
+      v[p] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w))));
+  }
+  // max is exact and order-free: wave butterfly, then across the waves
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
+  const float scale = amax > 0.0f ? amax / FMAX : 1.0f;
+  if (t == 0) scales[blockIdx.x] = scale;
+
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int r = rb * G + p * ROWS_PER_PASS + rsub;
+    if (r < rows) {
+      // v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 pack two E4M3 / E5M2 codes into
+      // the low or high 16 bits.
+      int packed;
+      if constexpr (FMT == 1) {
+        packed = __builtin_amdgcn_cvt_pk_bf8_f32(v[p].x / scale, v[p].y / scale, 0, false);
+        packed = __builtin_amdgcn_cvt_pk_bf8_f32(v[p].z / scale, v[p].w / scale, packed, true);
+      } else {
+        packed = __builtin_amdgcn_cvt_pk_fp8_f32(v[p].x / scale, v[p].y / scale, 0, false);
+        packed = __builtin_amdgcn_cvt_pk_fp8_f32(v[p].z / scale, v[p].w / scale, packed, true);
+      }
+      *reinterpret_cast<int*>(q + (int64_t)r * cols + col) = packed;
+    }
+  }
+}
+
+template <int G, int FMT>
+static hipError_t launch_g(const QuantArgs& p, hipStream_t stream) {
+  const int64_t nblocks = ((p.rows + G - 1) / G) * (p.cols / G);
+  hipLaunchKernelGGL((quant_fp8_blocks<G, FMT>), dim3((unsigned)nblocks), dim3(G == 256 ? 1024 : 256), 0, stream,
+                     p.x, p.q, p.scales, (int)p.rows, (int)p.cols);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_f(const QuantArgs& p, hipStream_t stream) {
+  switch (p.gran) {
+    case 64: return launch_g<64, FMT>(p, stream);
+    case 128: return launch_g<128, FMT>(p, stream);
+    case 256: return launch_g<256, FMT>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_quant(const QuantArgs& p, hipStream_t stream) {
+  return p.fmt == 1 ? launch_f<1>(p, stream) : launch_f<0>(p, stream);
+}
+
+}  // namespace dg

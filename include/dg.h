@@ -57,8 +57,11 @@ extern "C" {
  *   out  BF16 result, [M,N] row-major (ldc = N), fully overwritten. 2-byte
  *        aligned; must not overlap the inputs.
  *   M, N, K  > 0 and <= DG_MAX_DIM; K a multiple of gran.
- *   gran block granularity g: 64 or 128 (the pages' 64x64 and 128x128
- *        choices, DeepGEMM实战 §3.1).
+ *   gran block granularity g: 64, 128 or 256 (the pages' 64x64, 128x128 and
+ *        256x256 choices, DeepGEMM实战 §3.1). For 256 the kernels promote
+ *        every 128 K (each half of a 256 segment is accumulated in FP32 and
+ *        added with the block's factor), so results match the one-segment
+ *        definition up to FP32 rounding, inside the stated tolerance.
  *   stream hipStream_t to enqueue on (NULL = default stream).
  *
  * Rows of A beyond M and rows of B beyond N are never read, and nothing
@@ -69,6 +72,22 @@ extern "C" {
  */
 int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* sb, void* out,
                    int64_t M, int64_t N, int64_t K, int gran, void* stream);
+
+/* FP8 formats of the operands (DeepGEMM实战 §2.2 names both as the inputs).
+ * E5M2 is the OCP format torch.float8_e5m2 implements: bias 15, subnormals
+ * m/4 * 2^-14, largest finite 57344, exponent field 31 = inf/NaN. */
+#define DG_FMT_E4M3 0
+#define DG_FMT_E5M2 1
+
+/*
+ * dg_gemm_fp8_nt_fmt - dg_gemm_fp8_nt with each operand's format given:
+ * fmt_a, fmt_b each DG_FMT_E4M3 or DG_FMT_E5M2 (any of the four pairs).
+ * Everything else, including layouts, scales, gran and status codes, is as
+ * for dg_gemm_fp8_nt; (DG_FMT_E4M3, DG_FMT_E4M3) is that call. Codes that
+ * decode to infinity or NaN give unspecified results.
+ */
+int dg_gemm_fp8_nt_fmt(const void* a, const void* b, const float* sa, const float* sb, void* out,
+                       int64_t M, int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, void* stream);
 
 /* The tile-table entry a call with these sizes would use. */
 typedef struct dg_tile_info {
@@ -98,7 +117,8 @@ int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info)
  *   x       FP32 [rows][cols] row-major, 16-byte aligned.
  *   q       E4M3FN codes out, [rows][cols] row-major, 4-byte aligned.
  *   scales  FP32 out, [ceil(rows/gran)][cols/gran] row-major, 4-byte aligned.
- *   rows, cols > 0 and <= DG_MAX_DIM; cols a multiple of gran; gran 64 or 128.
+ *   rows, cols > 0 and <= DG_MAX_DIM; cols a multiple of gran; gran 64, 128
+ *   or 256.
  *
  * Per gran x gran block (rows past the end make edge blocks partial):
  * amax = max |x| over present elements, scale = amax / 448 in FP32 (1.0 for
@@ -108,6 +128,14 @@ int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info)
  */
 int dg_quantize_e4m3_blocks(const float* x, int64_t rows, int64_t cols, int gran, void* q, float* scales,
                             void* stream);
+
+/*
+ * dg_quantize_fp8_blocks - dg_quantize_e4m3_blocks for either format: fmt
+ * DG_FMT_E4M3 (scale = amax / 448) or DG_FMT_E5M2 (scale = amax / 57344,
+ * codes E5M2 with round-to-nearest-even). Same arguments otherwise.
+ */
+int dg_quantize_fp8_blocks(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q,
+                           float* scales, void* stream);
 
 /* Text for a status code (for DG_ELAUNCH: the last HIP error on this thread). */
 const char* dg_strerror(int code);

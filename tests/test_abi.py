@@ -56,7 +56,7 @@ def _call(dg, a=A, b=B, sa=SA, sb=SB, out=OUT, M=256, N=256, K=256, g=128):
 
 @pytest.mark.parametrize("kw", [dict(a=0), dict(b=0), dict(sa=0), dict(sb=0), dict(out=0),
                                 dict(M=0), dict(N=0), dict(K=0), dict(M=-5), dict(K=-128),
-                                dict(K=192), dict(K=100, g=64), dict(g=96), dict(g=256), dict(g=0),
+                                dict(K=192), dict(K=100, g=64), dict(g=96), dict(g=512), dict(K=384, g=256), dict(g=0),
                                 dict(M=(1 << 24) + 1), dict(K=1 << 25)])
 def test_einval(dg, kw):
     assert _call(dg, **kw) == dg.DG_EINVAL
@@ -65,6 +65,27 @@ def test_einval(dg, kw):
 @pytest.mark.parametrize("kw", [dict(a=A + 8), dict(b=B + 4), dict(sa=SA + 2), dict(sb=SB + 1), dict(out=OUT + 1)])
 def test_ealign(dg, kw):
     assert _call(dg, **kw) == dg.DG_EALIGN
+
+
+@pytest.mark.parametrize("fa,fb,kw", [(2, 0, {}), (0, -1, {}), (1, 7, {}), (1, 1, dict(K=384, g=256)),
+                                      (0, 1, dict(a=0)), (1, 0, dict(g=32))])
+def test_fmt_einval(dg, fa, fb, kw):
+    args = dict(a=A, b=B, sa=SA, sb=SB, out=OUT, M=256, N=256, K=256, g=128)
+    args.update(kw)
+    assert dg.lib.dg_gemm_fp8_nt_fmt(args["a"], args["b"], args["sa"], args["sb"], args["out"], args["M"], args["N"],
+                                     args["K"], args["g"], fa, fb, None) == dg.DG_EINVAL
+
+
+@pytest.mark.parametrize("fmt,g,cols", [(2, 128, 256), (-1, 128, 256), (1, 96, 192), (0, 256, 384)])
+def test_quantize_einval(dg, fmt, g, cols):
+    assert dg.lib.dg_quantize_fp8_blocks(A, 64, cols, g, fmt, B, SA, None) == dg.DG_EINVAL
+
+
+def test_format_codes_match_header(dg):
+    text = open(HEADER).read()
+    for name in ("DG_FMT_E4M3", "DG_FMT_E5M2"):
+        m = re.search(r"#define %s (\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(dg, name), name
 
 
 def test_strerror(dg):
@@ -100,6 +121,8 @@ def test_python_binding_rejects_bad_tensors(dg):
     (4096, 7168, 2048, 128, (256, 224, 1)),   # 512 tiles of 256x224 vs 448 of 256x256
     (8192, 8192, 8192, 128, (256, 256, 1)),   # 1024 tiles of 256x256
     (2000, 4000, 16384, 64, (256, 128, 1)),   # 256 tiles of 256x128 vs 128 of 256x256
+    (8192, 8192, 8192, 256, (256, 256, 1)),   # g = 256 runs the 128-segment kernels
+    (64, 4096, 7168, 256, (32, 32, 1)),
 ])
 def test_query_tile_choice(dg, M, N, K, g, cls):
     t = dg.dg_query_tile(M, N, K, g)
