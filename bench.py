@@ -6,10 +6,15 @@ A step is one call of dg_gemm_fp8_nt over one input set: the whole method
 FP32 promotion, BF16 epilogue) runs inside that one kernel launch.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--fmt e4m3|e5m2|e4m3xe5m2|e5m2xe4m3] [--gran 64|128|256]
+
+--fmt and --gran run the same workload with the operands in another FP8
+format or with another block granularity (default: E4M3 and the workload's
+own g); the default run is the E4M3 workload as specified.
 
 Inputs: FP32 matrices drawn from the seeded generators in ``synth`` (the
 workload's shapes and value distributions), copied to the GPU and block
-quantised there by the library's own quantiser (dg_quantize_e4m3_blocks), so
+quantised there by the library's own quantiser (dg_quantize_fp8_blocks), so
 every byte the GEMM reads is resident in HBM before the timed region. Input
 sets are cloned so that consecutive steps rotate over enough distinct
 buffers (> 2x the 256 MB Infinity Cache) that the operands come from HBM,
@@ -60,7 +65,7 @@ DEFAULT_WORKLOAD = 2      # small-M decode shape, M=64 N=4096 K=7168, g=128
 # workload and tagged with the hash of the kernel source the counters were
 # taken on. A different hash means the kernel changed since: traffic is null.
 TRAFFIC = {
-    "decode_m64_n4096_k7168": {"src": "c9fe07ef28c050d4", "bytes": 33663972},
+    "decode_m64_n4096_k7168": {"src": "75528380ed9bba60", "bytes": 33667037},
 }
 
 
@@ -68,7 +73,8 @@ def _kernel_source_hash() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in ("gemm_fp8_nt.hip", "gemm_fp8_nt.h", "gemm_common.h", "gemm_fp8_nt_big.hip", "gemm_fp8_nt_stream.hip", "dg_host.hip"):
+    for name in ("gemm_fp8_nt.hip", "gemm_fp8_nt.h", "gemm_common.h", "gemm_fp8_nt_big.hip", "gemm_fp8_nt_stream.hip",
+                 "dg_host.hip"):
         with open(os.path.join(ROOT, "fp8_block_scaled_scales_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -82,8 +88,12 @@ def workload_by_name(key: str) -> int:
         key, ", ".join("%d=%s" % (c, w["name"]) for c, w in synth.WORKLOADS.items())))
 
 
-def algorithmic(w) -> tuple[float, float]:
-    M, N, K, g = w["M"], w["N"], w["K"], w["g"]
+FORMATS = {"e4m3": (0, 0), "e5m2": (1, 1), "e4m3xe5m2": (0, 1), "e5m2xe4m3": (1, 0)}
+
+
+def algorithmic(w, g=None) -> tuple[float, float]:
+    M, N, K = w["M"], w["N"], w["K"]
+    g = g or w["g"]
     flops = 2.0 * M * N * K
     nbytes = M * K + N * K + 4 * (math.ceil(M / g) + math.ceil(N / g)) * (K // g) + 2 * M * N
     return flops, float(nbytes)
@@ -95,34 +105,32 @@ def bound_of(w) -> str:
     return "hbm" if flops / nbytes < PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
 
 
-def make_inputs(c: int, dev):
-    """Quantised GPU inputs of workload c: (a8, sa, b8, sb)."""
+def make_inputs(c: int, dev, g: int, fa: int = 0, fb: int = 0):
+    """Quantised GPU inputs of workload c at granularity g, formats fa/fb: (a8, sa, b8, sb)."""
     import torch
 
     import fp8_block_scaled_scales_amd as dg
 
-    w = synth.WORKLOADS[c]
-    g = w["g"]
     xa = torch.from_numpy(synth.make_a(c)).to(dev)
-    a8, sa = dg.dg_quantize_e4m3_blocks(xa, gran=g)
+    a8, sa = dg.dg_quantize_fp8_blocks(xa, gran=g, fmt=fa)
     del xa
     xb = torch.from_numpy(synth.make_b(c)).to(dev)
-    b8, sb = dg.dg_quantize_e4m3_blocks(xb, gran=g)
+    b8, sb = dg.dg_quantize_fp8_blocks(xb, gran=g, fmt=fb)
     del xb
     torch.cuda.synchronize(dev)
     return a8, sa, b8, sb
 
 
-def gpu_leg(c: int, steps: int, warmup: int, sets: int | None):
+def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int = 0, fb: int = 0):
     import torch
 
     import fp8_block_scaled_scales_amd as dg
 
     w = synth.WORKLOADS[c]
-    M, N, K, g = w["M"], w["N"], w["K"], w["g"]
+    M, N, K = w["M"], w["N"], w["K"]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    a8, sa, b8, sb = make_inputs(c, dev)
+    a8, sa, b8, sb = make_inputs(c, dev, g, fa, fb)
     set_bytes = a8.numel() + b8.numel() + 4 * (sa.numel() + sb.numel()) + 2 * M * N
     if sets is None:
         sets = max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes) + 1))
@@ -136,7 +144,10 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None):
 
     def launch(i, st):
         x = bufs[i % sets]
-        dg.dg_gemm_fp8_nt(x[0], x[2], x[1], x[3], out=x[4], gran=g, stream=st)
+        if fa == 0 and fb == 0:
+            dg.dg_gemm_fp8_nt(x[0], x[2], x[1], x[3], out=x[4], gran=g, stream=st)
+        else:
+            dg.dg_gemm_fp8_nt_fmt(x[0], x[2], x[1], x[3], out=x[4], gran=g, fmt_a=fa, fmt_b=fb, stream=st)
 
     # Warm-up, eager: also allocates the library's split-K workspace and runs
     # its one-time device check, neither of which may happen under capture.
@@ -178,28 +189,34 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None):
     return ms, sets, finite, L
 
 
-def cpu_leg(c: int, budget_s: float = 10.0):
+def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, budget_s: float = 10.0):
     """The oracle on a bounded sample of workload c, in TFLOP/s (FP64 on the host)."""
     import numpy as np
 
     import oracle
 
     w = synth.WORKLOADS[c]
-    M, N, K, g = w["M"], w["N"], w["K"], w["g"]
+    M, N, K = w["M"], w["N"], w["K"]
     threads = oracle.default_threads()
-    a8, sa = oracle.quantize_blocks(synth.make_a(c), g)
-    b8, sb = oracle.quantize_blocks(synth.make_b(c), g)
+    a8, sa = oracle.quantize_blocks_fmt(synth.make_a(c), g, fa)
+    b8, sb = oracle.quantize_blocks_fmt(synth.make_b(c), g, fb)
+
+    def ref(rows=None):
+        if fa == 0 and fb == 0:
+            return oracle.gemm_ref(a8, b8, sa, sb, g, rows=rows)
+        return oracle.gemm_ref_fmt(a8, b8, sa, sb, g, fa, fb, rows=rows)
+
     # probe: one row per thread
     probe = np.arange(min(M, threads), dtype=np.int64)
     t0 = time.perf_counter()
-    oracle.gemm_ref(a8, b8, sa, sb, g, rows=probe)
+    ref(probe)
     per_row = (time.perf_counter() - t0) / probe.size
     rows = int(budget_s / max(per_row, 1e-9))
     rows = max(threads, (rows // threads) * threads)
     if rows < M:
         sel = np.linspace(0, M - 1, rows).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.gemm_ref(a8, b8, sa, sb, g, rows=sel)
+        ref(sel)
         dt = time.perf_counter() - t0
         done = 2.0 * rows * N * K
         sample = "%d of %d output rows (evenly spaced) x all %d columns, K=%d" % (rows, M, N, K)
@@ -207,7 +224,7 @@ def cpu_leg(c: int, budget_s: float = 10.0):
         reps, dt, done = 0, 0.0, 0.0
         t0 = time.perf_counter()
         while dt < budget_s:
-            oracle.gemm_ref(a8, b8, sa, sb, g)
+            ref()
             reps += 1
             dt = time.perf_counter() - t0
         done = 2.0 * M * N * K * reps
@@ -225,6 +242,10 @@ def main():
                     help="workload number or name (default: the small-M decode shape)")
     ap.add_argument("--sets", type=int, default=None, help="input sets rotated over (default: defeat the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fmt", default="e4m3", choices=sorted(FORMATS),
+                    help="operand formats, A x B (default e4m3: both E4M3FN)")
+    ap.add_argument("--gran", type=int, default=None, choices=(64, 128, 256),
+                    help="block granularity (default: the workload's)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes three times (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -252,8 +273,12 @@ def main():
 
     c = workload_by_name(args.workload)
     w = synth.WORKLOADS[c]
-    flops, nbytes = algorithmic(w)
-    ms, sets, finite, glen = gpu_leg(c, args.steps, args.warmup, args.sets)
+    g = args.gran or w["g"]
+    if w["K"] % g:
+        raise SystemExit("--gran %d does not divide K = %d" % (g, w["K"]))
+    fa, fb = FORMATS[args.fmt]
+    flops, nbytes = algorithmic(w, g)
+    ms, sets, finite, glen = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb)
     if not finite:
         raise SystemExit("GEMM output holds non-finite values")
     sec = ms * 1e-3
@@ -263,10 +288,10 @@ def main():
         achieved, peak, unit = tflops, PEAK_FP8_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
-    tr = TRAFFIC.get(w["name"])
+    tr = TRAFFIC.get(w["name"]) if (fa, fb, g) == (0, 0, w["g"]) else None
     traffic = tr["bytes"] if tr and tr["src"] == _kernel_source_hash() else None
 
-    cpu = None if args.no_cpu_baseline else cpu_leg(c)
+    cpu = None if args.no_cpu_baseline else cpu_leg(c, g, fa, fb)
 
     line = {
         "metric": "FP8 block-scaled GEMM TFLOPS and % of MI355X dense FP8 peak (1 GPU)",
@@ -279,9 +304,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "fp8_e4m3" if args.fmt == "e4m3" else "fp8_" + args.fmt,
         "data": "synthetic",
-        "config": {"workload": w["name"], "M": w["M"], "N": w["N"], "K": w["K"], "gran": w["g"],
+        "config": {"workload": w["name"], "M": w["M"], "N": w["N"], "K": w["K"], "gran": g, "fmt": args.fmt,
                    "layout": "NT", "out": "bf16", "input_sets": sets,
                    "launch": "hipGraph of %d launches, replayed %d times" % (glen, args.steps // glen),
                    "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
