@@ -13,6 +13,9 @@ computes and which passage of the pages it follows:
   E4M3_RNE_SAT(x / scale) (DeepGEMM实战 §2.2, §4.4, §5.2).
 * ``gemm_ref``: ref[i,j] = sum_kb sa[i/g,kb]*sb[j/g,kb] * P[i,j,kb] with the
   exact FP64 segment partials P (DeepGEMM实战 §2.2, §3.2, §3.3, §4.2).
+* ``epilogue``: y = act(ref + bias[j]) in FP64, act none / ReLU / GELU (erf
+  form) (the template article §2.3, §6: bias add, ReLU, GELU before the
+  write-back).
 * ``e5m2_decode`` / ``e5m2_encode``, ``quantize_blocks_fmt``, ``gemm_ref_fmt``:
   the same with E5M2 operands (DeepGEMM实战 §2.2 names E4M3 and E5M2 as the
   input formats; OCP E5M2 as torch.float8_e5m2 implements it), and any block
@@ -89,6 +92,8 @@ def _load():
     lib.dgo_gemm_ref_fmt.restype = ctypes.c_int
     lib.dgo_gemm_ref_fmt.argtypes = [u8p, u8p, f32p, f32p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, i64p, i64, i64p, i64, f64p, ctypes.c_int]
+    lib.dgo_epilogue.restype = ctypes.c_int
+    lib.dgo_epilogue.argtypes = [f64p, i64, i64, i64p, f32p, ctypes.c_int]
     lib.dgo_hardware_threads.restype = ctypes.c_int
     lib.dgo_hardware_threads.argtypes = []
     _lib = lib
@@ -240,4 +245,21 @@ def gemm_ref_fmt(a8, b8, sa, sb, g: int, fmt_a: int, fmt_b: int, rows=None, cols
         _ptr(out, ctypes.c_double), nthreads or default_threads())
     if rc != 0:
         raise ValueError("dgo_gemm_ref_fmt rejected its arguments")
+    return out
+
+
+# Epilogue activations: 0 = none, 1 = ReLU, 2 = GELU (erf form).
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
+
+
+def epilogue(ref, bias=None, act: int = ACT_NONE, cols=None) -> np.ndarray:
+    """act(ref + bias[cols]) in FP64 on a copy of ref [rows, len(cols)] (cols: output column indices)."""
+    out = np.array(ref, dtype=np.float64, order="C", copy=True)
+    nr, nc = out.shape
+    c = None if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    rc = _load().dgo_epilogue(_ptr(out, ctypes.c_double), nr, nc, None if c is None else _ptr(c, ctypes.c_int64),
+                              None if b is None else _ptr(b, ctypes.c_float), act)
+    if rc != 0:
+        raise ValueError("dgo_epilogue rejected its arguments")
     return out

@@ -45,6 +45,13 @@
 //    more than 53 bits); its relative error stays below K * 2^-53 of the sum
 //    of the products' magnitudes, far inside the GEMM tolerance.
 //
+//  * Epilogue (the template article, §2.3 and §6: an extension point before
+//    the result is written back, e.g. bias add, ReLU, GELU):
+//        y[i,j] = act(ref[i,j] + bias[j])
+//    in FP64, act = identity, ReLU max(y, 0), or GELU y * Phi(y) =
+//    0.5 * y * (1 + erf(y / sqrt(2))) (the exact form; the pages name GELU
+//    without choosing an approximation).
+//
 // Scale tensors are row-major FP32: sa is [ceil(M/g)][K/g], sb is
 // [ceil(N/g)][K/g]. K must be a multiple of g.
 //
@@ -331,6 +338,22 @@ int dgo_gemm_ref_fmt(const uint8_t* a, const uint8_t* b, const float* sa, const 
       }
     }
   });
+  return 0;
+}
+
+// Epilogue on an oracle result in place: ref is [nrows][ncols] for output
+// columns cols (NULL = 0..ncols-1); bias is FP32 [N] or NULL; act 0 = none,
+// 1 = ReLU, 2 = GELU (erf form). Returns 0, or -1 on bad arguments.
+int dgo_epilogue(double* ref, int64_t nrows, int64_t ncols, const int64_t* cols, const float* bias, int act) {
+  if (!ref || nrows < 0 || ncols < 0 || act < 0 || act > 2) return -1;
+  for (int64_t r = 0; r < nrows; ++r)
+    for (int64_t c = 0; c < ncols; ++c) {
+      const int64_t j = cols ? cols[c] : c;
+      double y = ref[r * ncols + c] + (bias ? (double)bias[j] : 0.0);
+      if (act == 1) y = y > 0.0 ? y : 0.0;
+      if (act == 2) y = 0.5 * y * (1.0 + std::erf(y / std::sqrt(2.0)));
+      ref[r * ncols + c] = y;
+    }
   return 0;
 }
 
