@@ -29,6 +29,9 @@ DG_EUNSUPPORTED = -3
 DG_ELAUNCH = -4
 DG_FMT_E4M3 = 0
 DG_FMT_E5M2 = 1
+DG_ACT_NONE = 0
+DG_ACT_RELU = 1
+DG_ACT_GELU = 2
 
 
 class dg_tile_info(ctypes.Structure):
@@ -50,6 +53,9 @@ def _load():
     lib.dg_gemm_fp8_nt_fmt.restype = ctypes.c_int
     lib.dg_gemm_fp8_nt_fmt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        vp]
+    lib.dg_gemm_fp8_nt_epi.restype = ctypes.c_int
+    lib.dg_gemm_fp8_nt_epi.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       vp, ctypes.c_int, vp]
     lib.dg_quantize_e4m3_blocks.restype = ctypes.c_int
     lib.dg_quantize_e4m3_blocks.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp]
     lib.dg_quantize_fp8_blocks.restype = ctypes.c_int
@@ -115,7 +121,7 @@ def _check(t, name, dtypes, shape, device):
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
 
 
-def _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, where):
+def _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, where, bias=None, act=DG_ACT_NONE):
     if a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D")
     M, K = a.shape
@@ -134,9 +140,17 @@ def _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, where):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _check(out, "out", (torch.bfloat16,), (M, N), dev)
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), (N,), dev)
+    if act not in (DG_ACT_NONE, DG_ACT_RELU, DG_ACT_GELU):
+        raise ValueError("act must be DG_ACT_NONE, DG_ACT_RELU or DG_ACT_GELU")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
-        if fmt_a == DG_FMT_E4M3 and fmt_b == DG_FMT_E4M3 and where == "dg_gemm_fp8_nt":
+        if where == "dg_gemm_fp8_nt_epi":
+            rc = _lib.dg_gemm_fp8_nt_epi(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
+                                         M, N, K, gran, fmt_a, fmt_b, None if bias is None else bias.data_ptr(),
+                                         act, s.cuda_stream)
+        elif fmt_a == DG_FMT_E4M3 and fmt_b == DG_FMT_E4M3 and where == "dg_gemm_fp8_nt":
             rc = _lib.dg_gemm_fp8_nt(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
                                      M, N, K, gran, s.cuda_stream)
         else:
@@ -166,6 +180,15 @@ def dg_gemm_fp8_nt_fmt(a, b, sa, sb, out=None, gran: int = 128, fmt_a: int = DG_
     An E5M2 operand is float8_e5m2 (or uint8 holding E5M2 codes).
     """
     return _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, "dg_gemm_fp8_nt_fmt")
+
+
+def dg_gemm_fp8_nt_epi(a, b, sa, sb, out=None, gran: int = 128, fmt_a: int = DG_FMT_E4M3,
+                       fmt_b: int = DG_FMT_E4M3, bias=None, act: int = DG_ACT_NONE, stream=None):
+    """dg_gemm_fp8_nt_fmt with out = bf16(act(C + bias[None, :])) fused into the store.
+
+    bias: optional [N] float32; act: DG_ACT_NONE, DG_ACT_RELU or DG_ACT_GELU (exact erf form).
+    """
+    return _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, "dg_gemm_fp8_nt_epi", bias, act)
 
 
 def _quantize(x, gran, fmt, q, scales, stream, where):
@@ -216,6 +239,6 @@ def dg_quantize_fp8_blocks(x, gran: int = 128, fmt: int = DG_FMT_E4M3, q=None, s
     return _quantize(x, gran, fmt, q, scales, stream, "dg_quantize_fp8_blocks")
 
 
-__all__ = ["dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "dg_quantize_e4m3_blocks", "dg_quantize_fp8_blocks",
+__all__ = ["dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "dg_gemm_fp8_nt_epi", "DG_ACT_NONE", "DG_ACT_RELU", "DG_ACT_GELU", "dg_quantize_e4m3_blocks", "dg_quantize_fp8_blocks",
            "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError", "DG_OK", "DG_EINVAL",
            "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH", "DG_FMT_E4M3", "DG_FMT_E5M2", "LIB_PATH"]

@@ -182,10 +182,12 @@ int device_ready(int* dev_out = nullptr) {
 namespace {
 
 int gemm(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M, int64_t N, int64_t K,
-         int gran, int fmt_a, int fmt_b, void* stream) {
+         int gran, int fmt_a, int fmt_b, const float* bias, int act, void* stream) {
   if (!a || !b || !sa || !sb || !out) return DG_EINVAL;
   if ((fmt_a != DG_FMT_E4M3 && fmt_a != DG_FMT_E5M2) || (fmt_b != DG_FMT_E4M3 && fmt_b != DG_FMT_E5M2))
     return DG_EINVAL;
+  if (act != DG_ACT_NONE && act != DG_ACT_RELU && act != DG_ACT_GELU) return DG_EINVAL;
+  if ((uintptr_t)bias & 3) return DG_EALIGN;
   int rc = validate(M, N, K, gran);
   if (rc != DG_OK) return rc;
   if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)sa & 3) || ((uintptr_t)sb & 3) ||
@@ -219,12 +221,14 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   p.ksplit = pl.ksplit;
   p.ws = pl.ksplit > 1 ? g_ws[dev] : nullptr;
   p.counters = pl.ksplit > 1 ? g_counters[dev] : nullptr;
+  p.bias = bias;
+  p.act = act;
   if (log_enabled())
     std::fprintf(stderr,
-                 "dg_gemm_fp8_nt M=%lld N=%lld K=%lld g=%d fmt=%d,%d -> kernel %d (%dx%d, %d stages, %d waves) "
-                 "ksplit %d grid %lld\n",
-                 (long long)M, (long long)N, (long long)K, gran, fmt_a, fmt_b, e->id, e->bm, e->bn, e->stages,
-                 e->waves, pl.ksplit, (long long)(pl.tiles * pl.ksplit));
+                 "dg_gemm_fp8_nt M=%lld N=%lld K=%lld g=%d fmt=%d,%d bias=%d act=%d -> kernel %d (%dx%d, %d "
+                 "stages, %d waves) ksplit %d grid %lld\n",
+                 (long long)M, (long long)N, (long long)K, gran, fmt_a, fmt_b, bias ? 1 : 0, act, e->id, e->bm,
+                 e->bn, e->stages, e->waves, pl.ksplit, (long long)(pl.tiles * pl.ksplit));
   t_last_hip = e->launch(p, static_cast<hipStream_t>(stream));
   return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
 }
@@ -293,12 +297,18 @@ int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info)
 
 int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
                    int64_t N, int64_t K, int gran, void* stream) {
-  return gemm(a, b, sa, sb, out, M, N, K, gran, DG_FMT_E4M3, DG_FMT_E4M3, stream);
+  return gemm(a, b, sa, sb, out, M, N, K, gran, DG_FMT_E4M3, DG_FMT_E4M3, nullptr, DG_ACT_NONE, stream);
 }
 
 int dg_gemm_fp8_nt_fmt(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
                        int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, void* stream) {
-  return gemm(a, b, sa, sb, out, M, N, K, gran, fmt_a, fmt_b, stream);
+  return gemm(a, b, sa, sb, out, M, N, K, gran, fmt_a, fmt_b, nullptr, DG_ACT_NONE, stream);
+}
+
+int dg_gemm_fp8_nt_epi(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
+                       int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, const float* bias, int act,
+                       void* stream) {
+  return gemm(a, b, sa, sb, out, M, N, K, gran, fmt_a, fmt_b, bias, act, stream);
 }
 
 int dg_quantize_fp8_blocks(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q, float* scales,

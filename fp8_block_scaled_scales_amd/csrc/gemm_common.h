@@ -100,6 +100,31 @@ __device__ __forceinline__ void stage_slab(v4i rsrc, uint8_t* lds, uint32_t K, u
   for (int i = 0; i < GROUPS / NWAVES; ++i) stage_group<SW>(rsrc, lds, K, k0, i * NWAVES + wave, lane);
 }
 
+// Epilogue before the BF16 store (the template article's extension point
+// before the write-back, §2.3 and §6: bias add, ReLU, GELU), in FP32:
+// y = act(x + b) with b = bias[column] when a bias is given, act none, ReLU,
+// or GELU in its exact form 0.5 * y * (1 + erf(y / sqrt 2)). EPI selects the
+// compiled form: 0 = no bias and no activation (x passes unchanged, and the
+// kernel holds no epilogue state at all), 1 = optional bias and optional
+// ReLU, 2 = optional bias and GELU. It is a template parameter because the
+// epilogue is unrolled over every accumulator register: a runtime choice
+// would leave an inlined erf behind a branch at each of them, code the
+// instruction cache would fetch around per element.
+template <int EPI>
+__device__ __forceinline__ float epilogue_fn(float x, bool has_bias, float b, bool relu) {
+  if constexpr (EPI == 0) return x;
+  if (has_bias) x += b;
+  if constexpr (EPI == 1) {
+    if (relu) x = fmaxf(x, 0.0f);
+  }
+  if constexpr (EPI == 2) x = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+  return x;
+}
+
+// Compiled epilogue form of a call (see epilogue_fn): 0 without bias and
+// activation, 2 for GELU, 1 otherwise.
+inline int epilogue_form(const float* bias, int act) { return act == 2 ? 2 : (bias || act == 1) ? 1 : 0; }
+
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);  // v_cvt_pk_bf16_f32: nearest even
 }

@@ -20,6 +20,8 @@ struct GemmArgs {
   int ksplit;     // workgroups per output tile along K (1 = no split)
   float* ws;      // split-K partial tiles, tiles * ksplit * bm * bn floats (ksplit > 1)
   uint32_t* counters;  // split-K arrival counters, one per tile, zero between calls
+  const float* bias;   // FP32 [N] added before the activation, or null
+  int act;             // epilogue activation: 0 none, 1 ReLU, 2 GELU
 };
 
 typedef hipError_t (*Launcher)(const GemmArgs&, hipStream_t);

@@ -79,11 +79,12 @@ __device__ __forceinline__ void wait_steps(int steps) {
 // G is the K segment contracted before each promotion; the scale blocks are
 // sg x sg with sg = G << sshift (g = 256 runs G = 128 with one factor per two
 // segments).
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT>
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ b, const float* __restrict__ sa,
     const float* __restrict__ sb, uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
-    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, uint32_t* __restrict__ counters, int sshift) {
+    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, uint32_t* __restrict__ counters, int sshift,
+    const float* __restrict__ bias, int relu) {
   constexpr int NWAVES = WM * WN;
   constexpr int NT = 64 * NWAVES;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
@@ -132,6 +133,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (v16f){};
+
+  // The epilogue's bias for this lane's columns, loaded before the first
+  // copies: the step waits cover it, and no output store is in flight when
+  // the epilogue reads it.
+  const bool hb = EPI != 0 && bias != nullptr;
+  float bcol[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+    bcol[j] = hb && col < N ? bias[col] : 0.0f;
+  }
 
   // Prologue: fill STAGES-1 ring slots.
 #pragma unroll
@@ -297,7 +309,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
         // 32x32 accumulator layout: lane%32 is the column, (v/4)*8 + (lane/32)*4 + v%4 the row.
         const int r = wm * WTM + i * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
         const int c = wn * WTN + j * 32 + (lane & 31);
-        cs[r * LDC + c] = bf16_bits(acc[i][j][v]);
+        cs[r * LDC + c] = bf16_bits(epilogue_fn<EPI>(acc[i][j][v], hb, bcol[j], relu));
       }
   __syncthreads();
   constexpr int CHUNKS = BM * BN / 8;
@@ -322,14 +334,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
 
 // ---- launch table -------------------------------------------------------------
 
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT>
-static hipError_t launch_tiled_fmt(const GemmArgs& p, hipStream_t stream) {
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI>
+static hipError_t launch_tiled_fa(const GemmArgs& p, hipStream_t stream) {
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT>),
+  hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI>),
                      dim3(tiles_m * tiles_n * p.ksplit), dim3(64 * WM * WN), 0, stream, p.a, p.b, p.sa, p.sb, p.out,
                      (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.ksplit, p.ws, p.counters,
-                     p.sshift);
+                     p.sshift, p.bias, p.act == 1 ? 1 : 0);
   return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT>
+static hipError_t launch_tiled_fmt(const GemmArgs& p, hipStream_t stream) {
+  switch (epilogue_form(p.bias, p.act)) {
+    case 0: return launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 0>(p, stream);
+    case 1: return launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 1>(p, stream);
+    case 2: return launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 2>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT>

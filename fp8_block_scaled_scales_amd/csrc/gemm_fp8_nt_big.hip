@@ -94,11 +94,12 @@ struct Acc<64, WTM, WTN> {
 // G is the K segment the matrix cores contract before each promotion (64 or
 // 128). The scale blocks are sg x sg with sg = G << sshift: for g = 256 the
 // G = 128 kernel promotes every 128 K with its 256-block's factor.
-template <int G, int BN, int WM, int GROUP_M, int FMT>
+template <int G, int BN, int WM, int GROUP_M, int FMT, int EPI>
 __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
                                                       const float* __restrict__ sa, const float* __restrict__ sb,
                                                       uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
-                                                      int tiles_n, int vec_store, int sshift) {
+                                                      int tiles_n, int vec_store, int sshift,
+                                                      const float* __restrict__ bias, int relu) {
   static_assert(G == 64 || G == 128, "granularity");
   constexpr int WN = NW / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -250,12 +251,24 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       }
     }
   }
+  // The epilogue's bias for this lane's columns (none without a bias, so
+  // nothing is held in registers through the main loop), waited for with the
+  // last copies and before any output store is in flight.
+  constexpr int NBJ = G == 128 ? WTN / 16 : WTN / 32;
+  const bool hb = EPI != 0 && bias != nullptr;
+  float bj[NBJ];
+#pragma unroll
+  for (int j = 0; j < NBJ; ++j) {
+    const int col = wc0 + (G == 128 ? j * 16 + (lane & 15) : j * 32 + (lane & 31));
+    bj[j] = hb && col < N ? bias[col] : 0.0f;
+  }
   DG_WAIT_VMCNT(0);
 
   // Epilogue, two passes of 128 rows: the waves whose rows lie in the pass
   // write their BF16 sub-tiles to LDS, then all threads store the pass.
   uint16_t* cs = reinterpret_cast<uint16_t*>(smem);
   const int prow = wm * WTM % 128;  // first row of this wave inside its pass
+
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     __syncthreads();
@@ -263,22 +276,23 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       if constexpr (G == 128) {
         const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
-        for (int i = 0; i < WTM / 16; ++i)
+        for (int j = 0; j < WTN / 16; ++j)
 #pragma unroll
-          for (int j = 0; j < WTN / 16; ++j)
+          for (int i = 0; i < WTM / 16; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              cs[(prow + i * 16 + 4 * q + v) * LDC + wn * WTN + j * 16 + r16] = bf16_bits(acc.t[i][j][v]);
+              cs[(prow + i * 16 + 4 * q + v) * LDC + wn * WTN + j * 16 + r16] =
+                  bf16_bits(epilogue_fn<EPI>(acc.t[i][j][v], hb, bj[j], relu));
       } else {
         const int r32 = lane & 31, h2 = lane >> 5;
 #pragma unroll
-        for (int i = 0; i < WTM / 32; ++i)
+        for (int j = 0; j < WTN / 32; ++j)
 #pragma unroll
-          for (int j = 0; j < WTN / 32; ++j)
+          for (int i = 0; i < WTM / 32; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
               cs[(prow + i * 32 + 8 * (v >> 2) + 4 * h2 + (v & 3)) * LDC + wn * WTN + j * 32 + r32] =
-                  bf16_bits(acc.t[i][j][v]);
+                  bf16_bits(epilogue_fn<EPI>(acc.t[i][j][v], hb, bj[j], relu));
       }
     }
     __syncthreads();
@@ -301,12 +315,23 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   }
 }
 
+template <int G, int BN, int WM, int FMT, int EPI>
+hipError_t launch_fa(const GemmArgs& p, hipStream_t stream) {
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_fp8_nt_big<G, BN, WM, 4, FMT, EPI>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, p.a,
+                     p.b, p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.sshift,
+                     p.bias, p.act == 1 ? 1 : 0);
+  return hipGetLastError();
+}
+
 template <int G, int BN, int WM, int FMT>
 hipError_t launch_fmt(const GemmArgs& p, hipStream_t stream) {
-  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_big<G, BN, WM, 4, FMT>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, p.a, p.b,
-                     p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.sshift);
-  return hipGetLastError();
+  switch (epilogue_form(p.bias, p.act)) {
+    case 0: return launch_fa<G, BN, WM, FMT, 0>(p, stream);
+    case 1: return launch_fa<G, BN, WM, FMT, 1>(p, stream);
+    case 2: return launch_fa<G, BN, WM, FMT, 2>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int G, int BN, int WM>

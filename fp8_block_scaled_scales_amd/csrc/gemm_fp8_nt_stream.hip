@@ -59,13 +59,14 @@ __device__ __forceinline__ v8i frag(const uint8_t* slab, int row, int c0) {
 // G: K segment contracted before each promotion; scale blocks sg = G << sshift
 // (g = 256 runs the G = 128 kernel with one factor per two segments). FMT bit
 // 0: A is E5M2 (else E4M3), bit 1: B is E5M2.
-template <int G, int FMT>
+template <int G, int FMT, int EPI>
 __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __restrict__ a,
                                                               const uint8_t* __restrict__ b,
                                                               const float* __restrict__ sa,
                                                               const float* __restrict__ sb,
                                                               uint16_t* __restrict__ out, int M, int N, int K,
-                                                              int tiles_m, int tiles_n, int sshift) {
+                                                              int tiles_m, int tiles_n, int sshift,
+                                                              const float* __restrict__ bias, int relu) {
   static_assert(G == 64 || G == 128, "granularity");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NW * WAVE_LDS];
 
@@ -84,6 +85,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
   // 32 rows starting at a multiple of 32 lie in one g-block (g >= 64).
   const float* const sa_row = sa + (int64_t)(m0 / sg) * nks;
   const float* const sb_row = sb + (int64_t)(n0 / sg) * nks;
+
+  // The epilogue's bias for this lane's column, loaded first: it is older
+  // than every copy below, so the copies' waits cover it, and no output store
+  // is in flight when the epilogue reads it.
+  const int ocol = n0 + (lane & 31);
+  const bool hb = EPI != 0 && bias != nullptr;
+  const float bc = hb && ocol < N ? bias[ocol] : 0.0f;
 
   uint8_t* const a_ring = smem + wave * WAVE_LDS;
   uint8_t* const b_ring = a_ring + A_SLOTS * A_SLAB;
@@ -159,23 +167,37 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
   for (int v = 0; v < 16; ++v) red[(wave * 16 + v) * 64 + lane] = acc[v];
   __syncthreads();
   if (wave != 0) return;
+  uint16_t res[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     float tsum = red[v * 64 + lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) tsum += red[(w * 16 + v) * 64 + lane];
-    const int row = m0 + 8 * (v >> 2) + 4 * h2 + (v & 3);
-    const int col = n0 + r32;
-    if (row < M && col < N) out[(int64_t)row * N + col] = bf16_bits(tsum);
+    res[v] = bf16_bits(epilogue_fn<EPI>(tsum, hb, bc, relu));
   }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int row = m0 + 8 * (v >> 2) + 4 * h2 + (v & 3);
+    if (row < M && ocol < N) out[(int64_t)row * N + ocol] = res[v];
+  }
+}
+
+template <int G, int FMT, int EPI>
+hipError_t launch_fa(const GemmArgs& p, hipStream_t stream) {
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_fp8_nt_stream<G, FMT, EPI>), dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream, p.a,
+                     p.b, p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.sshift, p.bias, p.act == 1 ? 1 : 0);
+  return hipGetLastError();
 }
 
 template <int G, int FMT>
 hipError_t launch_fmt(const GemmArgs& p, hipStream_t stream) {
-  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_stream<G, FMT>), dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream, p.a, p.b,
-                     p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.sshift);
-  return hipGetLastError();
+  switch (epilogue_form(p.bias, p.act)) {
+    case 0: return launch_fa<G, FMT, 0>(p, stream);
+    case 1: return launch_fa<G, FMT, 1>(p, stream);
+    case 2: return launch_fa<G, FMT, 2>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int G>

@@ -89,6 +89,28 @@ int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* s
 int dg_gemm_fp8_nt_fmt(const void* a, const void* b, const float* sa, const float* sb, void* out,
                        int64_t M, int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, void* stream);
 
+/* Epilogue activations (the template article's epilogue extension point,
+ * §2.3 and §6: bias add, ReLU, GELU before the write-back). */
+#define DG_ACT_NONE 0
+#define DG_ACT_RELU 1
+#define DG_ACT_GELU 2 /* exact form: 0.5 * y * (1 + erf(y / sqrt 2)) */
+
+/*
+ * dg_gemm_fp8_nt_epi - dg_gemm_fp8_nt_fmt with an epilogue fused before the
+ * BF16 store:  out[i,j] = bf16( act( C[i,j] + bias[j] ) )  with C the FP32
+ * block-scaled product and everything in FP32.
+ *
+ *   bias  FP32 [N] device pointer, 4-byte aligned, or NULL for no bias.
+ *   act   DG_ACT_NONE, DG_ACT_RELU or DG_ACT_GELU.
+ *
+ * With bias NULL and DG_ACT_NONE this is dg_gemm_fp8_nt_fmt, bit for bit.
+ * DG_EINVAL for an unknown act, DG_EALIGN for a misaligned bias; otherwise as
+ * dg_gemm_fp8_nt_fmt.
+ */
+int dg_gemm_fp8_nt_epi(const void* a, const void* b, const float* sa, const float* sb, void* out,
+                       int64_t M, int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, const float* bias,
+                       int act, void* stream);
+
 /* The tile-table entry a call with these sizes would use. */
 typedef struct dg_tile_info {
   int kernel_id; /* index in the precompiled table */

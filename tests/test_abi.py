@@ -81,9 +81,15 @@ def test_quantize_einval(dg, fmt, g, cols):
     assert dg.lib.dg_quantize_fp8_blocks(A, 64, cols, g, fmt, B, SA, None) == dg.DG_EINVAL
 
 
+@pytest.mark.parametrize("act,bias,want", [(3, 0, "DG_EINVAL"), (-1, 0, "DG_EINVAL"), (1, SB + 2, "DG_EALIGN")])
+def test_epi_rejects(dg, act, bias, want):
+    assert dg.lib.dg_gemm_fp8_nt_epi(A, B, SA, SB, OUT, 256, 256, 256, 128, 0, 0, bias or None, act, None) == \
+        getattr(dg, want)
+
+
 def test_format_codes_match_header(dg):
     text = open(HEADER).read()
-    for name in ("DG_FMT_E4M3", "DG_FMT_E5M2"):
+    for name in ("DG_FMT_E4M3", "DG_FMT_E5M2", "DG_ACT_NONE", "DG_ACT_RELU", "DG_ACT_GELU"):
         m = re.search(r"#define %s (\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(dg, name), name
 
