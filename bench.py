@@ -7,10 +7,12 @@ FP32 promotion, BF16 epilogue) runs inside that one kernel launch.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--fmt e4m3|e5m2|e4m3xe5m2|e5m2xe4m3] [--gran 64|128|256]
+                  [--bias] [--act none|relu|gelu]
 
 --fmt and --gran run the same workload with the operands in another FP8
 format or with another block granularity (default: E4M3 and the workload's
-own g); the default run is the E4M3 workload as specified.
+own g); --bias and --act add the fused epilogue out = act(C + bias) (bias a
+seeded N(0, 0.5) vector); the default run is the E4M3 workload as specified.
 
 Inputs: FP32 matrices drawn from the seeded generators in ``synth`` (the
 workload's shapes and value distributions), copied to the GPU and block
@@ -65,7 +67,7 @@ DEFAULT_WORKLOAD = 2      # small-M decode shape, M=64 N=4096 K=7168, g=128
 # workload and tagged with the hash of the kernel source the counters were
 # taken on. A different hash means the kernel changed since: traffic is null.
 TRAFFIC = {
-    "decode_m64_n4096_k7168": {"src": "75528380ed9bba60", "bytes": 33667037},
+    "decode_m64_n4096_k7168": {"src": "489c5ba8a4ccd93a", "bytes": 33667468},
 }
 
 
@@ -89,6 +91,12 @@ def workload_by_name(key: str) -> int:
 
 
 FORMATS = {"e4m3": (0, 0), "e5m2": (1, 1), "e4m3xe5m2": (0, 1), "e5m2xe4m3": (1, 0)}
+ACTS = {"none": 0, "relu": 1, "gelu": 2}
+BIAS_SEED = 9901
+
+
+def make_bias(N: int):
+    return synth.normal(BIAS_SEED, (N,), sigma=0.5).astype("float32")
 
 
 def algorithmic(w, g=None) -> tuple[float, float]:
@@ -121,7 +129,8 @@ def make_inputs(c: int, dev, g: int, fa: int = 0, fb: int = 0):
     return a8, sa, b8, sb
 
 
-def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int = 0, fb: int = 0):
+def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int = 0, fb: int = 0,
+            bias: bool = False, act: int = 0):
     import torch
 
     import fp8_block_scaled_scales_amd as dg
@@ -142,9 +151,14 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
     print("bench: workload %d %s, %d input sets of %.1f MB, tile %s" % (
         c, w["name"], sets, set_bytes / 1e6, dg.dg_query_tile(M, N, K, g)), file=sys.stderr, flush=True)
 
+    tbias = torch.from_numpy(make_bias(N)).to(dev) if bias else None
+
     def launch(i, st):
         x = bufs[i % sets]
-        if fa == 0 and fb == 0:
+        if bias or act:
+            dg.dg_gemm_fp8_nt_epi(x[0], x[2], x[1], x[3], out=x[4], gran=g, fmt_a=fa, fmt_b=fb, bias=tbias, act=act,
+                                  stream=st)
+        elif fa == 0 and fb == 0:
             dg.dg_gemm_fp8_nt(x[0], x[2], x[1], x[3], out=x[4], gran=g, stream=st)
         else:
             dg.dg_gemm_fp8_nt_fmt(x[0], x[2], x[1], x[3], out=x[4], gran=g, fmt_a=fa, fmt_b=fb, stream=st)
@@ -189,7 +203,7 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
     return ms, sets, finite, L
 
 
-def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, budget_s: float = 10.0):
+def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, bias: bool = False, act: int = 0, budget_s: float = 10.0):
     """The oracle on a bounded sample of workload c, in TFLOP/s (FP64 on the host)."""
     import numpy as np
 
@@ -201,10 +215,14 @@ def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, budget_s: float = 10.0):
     a8, sa = oracle.quantize_blocks_fmt(synth.make_a(c), g, fa)
     b8, sb = oracle.quantize_blocks_fmt(synth.make_b(c), g, fb)
 
+    bvec = make_bias(N) if bias else None
+
     def ref(rows=None):
         if fa == 0 and fb == 0:
-            return oracle.gemm_ref(a8, b8, sa, sb, g, rows=rows)
-        return oracle.gemm_ref_fmt(a8, b8, sa, sb, g, fa, fb, rows=rows)
+            r = oracle.gemm_ref(a8, b8, sa, sb, g, rows=rows)
+        else:
+            r = oracle.gemm_ref_fmt(a8, b8, sa, sb, g, fa, fb, rows=rows)
+        return oracle.epilogue(r, bvec, act) if (bias or act) else r
 
     # probe: one row per thread
     probe = np.arange(min(M, threads), dtype=np.int64)
@@ -246,6 +264,8 @@ def main():
                     help="operand formats, A x B (default e4m3: both E4M3FN)")
     ap.add_argument("--gran", type=int, default=None, choices=(64, 128, 256),
                     help="block granularity (default: the workload's)")
+    ap.add_argument("--bias", action="store_true", help="fused epilogue: add a bias vector")
+    ap.add_argument("--act", default="none", choices=sorted(ACTS), help="fused epilogue activation")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes three times (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -278,7 +298,8 @@ def main():
         raise SystemExit("--gran %d does not divide K = %d" % (g, w["K"]))
     fa, fb = FORMATS[args.fmt]
     flops, nbytes = algorithmic(w, g)
-    ms, sets, finite, glen = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb)
+    act = ACTS[args.act]
+    ms, sets, finite, glen = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb, args.bias, act)
     if not finite:
         raise SystemExit("GEMM output holds non-finite values")
     sec = ms * 1e-3
@@ -288,10 +309,10 @@ def main():
         achieved, peak, unit = tflops, PEAK_FP8_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
-    tr = TRAFFIC.get(w["name"]) if (fa, fb, g) == (0, 0, w["g"]) else None
+    tr = TRAFFIC.get(w["name"]) if (fa, fb, g, args.bias, act) == (0, 0, w["g"], False, 0) else None
     traffic = tr["bytes"] if tr and tr["src"] == _kernel_source_hash() else None
 
-    cpu = None if args.no_cpu_baseline else cpu_leg(c, g, fa, fb)
+    cpu = None if args.no_cpu_baseline else cpu_leg(c, g, fa, fb, args.bias, act)
 
     line = {
         "metric": "FP8 block-scaled GEMM TFLOPS and % of MI355X dense FP8 peak (1 GPU)",
@@ -307,6 +328,7 @@ def main():
         "dtype": "fp8_e4m3" if args.fmt == "e4m3" else "fp8_" + args.fmt,
         "data": "synthetic",
         "config": {"workload": w["name"], "M": w["M"], "N": w["N"], "K": w["K"], "gran": g, "fmt": args.fmt,
+                   "epilogue": ("bias+" if args.bias else "") + args.act,
                    "layout": "NT", "out": "bf16", "input_sets": sets,
                    "launch": "hipGraph of %d launches, replayed %d times" % (glen, args.steps // glen),
                    "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),

@@ -110,6 +110,24 @@ __device__ __forceinline__ void stage_slab(v4i rsrc, uint8_t* lds, uint32_t K, u
 // epilogue is unrolled over every accumulator register: a runtime choice
 // would leave an inlined erf behind a branch at each of them, code the
 // instruction cache would fetch around per element.
+// erf by the rational approximation of Abramowitz and Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26: for z >= 0,
+// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2) with
+// t = 1 / (1 + p z), absolute error below 1.5e-7; odd in z. Straight-line
+// (one reciprocal, one exponential, a few FMAs): the epilogue inlines it once
+// per accumulator register.
+__device__ __forceinline__ float erf_as7126(float z) {
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, az, 1.0f));
+  float poly = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  poly = __builtin_fmaf(poly, t, 1.421413741f);
+  poly = __builtin_fmaf(poly, t, -0.284496736f);
+  poly = __builtin_fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-az * az * 1.4426950408889634f);  // exp(-z^2)
+  return copysignf(1.0f - poly * e, z);
+}
+
 template <int EPI>
 __device__ __forceinline__ float epilogue_fn(float x, bool has_bias, float b, bool relu) {
   if constexpr (EPI == 0) return x;
@@ -117,7 +135,7 @@ __device__ __forceinline__ float epilogue_fn(float x, bool has_bias, float b, bo
   if constexpr (EPI == 1) {
     if (relu) x = fmaxf(x, 0.0f);
   }
-  if constexpr (EPI == 2) x = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+  if constexpr (EPI == 2) x = 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752f));
   return x;
 }
 

@@ -166,6 +166,18 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       if (i * NW + wave < BN / 8) stage_group<1>(rb, slot + A_BYTES, uK, (uint32_t)t * BK, i * NW + wave, lane);
   };
 
+  // The epilogue's bias for this lane's columns, loaded before the first
+  // copies: the step waits cover it, and no output store is in flight when
+  // the epilogue reads it. The plain form (EPI 0) loads and holds nothing.
+  constexpr int NBJ = G == 128 ? WTN / 16 : WTN / 32;
+  const bool hb = EPI != 0 && bias != nullptr;
+  float bj[NBJ];
+#pragma unroll
+  for (int j = 0; j < NBJ; ++j) {
+    const int col = wc0 + (G == 128 ? j * 16 + (lane & 15) : j * 32 + (lane & 31));
+    bj[j] = hb && col < N ? bias[col] : 0.0f;
+  }
+
   issue_step(0);
 
   for (int s = 0; s < nsteps; ++s) {
@@ -251,18 +263,26 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       }
     }
   }
-  // The epilogue's bias for this lane's columns (none without a bias, so
-  // nothing is held in registers through the main loop), waited for with the
-  // last copies and before any output store is in flight.
-  constexpr int NBJ = G == 128 ? WTN / 16 : WTN / 32;
-  const bool hb = EPI != 0 && bias != nullptr;
-  float bj[NBJ];
-#pragma unroll
-  for (int j = 0; j < NBJ; ++j) {
-    const int col = wc0 + (G == 128 ? j * 16 + (lane & 15) : j * 32 + (lane & 31));
-    bj[j] = hb && col < N ? bias[col] : 0.0f;
-  }
   DG_WAIT_VMCNT(0);
+  // Bias and activation in place, by all eight waves at once (the passes
+  // below keep half of them idle).
+  if constexpr (EPI != 0) {
+    if constexpr (G == 128) {
+#pragma unroll
+      for (int j = 0; j < WTN / 16; ++j)
+#pragma unroll
+        for (int i = 0; i < WTM / 16; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc.t[i][j][v] = epilogue_fn<EPI>(acc.t[i][j][v], hb, bj[j], relu);
+    } else {
+#pragma unroll
+      for (int j = 0; j < WTN / 32; ++j)
+#pragma unroll
+        for (int i = 0; i < WTM / 32; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc.t[i][j][v] = epilogue_fn<EPI>(acc.t[i][j][v], hb, bj[j], relu);
+    }
+  }
 
   // Epilogue, two passes of 128 rows: the waves whose rows lie in the pass
   // write their BF16 sub-tiles to LDS, then all threads store the pass.
@@ -282,7 +302,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
 #pragma unroll
             for (int v = 0; v < 4; ++v)
               cs[(prow + i * 16 + 4 * q + v) * LDC + wn * WTN + j * 16 + r16] =
-                  bf16_bits(epilogue_fn<EPI>(acc.t[i][j][v], hb, bj[j], relu));
+                  bf16_bits(acc.t[i][j][v]);
       } else {
         const int r32 = lane & 31, h2 = lane >> 5;
 #pragma unroll
@@ -292,7 +312,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
 #pragma unroll
             for (int v = 0; v < 16; ++v)
               cs[(prow + i * 32 + 8 * (v >> 2) + 4 * h2 + (v & 3)) * LDC + wn * WTN + j * 32 + r32] =
-                  bf16_bits(epilogue_fn<EPI>(acc.t[i][j][v], hb, bj[j], relu));
+                  bf16_bits(acc.t[i][j][v]);
       }
     }
     __syncthreads();
