@@ -20,6 +20,10 @@ computes and which passage of the pages it follows:
   the same with E5M2 operands (DeepGEMM实战 §2.2 names E4M3 and E5M2 as the
   input formats; OCP E5M2 as torch.float8_e5m2 implements it), and any block
   granularity g (§3.1: 64, 128 and 256).
+* ``quantize_rows_fmt``, ``gemm_ref_rowa``: per-row A scales, one factor per
+  row and g-wide K segment (1 x g blocks), B keeping its g x g blocks (the
+  template article §3.4: per-tensor or per-channel factors, per channel the
+  usual choice).
 
 Parity status: every function above is pinned by the CPU tests
 (``tests/test_oracle_*.py``) against torch's float8 cast, brute force, exact
@@ -92,6 +96,11 @@ def _load():
     lib.dgo_gemm_ref_fmt.restype = ctypes.c_int
     lib.dgo_gemm_ref_fmt.argtypes = [u8p, u8p, f32p, f32p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, i64p, i64, i64p, i64, f64p, ctypes.c_int]
+    lib.dgo_quantize_rows_fmt.restype = ctypes.c_int
+    lib.dgo_quantize_rows_fmt.argtypes = [f32p, i64, i64, ctypes.c_int, ctypes.c_int, u8p, f32p, ctypes.c_int]
+    lib.dgo_gemm_ref_rowa.restype = ctypes.c_int
+    lib.dgo_gemm_ref_rowa.argtypes = [u8p, u8p, f32p, f32p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, i64p, i64, i64p, i64, f64p, ctypes.c_int]
     lib.dgo_epilogue.restype = ctypes.c_int
     lib.dgo_epilogue.argtypes = [f64p, i64, i64, i64p, f32p, ctypes.c_int]
     lib.dgo_hardware_threads.restype = ctypes.c_int
@@ -245,6 +254,50 @@ def gemm_ref_fmt(a8, b8, sa, sb, g: int, fmt_a: int, fmt_b: int, rows=None, cols
         _ptr(out, ctypes.c_double), nthreads or default_threads())
     if rc != 0:
         raise ValueError("dgo_gemm_ref_fmt rejected its arguments")
+    return out
+
+
+def quantize_rows_fmt(x, g: int, fmt: int = 0, nthreads: int | None = None):
+    """1 x g quantisation: one factor per row and g-wide column segment; scales [rows, cols/g]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    if cols % g:
+        raise ValueError("cols must be a multiple of g")
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty((rows, cols // g), dtype=np.float32)
+    rc = _load().dgo_quantize_rows_fmt(_ptr(x, ctypes.c_float), rows, cols, g, fmt, _ptr(q, ctypes.c_uint8),
+                                       _ptr(s, ctypes.c_float), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("dgo_quantize_rows_fmt rejected its arguments")
+    return q, s
+
+
+def gemm_ref_rowa(a8, b8, sa, sb, g: int, fmt_a: int = 0, fmt_b: int = 0, rows=None, cols=None,
+                  nthreads: int | None = None) -> np.ndarray:
+    """Reference GEMM with per-row A scales: sa [M, K/g], sb [ceil(N/g), K/g]."""
+    a8 = np.ascontiguousarray(a8, dtype=np.uint8)
+    b8 = np.ascontiguousarray(b8, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sb = np.ascontiguousarray(sb, dtype=np.float32)
+    M, K = a8.shape
+    N, K2 = b8.shape
+    if K2 != K or K % g:
+        raise ValueError("bad K")
+    if sa.shape != (M, K // g) or sb.shape != ((N + g - 1) // g, K // g):
+        raise ValueError("bad scale shapes")
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    c = None if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    nr = M if r is None else r.size
+    nc = N if c is None else c.size
+    out = np.empty((nr, nc), dtype=np.float64)
+    rc = _load().dgo_gemm_ref_rowa(
+        _ptr(a8, ctypes.c_uint8), _ptr(b8, ctypes.c_uint8), _ptr(sa, ctypes.c_float),
+        _ptr(sb, ctypes.c_float), M, N, K, g, fmt_a, fmt_b,
+        None if r is None else _ptr(r, ctypes.c_int64), nr,
+        None if c is None else _ptr(c, ctypes.c_int64), nc,
+        _ptr(out, ctypes.c_double), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("dgo_gemm_ref_rowa rejected its arguments")
     return out
 
 

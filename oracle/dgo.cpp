@@ -52,8 +52,15 @@
 //    0.5 * y * (1 + erf(y / sqrt(2))) (the exact form; the pages name GELU
 //    without choosing an approximation).
 //
-// Scale tensors are row-major FP32: sa is [ceil(M/g)][K/g], sb is
-// [ceil(N/g)][K/g]. K must be a multiple of g.
+//  * Per-row A scales (the DeepGEMM-style template article, §3.4: scale
+//    factors per tensor or per channel, per channel the more accurate and the
+//    one the method usually takes): A carries one factor per row and g-wide
+//    K segment (1 x g blocks), B keeps its g x g blocks:
+//        ref[i,j]  = sum_kb (sa[i,kb] * sb[j/g,kb]) * P[i,j,kb]
+//    and the quantiser's 1 x g variant takes amax over one row's segment.
+//
+// Scale tensors are row-major FP32: sa is [ceil(M/g)][K/g] ([M][K/g] with
+// per-row A scales), sb is [ceil(N/g)][K/g]. K must be a multiple of g.
 //
 // Build: g++ -O2 -std=c++17 -ffp-contract=off -fPIC -shared -pthread.
 // No fast-math: the arithmetic above must be IEEE single/double as written.
@@ -323,6 +330,73 @@ int dgo_gemm_ref_fmt(const uint8_t* a, const uint8_t* b, const float* sa, const 
       const int64_t i = rows ? rows[r] : r;
       const uint8_t* arow = a + i * K;
       const float* sarow = sa + (i / g) * nkb;
+      for (int64_t c = 0; c < ncols; ++c) {
+        const int64_t j = cols ? cols[c] : c;
+        const uint8_t* brow = b + j * K;
+        const float* sbrow = sb + (j / g) * nkb;
+        double ref = 0.0;
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+          double p = 0.0;
+          for (int64_t k = kb * g; k < kb * g + g; ++k) p += ta[arow[k]] * tb[brow[k]];
+          const double s = (double)sarow[kb] * (double)sbrow[kb];
+          ref += s * p;
+        }
+        out[r * ncols + c] = ref;
+      }
+    }
+  });
+  return 0;
+}
+
+// Quantiser with 1 x g blocks (one factor per row and g-wide column segment):
+// scales receives [rows][cols/g]; otherwise as dgo_quantize_blocks_fmt.
+int dgo_quantize_rows_fmt(const float* x, int64_t rows, int64_t cols, int g, int fmt, uint8_t* q, float* scales,
+                          int nthreads) {
+  if (!x || !q || !scales || rows <= 0 || cols <= 0 || g <= 0 || cols % g != 0 || (fmt != 0 && fmt != 1)) return -1;
+  const float fmax = fmt == 1 ? 57344.0f : 448.0f;
+  const int64_t ncb = cols / g;
+  parallel_for(rows, nthreads, [&](int64_t lo, int64_t hi) {
+    for (int64_t r = lo; r < hi; ++r)
+      for (int64_t cb = 0; cb < ncb; ++cb) {
+        const float* seg = x + r * cols + cb * g;
+        float amax = 0.0f;
+        for (int64_t c = 0; c < g; ++c)
+          if (std::fabs(seg[c]) > amax) amax = std::fabs(seg[c]);
+        const float scale = amax > 0.0f ? amax / fmax : 1.0f;
+        scales[r * ncb + cb] = scale;
+        for (int64_t c = 0; c < g; ++c) q[r * cols + cb * g + c] = encode_fmt(fmt, seg[c] / scale);
+      }
+  });
+  return 0;
+}
+
+// Reference GEMM with per-row A scales: sa is [M][K/g] (one factor per row of
+// A and K segment), sb is [ceil(N/g)][K/g]; formats as dgo_gemm_ref_fmt.
+//   ref[i,j] = sum_kb (sa[i,kb] * sb[j/g,kb]) * P[i,j,kb]   (kb ascending)
+int dgo_gemm_ref_rowa(const uint8_t* a, const uint8_t* b, const float* sa, const float* sb, int64_t M, int64_t N,
+                      int64_t K, int g, int fmt_a, int fmt_b, const int64_t* rows, int64_t nrows,
+                      const int64_t* cols, int64_t ncols, double* out, int nthreads) {
+  if (!a || !b || !sa || !sb || !out || M <= 0 || N <= 0 || K <= 0 || g <= 0 || K % g != 0) return -1;
+  if ((fmt_a != 0 && fmt_a != 1) || (fmt_b != 0 && fmt_b != 1)) return -1;
+  if (!rows) nrows = M;
+  if (!cols) ncols = N;
+  for (int64_t r = 0; rows && r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= M) return -1;
+  for (int64_t c = 0; cols && c < ncols; ++c)
+    if (cols[c] < 0 || cols[c] >= N) return -1;
+
+  double ta[256], tb[256];
+  for (int c = 0; c < 256; ++c) {
+    ta[c] = decode_fmt(fmt_a, (uint8_t)c);
+    tb[c] = decode_fmt(fmt_b, (uint8_t)c);
+  }
+  const int64_t nkb = K / g;
+
+  parallel_for(nrows, nthreads, [&](int64_t lo, int64_t hi) {
+    for (int64_t r = lo; r < hi; ++r) {
+      const int64_t i = rows ? rows[r] : r;
+      const uint8_t* arow = a + i * K;
+      const float* sarow = sa + i * nkb;  // this row's own factors
       for (int64_t c = 0; c < ncols; ++c) {
         const int64_t j = cols ? cols[c] : c;
         const uint8_t* brow = b + j * K;
