@@ -7,12 +7,14 @@ FP32 promotion, BF16 epilogue) runs inside that one kernel launch.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--fmt e4m3|e5m2|e4m3xe5m2|e5m2xe4m3] [--gran 64|128|256]
-                  [--bias] [--act none|relu|gelu]
+                  [--bias] [--act none|relu|gelu] [--sa-rows 1]
 
 --fmt and --gran run the same workload with the operands in another FP8
 format or with another block granularity (default: E4M3 and the workload's
 own g); --bias and --act add the fused epilogue out = act(C + bias) (bias a
-seeded N(0, 0.5) vector); the default run is the E4M3 workload as specified.
+seeded N(0, 0.5) vector); --sa-rows 1 scales A per row and K segment (1 x g
+blocks, quantised by dg_quantize_fp8_rows) instead of per g x g block; the
+default run is the E4M3 workload as specified.
 
 Inputs: FP32 matrices drawn from the seeded generators in ``synth`` (the
 workload's shapes and value distributions), copied to the GPU and block
@@ -67,16 +69,16 @@ DEFAULT_WORKLOAD = 2      # small-M decode shape, M=64 N=4096 K=7168, g=128
 # workload and tagged with the hash of the kernel source the counters were
 # taken on. A different hash means the kernel changed since: traffic is null.
 TRAFFIC = {
-    "decode_m64_n4096_k7168": {"src": "489c5ba8a4ccd93a", "bytes": 33667468},
+    "decode_m64_n4096_k7168": {"src": "594ce43a939b1e30", "bytes": 33667891},
 }
 
 
 def _kernel_source_hash() -> str:
     import hashlib
 
+    # the sources of the default workload's kernel (the streaming class) and of its dispatch
     h = hashlib.sha256()
-    for name in ("gemm_fp8_nt.hip", "gemm_fp8_nt.h", "gemm_common.h", "gemm_fp8_nt_big.hip", "gemm_fp8_nt_stream.hip",
-                 "dg_host.hip"):
+    for name in ("gemm_fp8_nt_stream.hip", "gemm_common.h", "gemm_fp8_nt.h", "dg_host.hip"):
         with open(os.path.join(ROOT, "fp8_block_scaled_scales_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -99,11 +101,12 @@ def make_bias(N: int):
     return synth.normal(BIAS_SEED, (N,), sigma=0.5).astype("float32")
 
 
-def algorithmic(w, g=None) -> tuple[float, float]:
+def algorithmic(w, g=None, sa_rows=None) -> tuple[float, float]:
     M, N, K = w["M"], w["N"], w["K"]
     g = g or w["g"]
+    ra = sa_rows or g  # A rows per factor
     flops = 2.0 * M * N * K
-    nbytes = M * K + N * K + 4 * (math.ceil(M / g) + math.ceil(N / g)) * (K // g) + 2 * M * N
+    nbytes = M * K + N * K + 4 * (math.ceil(M / ra) + math.ceil(N / g)) * (K // g) + 2 * M * N
     return flops, float(nbytes)
 
 
@@ -113,14 +116,17 @@ def bound_of(w) -> str:
     return "hbm" if flops / nbytes < PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
 
 
-def make_inputs(c: int, dev, g: int, fa: int = 0, fb: int = 0):
+def make_inputs(c: int, dev, g: int, fa: int = 0, fb: int = 0, sa_rows: int | None = None):
     """Quantised GPU inputs of workload c at granularity g, formats fa/fb: (a8, sa, b8, sb)."""
     import torch
 
     import fp8_block_scaled_scales_amd as dg
 
     xa = torch.from_numpy(synth.make_a(c)).to(dev)
-    a8, sa = dg.dg_quantize_fp8_blocks(xa, gran=g, fmt=fa)
+    if sa_rows == 1:
+        a8, sa = dg.dg_quantize_fp8_rows(xa, gran=g, fmt=fa)
+    else:
+        a8, sa = dg.dg_quantize_fp8_blocks(xa, gran=g, fmt=fa)
     del xa
     xb = torch.from_numpy(synth.make_b(c)).to(dev)
     b8, sb = dg.dg_quantize_fp8_blocks(xb, gran=g, fmt=fb)
@@ -130,7 +136,7 @@ def make_inputs(c: int, dev, g: int, fa: int = 0, fb: int = 0):
 
 
 def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int = 0, fb: int = 0,
-            bias: bool = False, act: int = 0):
+            bias: bool = False, act: int = 0, sa_rows: int | None = None):
     import torch
 
     import fp8_block_scaled_scales_amd as dg
@@ -139,7 +145,7 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
     M, N, K = w["M"], w["N"], w["K"]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    a8, sa, b8, sb = make_inputs(c, dev, g, fa, fb)
+    a8, sa, b8, sb = make_inputs(c, dev, g, fa, fb, sa_rows)
     set_bytes = a8.numel() + b8.numel() + 4 * (sa.numel() + sb.numel()) + 2 * M * N
     if sets is None:
         sets = max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes) + 1))
@@ -155,7 +161,10 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
 
     def launch(i, st):
         x = bufs[i % sets]
-        if bias or act:
+        if sa_rows == 1:
+            dg.dg_gemm_fp8_nt_ex(x[0], x[2], x[1], x[3], out=x[4], gran=g, sa_rows=1, fmt_a=fa, fmt_b=fb, bias=tbias,
+                                 act=act, stream=st)
+        elif bias or act:
             dg.dg_gemm_fp8_nt_epi(x[0], x[2], x[1], x[3], out=x[4], gran=g, fmt_a=fa, fmt_b=fb, bias=tbias, act=act,
                                   stream=st)
         elif fa == 0 and fb == 0:
@@ -203,7 +212,8 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
     return ms, sets, finite, L
 
 
-def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, bias: bool = False, act: int = 0, budget_s: float = 10.0):
+def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, bias: bool = False, act: int = 0, budget_s: float = 10.0,
+            sa_rows: int | None = None):
     """The oracle on a bounded sample of workload c, in TFLOP/s (FP64 on the host)."""
     import numpy as np
 
@@ -212,13 +222,18 @@ def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, bias: bool = False, act: i
     w = synth.WORKLOADS[c]
     M, N, K = w["M"], w["N"], w["K"]
     threads = oracle.default_threads()
-    a8, sa = oracle.quantize_blocks_fmt(synth.make_a(c), g, fa)
+    if sa_rows == 1:
+        a8, sa = oracle.quantize_rows_fmt(synth.make_a(c), g, fa)
+    else:
+        a8, sa = oracle.quantize_blocks_fmt(synth.make_a(c), g, fa)
     b8, sb = oracle.quantize_blocks_fmt(synth.make_b(c), g, fb)
 
     bvec = make_bias(N) if bias else None
 
     def ref(rows=None):
-        if fa == 0 and fb == 0:
+        if sa_rows == 1:
+            r = oracle.gemm_ref_rowa(a8, b8, sa, sb, g, fa, fb, rows=rows)
+        elif fa == 0 and fb == 0:
             r = oracle.gemm_ref(a8, b8, sa, sb, g, rows=rows)
         else:
             r = oracle.gemm_ref_fmt(a8, b8, sa, sb, g, fa, fb, rows=rows)
@@ -266,6 +281,8 @@ def main():
                     help="block granularity (default: the workload's)")
     ap.add_argument("--bias", action="store_true", help="fused epilogue: add a bias vector")
     ap.add_argument("--act", default="none", choices=sorted(ACTS), help="fused epilogue activation")
+    ap.add_argument("--sa-rows", type=int, default=None, choices=(1,),
+                    help="1: per-row A factors (1 x g blocks) instead of g x g blocks")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes three times (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -297,9 +314,9 @@ def main():
     if w["K"] % g:
         raise SystemExit("--gran %d does not divide K = %d" % (g, w["K"]))
     fa, fb = FORMATS[args.fmt]
-    flops, nbytes = algorithmic(w, g)
+    flops, nbytes = algorithmic(w, g, args.sa_rows)
     act = ACTS[args.act]
-    ms, sets, finite, glen = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb, args.bias, act)
+    ms, sets, finite, glen = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb, args.bias, act, args.sa_rows)
     if not finite:
         raise SystemExit("GEMM output holds non-finite values")
     sec = ms * 1e-3
@@ -309,10 +326,10 @@ def main():
         achieved, peak, unit = tflops, PEAK_FP8_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
-    tr = TRAFFIC.get(w["name"]) if (fa, fb, g, args.bias, act) == (0, 0, w["g"], False, 0) else None
+    tr = TRAFFIC.get(w["name"]) if (fa, fb, g, args.bias, act, args.sa_rows) == (0, 0, w["g"], False, 0, None) else None
     traffic = tr["bytes"] if tr and tr["src"] == _kernel_source_hash() else None
 
-    cpu = None if args.no_cpu_baseline else cpu_leg(c, g, fa, fb, args.bias, act)
+    cpu = None if args.no_cpu_baseline else cpu_leg(c, g, fa, fb, args.bias, act, sa_rows=args.sa_rows)
 
     line = {
         "metric": "FP8 block-scaled GEMM TFLOPS and % of MI355X dense FP8 peak (1 GPU)",
@@ -329,6 +346,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w["name"], "M": w["M"], "N": w["N"], "K": w["K"], "gran": g, "fmt": args.fmt,
                    "epilogue": ("bias+" if args.bias else "") + args.act,
+                   "a_scales": "1x%d" % g if args.sa_rows == 1 else "%dx%d" % (g, g),
                    "layout": "NT", "out": "bf16", "input_sets": sets,
                    "launch": "hipGraph of %d launches, replayed %d times" % (glen, args.steps // glen),
                    "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),

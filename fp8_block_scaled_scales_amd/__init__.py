@@ -56,6 +56,11 @@ def _load():
     lib.dg_gemm_fp8_nt_epi.restype = ctypes.c_int
     lib.dg_gemm_fp8_nt_epi.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        vp, ctypes.c_int, vp]
+    lib.dg_gemm_fp8_nt_ex.restype = ctypes.c_int
+    lib.dg_gemm_fp8_nt_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.dg_quantize_fp8_rows.restype = ctypes.c_int
+    lib.dg_quantize_fp8_rows.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.dg_quantize_e4m3_blocks.restype = ctypes.c_int
     lib.dg_quantize_e4m3_blocks.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp]
     lib.dg_quantize_fp8_blocks.restype = ctypes.c_int
@@ -121,21 +126,22 @@ def _check(t, name, dtypes, shape, device):
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
 
 
-def _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, where, bias=None, act=DG_ACT_NONE):
+def _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, where, bias=None, act=DG_ACT_NONE, sa_rows=None):
     if a.dim() != 2 or b.dim() != 2:
         raise ValueError("a and b must be 2-D")
     M, K = a.shape
     N = b.shape[0]
     dev = a.device
-    if dev.type != "cuda":
-        raise ValueError("a must be a GPU tensor")
     if gran not in _GRANS or K % gran:
         raise ValueError("gran must be 64, 128 or 256 and divide K")
     if fmt_a not in _FP8_OF or fmt_b not in _FP8_OF:
         raise ValueError("formats must be DG_FMT_E4M3 or DG_FMT_E5M2")
+    sa_rows = gran if sa_rows is None else sa_rows
+    if sa_rows not in (gran, 1):
+        raise ValueError("sa_rows must be gran (g x g blocks) or 1 (per-row factors)")
     _check(a, "a", _FP8_OF[fmt_a], (M, K), dev)
     _check(b, "b", _FP8_OF[fmt_b], (N, K), dev)
-    _check(sa, "sa", (torch.float32,), ((M + gran - 1) // gran, K // gran), dev)
+    _check(sa, "sa", (torch.float32,), ((M + sa_rows - 1) // sa_rows, K // gran), dev)
     _check(sb, "sb", (torch.float32,), ((N + gran - 1) // gran, K // gran), dev)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -144,9 +150,15 @@ def _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, where, bias=None, act=D
         _check(bias, "bias", (torch.float32,), (N,), dev)
     if act not in (DG_ACT_NONE, DG_ACT_RELU, DG_ACT_GELU):
         raise ValueError("act must be DG_ACT_NONE, DG_ACT_RELU or DG_ACT_GELU")
+    if dev.type != "cuda":
+        raise ValueError("a must be a GPU tensor")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
-        if where == "dg_gemm_fp8_nt_epi":
+        if where == "dg_gemm_fp8_nt_ex":
+            rc = _lib.dg_gemm_fp8_nt_ex(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
+                                        M, N, K, gran, sa_rows, fmt_a, fmt_b,
+                                        None if bias is None else bias.data_ptr(), act, s.cuda_stream)
+        elif where == "dg_gemm_fp8_nt_epi":
             rc = _lib.dg_gemm_fp8_nt_epi(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
                                          M, N, K, gran, fmt_a, fmt_b, None if bias is None else bias.data_ptr(),
                                          act, s.cuda_stream)
@@ -191,6 +203,17 @@ def dg_gemm_fp8_nt_epi(a, b, sa, sb, out=None, gran: int = 128, fmt_a: int = DG_
     return _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, "dg_gemm_fp8_nt_epi", bias, act)
 
 
+def dg_gemm_fp8_nt_ex(a, b, sa, sb, out=None, gran: int = 128, sa_rows: int | None = None,
+                      fmt_a: int = DG_FMT_E4M3, fmt_b: int = DG_FMT_E4M3, bias=None, act: int = DG_ACT_NONE,
+                      stream=None):
+    """dg_gemm_fp8_nt_epi with A's factor blocks chosen: sa_rows = gran (g x g, the default) or 1.
+
+    With sa_rows = 1, sa is [M, K/gran] float32: one factor per row of A and K
+    segment (per-row A scales); B keeps its g x g blocks.
+    """
+    return _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, "dg_gemm_fp8_nt_ex", bias, act, sa_rows)
+
+
 def _quantize(x, gran, fmt, q, scales, stream, where):
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be a 2-D tensor")
@@ -205,13 +228,17 @@ def _quantize(x, gran, fmt, q, scales, stream, where):
     _check(x, "x", (torch.float32,), (rows, cols), dev)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    brows = 1 if where == "dg_quantize_fp8_rows" else gran  # rows per block
     if scales is None:
-        scales = torch.empty(((rows + gran - 1) // gran, cols // gran), dtype=torch.float32, device=dev)
+        scales = torch.empty(((rows + brows - 1) // brows, cols // gran), dtype=torch.float32, device=dev)
     _check(q, "q", _FP8_OF[fmt], (rows, cols), dev)
-    _check(scales, "scales", (torch.float32,), ((rows + gran - 1) // gran, cols // gran), dev)
+    _check(scales, "scales", (torch.float32,), ((rows + brows - 1) // brows, cols // gran), dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
-        if fmt == DG_FMT_E4M3 and where == "dg_quantize_e4m3_blocks":
+        if where == "dg_quantize_fp8_rows":
+            rc = _lib.dg_quantize_fp8_rows(x.data_ptr(), rows, cols, gran, fmt, q.data_ptr(), scales.data_ptr(),
+                                           s.cuda_stream)
+        elif fmt == DG_FMT_E4M3 and where == "dg_quantize_e4m3_blocks":
             rc = _lib.dg_quantize_e4m3_blocks(x.data_ptr(), rows, cols, gran, q.data_ptr(), scales.data_ptr(),
                                               s.cuda_stream)
         else:
@@ -239,6 +266,12 @@ def dg_quantize_fp8_blocks(x, gran: int = 128, fmt: int = DG_FMT_E4M3, q=None, s
     return _quantize(x, gran, fmt, q, scales, stream, "dg_quantize_fp8_blocks")
 
 
-__all__ = ["dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "dg_gemm_fp8_nt_epi", "DG_ACT_NONE", "DG_ACT_RELU", "DG_ACT_GELU", "dg_quantize_e4m3_blocks", "dg_quantize_fp8_blocks",
+def dg_quantize_fp8_rows(x, gran: int = 128, fmt: int = DG_FMT_E4M3, q=None, scales=None, stream=None):
+    """1 x gran quantisation on the GPU: one factor per row and gran-wide segment, scales [rows, cols/gran]."""
+    return _quantize(x, gran, fmt, q, scales, stream, "dg_quantize_fp8_rows")
+
+
+__all__ = ["dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "dg_gemm_fp8_nt_epi", "dg_gemm_fp8_nt_ex", "DG_ACT_NONE",
+           "DG_ACT_RELU", "DG_ACT_GELU", "dg_quantize_e4m3_blocks", "dg_quantize_fp8_blocks", "dg_quantize_fp8_rows",
            "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError", "DG_OK", "DG_EINVAL",
            "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH", "DG_FMT_E4M3", "DG_FMT_E5M2", "LIB_PATH"]

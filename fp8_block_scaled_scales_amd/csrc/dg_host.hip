@@ -182,8 +182,9 @@ int device_ready(int* dev_out = nullptr) {
 namespace {
 
 int gemm(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M, int64_t N, int64_t K,
-         int gran, int fmt_a, int fmt_b, const float* bias, int act, void* stream) {
+         int gran, int sa_rows, int fmt_a, int fmt_b, const float* bias, int act, void* stream) {
   if (!a || !b || !sa || !sb || !out) return DG_EINVAL;
+  if (sa_rows != gran && sa_rows != 1) return DG_EINVAL;
   if ((fmt_a != DG_FMT_E4M3 && fmt_a != DG_FMT_E5M2) || (fmt_b != DG_FMT_E4M3 && fmt_b != DG_FMT_E5M2))
     return DG_EINVAL;
   if (act != DG_ACT_NONE && act != DG_ACT_RELU && act != DG_ACT_GELU) return DG_EINVAL;
@@ -217,6 +218,7 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   p.gran = kernel_gran(gran);
   p.sshift = gran == 256 ? 1 : 0;
   p.fmt = (fmt_a == DG_FMT_E5M2 ? 1 : 0) | (fmt_b == DG_FMT_E5M2 ? 2 : 0);
+  p.rowa = sa_rows == 1 ? 1 : 0;
   p.vec_store = (((uintptr_t)out & 15) == 0 && N % 8 == 0) ? 1 : 0;
   p.ksplit = pl.ksplit;
   p.ws = pl.ksplit > 1 ? g_ws[dev] : nullptr;
@@ -225,20 +227,23 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   p.act = act;
   if (log_enabled())
     std::fprintf(stderr,
-                 "dg_gemm_fp8_nt M=%lld N=%lld K=%lld g=%d fmt=%d,%d bias=%d act=%d -> kernel %d (%dx%d, %d "
-                 "stages, %d waves) ksplit %d grid %lld\n",
-                 (long long)M, (long long)N, (long long)K, gran, fmt_a, fmt_b, bias ? 1 : 0, act, e->id, e->bm,
+                 "dg_gemm_fp8_nt M=%lld N=%lld K=%lld g=%d sa_rows=%d fmt=%d,%d bias=%d act=%d -> kernel %d (%dx%d, "
+                 "%d stages, %d waves) ksplit %d grid %lld\n",
+                 (long long)M, (long long)N, (long long)K, gran, sa_rows, fmt_a, fmt_b, bias ? 1 : 0, act, e->id, e->bm,
                  e->bn, e->stages, e->waves, pl.ksplit, (long long)(pl.tiles * pl.ksplit));
   t_last_hip = e->launch(p, static_cast<hipStream_t>(stream));
   return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
 }
 
-int quantize(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q, float* scales, void* stream) {
+// block_rows: rows per block, gran (g x g blocks) or 1 (1 x g blocks).
+int quantize(const float* x, int64_t rows, int64_t cols, int gran, int block_rows, int fmt, void* q, float* scales,
+             void* stream) {
   if (!x || !q || !scales) return DG_EINVAL;
   if (fmt != DG_FMT_E4M3 && fmt != DG_FMT_E5M2) return DG_EINVAL;
   if (rows <= 0 || cols <= 0 || rows > DG_MAX_DIM || cols > DG_MAX_DIM) return DG_EINVAL;
   if ((gran != 64 && gran != 128 && gran != 256) || cols % gran != 0) return DG_EINVAL;
-  if (((rows + gran - 1) / gran) * (cols / gran) > 0x7fffffff) return DG_EINVAL;
+  if (block_rows != gran && block_rows != 1) return DG_EINVAL;
+  if (((rows + block_rows - 1) / block_rows) * (cols / gran) > 0x7fffffff) return DG_EINVAL;
   if (((uintptr_t)x & 15) || ((uintptr_t)q & 3) || ((uintptr_t)scales & 3)) return DG_EALIGN;
   const int rc = device_ready();
   if (rc != DG_OK) return rc;
@@ -251,9 +256,10 @@ int quantize(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void
   p.gran = gran;
   p.fmt = fmt;
   if (log_enabled())
-    std::fprintf(stderr, "dg_quantize_fp8_blocks rows=%lld cols=%lld g=%d fmt=%d\n", (long long)rows,
-                 (long long)cols, gran, fmt);
-  t_last_hip = dg::launch_quant(p, static_cast<hipStream_t>(stream));
+    std::fprintf(stderr, "dg_quantize_fp8 rows=%lld cols=%lld block %dx%d fmt=%d\n", (long long)rows,
+                 (long long)cols, block_rows, gran, fmt);
+  t_last_hip = block_rows == 1 ? dg::launch_quant_rows(p, static_cast<hipStream_t>(stream))
+                               : dg::launch_quant(p, static_cast<hipStream_t>(stream));
   return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
 }
 
@@ -268,7 +274,8 @@ const char* dg_strerror(int code) {
     case DG_OK: return "success";
     case DG_EINVAL:
       return "invalid argument (null pointer, bad dimension, K not a multiple of gran, gran not 64/128/256, "
-             "or a format code other than DG_FMT_E4M3/DG_FMT_E5M2)";
+             "sa_rows neither gran nor 1, a format code other than DG_FMT_E4M3/DG_FMT_E5M2, or an unknown "
+             "activation)";
     case DG_EALIGN: return "misaligned pointer (a, b need 16 bytes; sa, sb 4 bytes; out 2 bytes)";
     case DG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
     case DG_ELAUNCH:
@@ -297,28 +304,39 @@ int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info)
 
 int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
                    int64_t N, int64_t K, int gran, void* stream) {
-  return gemm(a, b, sa, sb, out, M, N, K, gran, DG_FMT_E4M3, DG_FMT_E4M3, nullptr, DG_ACT_NONE, stream);
+  return gemm(a, b, sa, sb, out, M, N, K, gran, gran, DG_FMT_E4M3, DG_FMT_E4M3, nullptr, DG_ACT_NONE, stream);
 }
 
 int dg_gemm_fp8_nt_fmt(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
                        int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, void* stream) {
-  return gemm(a, b, sa, sb, out, M, N, K, gran, fmt_a, fmt_b, nullptr, DG_ACT_NONE, stream);
+  return gemm(a, b, sa, sb, out, M, N, K, gran, gran, fmt_a, fmt_b, nullptr, DG_ACT_NONE, stream);
 }
 
 int dg_gemm_fp8_nt_epi(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
                        int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, const float* bias, int act,
                        void* stream) {
-  return gemm(a, b, sa, sb, out, M, N, K, gran, fmt_a, fmt_b, bias, act, stream);
+  return gemm(a, b, sa, sb, out, M, N, K, gran, gran, fmt_a, fmt_b, bias, act, stream);
+}
+
+int dg_gemm_fp8_nt_ex(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
+                      int64_t N, int64_t K, int gran, int sa_rows, int fmt_a, int fmt_b, const float* bias, int act,
+                      void* stream) {
+  return gemm(a, b, sa, sb, out, M, N, K, gran, sa_rows, fmt_a, fmt_b, bias, act, stream);
 }
 
 int dg_quantize_fp8_blocks(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q, float* scales,
                            void* stream) {
-  return quantize(x, rows, cols, gran, fmt, q, scales, stream);
+  return quantize(x, rows, cols, gran, gran, fmt, q, scales, stream);
+}
+
+int dg_quantize_fp8_rows(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q, float* scales,
+                         void* stream) {
+  return quantize(x, rows, cols, gran, 1, fmt, q, scales, stream);
 }
 
 int dg_quantize_e4m3_blocks(const float* x, int64_t rows, int64_t cols, int gran, void* q, float* scales,
                             void* stream) {
-  return quantize(x, rows, cols, gran, DG_FMT_E4M3, q, scales, stream);
+  return quantize(x, rows, cols, gran, gran, DG_FMT_E4M3, q, scales, stream);
 }
 
 }  // extern "C"

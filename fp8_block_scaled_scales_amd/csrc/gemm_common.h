@@ -65,6 +65,36 @@ __device__ __forceinline__ void lds_dma16(v4i rsrc, uint32_t lds_addr, uint32_t 
       : "memory", "m0");
 }
 
+// One 4-byte-per-lane HBM->LDS copy: lane L's 4 bytes land at LDS byte
+// lds_addr + 4*L; otherwise as lds_dma16.
+__device__ __forceinline__ void lds_dma4(v4i rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff = 0) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
+
+// Per-row A factors of one pipeline step (A scaled per row and K segment,
+// 1 x g blocks): an FP32 array [SEGS][ROWS] in LDS, entry seg*ROWS + r the
+// factor of tile row r for the step's K segment seg. Copied in 64-entry
+// pieces; piece p (entries 64p .. 64p+63) lands at lds + 256*p, entries past
+// ROWS*SEGS read zero into the padding. rsa covers the tile's rows of the
+// [M][nks] factor tensor from the tile's first row (rows past M read zero);
+// ks0 is the factor column of the step's first segment. valid = false moves
+// no data (both offsets past any descriptor range, without wrapping).
+template <int ROWS, int SEGS>
+__device__ __forceinline__ void stage_row_scales(v4i rsa, uint8_t* lds, uint32_t nks, uint32_t ks0, int piece,
+                                                 int lane, bool valid = true) {
+  const uint32_t e = (uint32_t)(piece * 64 + lane);
+  const uint32_t voff = e < (uint32_t)(ROWS * SEGS) ? ((e % ROWS) * nks + e / ROWS) * 4u : 0x40000000u;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  lds_dma4(rsa, __builtin_amdgcn_readfirstlane(lds_base + piece * 256), voff,
+           __builtin_amdgcn_readfirstlane(valid ? ks0 * 4u : 0x40000000u));
+}
+
 // One instruction of a slab copy: rows 8*grp .. 8*grp+7 of a [rows x 128-byte]
 // slab starting at column byte k0 of the rows the descriptor covers, into
 // LDS at lds + 1024*grp (64 lanes x 16 B, written lane-contiguously from the

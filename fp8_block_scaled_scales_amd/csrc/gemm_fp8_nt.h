@@ -16,6 +16,7 @@ struct GemmArgs {
   int gran;       // K segment of the kernel (64 or 128)
   int sshift;     // scale blocks are (gran << sshift) square: 1 for g = 256 on the gran-128 kernels
   int fmt;        // bit 0: A is E5M2 (else E4M3); bit 1: B is E5M2
+  int rowa;       // A's factors are per row and K segment (1 x g blocks): sa is [M][K/g]
   int vec_store;  // out is 16-byte aligned and N % 8 == 0: full-row chunks use 16-byte stores
   int ksplit;     // workgroups per output tile along K (1 = no split)
   float* ws;      // split-K partial tiles, tiles * ksplit * bm * bn floats (ksplit > 1)

@@ -24,6 +24,10 @@
 //     instruction, one (g=64) or two chained (g=128) instructions per segment
 //     starting from a zero accumulator;
 //   * promotion: acc = fma(partial, sa[mb,kb]*sb[nb,kb], acc), VALU, FP32;
+//     with per-row A factors (one per row of A and K segment, the template
+//     article's per-channel choice, §3.4) each step's factors for the tile's
+//     rows are copied into LDS beside its slabs and the lane's sixteen row
+//     factors replace sa[mb,kb];
 //   * epilogue: FP32 -> BF16 round-to-nearest-even, staged through LDS so each
 //     lane writes 16 contiguous bytes, masked at the M and N edges.
 //
@@ -78,8 +82,8 @@ __device__ __forceinline__ void wait_steps(int steps) {
 //
 // G is the K segment contracted before each promotion; the scale blocks are
 // sg x sg with sg = G << sshift (g = 256 runs G = 128 with one factor per two
-// segments).
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI>
+// segments). ROWA: A's factors are per row, sa is [M][K/sg].
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, bool ROWA>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ b, const float* __restrict__ sa,
     const float* __restrict__ sb, uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
@@ -89,15 +93,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
   constexpr int NT = 64 * NWAVES;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 sub-tiles per wave
-  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int SEGS = BK / G;      // K segments per pipeline step
   constexpr int KSTEPS = G / 64;    // MFMA K-steps per segment
-  constexpr int LOADS = (BM / 8 + BN / 8) / NWAVES;  // buffer_load ... lds per wave per step
+  constexpr int SCL = ROWA ? NWAVES * 256 : 0;  // per-row factors of a step: [SEGS][BM] FP32, a piece per wave
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE_BYTES = A_BYTES + B_BYTES + SCL;
+  // buffer_load ... lds per wave per step (the factor piece included)
+  constexpr int LOADS = (BM / 8 + BN / 8) / NWAVES + (ROWA ? 1 : 0);
   constexpr int LDC = BN + 8;       // bf16 pitch of the epilogue tile (16-byte pad)
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 sub-tiles");
   static_assert(G % 32 == 0 && BK % G == 0, "granularity must cover whole sub-tiles and steps");
   static_assert(BM * LDC * 2 <= STAGES * STAGE_BYTES, "epilogue tile must fit in the ring");
   static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(BM * SEGS <= NWAVES * 64, "a step's row factors: one 64-entry piece per wave");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
@@ -121,6 +128,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
   // (g >= 32, sub-tiles aligned to 32); sub-tiles past the edge clamp to the
   // last block row so the index stays inside the scale tensor.
   const int sg = G << sshift, nks = K / sg;  // scale blocks
+  const v4i rsa = ROWA ? rsrc_words(sa + (int64_t)m0 * nks, (uint32_t)min(BM, M - m0) * (uint32_t)nks * 4u) : (v4i){};
+  auto stage_step = [&](int s) {  // the copies of this split's step s into its ring slot
+    uint8_t* slot = smem + (s % STAGES) * STAGE_BYTES;
+    const int st = st0 + s;
+    if constexpr (ROWA)
+      stage_row_scales<BM, SEGS>(rsa, slot + A_BYTES + B_BYTES, (uint32_t)nks, (uint32_t)((st * SEGS) >> sshift), wave,
+                                 lane);
+    stage_slab<BM, NWAVES>(ra, slot, uK, st * BK, wave, lane);
+    stage_slab<BN, NWAVES>(rb, slot + A_BYTES, uK, st * BK, wave, lane);
+  };
   const float* sa_row[TM];
   const float* sb_row[TN];
 #pragma unroll
@@ -147,13 +164,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
 
   // Prologue: fill STAGES-1 ring slots.
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
-    if (s < nsteps) {
-      uint8_t* slot = smem + s * STAGE_BYTES;
-      stage_slab<BM, NWAVES>(ra, slot, uK, (st0 + s) * BK, wave, lane);
-      stage_slab<BN, NWAVES>(rb, slot + A_BYTES, uK, (st0 + s) * BK, wave, lane);
-    }
-  }
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nsteps) stage_step(s);
 
   const int arow = wm * WTM + (lane & 31);
   const int brow = wn * WTN + (lane & 31);
@@ -164,15 +176,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     wait_steps<LOADS, STAGES - 2>(min(STAGES - 2, nsteps - 1 - s));
     __syncthreads();  // step s visible to all waves; slot (s-1)%STAGES free
 
-    if (s + STAGES - 1 < nsteps) {
-      const int sn = s + STAGES - 1;
-      uint8_t* slot = smem + (sn % STAGES) * STAGE_BYTES;
-      stage_slab<BM, NWAVES>(ra, slot, uK, (st0 + sn) * BK, wave, lane);
-      stage_slab<BN, NWAVES>(rb, slot + A_BYTES, uK, (st0 + sn) * BK, wave, lane);
-    }
+    if (s + STAGES - 1 < nsteps) stage_step(s + STAGES - 1);
 
     const uint8_t* As = smem + (s % STAGES) * STAGE_BYTES;
     const uint8_t* Bs = As + A_BYTES;
+    // ROWA: the step's factors [SEGS][BM]; this lane's rows of sub-tile i are
+    // wm*WTM + 32i + 8c + 4*half .. +3
+    const float* const scl = reinterpret_cast<const float*>(As + A_BYTES + B_BYTES) + wm * WTM + 4 * half;
 #pragma unroll
     for (int seg = 0; seg < SEGS; ++seg) {
       const int kb = (st0 + s) * SEGS + seg;
@@ -191,15 +201,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
       for (int j = 0; j < TN; ++j) sbv[j] = sb_row[j][kb >> sshift];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const float sav = sa_row[i][kb >> sshift];
+        const float sav = ROWA ? 0.0f : sa_row[i][kb >> sshift];
+        v4f sr[4];
+        if constexpr (ROWA) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sr[c] = *reinterpret_cast<const v4f*>(scl + seg * BM + i * 32 + 8 * c);
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           v16f p = mfma_fp8<FMT>(af[i][0], bfr[j][0], (v16f){});
 #pragma unroll
           for (int ks = 1; ks < KSTEPS; ++ks) p = mfma_fp8<FMT>(af[i][ks], bfr[j][ks], p);
-          const float sc = sav * sbv[j];
+          if constexpr (ROWA) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc, acc[i][j][v]);
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sr[v >> 2][v & 3] * sbv[j], acc[i][j][v]);
+          } else {
+            const float sc = sav * sbv[j];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc, acc[i][j][v]);
+          }
         }
       }
     }
@@ -334,22 +354,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
 
 // ---- launch table -------------------------------------------------------------
 
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI>
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, bool ROWA>
 static hipError_t launch_tiled_fa(const GemmArgs& p, hipStream_t stream) {
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI>),
+  hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, ROWA>),
                      dim3(tiles_m * tiles_n * p.ksplit), dim3(64 * WM * WN), 0, stream, p.a, p.b, p.sa, p.sb, p.out,
                      (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.ksplit, p.ws, p.counters,
                      p.sshift, p.bias, p.act == 1 ? 1 : 0);
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI>
+static hipError_t launch_tiled_sa(const GemmArgs& p, hipStream_t stream) {
+  return p.rowa ? launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, true>(p, stream)
+                : launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, false>(p, stream);
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT>
 static hipError_t launch_tiled_fmt(const GemmArgs& p, hipStream_t stream) {
   switch (epilogue_form(p.bias, p.act)) {
-    case 0: return launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 0>(p, stream);
-    case 1: return launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 1>(p, stream);
-    case 2: return launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 2>(p, stream);
+    case 0: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 0>(p, stream);
+    case 1: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 1>(p, stream);
+    case 2: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -39,6 +39,13 @@
 // Epilogue: the BF16 tile goes through LDS in two 128-row passes so every
 // lane stores 16 contiguous bytes, masked at the M and N edges.
 //
+// Per-row A factors (ROWA; one factor per row of A and K segment, the
+// template article's per-channel choice, §3.4): each step's factors for the
+// tile's 256 rows are copied with the step's slabs into a 2 KB area after
+// them (one 4-byte-per-lane copy per wave), and a promotion multiplies the
+// lane's four (16x16 layout) or sixteen (32x32 layout) row factors by the
+// column block's factor in place of the one block product.
+//
 // MFMA layouts used. 16x16x128: lane l supplies row (A) or column (B) l%16
 // and 32 K bytes starting at 32*(l/16); result register v of lane l is row
 // 4*(l/16)+v, column l%16. 32x32x64: lane l supplies row/column l%32 and 32 K
@@ -93,8 +100,9 @@ struct Acc<64, WTM, WTN> {
 
 // G is the K segment the matrix cores contract before each promotion (64 or
 // 128). The scale blocks are sg x sg with sg = G << sshift: for g = 256 the
-// G = 128 kernel promotes every 128 K with its 256-block's factor.
-template <int G, int BN, int WM, int GROUP_M, int FMT, int EPI>
+// G = 128 kernel promotes every 128 K with its 256-block's factor. ROWA: A's
+// factors are per row, sa is [M][K/sg].
+template <int G, int BN, int WM, int GROUP_M, int FMT, int EPI, bool ROWA>
 __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
                                                       const float* __restrict__ sa, const float* __restrict__ sb,
                                                       uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
@@ -104,13 +112,17 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   constexpr int WN = NW / WM;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int STAGE = A_BYTES + BN * BK;
+  constexpr int SEGS = BK / G;                    // K segments per step
+  constexpr int SCL = ROWA ? NW * 256 : 0;        // per-row factors of a step: [SEGS][BM] FP32, one piece per wave
+  constexpr int SLOT = STAGE + SCL;
   constexpr int LDC = BN + 8;  // bf16 pitch of an epilogue pass
   static_assert(WTM == 64 || WTM == 128, "a wave's rows lie in one 128-row scale block");
   static_assert(WTN % 16 == 0 && WTN <= 128, "a wave's columns touch at most two 128-column scale blocks");
   static_assert(G == 128 || WTN == 64, "g = 64: one 64-column scale block per wave");
   static_assert(BN % 8 == 0 && BN / 8 <= 4 * NW, "B copies: at most four row groups per wave");
   static_assert(128 * LDC * 2 <= 2 * STAGE, "an epilogue pass must fit in the ring");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  static_assert(BM * SEGS <= NW * 64, "a step's row factors: one 64-entry piece per wave");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOT];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -128,6 +140,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   const int nkb = K / G;  // K segments
   const int sg = G << sshift, nks = K / sg;  // scale blocks
   const int nsteps = (K + BK - 1) / BK;
+  const v4i rsa = ROWA ? rsrc_words(sa + (int64_t)m0 * nks, (uint32_t)min(BM, M - m0) * (uint32_t)nks * 4u) : (v4i){};
 
   // Scale rows of this wave. Blocks past the edge clamp to the last block
   // (their data is zero). g >= 128: one A block; the wave's columns may cross
@@ -158,7 +171,8 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   // This wave's share of a step's copies: A row groups 8i + wave (i < 4) and
   // B row groups 8i + wave below BN / 8, into the slot of step t.
   auto issue_step = [&](int t) {
-    uint8_t* slot = smem + (t & 1) * STAGE;
+    uint8_t* slot = smem + (t & 1) * SLOT;
+    if constexpr (ROWA) stage_row_scales<BM, SEGS>(rsa, slot + STAGE, (uint32_t)nks, (uint32_t)((t * SEGS) >> sshift), wave, lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i) stage_group<1>(ra, slot, uK, (uint32_t)t * BK, i * NW + wave, lane);
 #pragma unroll
@@ -186,8 +200,9 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
     auto issue_next = [&](int who) {
       if (s + 1 < nsteps && grp == who) issue_step(s + 1);
     };
-    const uint8_t* As = smem + (s & 1) * STAGE + wm * WTM * BK;
-    const uint8_t* Bs = smem + (s & 1) * STAGE + A_BYTES + wn * WTN * BK;
+    const uint8_t* As = smem + (s & 1) * SLOT + wm * WTM * BK;
+    const uint8_t* Bs = smem + (s & 1) * SLOT + A_BYTES + wn * WTN * BK;
+    const float* scl = reinterpret_cast<const float*>(smem + (s & 1) * SLOT + STAGE);  // [SEGS][BM] (ROWA)
 
     if constexpr (G == 128) {
       // Slots t = (row block i, column block j). Slot t issues MFMA t and the
@@ -198,8 +213,13 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       constexpr int NJ = WTN / 16, SLOTS = (WTM / 16) * NJ, DSLOT = SLOTS / 4;
       const int r16 = lane & 15, q = lane >> 4;
       const int ksc = s >> sshift;
-      const float a_s = sa0[ksc];
-      const float sc0 = a_s * sb0[ksc], sc1 = a_s * sb1[ksc];
+      const float a_s = ROWA ? 0.0f : sa0[ksc];
+      const float sbv0 = sb0[ksc], sbv1 = sb1[ksc];
+      const float sc0 = a_s * sbv0, sc1 = a_s * sbv1;
+      // ROWA: factors of rows 16i + 4q .. +3 of the wave tile, read one row block ahead
+      const float* const srow = scl + wm * WTM + 4 * q;
+      v4f sr[WTM / 16];
+      if constexpr (ROWA) sr[0] = *reinterpret_cast<const v4f*>(srow);
       v8i bf[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bf[j] = frag(Bs, j * 16 + r16, 2 * q);
@@ -211,23 +231,35 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
         if (t == 0) issue_next(0);
         if (t == DSLOT) issue_next(1);
         if (t < SLOTS) {
-          if (j == 0 && i + 1 < WTM / 16) a_nxt = frag(As, (i + 1) * 16 + r16, 2 * q);
+          if (j == 0 && i + 1 < WTM / 16) {
+            a_nxt = frag(As, (i + 1) * 16 + r16, 2 * q);
+            if constexpr (ROWA) sr[i + 1] = *reinterpret_cast<const v4f*>(srow + (i + 1) * 16);
+          }
           pr[t % (LAG + 1)] = mfma16<FMT>(a_cur, bf[j]);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (t >= LAG) {
           const int u = t - LAG, ui = u / NJ, uj = u % NJ;
-          const float sc = uj < jsplit ? sc0 : sc1;
+          if constexpr (ROWA) {
+            const float sbs = uj < jsplit ? sbv0 : sbv1;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], sc, acc.t[ui][uj][v]);
+            for (int v = 0; v < 4; ++v)
+              acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], sr[ui][v] * sbs, acc.t[ui][uj][v]);
+          } else {
+            const float sc = uj < jsplit ? sc0 : sc1;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], sc, acc.t[ui][uj][v]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         if (t < SLOTS && j == NJ - 1) a_cur = a_nxt;
       }
     } else {
       // The same schedule over the 32 x 32 blocks of each segment; waves 4-7
-      // issue their copies at the second segment.
-      constexpr int LAG = 2;
+      // issue their copies at the second segment. With per-row factors (16
+      // more registers per row block in flight) the promotion runs one MFMA
+      // behind instead of two, which keeps the kernel inside 256 registers.
+      constexpr int LAG = ROWA ? 1 : 2;
       constexpr int NJ = WTN / 32, SLOTS = (WTM / 32) * NJ;
       const int r32 = lane & 31, h2 = lane >> 5;
 #pragma unroll
@@ -236,7 +268,11 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
         issue_next(h);
         if (kb < nkb) {  // K % 128 == 64: the last step holds one segment
           const float sbv = sb0[kb];
-          const float f0 = sa0[kb] * sbv, f1 = sa1[kb] * sbv;
+          const float f0 = ROWA ? 0.0f : sa0[kb] * sbv, f1 = ROWA ? 0.0f : sa1[kb] * sbv;
+          // ROWA: factors of rows 32i + 8(v/4) + 4*h2 + v%4, read with the row
+          // block's first MFMA
+          const float* const srow = scl + h * BM + wm * WTM + 4 * h2;
+          v4f sr[WTM / 32][4];
           v8i bf[NJ];
 #pragma unroll
           for (int j = 0; j < NJ; ++j) bf[j] = frag(Bs, j * 32 + r32, 4 * h + 2 * h2);
@@ -247,14 +283,26 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
             const int i = t / NJ, j = t % NJ;
             if (t < SLOTS) {
               if (j == 0 && i + 1 < WTM / 32) a_nxt = frag(As, (i + 1) * 32 + r32, 4 * h + 2 * h2);
+              if (ROWA && j == 0) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) sr[i][c] = *reinterpret_cast<const v4f*>(srow + i * 32 + 8 * c);
+              }
               pr[t % (LAG + 1)] = mfma32<FMT>(a_cur, bf[j]);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (t >= LAG) {
               const int u = t - LAG, ui = u / NJ, uj = u % NJ;
-              const float f = ui < 2 ? f0 : f1;  // rows 64.. of a 128-row wave tile use the next A block
+              if constexpr (ROWA) {
 #pragma unroll
-              for (int v = 0; v < 16; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], f, acc.t[ui][uj][v]);
+                for (int v = 0; v < 16; ++v)
+                  acc.t[ui][uj][v] =
+                      __builtin_fmaf(pr[u % (LAG + 1)][v], sr[ui][v >> 2][v & 3] * sbv, acc.t[ui][uj][v]);
+              } else {
+                const float f = ui < 2 ? f0 : f1;  // rows 64.. of a 128-row wave tile use the next A block
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                  acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], f, acc.t[ui][uj][v]);
+              }
             }
             __builtin_amdgcn_sched_barrier(0);
             if (t < SLOTS && j == NJ - 1) a_cur = a_nxt;
@@ -335,21 +383,26 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   }
 }
 
-template <int G, int BN, int WM, int FMT, int EPI>
+template <int G, int BN, int WM, int FMT, int EPI, bool ROWA>
 hipError_t launch_fa(const GemmArgs& p, hipStream_t stream) {
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_big<G, BN, WM, 4, FMT, EPI>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, p.a,
+  hipLaunchKernelGGL((gemm_fp8_nt_big<G, BN, WM, 4, FMT, EPI, ROWA>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, p.a,
                      p.b, p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.sshift,
                      p.bias, p.act == 1 ? 1 : 0);
   return hipGetLastError();
 }
 
+template <int G, int BN, int WM, int FMT, int EPI>
+hipError_t launch_sa(const GemmArgs& p, hipStream_t stream) {
+  return p.rowa ? launch_fa<G, BN, WM, FMT, EPI, true>(p, stream) : launch_fa<G, BN, WM, FMT, EPI, false>(p, stream);
+}
+
 template <int G, int BN, int WM, int FMT>
 hipError_t launch_fmt(const GemmArgs& p, hipStream_t stream) {
   switch (epilogue_form(p.bias, p.act)) {
-    case 0: return launch_fa<G, BN, WM, FMT, 0>(p, stream);
-    case 1: return launch_fa<G, BN, WM, FMT, 1>(p, stream);
-    case 2: return launch_fa<G, BN, WM, FMT, 2>(p, stream);
+    case 0: return launch_sa<G, BN, WM, FMT, 0>(p, stream);
+    case 1: return launch_sa<G, BN, WM, FMT, 1>(p, stream);
+    case 2: return launch_sa<G, BN, WM, FMT, 2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

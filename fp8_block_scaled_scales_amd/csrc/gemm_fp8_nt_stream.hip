@@ -20,6 +20,11 @@
 //
 // Per CU this reads 32 rows of A and 32 rows of B over the whole K (458 KB for
 // K = 7168); A comes from L2 after its first touch, so HBM sees B once.
+//
+// Per-row A factors (ROWA; one factor per row of A and K segment, the
+// template article's per-channel choice, §3.4): each A slot carries the
+// step's 32 (g >= 128) or 64 (g = 64) row factors, copied ahead of the slab
+// by one 4-byte-per-lane copy; the B ring gives up a slot to make room.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,21 +38,30 @@ namespace stream {
 
 constexpr int BM = 32, BN = 32, BK = 128;
 constexpr int NW = 4;
+constexpr int A_SLAB = BM * BK, B_SLAB = BN * BK;  // 4 KB each per step
+
 // Per wave: A slabs (L2 hits after their first touch) are copied two steps
 // ahead into a 3-slot ring, B slabs (streamed from HBM, whose loaded latency
 // is several microseconds) six steps ahead into a 7-slot ring. 40 KB per
-// wave, the whole 160 KB LDS for four waves.
-constexpr int A_SLOTS = 3, B_SLOTS = 7, A_AHEAD = A_SLOTS - 1, B_AHEAD = B_SLOTS - 1;
-constexpr int A_SLAB = BM * BK, B_SLAB = BN * BK;  // 4 KB each per step
-constexpr int WAVE_LDS = A_SLOTS * A_SLAB + B_SLOTS * B_SLAB;
-constexpr int A_LOADS = BM / 8, B_LOADS = BN / 8;  // copy instructions per step and operand (one wave)
-// Issue order per iteration t: A(t + A_AHEAD), then B(t + B_AHEAD). Waiting for
-// A(t) (the later-issued of A(t), B(t)) leaves in flight what followed it:
-// B(t + B_AHEAD - 1), then A(t + A_AHEAD) .. the copies of A_AHEAD - 1 more
-// iterations.
-constexpr int WAIT_AFTER_A = (A_AHEAD - 1) * (A_LOADS + B_LOADS) + B_LOADS;
-static_assert(NW * WAVE_LDS <= 160 * 1024, "LDS");
-static_assert(A_AHEAD * (A_LOADS + B_LOADS) + (B_AHEAD - A_AHEAD) * B_LOADS < 64, "vmcnt range");
+// wave, the whole 160 KB LDS for four waves. With per-row A factors each A
+// slot also holds the step's factors (256 bytes) and B keeps 6 slots.
+template <bool ROWA>
+struct Ring {
+  static constexpr int A_SLOTS = 3, B_SLOTS = ROWA ? 6 : 7;
+  static constexpr int A_AHEAD = A_SLOTS - 1, B_AHEAD = B_SLOTS - 1;
+  static constexpr int SA_SLAB = ROWA ? 256 : 0;            // [SEGS][32] FP32 row factors of the step
+  static constexpr int A_PITCH = A_SLAB + SA_SLAB;          // one A slot
+  static constexpr int WAVE_LDS = A_SLOTS * A_PITCH + B_SLOTS * B_SLAB;
+  // copy instructions per step and operand (one wave); the factor copy goes with A, ahead of it
+  static constexpr int A_LOADS = BM / 8 + (ROWA ? 1 : 0), B_LOADS = BN / 8;
+  // Issue order per iteration t: A(t + A_AHEAD), then B(t + B_AHEAD). Waiting
+  // for A(t) (the later-issued of A(t), B(t)) leaves in flight what followed
+  // it: B(t + B_AHEAD - A_AHEAD), then the copies of A_AHEAD - 1 more
+  // iterations.
+  static constexpr int WAIT_AFTER_A = (A_AHEAD - 1) * (A_LOADS + B_LOADS) + B_LOADS;
+  static_assert(NW * WAVE_LDS <= 160 * 1024, "LDS");
+  static_assert(A_AHEAD * (A_LOADS + B_LOADS) + (B_AHEAD - A_AHEAD) * B_LOADS < 64, "vmcnt range");
+};
 
 __device__ __forceinline__ v8i frag(const uint8_t* slab, int row, int c0) {
   const int sw = (row >> 1) & 7;
@@ -58,8 +72,9 @@ __device__ __forceinline__ v8i frag(const uint8_t* slab, int row, int c0) {
 
 // G: K segment contracted before each promotion; scale blocks sg = G << sshift
 // (g = 256 runs the G = 128 kernel with one factor per two segments). FMT bit
-// 0: A is E5M2 (else E4M3), bit 1: B is E5M2.
-template <int G, int FMT, int EPI>
+// 0: A is E5M2 (else E4M3), bit 1: B is E5M2. ROWA: A's factors are per row,
+// sa is [M][K/sg].
+template <int G, int FMT, int EPI, bool ROWA>
 __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __restrict__ a,
                                                               const uint8_t* __restrict__ b,
                                                               const float* __restrict__ sa,
@@ -68,7 +83,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
                                                               int tiles_m, int tiles_n, int sshift,
                                                               const float* __restrict__ bias, int relu) {
   static_assert(G == 64 || G == 128, "granularity");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NW * WAVE_LDS];
+  using R = Ring<ROWA>;
+  constexpr int SEGS = BK / G;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NW * R::WAVE_LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -85,6 +102,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
   // 32 rows starting at a multiple of 32 lie in one g-block (g >= 64).
   const float* const sa_row = sa + (int64_t)(m0 / sg) * nks;
   const float* const sb_row = sb + (int64_t)(n0 / sg) * nks;
+  const v4i rsa = ROWA ? rsrc_words(sa + (int64_t)m0 * nks, (uint32_t)min(BM, M - m0) * (uint32_t)nks * 4u) : (v4i){};
 
   // The epilogue's bias for this lane's column, loaded first: it is older
   // than every copy below, so the copies' waits cover it, and no output store
@@ -93,41 +111,61 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
   const bool hb = EPI != 0 && bias != nullptr;
   const float bc = hb && ocol < N ? bias[ocol] : 0.0f;
 
-  uint8_t* const a_ring = smem + wave * WAVE_LDS;
-  uint8_t* const b_ring = a_ring + A_SLOTS * A_SLAB;
+  uint8_t* const a_ring = smem + wave * R::WAVE_LDS;
+  uint8_t* const b_ring = a_ring + R::A_SLOTS * R::A_PITCH;
   // This wave's step t is global step wave + NW*t. Steps past the end issue
   // copies of nothing, so every wait below counts exactly.
   auto issue_a = [&](int t) {
     const int st = wave + NW * t;
+    uint8_t* const slot = a_ring + (t % R::A_SLOTS) * R::A_PITCH;
+    if constexpr (ROWA)
+      stage_row_scales<BM, SEGS>(rsa, slot + A_SLAB, (uint32_t)nks, (uint32_t)((st * SEGS) >> sshift), 0, lane,
+                                 st < nsteps);
 #pragma unroll
-    for (int g = 0; g < BM / 8; ++g)
-      stage_group<1>(ra, a_ring + (t % A_SLOTS) * A_SLAB, uK, (uint32_t)st * BK, g, lane, st < nsteps);
+    for (int g = 0; g < BM / 8; ++g) stage_group<1>(ra, slot, uK, (uint32_t)st * BK, g, lane, st < nsteps);
   };
   auto issue_b = [&](int t) {
     const int st = wave + NW * t;
 #pragma unroll
     for (int g = 0; g < BN / 8; ++g)
-      stage_group<1>(rb, b_ring + (t % B_SLOTS) * B_SLAB, uK, (uint32_t)st * BK, g, lane, st < nsteps);
+      stage_group<1>(rb, b_ring + (t % R::B_SLOTS) * B_SLAB, uK, (uint32_t)st * BK, g, lane, st < nsteps);
   };
 
   v16f acc = {};
+  // acc += p * (A factor * B factor): one block product, or (ROWA) the lane's
+  // sixteen row factors from LDS, each times the B factor.
+  auto promote = [&](const v16f& p, const float* fr, float sbv, float sav) {
+    if constexpr (ROWA) {
+      v4f r[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) r[c] = *reinterpret_cast<const v4f*>(fr + 8 * c);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = __builtin_fmaf(p[v], r[v >> 2][v & 3] * sbv, acc[v]);
+    } else {
+      const float sc = sav * sbv;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = __builtin_fmaf(p[v], sc, acc[v]);
+    }
+  };
   const int my_steps = nsteps > wave ? (nsteps - wave + NW - 1) / NW : 0;
   // Prologue in the steady-state order: B(0) .. B(B_AHEAD - A_AHEAD - 1), then
   // for j = 0 .. A_AHEAD-1 the pair A(j), B(B_AHEAD - A_AHEAD + j).
 #pragma unroll
-  for (int t = 0; t < B_AHEAD - A_AHEAD; ++t) issue_b(t);
+  for (int t = 0; t < R::B_AHEAD - R::A_AHEAD; ++t) issue_b(t);
 #pragma unroll
-  for (int j = 0; j < A_AHEAD; ++j) {
+  for (int j = 0; j < R::A_AHEAD; ++j) {
     issue_a(j);
-    issue_b(B_AHEAD - A_AHEAD + j);
+    issue_b(R::B_AHEAD - R::A_AHEAD + j);
   }
 
   const int r32 = lane & 31, h2 = lane >> 5;
   for (int t = 0; t < my_steps; ++t) {
-    DG_WAIT_VMCNT(WAIT_AFTER_A);  // A(t) and the earlier-issued B(t) have landed
+    DG_WAIT_VMCNT(R::WAIT_AFTER_A);  // A(t) and the earlier-issued B(t) have landed
     const int st = wave + NW * t;
-    const uint8_t* As = a_ring + (t % A_SLOTS) * A_SLAB;
-    const uint8_t* Bs = b_ring + (t % B_SLOTS) * B_SLAB;
+    const uint8_t* As = a_ring + (t % R::A_SLOTS) * R::A_PITCH;
+    const uint8_t* Bs = b_ring + (t % R::B_SLOTS) * B_SLAB;
+    // ROWA: factors [SEGS][32] of the step; this lane's rows 8c + 4*h2 .. +3
+    const float* const srow = reinterpret_cast<const float*>(As + A_SLAB) + 4 * h2;
 #pragma unroll
     for (int h = 0; h < BK / 64; ++h) {
       const int kb = G == 128 ? st : 2 * st + h;
@@ -142,21 +180,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
           const v8i bf1 = frag(Bs, r32, c0 + 4);
           v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, (v16f){}, FMT & 1, FMT >> 1, 0, 0, 0, 0);
           p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af1, bf1, p, FMT & 1, FMT >> 1, 0, 0, 0, 0);
-          const float sc = sa_row[kb >> sshift] * sb_row[kb >> sshift];
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[v] = __builtin_fmaf(p[v], sc, acc[v]);
+          promote(p, srow, sb_row[kb >> sshift], sa_row[kb >> sshift]);
         }
       } else {
         const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, (v16f){}, FMT & 1, FMT >> 1, 0, 0, 0, 0);
-        const float sc = sa_row[kb] * sb_row[kb];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = __builtin_fmaf(p[v], sc, acc[v]);
+        promote(p, srow + 32 * h, sb_row[kb], sa_row[kb]);
       }
     }
     // Refill the slots of step t-1, read by this wave only and done with one
     // iteration ago.
-    issue_a(t + A_AHEAD);
-    issue_b(t + B_AHEAD);
+    issue_a(t + R::A_AHEAD);
+    issue_b(t + R::B_AHEAD);
   }
   DG_WAIT_VMCNT(0);  // copies of nothing issued past this wave's last step
 
@@ -182,20 +216,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
   }
 }
 
-template <int G, int FMT, int EPI>
+template <int G, int FMT, int EPI, bool ROWA>
 hipError_t launch_fa(const GemmArgs& p, hipStream_t stream) {
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_stream<G, FMT, EPI>), dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream, p.a,
+  hipLaunchKernelGGL((gemm_fp8_nt_stream<G, FMT, EPI, ROWA>), dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream, p.a,
                      p.b, p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.sshift, p.bias, p.act == 1 ? 1 : 0);
   return hipGetLastError();
+}
+
+template <int G, int FMT, int EPI>
+hipError_t launch_sa(const GemmArgs& p, hipStream_t stream) {
+  return p.rowa ? launch_fa<G, FMT, EPI, true>(p, stream) : launch_fa<G, FMT, EPI, false>(p, stream);
 }
 
 template <int G, int FMT>
 hipError_t launch_fmt(const GemmArgs& p, hipStream_t stream) {
   switch (epilogue_form(p.bias, p.act)) {
-    case 0: return launch_fa<G, FMT, 0>(p, stream);
-    case 1: return launch_fa<G, FMT, 1>(p, stream);
-    case 2: return launch_fa<G, FMT, 2>(p, stream);
+    case 0: return launch_sa<G, FMT, 0>(p, stream);
+    case 1: return launch_sa<G, FMT, 1>(p, stream);
+    case 2: return launch_sa<G, FMT, 2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -15,6 +15,7 @@ struct QuantArgs {
   int fmt;   // 0 = E4M3FN, 1 = E5M2
 };
 
-hipError_t launch_quant(const QuantArgs& p, hipStream_t stream);
+hipError_t launch_quant(const QuantArgs& p, hipStream_t stream);       // g x g blocks: scales [ceil(rows/g)][cols/g]
+hipError_t launch_quant_rows(const QuantArgs& p, hipStream_t stream);  // 1 x g blocks: scales [rows][cols/g]
 
 }  // namespace dg

@@ -111,6 +111,27 @@ int dg_gemm_fp8_nt_epi(const void* a, const void* b, const float* sa, const floa
                        int64_t M, int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, const float* bias,
                        int act, void* stream);
 
+/*
+ * dg_gemm_fp8_nt_ex - dg_gemm_fp8_nt_epi with A's scale blocks chosen:
+ * sa_rows is the number of A rows one factor covers, gran (g x g blocks, as
+ * in every call above) or 1 (per-row factors, 1 x g blocks: the per-channel
+ * factors of the DeepGEMM-style template article, §3.4). With sa_rows = 1:
+ *
+ *   out[i,j] = bf16( act( sum_kb  sa[i, kb] * sb[j/g, kb] * P[i,j,kb] + bias[j] ) )
+ *
+ *   sa   FP32 [M][K/gran] row-major, 4-byte aligned (one factor per row of A
+ *        and K segment; for gran 256 one per row and 256-wide segment).
+ *
+ * B keeps its g x g blocks. Same tile choice as the other calls (the mode
+ * changes no tile). With sa_rows = gran this is dg_gemm_fp8_nt_epi, bit for
+ * bit; with sa_rows = 1 and every row's factors equal to its g-block's, the
+ * result equals the block-scaled call's bit for bit. DG_EINVAL for sa_rows
+ * other than gran or 1; otherwise as dg_gemm_fp8_nt_epi.
+ */
+int dg_gemm_fp8_nt_ex(const void* a, const void* b, const float* sa, const float* sb, void* out,
+                      int64_t M, int64_t N, int64_t K, int gran, int sa_rows, int fmt_a, int fmt_b,
+                      const float* bias, int act, void* stream);
+
 /* The tile-table entry a call with these sizes would use. */
 typedef struct dg_tile_info {
   int kernel_id; /* index in the precompiled table */
@@ -158,6 +179,20 @@ int dg_quantize_e4m3_blocks(const float* x, int64_t rows, int64_t cols, int gran
  */
 int dg_quantize_fp8_blocks(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q,
                            float* scales, void* stream);
+
+/*
+ * dg_quantize_fp8_rows - dg_quantize_fp8_blocks with 1 x gran blocks: one
+ * factor per row and gran-wide column segment (the per-row A factors that
+ * dg_gemm_fp8_nt_ex takes with sa_rows = 1).
+ *
+ *   scales  FP32 out, [rows][cols/gran] row-major, 4-byte aligned.
+ *
+ * Per segment: amax = max |x| over its gran elements, scale = amax / fmax
+ * (448 or 57344) in FP32 (1.0 for an all-zero segment), codes as
+ * dg_quantize_fp8_blocks. Same arguments and status codes otherwise.
+ */
+int dg_quantize_fp8_rows(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q,
+                         float* scales, void* stream);
 
 /* Text for a status code (for DG_ELAUNCH: the last HIP error on this thread). */
 const char* dg_strerror(int code);

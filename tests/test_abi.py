@@ -87,6 +87,40 @@ def test_epi_rejects(dg, act, bias, want):
         getattr(dg, want)
 
 
+@pytest.mark.parametrize("g,sa_rows,kw,want", [(128, 2, {}, "DG_EINVAL"), (128, 64, {}, "DG_EINVAL"),
+                                                (128, 0, {}, "DG_EINVAL"), (64, 128, {}, "DG_EINVAL"),
+                                                (256, 1, dict(K=384), "DG_EINVAL"), (128, 1, dict(sa=SA + 2), "DG_EALIGN"),
+                                                (128, 1, dict(a=0), "DG_EINVAL"), (128, 1, dict(fa=2), "DG_EINVAL"),
+                                                (128, 1, dict(act=5), "DG_EINVAL")])
+def test_ex_rejects(dg, g, sa_rows, kw, want):
+    args = dict(a=A, sa=SA, K=256, fa=0, act=0)
+    args.update(kw)
+    assert dg.lib.dg_gemm_fp8_nt_ex(args["a"], B, args["sa"], SB, OUT, 256, 256, args["K"], g, sa_rows, args["fa"], 0,
+                                    None, args["act"], None) == getattr(dg, want)
+
+
+@pytest.mark.parametrize("fmt,g,cols", [(2, 128, 256), (1, 96, 192), (0, 256, 384), (0, 128, 0)])
+def test_quantize_rows_einval(dg, fmt, g, cols):
+    assert dg.lib.dg_quantize_fp8_rows(A, 64, cols, g, fmt, B, SA, None) == dg.DG_EINVAL
+
+
+def test_python_binding_checks_row_scale_shapes(dg):
+    import torch
+
+    # the tensor checks run before the device check, so CPU tensors reach them
+    a = torch.zeros((300, 256), dtype=torch.float8_e4m3fn)
+    b = torch.zeros((64, 256), dtype=torch.float8_e4m3fn)
+    sb = torch.zeros((1, 2))
+    with pytest.raises(ValueError, match="sa has shape"):
+        dg.dg_gemm_fp8_nt_ex(a, b, torch.zeros((3, 2)), sb, sa_rows=1)
+    with pytest.raises(ValueError, match="sa has shape"):
+        dg.dg_gemm_fp8_nt_ex(a, b, torch.zeros((300, 2)), sb)  # per-row factors for a block-scaled call
+    with pytest.raises(ValueError, match="sa_rows"):
+        dg.dg_gemm_fp8_nt_ex(a, b, torch.zeros((300, 2)), sb, sa_rows=7)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dg.dg_gemm_fp8_nt_ex(a, b, torch.zeros((300, 2)), sb, sa_rows=1)  # well-formed, but on the CPU
+
+
 def test_format_codes_match_header(dg):
     text = open(HEADER).read()
     for name in ("DG_FMT_E4M3", "DG_FMT_E5M2", "DG_ACT_NONE", "DG_ACT_RELU", "DG_ACT_GELU"):
