@@ -122,6 +122,9 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   static_assert(BN % 8 == 0 && BN / 8 <= 4 * NW, "B copies: at most four row groups per wave");
   static_assert(128 * LDC * 2 <= 2 * STAGE, "an epilogue pass must fit in the ring");
   static_assert(BM * SEGS <= NW * 64, "a step's row factors: one 64-entry piece per wave");
+  // Every wave's columns lie in one 128- (or 256-) column scale block when the
+  // tile width is a multiple of 128 and the wave width divides 128.
+  constexpr bool ONE_B = BN % 128 == 0 && 128 % WTN == 0;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOT];
 
   const int lane = threadIdx.x & 63;
@@ -172,7 +175,8 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   // B row groups 8i + wave below BN / 8, into the slot of step t.
   auto issue_step = [&](int t) {
     uint8_t* slot = smem + (t & 1) * SLOT;
-    if constexpr (ROWA) stage_row_scales<BM, SEGS>(rsa, slot + STAGE, (uint32_t)nks, (uint32_t)((t * SEGS) >> sshift), wave, lane);
+    if (ROWA && wave * 64 < BM * SEGS)  // pieces past the factors would only write padding
+      stage_row_scales<BM, SEGS>(rsa, slot + STAGE, (uint32_t)nks, (uint32_t)((t * SEGS) >> sshift), wave, lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i) stage_group<1>(ra, slot, uK, (uint32_t)t * BK, i * NW + wave, lane);
 #pragma unroll
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       const float sc0 = a_s * sbv0, sc1 = a_s * sbv1;
       // ROWA: factors of rows 16i + 4q .. +3 of the wave tile, read one row block ahead
       const float* const srow = scl + wm * WTM + 4 * q;
-      v4f sr[WTM / 16];
+      v4f sr[WTM / 16], fr;
       if constexpr (ROWA) sr[0] = *reinterpret_cast<const v4f*>(srow);
       v8i bf[NJ];
 #pragma unroll
@@ -241,10 +245,15 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
         if (t >= LAG) {
           const int u = t - LAG, ui = u / NJ, uj = u % NJ;
           if constexpr (ROWA) {
-            const float sbs = uj < jsplit ? sbv0 : sbv1;
+            // the row block's products, shared by its column blocks; formed
+            // again where the wave's columns enter the second B block
+            // (jsplit >= 1 is wave-uniform)
+            if (uj == 0) fr = sr[ui] * sbv0;
+            if constexpr (!ONE_B) {
+              if (uj == jsplit) fr = sr[ui] * sbv1;
+            }
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], sr[ui][v] * sbs, acc.t[ui][uj][v]);
+            for (int v = 0; v < 4; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], fr[v], acc.t[ui][uj][v]);
           } else {
             const float sc = uj < jsplit ? sc0 : sc1;
 #pragma unroll
@@ -256,10 +265,11 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       }
     } else {
       // The same schedule over the 32 x 32 blocks of each segment; waves 4-7
-      // issue their copies at the second segment. With per-row factors (16
-      // more registers per row block in flight) the promotion runs one MFMA
-      // behind instead of two, which keeps the kernel inside 256 registers.
-      constexpr int LAG = ROWA ? 1 : 2;
+      // issue their copies at the second segment. With per-row factors on the
+      // 256-wide tile (16 more registers per row block in flight) the
+      // promotion runs one MFMA behind instead of two, which keeps the kernel
+      // inside 256 registers.
+      constexpr int LAG = ROWA && BN == 256 ? 1 : 2;
       constexpr int NJ = WTN / 32, SLOTS = (WTM / 32) * NJ;
       const int r32 = lane & 31, h2 = lane >> 5;
 #pragma unroll
@@ -273,6 +283,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
           // block's first MFMA
           const float* const srow = scl + h * BM + wm * WTM + 4 * h2;
           v4f sr[WTM / 32][4];
+          float fr[16];
           v8i bf[NJ];
 #pragma unroll
           for (int j = 0; j < NJ; ++j) bf[j] = frag(Bs, j * 32 + r32, 4 * h + 2 * h2);
@@ -293,10 +304,13 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
             if (t >= LAG) {
               const int u = t - LAG, ui = u / NJ, uj = u % NJ;
               if constexpr (ROWA) {
+                if (uj == 0) {  // the row block's products, shared by its column blocks (one B block per wave)
+#pragma unroll
+                  for (int v = 0; v < 16; ++v) fr[v] = sr[ui][v >> 2][v & 3] * sbv;
+                }
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
-                  acc.t[ui][uj][v] =
-                      __builtin_fmaf(pr[u % (LAG + 1)][v], sr[ui][v >> 2][v & 3] * sbv, acc.t[ui][uj][v]);
+                  acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], fr[v], acc.t[ui][uj][v]);
               } else {
                 const float f = ui < 2 ? f0 : f1;  // rows 64.. of a 128-row wave tile use the next A block
 #pragma unroll
