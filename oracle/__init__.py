@@ -20,6 +20,9 @@ computes and which passage of the pages it follows:
   the same with E5M2 operands (DeepGEMM实战 §2.2 names E4M3 and E5M2 as the
   input formats; OCP E5M2 as torch.float8_e5m2 implements it), and any block
   granularity g (§3.1: 64, 128 and 256).
+* ``gemm_ref_layout``: the reference GEMM with A stored [M,K] or [K,M] and B
+  stored [N,K] or [K,N] (DeepGEMM实战 §3.3: either operand may be stored
+  transposed); layout codes NT 0, NN 1, TT 2, TN 3.
 * ``quantize_rows_fmt``, ``gemm_ref_rowa``: per-row A scales, one factor per
   row and g-wide K segment (1 x g blocks), B keeping its g x g blocks (the
   template article §3.4: per-tensor or per-channel factors, per channel the
@@ -101,6 +104,9 @@ def _load():
     lib.dgo_gemm_ref_rowa.restype = ctypes.c_int
     lib.dgo_gemm_ref_rowa.argtypes = [u8p, u8p, f32p, f32p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, i64p, i64, i64p, i64, f64p, ctypes.c_int]
+    lib.dgo_gemm_ref_layout.restype = ctypes.c_int
+    lib.dgo_gemm_ref_layout.argtypes = [u8p, u8p, f32p, f32p, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, i64p, i64, i64p, i64, f64p, ctypes.c_int]
     lib.dgo_epilogue.restype = ctypes.c_int
     lib.dgo_epilogue.argtypes = [f64p, i64, i64, i64p, f32p, ctypes.c_int]
     lib.dgo_hardware_threads.restype = ctypes.c_int
@@ -298,6 +304,39 @@ def gemm_ref_rowa(a8, b8, sa, sb, g: int, fmt_a: int = 0, fmt_b: int = 0, rows=N
         _ptr(out, ctypes.c_double), nthreads or default_threads())
     if rc != 0:
         raise ValueError("dgo_gemm_ref_rowa rejected its arguments")
+    return out
+
+
+# Operand layouts: bit 1 = A stored [K, M], bit 0 = B stored [K, N].
+NT, NN, TT, TN = 0, 1, 2, 3
+
+
+def gemm_ref_layout(a, b, sa, sb, g: int, layout: int, M: int, N: int, K: int, fmt_a: int = 0, fmt_b: int = 0,
+                    rows=None, cols=None, nthreads: int | None = None) -> np.ndarray:
+    """Reference GEMM with stored operands a ([M,K] or [K,M]) and b ([N,K] or [K,N]) per layout."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sb = np.ascontiguousarray(sb, dtype=np.float32)
+    want_a = (K, M) if layout & 2 else (M, K)
+    want_b = (K, N) if layout & 1 else (N, K)
+    if a.shape != want_a or b.shape != want_b or K % g:
+        raise ValueError("operand shapes do not match the layout")
+    if sa.shape != ((M + g - 1) // g, K // g) or sb.shape != ((N + g - 1) // g, K // g):
+        raise ValueError("bad scale shapes")
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    c = None if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    nr = M if r is None else r.size
+    nc = N if c is None else c.size
+    out = np.empty((nr, nc), dtype=np.float64)
+    rc = _load().dgo_gemm_ref_layout(
+        _ptr(a, ctypes.c_uint8), _ptr(b, ctypes.c_uint8), _ptr(sa, ctypes.c_float), _ptr(sb, ctypes.c_float),
+        M, N, K, g, layout, fmt_a, fmt_b,
+        None if r is None else _ptr(r, ctypes.c_int64), nr,
+        None if c is None else _ptr(c, ctypes.c_int64), nc,
+        _ptr(out, ctypes.c_double), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("dgo_gemm_ref_layout rejected its arguments")
     return out
 
 

@@ -59,6 +59,14 @@
 //        ref[i,j]  = sum_kb (sa[i,kb] * sb[j/g,kb]) * P[i,j,kb]
 //    and the quantiser's 1 x g variant takes amax over one row's segment.
 //
+//  * Operand layouts (DeepGEMM实战 §3.3: A and B may each be stored
+//    transposed; the product is the same). Layout code bit 1: A stored
+//    [K][M] (A[i,k] at a[k*M + i]) instead of [M][K]; bit 0: B stored [K][N]
+//    (B[j,k] at b[k*N + j]) instead of [N][K]. Codes: 0 = NT (the default),
+//    1 = NN, 2 = TT, 3 = TN (first letter A, second B, as in C = op(A) op(B)
+//    with op(B) = B^T for B stored [N][K]). The scales keep their logical
+//    shapes: sa [ceil(M/g)][K/g], sb [ceil(N/g)][K/g].
+//
 // Scale tensors are row-major FP32: sa is [ceil(M/g)][K/g] ([M][K/g] with
 // per-row A scales), sb is [ceil(N/g)][K/g]. K must be a multiple of g.
 //
@@ -405,6 +413,54 @@ int dgo_gemm_ref_rowa(const uint8_t* a, const uint8_t* b, const float* sa, const
         for (int64_t kb = 0; kb < nkb; ++kb) {
           double p = 0.0;
           for (int64_t k = kb * g; k < kb * g + g; ++k) p += ta[arow[k]] * tb[brow[k]];
+          const double s = (double)sarow[kb] * (double)sbrow[kb];
+          ref += s * p;
+        }
+        out[r * ncols + c] = ref;
+      }
+    }
+  });
+  return 0;
+}
+
+// Reference GEMM with the operands in any of the four layouts (see the
+// header): the same sums as dgo_gemm_ref_fmt, each element read from where
+// the layout stores it.
+int dgo_gemm_ref_layout(const uint8_t* a, const uint8_t* b, const float* sa, const float* sb, int64_t M, int64_t N,
+                        int64_t K, int g, int layout, int fmt_a, int fmt_b, const int64_t* rows, int64_t nrows,
+                        const int64_t* cols, int64_t ncols, double* out, int nthreads) {
+  if (!a || !b || !sa || !sb || !out || M <= 0 || N <= 0 || K <= 0 || g <= 0 || K % g != 0) return -1;
+  if ((fmt_a != 0 && fmt_a != 1) || (fmt_b != 0 && fmt_b != 1) || layout < 0 || layout > 3) return -1;
+  if (!rows) nrows = M;
+  if (!cols) ncols = N;
+  for (int64_t r = 0; rows && r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= M) return -1;
+  for (int64_t c = 0; cols && c < ncols; ++c)
+    if (cols[c] < 0 || cols[c] >= N) return -1;
+  const bool a_km = (layout & 2) != 0, b_kn = (layout & 1) != 0;
+
+  double ta[256], tb[256];
+  for (int c = 0; c < 256; ++c) {
+    ta[c] = decode_fmt(fmt_a, (uint8_t)c);
+    tb[c] = decode_fmt(fmt_b, (uint8_t)c);
+  }
+  const int64_t nkb = K / g;
+
+  parallel_for(nrows, nthreads, [&](int64_t lo, int64_t hi) {
+    for (int64_t r = lo; r < hi; ++r) {
+      const int64_t i = rows ? rows[r] : r;
+      const float* sarow = sa + (i / g) * nkb;
+      for (int64_t c = 0; c < ncols; ++c) {
+        const int64_t j = cols ? cols[c] : c;
+        const float* sbrow = sb + (j / g) * nkb;
+        double ref = 0.0;
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+          double p = 0.0;
+          for (int64_t k = kb * g; k < kb * g + g; ++k) {
+            const uint8_t ca = a_km ? a[k * M + i] : a[i * K + k];
+            const uint8_t cb = b_kn ? b[k * N + j] : b[j * K + k];
+            p += ta[ca] * tb[cb];
+          }
           const double s = (double)sarow[kb] * (double)sbrow[kb];
           ref += s * p;
         }
