@@ -7,14 +7,16 @@ FP32 promotion, BF16 epilogue) runs inside that one kernel launch.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--fmt e4m3|e5m2|e4m3xe5m2|e5m2xe4m3] [--gran 64|128|256]
-                  [--bias] [--act none|relu|gelu] [--sa-rows 1]
+                  [--bias] [--act none|relu|gelu] [--sa-rows 1] [--layout nt|nn|tt|tn]
 
 --fmt and --gran run the same workload with the operands in another FP8
 format or with another block granularity (default: E4M3 and the workload's
 own g); --bias and --act add the fused epilogue out = act(C + bias) (bias a
 seeded N(0, 0.5) vector); --sa-rows 1 scales A per row and K segment (1 x g
-blocks, quantised by dg_quantize_fp8_rows) instead of per g x g block; the
-default run is the E4M3 workload as specified.
+blocks, quantised by dg_quantize_fp8_rows) instead of per g x g block;
+--layout stores A as [K,M] (tt, tn) and/or B as [K,N] (nn, tn), transposed
+on the GPU before timing, and calls dg_gemm_fp8_layout; the default run is
+the E4M3 NT workload as specified.
 
 Inputs: FP32 matrices drawn from the seeded generators in ``synth`` (the
 workload's shapes and value distributions), copied to the GPU and block
@@ -135,8 +137,11 @@ def make_inputs(c: int, dev, g: int, fa: int = 0, fb: int = 0, sa_rows: int | No
     return a8, sa, b8, sb
 
 
+LAYOUTS = {"nt": 0, "nn": 1, "tt": 2, "tn": 3}
+
+
 def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int = 0, fb: int = 0,
-            bias: bool = False, act: int = 0, sa_rows: int | None = None):
+            bias: bool = False, act: int = 0, sa_rows: int | None = None, layout: int = 0):
     import torch
 
     import fp8_block_scaled_scales_amd as dg
@@ -146,6 +151,10 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     a8, sa, b8, sb = make_inputs(c, dev, g, fa, fb, sa_rows)
+    if layout & 2:
+        a8 = a8.t().contiguous()  # A stored [K, M]
+    if layout & 1:
+        b8 = b8.t().contiguous()  # B stored [K, N]
     set_bytes = a8.numel() + b8.numel() + 4 * (sa.numel() + sb.numel()) + 2 * M * N
     if sets is None:
         sets = max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes) + 1))
@@ -155,13 +164,16 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
                      torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
     stream = torch.cuda.current_stream(dev)
     print("bench: workload %d %s, %d input sets of %.1f MB, tile %s" % (
-        c, w["name"], sets, set_bytes / 1e6, dg.dg_query_tile(M, N, K, g)), file=sys.stderr, flush=True)
+        c, w["name"], sets, set_bytes / 1e6, dg.dg_query_tile(M, N, K, g, layout)), file=sys.stderr, flush=True)
 
     tbias = torch.from_numpy(make_bias(N)).to(dev) if bias else None
 
     def launch(i, st):
         x = bufs[i % sets]
-        if sa_rows == 1:
+        if layout:
+            dg.dg_gemm_fp8_layout(x[0], x[2], x[1], x[3], out=x[4], gran=g, layout=layout, fmt_a=fa, fmt_b=fb,
+                                  bias=tbias, act=act, stream=st)
+        elif sa_rows == 1:
             dg.dg_gemm_fp8_nt_ex(x[0], x[2], x[1], x[3], out=x[4], gran=g, sa_rows=1, fmt_a=fa, fmt_b=fb, bias=tbias,
                                  act=act, stream=st)
         elif bias or act:
@@ -213,7 +225,7 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
 
 
 def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, bias: bool = False, act: int = 0, budget_s: float = 10.0,
-            sa_rows: int | None = None):
+            sa_rows: int | None = None, layout: int = 0):
     """The oracle on a bounded sample of workload c, in TFLOP/s (FP64 on the host)."""
     import numpy as np
 
@@ -230,8 +242,13 @@ def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, bias: bool = False, act: i
 
     bvec = make_bias(N) if bias else None
 
+    a_st = np.ascontiguousarray(a8.T) if layout & 2 else a8
+    b_st = np.ascontiguousarray(b8.T) if layout & 1 else b8
+
     def ref(rows=None):
-        if sa_rows == 1:
+        if layout:
+            r = oracle.gemm_ref_layout(a_st, b_st, sa, sb, g, layout, M, N, K, fa, fb, rows=rows)
+        elif sa_rows == 1:
             r = oracle.gemm_ref_rowa(a8, b8, sa, sb, g, fa, fb, rows=rows)
         elif fa == 0 and fb == 0:
             r = oracle.gemm_ref(a8, b8, sa, sb, g, rows=rows)
@@ -281,6 +298,8 @@ def main():
                     help="block granularity (default: the workload's)")
     ap.add_argument("--bias", action="store_true", help="fused epilogue: add a bias vector")
     ap.add_argument("--act", default="none", choices=sorted(ACTS), help="fused epilogue activation")
+    ap.add_argument("--layout", default="nt", choices=sorted(LAYOUTS),
+                    help="operand storage: A [M,K] or [K,M] (first letter n / t), B [N,K] or [K,N] (t / n)")
     ap.add_argument("--sa-rows", type=int, default=None, choices=(1,),
                     help="1: per-row A factors (1 x g blocks) instead of g x g blocks")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
@@ -316,7 +335,11 @@ def main():
     fa, fb = FORMATS[args.fmt]
     flops, nbytes = algorithmic(w, g, args.sa_rows)
     act = ACTS[args.act]
-    ms, sets, finite, glen = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb, args.bias, act, args.sa_rows)
+    layout = LAYOUTS[args.layout]
+    if layout and args.sa_rows == 1:
+        raise SystemExit("--sa-rows 1 runs the NT layout only")
+    ms, sets, finite, glen = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb, args.bias, act, args.sa_rows,
+                                     layout)
     if not finite:
         raise SystemExit("GEMM output holds non-finite values")
     sec = ms * 1e-3
@@ -326,10 +349,11 @@ def main():
         achieved, peak, unit = tflops, PEAK_FP8_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
-    tr = TRAFFIC.get(w["name"]) if (fa, fb, g, args.bias, act, args.sa_rows) == (0, 0, w["g"], False, 0, None) else None
+    default_variant = (fa, fb, g, args.bias, act, args.sa_rows, layout) == (0, 0, w["g"], False, 0, None, 0)
+    tr = TRAFFIC.get(w["name"]) if default_variant else None
     traffic = tr["bytes"] if tr and tr["src"] == _kernel_source_hash() else None
 
-    cpu = None if args.no_cpu_baseline else cpu_leg(c, g, fa, fb, args.bias, act, sa_rows=args.sa_rows)
+    cpu = None if args.no_cpu_baseline else cpu_leg(c, g, fa, fb, args.bias, act, sa_rows=args.sa_rows, layout=layout)
 
     line = {
         "metric": "FP8 block-scaled GEMM TFLOPS and % of MI355X dense FP8 peak (1 GPU)",
@@ -347,7 +371,7 @@ def main():
         "config": {"workload": w["name"], "M": w["M"], "N": w["N"], "K": w["K"], "gran": g, "fmt": args.fmt,
                    "epilogue": ("bias+" if args.bias else "") + args.act,
                    "a_scales": "1x%d" % g if args.sa_rows == 1 else "%dx%d" % (g, g),
-                   "layout": "NT", "out": "bf16", "input_sets": sets,
+                   "layout": args.layout.upper(), "out": "bf16", "input_sets": sets,
                    "launch": "hipGraph of %d launches, replayed %d times" % (glen, args.steps // glen),
                    "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
                    "alg_GBps": round(nbytes / sec / 1e9, 1)},

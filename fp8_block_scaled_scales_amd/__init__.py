@@ -59,6 +59,11 @@ def _load():
     lib.dg_gemm_fp8_nt_ex.restype = ctypes.c_int
     lib.dg_gemm_fp8_nt_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.dg_gemm_fp8_layout.restype = ctypes.c_int
+    lib.dg_gemm_fp8_layout.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.dg_query_tile_layout.restype = ctypes.c_int
+    lib.dg_query_tile_layout.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(dg_tile_info)]
     lib.dg_quantize_fp8_rows.restype = ctypes.c_int
     lib.dg_quantize_fp8_rows.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.dg_quantize_e4m3_blocks.restype = ctypes.c_int
@@ -100,9 +105,9 @@ def dg_version() -> int:
     return _lib.dg_version()
 
 
-def dg_query_tile(M: int, N: int, K: int, gran: int = 128) -> dict:
+def dg_query_tile(M: int, N: int, K: int, gran: int = 128, layout: int = 0) -> dict:
     info = dg_tile_info()
-    rc = _lib.dg_query_tile(M, N, K, gran, ctypes.byref(info))
+    rc = _lib.dg_query_tile_layout(M, N, K, gran, layout, ctypes.byref(info))
     if rc != DG_OK:
         _raise(rc, "dg_query_tile")
     return {name: getattr(info, name) for name, _ in dg_tile_info._fields_}
@@ -214,6 +219,53 @@ def dg_gemm_fp8_nt_ex(a, b, sa, sb, out=None, gran: int = 128, sa_rows: int | No
     return _gemm(a, b, sa, sb, out, gran, fmt_a, fmt_b, stream, "dg_gemm_fp8_nt_ex", bias, act, sa_rows)
 
 
+# Operand layouts: bit 1 = A stored [K, M], bit 0 = B stored [K, N].
+DG_LAYOUT_NT, DG_LAYOUT_NN, DG_LAYOUT_TT, DG_LAYOUT_TN = 0, 1, 2, 3
+
+
+def dg_gemm_fp8_layout(a, b, sa, sb, out=None, gran: int = 128, layout: int = DG_LAYOUT_NT,
+                       fmt_a: int = DG_FMT_E4M3, fmt_b: int = DG_FMT_E4M3, bias=None, act: int = DG_ACT_NONE,
+                       stream=None):
+    """dg_gemm_fp8_nt_epi with A stored [M,K] or [K,M] and B stored [N,K] or [K,N] per ``layout``.
+
+    a: [M,K] (NT, NN) or [K,M] (TT, TN); b: [N,K] (NT, TT) or [K,N] (NN, TN); sa and
+    sb keep their logical shapes [ceil(M/g), K/g] and [ceil(N/g), K/g]. A stored
+    [K,M] needs M % 16 == 0, B stored [K,N] needs N % 16 == 0.
+    """
+    if layout not in (DG_LAYOUT_NT, DG_LAYOUT_NN, DG_LAYOUT_TT, DG_LAYOUT_TN):
+        raise ValueError("layout must be DG_LAYOUT_NT, _NN, _TT or _TN")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    K, M = a.shape if layout & 2 else a.shape[::-1]
+    N = b.shape[1] if layout & 1 else b.shape[0]
+    dev = a.device
+    if gran not in _GRANS or K % gran:
+        raise ValueError("gran must be 64, 128 or 256 and divide K")
+    if fmt_a not in _FP8_OF or fmt_b not in _FP8_OF:
+        raise ValueError("formats must be DG_FMT_E4M3 or DG_FMT_E5M2")
+    _check(a, "a", _FP8_OF[fmt_a], (K, M) if layout & 2 else (M, K), dev)
+    _check(b, "b", _FP8_OF[fmt_b], (K, N) if layout & 1 else (N, K), dev)
+    _check(sa, "sa", (torch.float32,), ((M + gran - 1) // gran, K // gran), dev)
+    _check(sb, "sb", (torch.float32,), ((N + gran - 1) // gran, K // gran), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", (torch.bfloat16,), (M, N), dev)
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), (N,), dev)
+    if act not in (DG_ACT_NONE, DG_ACT_RELU, DG_ACT_GELU):
+        raise ValueError("act must be DG_ACT_NONE, DG_ACT_RELU or DG_ACT_GELU")
+    if dev.type != "cuda":
+        raise ValueError("a must be a GPU tensor")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = _lib.dg_gemm_fp8_layout(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
+                                     M, N, K, gran, layout, fmt_a, fmt_b, None if bias is None else bias.data_ptr(),
+                                     act, s.cuda_stream)
+    if rc != DG_OK:
+        _raise(rc, "dg_gemm_fp8_layout")
+    return out
+
+
 def _quantize(x, gran, fmt, q, scales, stream, where):
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be a 2-D tensor")
@@ -271,7 +323,8 @@ def dg_quantize_fp8_rows(x, gran: int = 128, fmt: int = DG_FMT_E4M3, q=None, sca
     return _quantize(x, gran, fmt, q, scales, stream, "dg_quantize_fp8_rows")
 
 
-__all__ = ["dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "dg_gemm_fp8_nt_epi", "dg_gemm_fp8_nt_ex", "DG_ACT_NONE",
+__all__ = ["dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "dg_gemm_fp8_nt_epi", "dg_gemm_fp8_nt_ex", "dg_gemm_fp8_layout",
+           "DG_LAYOUT_NT", "DG_LAYOUT_NN", "DG_LAYOUT_TT", "DG_LAYOUT_TN", "DG_ACT_NONE",
            "DG_ACT_RELU", "DG_ACT_GELU", "dg_quantize_e4m3_blocks", "dg_quantize_fp8_blocks", "dg_quantize_fp8_rows",
            "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError", "DG_OK", "DG_EINVAL",
            "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH", "DG_FMT_E4M3", "DG_FMT_E5M2", "LIB_PATH"]

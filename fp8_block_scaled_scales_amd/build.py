@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdg.so")
-SOURCES = ["dg_host.hip", "gemm_fp8_nt.hip", "gemm_fp8_nt_big.hip", "gemm_fp8_nt_stream.hip", "quant_fp8.hip"]
+SOURCES = ["dg_host.hip", "gemm_fp8_nt.hip", "gemm_fp8_nt_big.hip", "gemm_fp8_nt_stream.hip", "gemm_fp8_layouts.hip",
+           "quant_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -103,10 +103,18 @@ int64_t splits_for(const dg::KernelEntry* e, int64_t tiles, int64_t nsteps) {
   return std::max<int64_t>(ks, 1);
 }
 
-Plan plan(int64_t M, int64_t N, int64_t K, int sgran) {
+// Transposed layouts (layout != NT) run the tiled classes only: split-K 64x64
+// tiles for M <= 128, 128x128 tiles otherwise.
+Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout = DG_LAYOUT_NT) {
   Plan p{nullptr, 1, 0};
   const int gran = kernel_gran(sgran);
   const int64_t nsteps = (K + 127) / 128;
+  if (layout != DG_LAYOUT_NT) {
+    p.e = find(M <= 128 ? dg::kClassSplitK : dg::kClassTiled, gran);
+    p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
+    if (p.e->cls == dg::kClassSplitK) p.ksplit = (int)splits_for(p.e, p.tiles, nsteps);
+    return p;
+  }
   const int force = forced_tile();
   if (force >= 0) {
     for (int i = 0; i < dg::kTableSize; ++i)
@@ -181,10 +189,21 @@ int device_ready(int* dev_out = nullptr) {
 
 namespace {
 
+// Layout checks shared by the GEMM and the tile query: a known code, and the
+// stored row length of a transposed operand (M for A [K,M], N for B [K,N]) a
+// multiple of 16 bytes, the granule its tiles are copied in.
+int validate_layout(int64_t M, int64_t N, int layout) {
+  if (layout < DG_LAYOUT_NT || layout > DG_LAYOUT_TN) return DG_EINVAL;
+  if (((layout & 2) && M % 16 != 0) || ((layout & 1) && N % 16 != 0)) return DG_EINVAL;
+  return DG_OK;
+}
+
 int gemm(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M, int64_t N, int64_t K,
-         int gran, int sa_rows, int fmt_a, int fmt_b, const float* bias, int act, void* stream) {
+         int gran, int layout, int sa_rows, int fmt_a, int fmt_b, const float* bias, int act, void* stream) {
   if (!a || !b || !sa || !sb || !out) return DG_EINVAL;
   if (sa_rows != gran && sa_rows != 1) return DG_EINVAL;
+  if (validate_layout(M, N, layout) != DG_OK) return DG_EINVAL;
+  if (layout != DG_LAYOUT_NT && sa_rows == 1) return DG_EINVAL;  // per-row factors are compiled for NT only
   if ((fmt_a != DG_FMT_E4M3 && fmt_a != DG_FMT_E5M2) || (fmt_b != DG_FMT_E4M3 && fmt_b != DG_FMT_E5M2))
     return DG_EINVAL;
   if (act != DG_ACT_NONE && act != DG_ACT_RELU && act != DG_ACT_GELU) return DG_EINVAL;
@@ -194,7 +213,7 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)sa & 3) || ((uintptr_t)sb & 3) ||
       ((uintptr_t)out & 1))
     return DG_EALIGN;
-  Plan pl = plan(M, N, K, gran);
+  Plan pl = plan(M, N, K, gran, layout);
   if (!pl.e || pl.tiles * pl.ksplit > 0x7fffffff) return DG_EINVAL;
 
   int dev = 0;
@@ -219,6 +238,7 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   p.sshift = gran == 256 ? 1 : 0;
   p.fmt = (fmt_a == DG_FMT_E5M2 ? 1 : 0) | (fmt_b == DG_FMT_E5M2 ? 2 : 0);
   p.rowa = sa_rows == 1 ? 1 : 0;
+  p.layout = layout;
   p.vec_store = (((uintptr_t)out & 15) == 0 && N % 8 == 0) ? 1 : 0;
   p.ksplit = pl.ksplit;
   p.ws = pl.ksplit > 1 ? g_ws[dev] : nullptr;
@@ -227,11 +247,13 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   p.act = act;
   if (log_enabled())
     std::fprintf(stderr,
-                 "dg_gemm_fp8_nt M=%lld N=%lld K=%lld g=%d sa_rows=%d fmt=%d,%d bias=%d act=%d -> kernel %d (%dx%d, "
-                 "%d stages, %d waves) ksplit %d grid %lld\n",
-                 (long long)M, (long long)N, (long long)K, gran, sa_rows, fmt_a, fmt_b, bias ? 1 : 0, act, e->id, e->bm,
+                 "dg_gemm_fp8 M=%lld N=%lld K=%lld g=%d layout=%d sa_rows=%d fmt=%d,%d bias=%d act=%d -> kernel %d "
+                 "(%dx%d, %d stages, %d waves) ksplit %d grid %lld\n",
+                 (long long)M, (long long)N, (long long)K, gran, layout, sa_rows, fmt_a, fmt_b, bias ? 1 : 0, act, e->id,
+                 e->bm,
                  e->bn, e->stages, e->waves, pl.ksplit, (long long)(pl.tiles * pl.ksplit));
-  t_last_hip = e->launch(p, static_cast<hipStream_t>(stream));
+  t_last_hip = layout == DG_LAYOUT_NT ? e->launch(p, static_cast<hipStream_t>(stream))
+                                      : dg::launch_layout(e->id, p, static_cast<hipStream_t>(stream));
   return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
 }
 
@@ -274,8 +296,8 @@ const char* dg_strerror(int code) {
     case DG_OK: return "success";
     case DG_EINVAL:
       return "invalid argument (null pointer, bad dimension, K not a multiple of gran, gran not 64/128/256, "
-             "sa_rows neither gran nor 1, a format code other than DG_FMT_E4M3/DG_FMT_E5M2, or an unknown "
-             "activation)";
+             "sa_rows neither gran nor 1, a format code other than DG_FMT_E4M3/DG_FMT_E5M2, an unknown "
+             "activation or layout, or a transposed operand whose stored row length is not a multiple of 16)";
     case DG_EALIGN: return "misaligned pointer (a, b need 16 bytes; sa, sb 4 bytes; out 2 bytes)";
     case DG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
     case DG_ELAUNCH:
@@ -285,11 +307,12 @@ const char* dg_strerror(int code) {
   }
 }
 
-int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info) {
+int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, dg_tile_info* info) {
   if (!info) return DG_EINVAL;
-  const int rc = validate(M, N, K, gran);
+  int rc = validate(M, N, K, gran);
   if (rc != DG_OK) return rc;
-  const Plan p = plan(M, N, K, gran);
+  if ((rc = validate_layout(M, N, layout)) != DG_OK) return rc;
+  const Plan p = plan(M, N, K, gran, layout);
   if (!p.e || p.tiles * p.ksplit > 0x7fffffff) return DG_EINVAL;
   info->kernel_id = p.e->id;
   info->bm = p.e->bm;
@@ -302,26 +325,37 @@ int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info)
   return DG_OK;
 }
 
+int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info) {
+  return dg_query_tile_layout(M, N, K, gran, DG_LAYOUT_NT, info);
+}
+
 int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
                    int64_t N, int64_t K, int gran, void* stream) {
-  return gemm(a, b, sa, sb, out, M, N, K, gran, gran, DG_FMT_E4M3, DG_FMT_E4M3, nullptr, DG_ACT_NONE, stream);
+  return gemm(a, b, sa, sb, out, M, N, K, gran, DG_LAYOUT_NT, gran, DG_FMT_E4M3, DG_FMT_E4M3, nullptr, DG_ACT_NONE,
+              stream);
 }
 
 int dg_gemm_fp8_nt_fmt(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
                        int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, void* stream) {
-  return gemm(a, b, sa, sb, out, M, N, K, gran, gran, fmt_a, fmt_b, nullptr, DG_ACT_NONE, stream);
+  return gemm(a, b, sa, sb, out, M, N, K, gran, DG_LAYOUT_NT, gran, fmt_a, fmt_b, nullptr, DG_ACT_NONE, stream);
 }
 
 int dg_gemm_fp8_nt_epi(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
                        int64_t N, int64_t K, int gran, int fmt_a, int fmt_b, const float* bias, int act,
                        void* stream) {
-  return gemm(a, b, sa, sb, out, M, N, K, gran, gran, fmt_a, fmt_b, bias, act, stream);
+  return gemm(a, b, sa, sb, out, M, N, K, gran, DG_LAYOUT_NT, gran, fmt_a, fmt_b, bias, act, stream);
 }
 
 int dg_gemm_fp8_nt_ex(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
                       int64_t N, int64_t K, int gran, int sa_rows, int fmt_a, int fmt_b, const float* bias, int act,
                       void* stream) {
-  return gemm(a, b, sa, sb, out, M, N, K, gran, sa_rows, fmt_a, fmt_b, bias, act, stream);
+  return gemm(a, b, sa, sb, out, M, N, K, gran, DG_LAYOUT_NT, sa_rows, fmt_a, fmt_b, bias, act, stream);
+}
+
+int dg_gemm_fp8_layout(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
+                       int64_t N, int64_t K, int gran, int layout, int fmt_a, int fmt_b, const float* bias, int act,
+                       void* stream) {
+  return gemm(a, b, sa, sb, out, M, N, K, gran, layout, gran, fmt_a, fmt_b, bias, act, stream);
 }
 
 int dg_quantize_fp8_blocks(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q, float* scales,

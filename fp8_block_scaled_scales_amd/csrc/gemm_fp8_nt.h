@@ -17,6 +17,7 @@ struct GemmArgs {
   int sshift;     // scale blocks are (gran << sshift) square: 1 for g = 256 on the gran-128 kernels
   int fmt;        // bit 0: A is E5M2 (else E4M3); bit 1: B is E5M2
   int rowa;       // A's factors are per row and K segment (1 x g blocks): sa is [M][K/g]
+  int layout;     // bit 1: A stored [K,M]; bit 0: B stored [K,N] (0 = NT: A [M,K], B [N,K])
   int vec_store;  // out is 16-byte aligned and N % 8 == 0: full-row chunks use 16-byte stores
   int ksplit;     // workgroups per output tile along K (1 = no split)
   float* ws;      // split-K partial tiles, tiles * ksplit * bm * bn floats (ksplit > 1)
@@ -51,6 +52,10 @@ hipError_t launch_big_g64(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_big224_g128(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_big128_g128(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_big128_g64(const GemmArgs& p, hipStream_t stream);
+
+// The transposed layouts (GemmArgs::layout != 0) of tiled / split-K table
+// entry `id` (0-3).
+hipError_t launch_layout(int id, const GemmArgs& p, hipStream_t stream);
 
 extern KernelEntry kTable[];
 extern const int kTableSize;

@@ -39,358 +39,9 @@
 
 #include "gemm_common.h"
 #include "gemm_fp8_nt.h"
+#include "gemm_fp8_tiled.h"
 
 namespace dg {
-
-constexpr int BK = 128;  // K bytes per pipeline step (row pitch of a staged slab)
-
-// 32 bytes of K (logical 16-byte chunks c0 and c0+1) of one staged row.
-__device__ __forceinline__ v8i frag32(const uint8_t* slab, int row, int c0) {
-  const int sw = row & 7;
-  const v4i lo = *reinterpret_cast<const v4i*>(slab + row * BK + ((c0 ^ sw) << 4));
-  const v4i hi = *reinterpret_cast<const v4i*>(slab + row * BK + (((c0 + 1) ^ sw) << 4));
-  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-}
-
-// FMT bit 0: A is E5M2 (else E4M3), bit 1: B is E5M2 -- the instruction's
-// operand-format fields (0 = E4M3, 1 = E5M2); no block-exponent scaling.
-template <int FMT>
-__device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT & 1, FMT >> 1, 0, 0, 0, 0);
-}
-
-// Wait until at most `steps` later pipeline steps' loads (LOADS each) are
-// still in flight for this wave; steps is 0 .. MAXS.
-template <int LOADS, int MAXS>
-__device__ __forceinline__ void wait_steps(int steps) {
-  if constexpr (MAXS == 0) {
-    DG_WAIT_VMCNT(0);
-  } else {
-    if (steps >= MAXS) {
-      DG_WAIT_VMCNT(LOADS * MAXS);
-    } else {
-      wait_steps<LOADS, MAXS - 1>(steps);
-    }
-  }
-}
-
-// Split-K: ksplit workgroups share one output tile, each covering a contiguous
-// range of 128-byte K steps. Each writes its FP32 partial tile to ws; the
-// last to arrive (per-tile arrival counter) adds the partials in split order
-// (so the result does not depend on which arrives last), resets the counter
-// and writes the BF16 tile. ksplit == 1 skips all of this.
-//
-// G is the K segment contracted before each promotion; the scale blocks are
-// sg x sg with sg = G << sshift (g = 256 runs G = 128 with one factor per two
-// segments). ROWA: A's factors are per row, sa is [M][K/sg].
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, bool ROWA>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
-    const uint8_t* __restrict__ a, const uint8_t* __restrict__ b, const float* __restrict__ sa,
-    const float* __restrict__ sb, uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
-    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, uint32_t* __restrict__ counters, int sshift,
-    const float* __restrict__ bias, int relu) {
-  constexpr int NWAVES = WM * WN;
-  constexpr int NT = 64 * NWAVES;
-  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
-  constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 sub-tiles per wave
-  constexpr int SEGS = BK / G;      // K segments per pipeline step
-  constexpr int KSTEPS = G / 64;    // MFMA K-steps per segment
-  constexpr int SCL = ROWA ? NWAVES * 256 : 0;  // per-row factors of a step: [SEGS][BM] FP32, a piece per wave
-  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE_BYTES = A_BYTES + B_BYTES + SCL;
-  // buffer_load ... lds per wave per step (the factor piece included)
-  constexpr int LOADS = (BM / 8 + BN / 8) / NWAVES + (ROWA ? 1 : 0);
-  constexpr int LDC = BN + 8;       // bf16 pitch of the epilogue tile (16-byte pad)
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 sub-tiles");
-  static_assert(G % 32 == 0 && BK % G == 0, "granularity must cover whole sub-tiles and steps");
-  static_assert(BM * LDC * 2 <= STAGES * STAGE_BYTES, "epilogue tile must fit in the ring");
-  static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
-  static_assert(BM * SEGS <= NWAVES * 64, "a step's row factors: one 64-entry piece per wave");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-
-  int ks, tmi, tni;
-  map_tile<GROUP_M>(tiles_m, tiles_n, ks, tmi, tni);
-  const int m0 = tmi * BM, n0 = tni * BN;
-  const uint32_t uK = (uint32_t)K;
-  const v4i ra = rsrc_words(a + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * uK);
-  const v4i rb = rsrc_words(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
-
-  const int nkb = K / G;                       // K segments
-  const int nsteps_all = (K + BK - 1) / BK;    // pipeline steps over the whole K
-  const int st0 = (int)((int64_t)ks * nsteps_all / ksplit);
-  const int nsteps = (int)((int64_t)(ks + 1) * nsteps_all / ksplit) - st0;  // this split's steps
-
-  // Scale rows of this wave's sub-tiles. A sub-tile lies inside one g-block
-  // (g >= 32, sub-tiles aligned to 32); sub-tiles past the edge clamp to the
-  // last block row so the index stays inside the scale tensor.
-  const int sg = G << sshift, nks = K / sg;  // scale blocks
-  const v4i rsa = ROWA ? rsrc_words(sa + (int64_t)m0 * nks, (uint32_t)min(BM, M - m0) * (uint32_t)nks * 4u) : (v4i){};
-  auto stage_step = [&](int s) {  // the copies of this split's step s into its ring slot
-    uint8_t* slot = smem + (s % STAGES) * STAGE_BYTES;
-    const int st = st0 + s;
-    if constexpr (ROWA)
-      stage_row_scales<BM, SEGS>(rsa, slot + A_BYTES + B_BYTES, (uint32_t)nks, (uint32_t)((st * SEGS) >> sshift), wave,
-                                 lane);
-    stage_slab<BM, NWAVES>(ra, slot, uK, st * BK, wave, lane);
-    stage_slab<BN, NWAVES>(rb, slot + A_BYTES, uK, st * BK, wave, lane);
-  };
-  const float* sa_row[TM];
-  const float* sb_row[TN];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) sa_row[t] = sa + (int64_t)min((m0 + wm * WTM + t * 32) / sg, (M - 1) / sg) * nks;
-#pragma unroll
-  for (int t = 0; t < TN; ++t) sb_row[t] = sb + (int64_t)min((n0 + wn * WTN + t * 32) / sg, (N - 1) / sg) * nks;
-
-  v16f acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = (v16f){};
-
-  // The epilogue's bias for this lane's columns, loaded before the first
-  // copies: the step waits cover it, and no output store is in flight when
-  // the epilogue reads it.
-  const bool hb = EPI != 0 && bias != nullptr;
-  float bcol[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-    bcol[j] = hb && col < N ? bias[col] : 0.0f;
-  }
-
-  // Prologue: fill STAGES-1 ring slots.
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nsteps) stage_step(s);
-
-  const int arow = wm * WTM + (lane & 31);
-  const int brow = wn * WTN + (lane & 31);
-  const int half = lane >> 5;
-
-  for (int s = 0; s < nsteps; ++s) {
-    // Step s landed once only the later steps' loads are outstanding.
-    wait_steps<LOADS, STAGES - 2>(min(STAGES - 2, nsteps - 1 - s));
-    __syncthreads();  // step s visible to all waves; slot (s-1)%STAGES free
-
-    if (s + STAGES - 1 < nsteps) stage_step(s + STAGES - 1);
-
-    const uint8_t* As = smem + (s % STAGES) * STAGE_BYTES;
-    const uint8_t* Bs = As + A_BYTES;
-    // ROWA: the step's factors [SEGS][BM]; this lane's rows of sub-tile i are
-    // wm*WTM + 32i + 8c + 4*half .. +3
-    const float* const scl = reinterpret_cast<const float*>(As + A_BYTES + B_BYTES) + wm * WTM + 4 * half;
-#pragma unroll
-    for (int seg = 0; seg < SEGS; ++seg) {
-      const int kb = (st0 + s) * SEGS + seg;
-      if (kb >= nkb) break;  // K % 128 == 64 with g = 64: the last step holds one segment
-      v8i af[TM][KSTEPS], bfr[TN][KSTEPS];
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int c0 = (seg * KSTEPS + ks) * 4 + half * 2;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[i][ks] = frag32(As, arow + i * 32, c0);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[j][ks] = frag32(Bs, brow + j * 32, c0);
-      }
-      float sbv[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sbv[j] = sb_row[j][kb >> sshift];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const float sav = ROWA ? 0.0f : sa_row[i][kb >> sshift];
-        v4f sr[4];
-        if constexpr (ROWA) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) sr[c] = *reinterpret_cast<const v4f*>(scl + seg * BM + i * 32 + 8 * c);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          v16f p = mfma_fp8<FMT>(af[i][0], bfr[j][0], (v16f){});
-#pragma unroll
-          for (int ks = 1; ks < KSTEPS; ++ks) p = mfma_fp8<FMT>(af[i][ks], bfr[j][ks], p);
-          if constexpr (ROWA) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sr[v >> 2][v & 3] * sbv[j], acc[i][j][v]);
-          } else {
-            const float sc = sav * sbv[j];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc, acc[i][j][v]);
-          }
-        }
-      }
-    }
-  }
-
-  if (SPLIT && ksplit > 1) {
-    // Partial tile layout: [split][wave][i][j][quarter][lane] of float4 within
-    // the tile's slice of ws, so each store and load below moves 1 KB
-    // contiguous per wave.
-    //
-    // Publication without cache-wide write-back or invalidate: the partials
-    // are written and read with device-scope (sc1) buffer stores and loads,
-    // which go to the point of coherence shared by all XCDs (the per-XCD L2s
-    // are not coherent with each other). The stores are waited for before
-    // the workgroup arrives at the tile's counter, and the last arrival's
-    // loads are issued only after its arrival returned, so it reads every
-    // split's finished partial.
-    constexpr int CPOL_SC1 = 16;  // device-scope coherence bit of the buffer instructions
-    constexpr int TILE_F = BM * BN, WAVE_F = TM * TN * 16 * 64;
-    const int tile = tmi * tiles_n + tni;
-    const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
-        ws + (int64_t)tile * ksplit * TILE_F, (short)0, ksplit * TILE_F * 4, 0x00020000);
-    const uint32_t lane_off = (uint32_t)(wave * WAVE_F + lane * 4) * 4;  // bytes
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const v4f v = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rws,
-                                                 lane_off + (uint32_t)(((i * TN + j) * 4 + c) * 256 * 4),
-                                                 (uint32_t)ks * TILE_F * 4, CPOL_SC1);
-        }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores have completed
-    __syncthreads();
-    __shared__ int last;
-    if (threadIdx.x == 0)
-      last = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (uint32_t)(ksplit - 1);
-    __syncthreads();
-    if (!last) return;
-    // Sum in split order 0, 1, ..., ksplit-1 (this split's own partial from
-    // registers): the same additions whichever split arrived last. The other
-    // splits' partials are fetched four splits at a time, all loads of a
-    // batch in flight together.
-    v4f tot[TM][TN][4];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) tot[i][j][c] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-    for (int sp0 = 0; sp0 < ksplit; sp0 += 4) {
-      v4f got[4][TM][TN][4];
-#pragma unroll
-      for (int bsp = 0; bsp < 4; ++bsp) {
-        // splits past the end and this split's own slot read nothing (an
-        // offset past the range reads zero) and are not added
-        const int sp = sp0 + bsp;
-        const uint32_t soff = (sp < ksplit && sp != ks) ? (uint32_t)sp * TILE_F * 4 : 0x80000000u;
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              got[bsp][i][j][c] = __builtin_bit_cast(
-                  v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                           rws, lane_off + (uint32_t)(((i * TN + j) * 4 + c) * 256 * 4), soff, CPOL_SC1));
-      }
-#pragma unroll
-      for (int bsp = 0; bsp < 4; ++bsp) {
-        const int sp = sp0 + bsp;
-        if (sp < ksplit) {
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                tot[i][j][c] += sp == ks ? (v4f){acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
-                                                 acc[i][j][4 * c + 3]}
-                                         : got[bsp][i][j][c];
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * c + e] = tot[i][j][c][e];
-  }
-
-  // Epilogue: BF16 tile through LDS, then 16-byte row-contiguous stores.
-  __syncthreads();
-  uint16_t* cs = reinterpret_cast<uint16_t*>(smem);
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        // 32x32 accumulator layout: lane%32 is the column, (v/4)*8 + (lane/32)*4 + v%4 the row.
-        const int r = wm * WTM + i * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
-        const int c = wn * WTN + j * 32 + (lane & 31);
-        cs[r * LDC + c] = bf16_bits(epilogue_fn<EPI>(acc[i][j][v], hb, bcol[j], relu));
-      }
-  __syncthreads();
-  constexpr int CHUNKS = BM * BN / 8;
-  for (int idx = threadIdx.x; idx < CHUNKS; idx += NT) {
-    const int r = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
-    const int gr = m0 + r, gc = n0 + c;
-    if (gr >= M || gc >= N) continue;
-    const v4i val = *reinterpret_cast<const v4i*>(cs + r * LDC + c);
-    uint16_t* dst = out + (int64_t)gr * N + gc;
-    if (vec_store && gc + 8 <= N) {
-      *reinterpret_cast<v4i*>(dst) = val;
-    } else {
-      for (int t = 0; t < 8 && gc + t < N; ++t) dst[t] = (uint16_t)((uint32_t)val[t >> 1] >> (16 * (t & 1)));
-    }
-  }
-  // The reducer returns the tile's arrival counter to zero for the next call.
-  // It is issued last: a device-coherent store ahead of the output stores
-  // holds them up.
-  if (SPLIT && ksplit > 1 && threadIdx.x == 0)
-    __hip_atomic_store(&counters[tmi * tiles_n + tni], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// ---- launch table -------------------------------------------------------------
-
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, bool ROWA>
-static hipError_t launch_tiled_fa(const GemmArgs& p, hipStream_t stream) {
-  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, ROWA>),
-                     dim3(tiles_m * tiles_n * p.ksplit), dim3(64 * WM * WN), 0, stream, p.a, p.b, p.sa, p.sb, p.out,
-                     (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.ksplit, p.ws, p.counters,
-                     p.sshift, p.bias, p.act == 1 ? 1 : 0);
-  return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI>
-static hipError_t launch_tiled_sa(const GemmArgs& p, hipStream_t stream) {
-  return p.rowa ? launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, true>(p, stream)
-                : launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, false>(p, stream);
-}
-
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT>
-static hipError_t launch_tiled_fmt(const GemmArgs& p, hipStream_t stream) {
-  switch (epilogue_form(p.bias, p.act)) {
-    case 0: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 0>(p, stream);
-    case 1: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 1>(p, stream);
-    case 2: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 2>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT>
-static hipError_t launch_tiled(const GemmArgs& p, hipStream_t stream) {
-  if ((!SPLIT && p.ksplit != 1) || p.sshift < 0 || p.sshift > 1) return hipErrorInvalidValue;
-  switch (p.fmt) {
-    case 0: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 0>(p, stream);
-    case 1: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 1>(p, stream);
-    case 2: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 2>(p, stream);
-    case 3: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 3>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
 
 KernelEntry kTable[] = {
     // id, class, bm, bn, stages, waves, gran, launcher
@@ -409,3 +60,4 @@ KernelEntry kTable[] = {
 const int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
 }  // namespace dg
+

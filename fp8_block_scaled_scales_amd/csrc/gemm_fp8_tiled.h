@@ -1,0 +1,471 @@
+// The tiled and split-K block-scaled FP8 GEMM kernel for gfx950 (template
+// and launch helpers), shared by the NT table entries (gemm_fp8_nt.hip) and
+// the transposed-operand layouts (gemm_fp8_layouts.hip). What the kernel
+// computes and how is described at the top of gemm_fp8_nt.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.h"
+#include "gemm_fp8_nt.h"
+
+namespace dg {
+
+constexpr int BK = 128;  // K bytes per pipeline step (row pitch of a staged slab)
+
+// 32 bytes of K (logical 16-byte chunks c0 and c0+1) of one staged row.
+__device__ __forceinline__ v8i frag32(const uint8_t* slab, int row, int c0) {
+  const int sw = row & 7;
+  const v4i lo = *reinterpret_cast<const v4i*>(slab + row * BK + ((c0 ^ sw) << 4));
+  const v4i hi = *reinterpret_cast<const v4i*>(slab + row * BK + (((c0 + 1) ^ sw) << 4));
+  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// Transposed operands (DeepGEMM实战 §3.3: A stored [K,M] or B stored [K,N]).
+// A step's tile of such an operand is staged as its 128 K rows of W bytes
+// (the tile's M or N extent, 64 or 128), 16-byte chunks XOR-swizzled by row,
+// and read into the MFMA fragment with the transposing LDS read.
+//
+// Swizzle key of row r: the eight consecutive rows one transposing read
+// touches at one logical chunk land on distinct banks (128-byte rows: all
+// eight chunks differ; 64-byte rows: rows four apart, which share a bank
+// offset, get different chunks).
+template <int W>
+__device__ __forceinline__ int tkey(int row) {
+  return W == 128 ? (row & 7) : ((row >> 2) & 3);
+}
+
+// One instruction of a transposed tile's copy: rows RPI*grp .. RPI*grp+RPI-1
+// (RPI = 1024/W) of the step's K rows, all W bytes, into LDS at
+// lds + 1024*grp. Lane L writes physical chunk L % (W/16) of its row, so it
+// fetches the logical chunk that belongs there. rsrc's base is the step's first
+// K row at the tile's first column; pitch is the stored row length (M or N).
+template <int W>
+__device__ __forceinline__ void stage_group_t(v4i rsrc, uint8_t* lds, uint32_t pitch, int grp, int lane) {
+  constexpr int CPR = W / 16, RPI = 64 / CPR;
+  const int r_in = lane / CPR, p = lane % CPR;
+  const uint32_t c = (uint32_t)(p ^ tkey<W>(grp * RPI + r_in));
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  lds_dma16(rsrc, __builtin_amdgcn_readfirstlane(lds_base + grp * 1024), (uint32_t)r_in * pitch + c * 16,
+            __builtin_amdgcn_readfirstlane((uint32_t)grp * RPI * pitch));
+}
+
+// The 32 K bytes of this lane's 32x32x64 fragment from a transposed tile:
+// lane l needs column col0 + l%32 (its row of A, or of B) at K bytes
+// kofs + 32*(l/32) .. +31. ds_read_b64_tr_b8 works on 16-lane groups: lane
+// 16G + 8h + j receives byte j of the eight 8-byte rows addressed by lanes
+// 16G + h, 16G + 2 + h, ..., 16G + 14 + h, in that order (measured on gfx950
+// with an address-coded LDS pattern). So lane x addresses row
+// kofs + 32*(x/32) + 8q + (x%16)/2 at column col0 + 16*((x/16)%2) + 8*(x%2),
+// and read q = 0..3 brings K bytes 8q .. 8q+7 of the lane's own column.
+template <int W>
+__device__ __forceinline__ v8i frag_tr(const uint8_t* slab, int col0, int kofs, int lane) {
+  typedef __attribute__((address_space(3))) v2i lds_v2i;
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+  const int row0 = kofs + 32 * (lane >> 5) + ((lane & 15) >> 1);
+  v2i r[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = row0 + 8 * q;
+    const int off = row * W + (((col >> 4) ^ tkey<W>(row)) << 4) + (col & 15);
+    r[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(lds_void_t*)(const_cast<uint8_t*>(slab) + off));
+  }
+  return (v8i){r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+}
+
+// FMT bit 0: A is E5M2 (else E4M3), bit 1: B is E5M2 -- the instruction's
+// operand-format fields (0 = E4M3, 1 = E5M2); no block-exponent scaling.
+template <int FMT>
+__device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT & 1, FMT >> 1, 0, 0, 0, 0);
+}
+
+// Wait until at most `steps` later pipeline steps' loads (LOADS each) are
+// still in flight for this wave; steps is 0 .. MAXS.
+template <int LOADS, int MAXS>
+__device__ __forceinline__ void wait_steps(int steps) {
+  if constexpr (MAXS == 0) {
+    DG_WAIT_VMCNT(0);
+  } else {
+    if (steps >= MAXS) {
+      DG_WAIT_VMCNT(LOADS * MAXS);
+    } else {
+      wait_steps<LOADS, MAXS - 1>(steps);
+    }
+  }
+}
+
+// Split-K: ksplit workgroups share one output tile, each covering a contiguous
+// range of 128-byte K steps. Each writes its FP32 partial tile to ws; the
+// last to arrive (per-tile arrival counter) adds the partials in split order
+// (so the result does not depend on which arrives last), resets the counter
+// and writes the BF16 tile. ksplit == 1 skips all of this.
+//
+// G is the K segment contracted before each promotion; the scale blocks are
+// sg x sg with sg = G << sshift (g = 256 runs G = 128 with one factor per two
+// segments). ROWA: A's factors are per row, sa is [M][K/sg]. LAYOUT bit 1: A
+// stored [K,M]; bit 0: B stored [K,N] (M resp. N a multiple of 16).
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, bool ROWA,
+          int LAYOUT>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
+    const uint8_t* __restrict__ a, const uint8_t* __restrict__ b, const float* __restrict__ sa,
+    const float* __restrict__ sb, uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
+    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, uint32_t* __restrict__ counters, int sshift,
+    const float* __restrict__ bias, int relu) {
+  constexpr int NWAVES = WM * WN;
+  constexpr int NT = 64 * NWAVES;
+  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+  constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 sub-tiles per wave
+  constexpr int SEGS = BK / G;      // K segments per pipeline step
+  constexpr int KSTEPS = G / 64;    // MFMA K-steps per segment
+  constexpr int SCL = ROWA ? NWAVES * 256 : 0;  // per-row factors of a step: [SEGS][BM] FP32, a piece per wave
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE_BYTES = A_BYTES + B_BYTES + SCL;
+  // buffer_load ... lds per wave per step (the factor piece included)
+  constexpr int LOADS = (BM / 8 + BN / 8) / NWAVES + (ROWA ? 1 : 0);
+  constexpr int LDC = BN + 8;       // bf16 pitch of the epilogue tile (16-byte pad)
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 sub-tiles");
+  static_assert(G % 32 == 0 && BK % G == 0, "granularity must cover whole sub-tiles and steps");
+  static_assert(BM * LDC * 2 <= STAGES * STAGE_BYTES, "epilogue tile must fit in the ring");
+  static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(BM * SEGS <= NWAVES * 64, "a step's row factors: one 64-entry piece per wave");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  int ks, tmi, tni;
+  map_tile<GROUP_M>(tiles_m, tiles_n, ks, tmi, tni);
+  const int m0 = tmi * BM, n0 = tni * BN;
+  const uint32_t uK = (uint32_t)K;
+  const v4i ra = rsrc_words(a + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * uK);
+  const v4i rb = rsrc_words(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
+
+  const int nkb = K / G;                       // K segments
+  const int nsteps_all = (K + BK - 1) / BK;    // pipeline steps over the whole K
+  const int st0 = (int)((int64_t)ks * nsteps_all / ksplit);
+  const int nsteps = (int)((int64_t)(ks + 1) * nsteps_all / ksplit) - st0;  // this split's steps
+
+  // Scale rows of this wave's sub-tiles. A sub-tile lies inside one g-block
+  // (g >= 32, sub-tiles aligned to 32); sub-tiles past the edge clamp to the
+  // last block row so the index stays inside the scale tensor.
+  const int sg = G << sshift, nks = K / sg;  // scale blocks
+  const v4i rsa = ROWA ? rsrc_words(sa + (int64_t)m0 * nks, (uint32_t)min(BM, M - m0) * (uint32_t)nks * 4u) : (v4i){};
+  auto stage_step = [&](int s) {  // the copies of this split's step s into its ring slot
+    uint8_t* slot = smem + (s % STAGES) * STAGE_BYTES;
+    const int st = st0 + s;
+    if constexpr (ROWA)
+      stage_row_scales<BM, SEGS>(rsa, slot + A_BYTES + B_BYTES, (uint32_t)nks, (uint32_t)((st * SEGS) >> sshift), wave,
+                                 lane);
+    const int64_t k0 = (int64_t)st * BK;
+    if constexpr ((LAYOUT & 2) != 0) {
+      // the step's K rows of A^T from column m0; past the tensor reads zero
+      const v4i rat = rsrc_words(a + k0 * M + m0, (uint32_t)(min((int64_t)BK, (int64_t)K - k0) * M - m0));
+#pragma unroll
+      for (int i = 0; i < BM / 8 / NWAVES; ++i) stage_group_t<BM>(rat, slot, (uint32_t)M, i * NWAVES + wave, lane);
+    } else {
+      stage_slab<BM, NWAVES>(ra, slot, uK, st * BK, wave, lane);
+    }
+    if constexpr ((LAYOUT & 1) != 0) {
+      const v4i rbt = rsrc_words(b + k0 * N + n0, (uint32_t)(min((int64_t)BK, (int64_t)K - k0) * N - n0));
+#pragma unroll
+      for (int i = 0; i < BN / 8 / NWAVES; ++i)
+        stage_group_t<BN>(rbt, slot + A_BYTES, (uint32_t)N, i * NWAVES + wave, lane);
+    } else {
+      stage_slab<BN, NWAVES>(rb, slot + A_BYTES, uK, st * BK, wave, lane);
+    }
+  };
+  const float* sa_row[TM];
+  const float* sb_row[TN];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) sa_row[t] = sa + (int64_t)min((m0 + wm * WTM + t * 32) / sg, (M - 1) / sg) * nks;
+#pragma unroll
+  for (int t = 0; t < TN; ++t) sb_row[t] = sb + (int64_t)min((n0 + wn * WTN + t * 32) / sg, (N - 1) / sg) * nks;
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (v16f){};
+
+  // The epilogue's bias for this lane's columns, loaded before the first
+  // copies: the step waits cover it, and no output store is in flight when
+  // the epilogue reads it.
+  const bool hb = EPI != 0 && bias != nullptr;
+  float bcol[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+    bcol[j] = hb && col < N ? bias[col] : 0.0f;
+  }
+
+  // Prologue: fill STAGES-1 ring slots.
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nsteps) stage_step(s);
+
+  const int arow = wm * WTM + (lane & 31);
+  const int brow = wn * WTN + (lane & 31);
+  const int half = lane >> 5;
+
+  for (int s = 0; s < nsteps; ++s) {
+    // Step s landed once only the later steps' loads are outstanding.
+    wait_steps<LOADS, STAGES - 2>(min(STAGES - 2, nsteps - 1 - s));
+    __syncthreads();  // step s visible to all waves; slot (s-1)%STAGES free
+
+    if (s + STAGES - 1 < nsteps) stage_step(s + STAGES - 1);
+
+    const uint8_t* As = smem + (s % STAGES) * STAGE_BYTES;
+    const uint8_t* Bs = As + A_BYTES;
+    // ROWA: the step's factors [SEGS][BM]; this lane's rows of sub-tile i are
+    // wm*WTM + 32i + 8c + 4*half .. +3
+    const float* const scl = reinterpret_cast<const float*>(As + A_BYTES + B_BYTES) + wm * WTM + 4 * half;
+#pragma unroll
+    for (int seg = 0; seg < SEGS; ++seg) {
+      const int kb = (st0 + s) * SEGS + seg;
+      if (kb >= nkb) break;  // K % 128 == 64 with g = 64: the last step holds one segment
+      v8i af[TM][KSTEPS], bfr[TN][KSTEPS];
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int c0 = (seg * KSTEPS + ks) * 4 + half * 2;
+        const int kofs = (seg * KSTEPS + ks) * 64;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if constexpr ((LAYOUT & 2) != 0) {
+            af[i][ks] = frag_tr<BM>(As, wm * WTM + i * 32, kofs, lane);
+          } else {
+            af[i][ks] = frag32(As, arow + i * 32, c0);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          if constexpr ((LAYOUT & 1) != 0) {
+            bfr[j][ks] = frag_tr<BN>(Bs, wn * WTN + j * 32, kofs, lane);
+          } else {
+            bfr[j][ks] = frag32(Bs, brow + j * 32, c0);
+          }
+        }
+      }
+      float sbv[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sbv[j] = sb_row[j][kb >> sshift];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const float sav = ROWA ? 0.0f : sa_row[i][kb >> sshift];
+        v4f sr[4];
+        if constexpr (ROWA) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sr[c] = *reinterpret_cast<const v4f*>(scl + seg * BM + i * 32 + 8 * c);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          v16f p = mfma_fp8<FMT>(af[i][0], bfr[j][0], (v16f){});
+#pragma unroll
+          for (int ks = 1; ks < KSTEPS; ++ks) p = mfma_fp8<FMT>(af[i][ks], bfr[j][ks], p);
+          if constexpr (ROWA) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sr[v >> 2][v & 3] * sbv[j], acc[i][j][v]);
+          } else {
+            const float sc = sav * sbv[j];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc, acc[i][j][v]);
+          }
+        }
+      }
+    }
+  }
+
+  if (SPLIT && ksplit > 1) {
+    // Partial tile layout: [split][wave][i][j][quarter][lane] of float4 within
+    // the tile's slice of ws, so each store and load below moves 1 KB
+    // contiguous per wave.
+    //
+    // Publication without cache-wide write-back or invalidate: the partials
+    // are written and read with device-scope (sc1) buffer stores and loads,
+    // which go to the point of coherence shared by all XCDs (the per-XCD L2s
+    // are not coherent with each other). The stores are waited for before
+    // the workgroup arrives at the tile's counter, and the last arrival's
+    // loads are issued only after its arrival returned, so it reads every
+    // split's finished partial.
+    constexpr int CPOL_SC1 = 16;  // device-scope coherence bit of the buffer instructions
+    constexpr int TILE_F = BM * BN, WAVE_F = TM * TN * 16 * 64;
+    const int tile = tmi * tiles_n + tni;
+    const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
+        ws + (int64_t)tile * ksplit * TILE_F, (short)0, ksplit * TILE_F * 4, 0x00020000);
+    const uint32_t lane_off = (uint32_t)(wave * WAVE_F + lane * 4) * 4;  // bytes
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const v4f v = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rws,
+                                                 lane_off + (uint32_t)(((i * TN + j) * 4 + c) * 256 * 4),
+                                                 (uint32_t)ks * TILE_F * 4, CPOL_SC1);
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores have completed
+    __syncthreads();
+    __shared__ int last;
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(ksplit - 1);
+    __syncthreads();
+    if (!last) return;
+    // Sum in split order 0, 1, ..., ksplit-1 (this split's own partial from
+    // registers): the same additions whichever split arrived last. The other
+    // splits' partials are fetched four splits at a time, all loads of a
+    // batch in flight together.
+    v4f tot[TM][TN][4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) tot[i][j][c] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sp0 = 0; sp0 < ksplit; sp0 += 4) {
+      v4f got[4][TM][TN][4];
+#pragma unroll
+      for (int bsp = 0; bsp < 4; ++bsp) {
+        // splits past the end and this split's own slot read nothing (an
+        // offset past the range reads zero) and are not added
+        const int sp = sp0 + bsp;
+        const uint32_t soff = (sp < ksplit && sp != ks) ? (uint32_t)sp * TILE_F * 4 : 0x80000000u;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              got[bsp][i][j][c] = __builtin_bit_cast(
+                  v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                           rws, lane_off + (uint32_t)(((i * TN + j) * 4 + c) * 256 * 4), soff, CPOL_SC1));
+      }
+#pragma unroll
+      for (int bsp = 0; bsp < 4; ++bsp) {
+        const int sp = sp0 + bsp;
+        if (sp < ksplit) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                tot[i][j][c] += sp == ks ? (v4f){acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
+                                                 acc[i][j][4 * c + 3]}
+                                         : got[bsp][i][j][c];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * c + e] = tot[i][j][c][e];
+  }
+
+  // Epilogue: BF16 tile through LDS, then 16-byte row-contiguous stores.
+  __syncthreads();
+  uint16_t* cs = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        // 32x32 accumulator layout: lane%32 is the column, (v/4)*8 + (lane/32)*4 + v%4 the row.
+        const int r = wm * WTM + i * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
+        const int c = wn * WTN + j * 32 + (lane & 31);
+        cs[r * LDC + c] = bf16_bits(epilogue_fn<EPI>(acc[i][j][v], hb, bcol[j], relu));
+      }
+  __syncthreads();
+  constexpr int CHUNKS = BM * BN / 8;
+  for (int idx = threadIdx.x; idx < CHUNKS; idx += NT) {
+    const int r = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
+    const int gr = m0 + r, gc = n0 + c;
+    if (gr >= M || gc >= N) continue;
+    const v4i val = *reinterpret_cast<const v4i*>(cs + r * LDC + c);
+    uint16_t* dst = out + (int64_t)gr * N + gc;
+    if (vec_store && gc + 8 <= N) {
+      *reinterpret_cast<v4i*>(dst) = val;
+    } else {
+      for (int t = 0; t < 8 && gc + t < N; ++t) dst[t] = (uint16_t)((uint32_t)val[t >> 1] >> (16 * (t & 1)));
+    }
+  }
+  // The reducer returns the tile's arrival counter to zero for the next call.
+  // It is issued last: a device-coherent store ahead of the output stores
+  // holds them up.
+  if (SPLIT && ksplit > 1 && threadIdx.x == 0)
+    __hip_atomic_store(&counters[tmi * tiles_n + tni], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- launch table -------------------------------------------------------------
+
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, bool ROWA,
+          int LAYOUT>
+static hipError_t launch_tiled_fa(const GemmArgs& p, hipStream_t stream) {
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, ROWA, LAYOUT>),
+                     dim3(tiles_m * tiles_n * p.ksplit), dim3(64 * WM * WN), 0, stream, p.a, p.b, p.sa, p.sb, p.out,
+                     (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.ksplit, p.ws, p.counters,
+                     p.sshift, p.bias, p.act == 1 ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Per-row A factors are compiled for the NT layout only.
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, int LAYOUT>
+static hipError_t launch_tiled_sa(const GemmArgs& p, hipStream_t stream) {
+  if constexpr (LAYOUT != 0) {
+    return p.rowa ? hipErrorInvalidValue
+                  : launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, false, LAYOUT>(p, stream);
+  } else {
+    return p.rowa ? launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, true, 0>(p, stream)
+                  : launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, false, 0>(p, stream);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int LAYOUT>
+static hipError_t launch_tiled_fmt(const GemmArgs& p, hipStream_t stream) {
+  switch (epilogue_form(p.bias, p.act)) {
+    case 0: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 0, LAYOUT>(p, stream);
+    case 1: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 1, LAYOUT>(p, stream);
+    case 2: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 2, LAYOUT>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int LAYOUT>
+static hipError_t launch_tiled_l(const GemmArgs& p, hipStream_t stream) {
+  if ((!SPLIT && p.ksplit != 1) || p.sshift < 0 || p.sshift > 1) return hipErrorInvalidValue;
+  switch (p.fmt) {
+    case 0: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 0, LAYOUT>(p, stream);
+    case 1: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 1, LAYOUT>(p, stream);
+    case 2: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 2, LAYOUT>(p, stream);
+    case 3: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 3, LAYOUT>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The NT table entries.
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT>
+static hipError_t launch_tiled(const GemmArgs& p, hipStream_t stream) {
+  return p.layout == 0 ? launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 0>(p, stream) : hipErrorInvalidValue;
+}
+
+// The transposed layouts on the same tile (instantiated in gemm_fp8_layouts.hip).
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT>
+static hipError_t launch_tiled_layout(const GemmArgs& p, hipStream_t stream) {
+  switch (p.layout) {
+    case 1: return launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 1>(p, stream);
+    case 2: return launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 2>(p, stream);
+    case 3: return launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 3>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dg

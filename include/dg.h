@@ -132,6 +132,38 @@ int dg_gemm_fp8_nt_ex(const void* a, const void* b, const float* sa, const float
                       int64_t M, int64_t N, int64_t K, int gran, int sa_rows, int fmt_a, int fmt_b,
                       const float* bias, int act, void* stream);
 
+/* Operand layouts (DeepGEMM实战 §3.3: each of A and B may be stored
+ * transposed; the kernels read it that way, with no transposed copy in
+ * memory). Named as C = op(A) op(B): first letter A, second B, with op(B) = B^T
+ * for B stored [N,K]. Bit 1: A stored [K,M]; bit 0: B stored [K,N]. */
+#define DG_LAYOUT_NT 0 /* A [M,K], B [N,K]: both K-contiguous (the other calls) */
+#define DG_LAYOUT_NN 1 /* A [M,K], B [K,N] */
+#define DG_LAYOUT_TT 2 /* A [K,M], B [N,K] */
+#define DG_LAYOUT_TN 3 /* A [K,M], B [K,N] */
+
+/*
+ * dg_gemm_fp8_layout - dg_gemm_fp8_nt_epi with the operands stored in any of
+ * the four layouts:
+ *
+ *   a    A[i,k] at a[i*K + k] (NT, NN: [M,K]) or at a[k*M + i] (TT, TN: [K,M]).
+ *   b    B[j,k] at b[j*K + k] (NT, TT: [N,K]) or at b[k*N + j] (NN, TN: [K,N]).
+ *   sa, sb  the logical block factors, as in dg_gemm_fp8_nt: sa
+ *        [ceil(M/g)][K/g], sb [ceil(N/g)][K/g], whatever the layout (a
+ *        quantiser run on a stored [K,M] matrix gives the transpose of sa).
+ *   layout  DG_LAYOUT_NT, _NN, _TT or _TN.
+ *
+ * The result is the same product, out[i,j] as in dg_gemm_fp8_nt_epi. A stored
+ * [K,M] needs M % 16 == 0 and B stored [K,N] needs N % 16 == 0 (DG_EINVAL
+ * otherwise); a and b 16-byte aligned as before. DG_LAYOUT_NT is
+ * dg_gemm_fp8_nt_epi bit for bit. The other layouts run the tiled classes
+ * (split-K 64x64 tiles for M <= 128, 128x128 tiles otherwise; see
+ * dg_query_tile_layout), which the pages' remark that NT is the fastest layout
+ * holds for here too. Per-row A factors are NT only (dg_gemm_fp8_nt_ex).
+ */
+int dg_gemm_fp8_layout(const void* a, const void* b, const float* sa, const float* sb, void* out,
+                       int64_t M, int64_t N, int64_t K, int gran, int layout, int fmt_a, int fmt_b,
+                       const float* bias, int act, void* stream);
+
 /* The tile-table entry a call with these sizes would use. */
 typedef struct dg_tile_info {
   int kernel_id; /* index in the precompiled table */
@@ -149,6 +181,11 @@ typedef struct dg_tile_info {
  * DG_EINVAL for arguments dg_gemm_fp8_nt would reject.
  */
 int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info);
+
+/* dg_query_tile for dg_gemm_fp8_layout: the entry a call with this layout
+ * would use (DG_EINVAL for a layout or a transposed row length that call
+ * would reject). */
+int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, dg_tile_info* info);
 
 /*
  * dg_quantize_e4m3_blocks - block quantisation FP32 -> E4M3FN, the step that

@@ -121,6 +121,44 @@ def test_python_binding_checks_row_scale_shapes(dg):
         dg.dg_gemm_fp8_nt_ex(a, b, torch.zeros((300, 2)), sb, sa_rows=1)  # well-formed, but on the CPU
 
 
+@pytest.mark.parametrize("layout,M,N,want", [(4, 256, 256, "DG_EINVAL"), (-1, 256, 256, "DG_EINVAL"),
+                                              (2, 1000, 256, "DG_EINVAL"), (3, 1000, 256, "DG_EINVAL"),
+                                              (1, 256, 1000, "DG_EINVAL"), (3, 256, 1000, "DG_EINVAL")])
+def test_layout_rejects(dg, layout, M, N, want):
+    assert dg.lib.dg_gemm_fp8_layout(A, B, SA, SB, OUT, M, N, 256, 128, layout, 0, 0, None, 0, None) == getattr(dg, want)
+    info = dg.dg_tile_info()
+    assert dg.lib.dg_query_tile_layout(M, N, 256, 128, layout, ctypes.byref(info)) == getattr(dg, want)
+
+
+@pytest.mark.parametrize("M,N,K,g,layout,cls_bm", [(64, 4096, 7168, 128, 1, 64), (4096, 7168, 2048, 128, 3, 128),
+                                                   (1008, 3008, 512, 64, 2, 128), (128, 512, 1024, 256, 3, 64)])
+def test_layout_tile_choice(dg, M, N, K, g, layout, cls_bm):
+    t = dg.dg_query_tile(M, N, K, g, layout)
+    assert t["bm"] == cls_bm and t["bn"] == cls_bm  # transposed layouts run the 64x64 split-K or 128x128 tiles
+    assert dg.dg_query_tile(M, N, K, g, 0) == dg.dg_query_tile(M, N, K, g)
+
+
+def test_layout_codes_match_header(dg):
+    text = open(HEADER).read()
+    for name in ("DG_LAYOUT_NT", "DG_LAYOUT_NN", "DG_LAYOUT_TT", "DG_LAYOUT_TN"):
+        m = re.search(r"#define %s (\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(dg, name), name
+
+
+def test_python_binding_checks_layout_shapes(dg):
+    import torch
+
+    a_km = torch.zeros((256, 64), dtype=torch.float8_e4m3fn)   # A stored [K, M]
+    b_nk = torch.zeros((32, 256), dtype=torch.float8_e4m3fn)   # B stored [N, K]
+    sa, sb = torch.zeros((1, 2)), torch.zeros((1, 2))
+    with pytest.raises(ValueError, match="b has shape"):
+        dg.dg_gemm_fp8_layout(a_km, b_nk, sa, sb, layout=dg.DG_LAYOUT_TN)  # TN wants B [K, N]
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dg.dg_gemm_fp8_layout(a_km, b_nk, sa, sb, layout=dg.DG_LAYOUT_TT)  # well-formed, but on the CPU
+    with pytest.raises(ValueError, match="layout"):
+        dg.dg_gemm_fp8_layout(a_km, b_nk, sa, sb, layout=5)
+
+
 def test_format_codes_match_header(dg):
     text = open(HEADER).read()
     for name in ("DG_FMT_E4M3", "DG_FMT_E5M2", "DG_ACT_NONE", "DG_ACT_RELU", "DG_ACT_GELU"):

@@ -1,0 +1,172 @@
+"""The transposed operand layouts on the GPU (through the C ABI) against the
+CPU oracle.
+
+DeepGEMM实战 §3.3: A and B may each be stored transposed ([K,M], [K,N]) and are
+read that way. Every layout runs on shapes of both classes the transposed
+layouts use (split-K 64x64 for M <= 128, 128x128 otherwise), with ragged M
+and N (multiples of 16), K % 128 == 64 at g = 64, and g = 256. Bars: the
+elementwise tolerance against the oracle's layout reference; bit for bit
+across NN, TT and TN (one kernel family, the same K order), for all-ones
+closed forms, and for NT through the layout call against the NT call.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _common
+from tests._gpu import say
+
+pytestmark = pytest.mark.gpu
+
+NT, NN, TT, TN = 0, 1, 2, 3
+TRANSPOSED = [NN, TT, TN]
+
+# (M, N, K, g, expected tile): ragged M, N (multiples of 16)
+SHAPES = [
+    (64, 4096, 1024, 128, (64, 64)),    # split-K
+    (96, 528, 1088, 64, (64, 64)),
+    (128, 512, 1024, 256, (64, 64)),
+    (1008, 3008, 512, 128, (128, 128)),  # tiled
+    (1024, 2000, 576, 64, (128, 128)),
+    (512, 1040, 768, 256, (128, 128)),
+]
+
+
+def _store(a8, b8, layout):
+    a_st = np.ascontiguousarray(a8.T) if layout & 2 else a8
+    b_st = np.ascontiguousarray(b8.T) if layout & 1 else b8
+    return a_st, b_st
+
+
+def _run(a_st, b_st, sa, sb, g, layout, fa=0, fb=0, bias=None, act=0):
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    dev = "cuda:0"
+    ta = torch.from_numpy(a_st).to(dev)
+    tb = torch.from_numpy(b_st).to(dev)
+    tsa = torch.from_numpy(np.ascontiguousarray(sa)).to(dev)
+    tsb = torch.from_numpy(np.ascontiguousarray(sb)).to(dev)
+    tbias = None if bias is None else torch.from_numpy(bias).to(dev)
+    out = dg.dg_gemm_fp8_layout(ta, tb, tsa, tsb, gran=g, layout=layout, fmt_a=fa, fmt_b=fb, bias=tbias, act=act)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _operands(M, N, K, g, fa, fb, seed):
+    a8, sa = oracle.quantize_blocks_fmt(synth.normal(seed, (M, K)), g, fa)
+    b8, sb = oracle.quantize_blocks_fmt(synth.normal(seed + 1, (N, K), sigma=0.02), g, fb)
+    return a8, sa, b8, sb
+
+
+def _sample(M, N, tile, seed):
+    rows = np.unique(np.concatenate([_common.sample_indices(M, 120, seed=seed), np.arange(0, M, tile[0]),
+                                     np.arange(tile[0] - 1, M, tile[0]), [M - 1]]))
+    cols = np.unique(np.concatenate([_common.sample_indices(N, 120, seed=seed + 1), np.arange(0, N, tile[1]),
+                                     np.arange(tile[1] - 1, N, tile[1]), [N - 1]]))
+    return rows, cols
+
+
+def _assert_parity(got, ref, label):
+    ok, rms = _common.within_tolerance(got, ref)
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        detail = ", ".join("(%d,%d) got %.6g ref %.6g" % (i, j, got[i, j], ref[i, j]) for i, j in idx)
+        raise AssertionError("%s: %d of %d outside tolerance: %s" % (label, int((~ok).sum()), ok.size, detail))
+    say("%s: max|err|/rms = %.3g" % (label, np.max(np.abs(got - ref)) / rms))
+
+
+@pytest.mark.parametrize("layout", TRANSPOSED)
+@pytest.mark.parametrize("M,N,K,g,tile", SHAPES)
+def test_layout_parity(M, N, K, g, tile, layout):
+    import fp8_block_scaled_scales_amd as dg
+
+    t = dg.dg_query_tile(M, N, K, g, layout)
+    assert (t["bm"], t["bn"]) == tile, t
+    a8, sa, b8, sb = _operands(M, N, K, g, 0, 0, seed=11000 + M + K)
+    a_st, b_st = _store(a8, b8, layout)
+    say("layout %d M=%d N=%d K=%d g=%d" % (layout, M, N, K, g))
+    got, _ = _run(a_st, b_st, sa, sb, g, layout)
+    rows, cols = _sample(M, N, tile, M + N)
+    ref = oracle.gemm_ref_layout(a_st, b_st, sa, sb, g, layout, M, N, K, rows=rows, cols=cols)
+    _assert_parity(got[np.ix_(rows, cols)], ref, "layout %d %dx%dx%d g=%d" % (layout, M, N, K, g))
+
+
+@pytest.mark.parametrize("layout,fa,fb,act,with_bias", [(NN, 1, 0, 0, False), (TN, 0, 1, 2, True),
+                                                        (TT, 1, 1, 1, True)])
+@pytest.mark.parametrize("M,N,K,g,tile", [SHAPES[1], SHAPES[3]])
+def test_layout_with_formats_and_epilogue(M, N, K, g, tile, layout, fa, fb, act, with_bias):
+    a8, sa, b8, sb = _operands(M, N, K, g, fa, fb, seed=12000 + M + 10 * layout)
+    bias = synth.normal(12100 + N, (N,), sigma=0.5).astype(np.float32) if with_bias else None
+    a_st, b_st = _store(a8, b8, layout)
+    say("layout %d fmt %d,%d act=%d bias=%d M=%d N=%d K=%d g=%d" % (layout, fa, fb, act, with_bias, M, N, K, g))
+    got, _ = _run(a_st, b_st, sa, sb, g, layout, fa, fb, bias, act)
+    rows, cols = _sample(M, N, tile, M + 3 * N)
+    ref = oracle.epilogue(oracle.gemm_ref_layout(a_st, b_st, sa, sb, g, layout, M, N, K, fa, fb, rows, cols),
+                          bias, act, cols)
+    _assert_parity(got[np.ix_(rows, cols)], ref, "layout %d fmt %d,%d act %d" % (layout, fa, fb, act))
+
+
+@pytest.mark.parametrize("M,N,K,g,tile", SHAPES)
+def test_transposed_layouts_agree_bitwise(M, N, K, g, tile):
+    a8, sa, b8, sb = _operands(M, N, K, g, 0, 0, seed=13000 + M + K)
+    bits = {}
+    for layout in TRANSPOSED:
+        a_st, b_st = _store(a8, b8, layout)
+        say("layout %d bits M=%d N=%d K=%d g=%d" % (layout, M, N, K, g))
+        bits[layout] = _run(a_st, b_st, sa, sb, g, layout)[1]
+    assert np.array_equal(bits[NN], bits[TT]) and np.array_equal(bits[NN], bits[TN])
+
+
+@pytest.mark.parametrize("layout", TRANSPOSED)
+@pytest.mark.parametrize("M,N,K,g,tile", [SHAPES[0], SHAPES[1], SHAPES[3], SHAPES[5]])
+def test_layout_closed_form_all_ones_bitwise(M, N, K, g, tile, layout):
+    a8 = np.full((M, K), 0x38, np.uint8)
+    b8 = np.full((N, K), 0x38, np.uint8)
+    nkb = K // g
+    sa = (2.0 ** ((np.arange((M + g - 1) // g)[:, None] - np.arange(nkb)[None, :]) % 7 - 3)).astype(np.float32)
+    sb = (2.0 ** ((2 * np.arange((N + g - 1) // g)[:, None] + np.arange(nkb)[None, :]) % 3)).astype(np.float32)
+    a_st, b_st = _store(a8, b8, layout)
+    say("layout %d closed form M=%d N=%d K=%d g=%d" % (layout, M, N, K, g))
+    _, bits = _run(a_st, b_st, sa, sb, g, layout)
+    rows = np.unique(np.concatenate([np.arange(0, M, 7), [M - 1]]))
+    cols = np.unique(np.concatenate([np.arange(0, N, 37), [N - 1]]))
+    ref = oracle.gemm_ref_layout(a_st, b_st, sa, sb, g, layout, M, N, K, rows=rows, cols=cols)
+    assert np.array_equal(bits[np.ix_(rows, cols)], _common.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+def test_layout_permutation_closed_form_bitwise():
+    # A[i,k] = 1 where k = p(i): out[i,j] = sa*sb*B[j, p(i)], one element each,
+    # which any transposed index or misplaced transposing read gets wrong
+    M, N, K, g = 1008, 528, 1024, 128
+    rng = np.random.default_rng(14000)
+    p = rng.integers(0, K, size=M)
+    a8 = np.zeros((M, K), np.uint8)
+    a8[np.arange(M), p] = 0x38
+    b8 = rng.integers(0, 0x7F, size=(N, K), dtype=np.uint8)
+    sa = np.ones(((M + g - 1) // g, K // g), np.float32)
+    sb = np.ones(((N + g - 1) // g, K // g), np.float32)
+    for layout in TRANSPOSED:
+        a_st, b_st = _store(a8, b8, layout)
+        say("layout %d permutation closed form" % layout)
+        _, bits = _run(a_st, b_st, sa, sb, g, layout)
+        ref = oracle.gemm_ref_layout(a_st, b_st, sa, sb, g, layout, M, N, K)
+        assert np.array_equal(bits, _common.f32_to_bf16_bits(ref.astype(np.float32))), layout
+
+
+def test_nt_through_the_layout_call_is_the_nt_call_bitwise():
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    M, N, K, g = 1000, 3000, 512, 128
+    a8, sa, b8, sb = _operands(M, N, K, g, 0, 0, seed=15000)
+    o1 = _run(a8, b8, sa, sb, g, NT)[1]
+    dev = "cuda:0"
+    o2 = dg.dg_gemm_fp8_nt(torch.from_numpy(a8).to(dev), torch.from_numpy(b8).to(dev),
+                           torch.from_numpy(sa).to(dev), torch.from_numpy(sb).to(dev), gran=g)
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, o2.view(torch.int16).cpu().numpy().view(np.uint16))
