@@ -103,19 +103,20 @@ int64_t splits_for(const dg::KernelEntry* e, int64_t tiles, int64_t nsteps) {
   return std::max<int64_t>(ks, 1);
 }
 
-// Transposed layouts (layout != NT) run the tiled classes only: split-K 64x64
-// tiles for M <= 128, 128x128 tiles otherwise.
+// Transposed layouts (layout != NT) take split-K 64x64 tiles for M <= 128, and
+// otherwise the 256-row tiles 256 or 128 wide (not 224) or 128x128 tiles by the
+// rule below.
 Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout = DG_LAYOUT_NT) {
   Plan p{nullptr, 1, 0};
   const int gran = kernel_gran(sgran);
   const int64_t nsteps = (K + 127) / 128;
-  if (layout != DG_LAYOUT_NT) {
-    p.e = find(M <= 128 ? dg::kClassSplitK : dg::kClassTiled, gran);
+  if (layout != DG_LAYOUT_NT && M <= 128) {
+    p.e = find(dg::kClassSplitK, gran);
     p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
-    if (p.e->cls == dg::kClassSplitK) p.ksplit = (int)splits_for(p.e, p.tiles, nsteps);
+    p.ksplit = (int)splits_for(p.e, p.tiles, nsteps);
     return p;
   }
-  const int force = forced_tile();
+  const int force = layout == DG_LAYOUT_NT ? forced_tile() : -1;
   if (force >= 0) {
     for (int i = 0; i < dg::kTableSize; ++i)
       if (dg::kTable[i].id == force && dg::kTable[i].gran == gran) p.e = &dg::kTable[i];
@@ -147,6 +148,7 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout = DG_LAYOUT_NT)
   for (int i = 0; i < dg::kTableSize; ++i) {
     const dg::KernelEntry* e = &dg::kTable[i];
     if (e->cls != dg::kClassBig || e->gran != gran) continue;
+    if (layout != DG_LAYOUT_NT && e->bn == 224) continue;  // transposed tiles are 256 or 128 wide
     const int64_t t = ((M + e->bm - 1) / e->bm) * ((N + e->bn - 1) / e->bn);
     const double fill = (double)t / (double)(256 * ((t + 255) / 256));
     const double per_cu = e->bn == 256 ? 1.0 : e->bn == 224 ? 0.97 : 0.8;

@@ -1,0 +1,454 @@
+// The 256-row-tile block-scaled FP8 GEMM kernel for gfx950 (template and
+// launch helpers), shared by the NT table entries (gemm_fp8_nt_big.hip) and
+// the transposed-operand layouts (gemm_fp8_big_layouts.hip). What the kernel
+// computes and how is described at the top of gemm_fp8_nt_big.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.h"
+#include "gemm_fp8_nt.h"
+
+namespace dg {
+
+namespace big {
+
+constexpr int BM = 256, BK = 128, NW = 8, NT = 64 * NW;
+constexpr int A_BYTES = BM * BK;
+
+// 32 K bytes (logical 16-byte chunks c0, c0+1) of staged row `row` under the
+// SW = 1 swizzle.
+__device__ __forceinline__ v8i frag(const uint8_t* slab, int row, int c0) {
+  const int sw = (row >> 1) & 7;
+  const v4i lo = *reinterpret_cast<const v4i*>(slab + row * BK + ((c0 ^ sw) << 4));
+  const v4i hi = *reinterpret_cast<const v4i*>(slab + row * BK + (((c0 + 1) ^ sw) << 4));
+  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// FMT bit 0: A is E5M2 (else E4M3), bit 1: B is E5M2; the instructions'
+// operand-format fields (0 = E4M3, 1 = E5M2), no block-exponent scaling.
+template <int FMT>
+__device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, (v4f){}, FMT & 1, FMT >> 1, 0, 0, 0, 0);
+}
+
+template <int FMT>
+__device__ __forceinline__ v16f mfma32(const v8i& a, const v8i& b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, (v16f){}, FMT & 1, FMT >> 1, 0, 0, 0, 0);
+}
+
+template <int G, int WTM, int WTN>
+struct Acc;
+template <int WTM, int WTN>
+struct Acc<128, WTM, WTN> {
+  v4f t[WTM / 16][WTN / 16];
+};
+template <int WTM, int WTN>
+struct Acc<64, WTM, WTN> {
+  v16f t[WTM / 32][WTN / 32];
+};
+
+// G is the K segment the matrix cores contract before each promotion (64 or
+// 128). The scale blocks are sg x sg with sg = G << sshift: for g = 256 the
+// G = 128 kernel promotes every 128 K with its 256-block's factor. ROWA: A's
+// factors are per row, sa is [M][K/sg].
+// LAYOUT bit 1: A stored [K,M]; bit 0: B stored [K,N] (M resp. N a multiple
+// of 16; B transposed on the 256- and 128-wide tiles only). A transposed tile
+// is staged as its 128 K rows and read with the transposing LDS read
+// (frag_tr16 / frag_tr in gemm_common.h); the K order inside a fragment is
+// the NT order.
+template <int G, int BN, int WM, int GROUP_M, int FMT, int EPI, bool ROWA, int LAYOUT>
+__global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
+                                                      const float* __restrict__ sa, const float* __restrict__ sb,
+                                                      uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
+                                                      int tiles_n, int vec_store, int sshift,
+                                                      const float* __restrict__ bias, int relu) {
+  static_assert(G == 64 || G == 128, "granularity");
+  constexpr int WN = NW / WM;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int STAGE = A_BYTES + BN * BK;
+  constexpr int SEGS = BK / G;                    // K segments per step
+  constexpr int SCL = ROWA ? NW * 256 : 0;        // per-row factors of a step: [SEGS][BM] FP32, one piece per wave
+  constexpr int SLOT = STAGE + SCL;
+  constexpr int LDC = BN + 8;  // bf16 pitch of an epilogue pass
+  static_assert(WTM == 64 || WTM == 128, "a wave's rows lie in one 128-row scale block");
+  static_assert(WTN % 16 == 0 && WTN <= 128, "a wave's columns touch at most two 128-column scale blocks");
+  static_assert(G == 128 || WTN == 64, "g = 64: one 64-column scale block per wave");
+  static_assert(BN % 8 == 0 && BN / 8 <= 4 * NW, "B copies: at most four row groups per wave");
+  static_assert(128 * LDC * 2 <= 2 * STAGE, "an epilogue pass must fit in the ring");
+  static_assert(BM * SEGS <= NW * 64, "a step's row factors: one 64-entry piece per wave");
+  static_assert((LAYOUT & 1) == 0 || BN == 256 || BN == 128, "transposed B: 256- or 128-byte K rows");
+  static_assert(LAYOUT == 0 || !ROWA, "per-row A factors: NT only");
+  // Every wave's columns lie in one 128- (or 256-) column scale block when the
+  // tile width is a multiple of 128 and the wave width divides 128.
+  constexpr bool ONE_B = BN % 128 == 0 && 128 % WTN == 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOT];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int grp = wave >> 2;  // copy-issue group: one wave per SIMD in each
+
+  int ks, tmi, tni;
+  map_tile<GROUP_M>(tiles_m, tiles_n, ks, tmi, tni);
+  const int m0 = tmi * BM, n0 = tni * BN;
+
+  const uint32_t uK = (uint32_t)K;
+  const v4i ra = rsrc_words(a + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * uK);
+  const v4i rb = rsrc_words(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
+
+  const int nkb = K / G;  // K segments
+  const int sg = G << sshift, nks = K / sg;  // scale blocks
+  const int nsteps = (K + BK - 1) / BK;
+  const v4i rsa = ROWA ? rsrc_words(sa + (int64_t)m0 * nks, (uint32_t)min(BM, M - m0) * (uint32_t)nks * 4u) : (v4i){};
+
+  // Scale rows of this wave. Blocks past the edge clamp to the last block
+  // (their data is zero). g >= 128: one A block; the wave's columns may cross
+  // into a second B block after jsplit 16-column blocks. g = 64: A blocks of
+  // rows wr0 and wr0 + 64, one B block.
+  const int wr0 = m0 + wm * WTM, wc0 = n0 + wn * WTN;
+  const int lastm = (M - 1) / sg, lastn = (N - 1) / sg;
+  const float* const sa0 = sa + (int64_t)min(wr0 / sg, lastm) * nks;
+  const float* const sa1 = sa + (int64_t)min((wr0 + 64) / sg, lastm) * nks;
+  const int bn0 = wc0 / sg;
+  const float* const sb0 = sb + (int64_t)min(bn0, lastn) * nks;
+  const float* const sb1 = sb + (int64_t)min(bn0 + 1, lastn) * nks;
+  const int jsplit = ((bn0 + 1) * sg - wc0) / 16;  // g >= 128: column blocks in the first B block
+
+  Acc<G, WTM, WTN> acc;
+  if constexpr (G == 128) {
+#pragma unroll
+    for (int i = 0; i < WTM / 16; ++i)
+#pragma unroll
+      for (int j = 0; j < WTN / 16; ++j) acc.t[i][j] = (v4f){};
+  } else {
+#pragma unroll
+    for (int i = 0; i < WTM / 32; ++i)
+#pragma unroll
+      for (int j = 0; j < WTN / 32; ++j) acc.t[i][j] = (v16f){};
+  }
+
+  // This wave's share of a step's copies: A row groups 8i + wave (i < 4) and
+  // B row groups 8i + wave below BN / 8, into the slot of step t.
+  auto issue_step = [&](int t) {
+    uint8_t* slot = smem + (t & 1) * SLOT;
+    if (ROWA && wave * 64 < BM * SEGS)  // pieces past the factors would only write padding
+      stage_row_scales<BM, SEGS>(rsa, slot + STAGE, (uint32_t)nks, (uint32_t)((t * SEGS) >> sshift), wave, lane);
+    const int64_t k0 = (int64_t)t * BK;
+    if constexpr ((LAYOUT & 2) != 0) {
+      // the step's K rows of A^T from column m0; past the tensor reads zero
+      const v4i rat = rsrc_words(a + k0 * M + m0, (uint32_t)(min((int64_t)BK, (int64_t)K - k0) * M - m0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stage_group_t<BM>(rat, slot, (uint32_t)M, i * NW + wave, lane);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stage_group<1>(ra, slot, uK, (uint32_t)t * BK, i * NW + wave, lane);
+    }
+    if constexpr ((LAYOUT & 1) != 0) {
+      const v4i rbt = rsrc_words(b + k0 * N + n0, (uint32_t)(min((int64_t)BK, (int64_t)K - k0) * N - n0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i * NW + wave < BN / 8) stage_group_t<BN>(rbt, slot + A_BYTES, (uint32_t)N, i * NW + wave, lane);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i * NW + wave < BN / 8) stage_group<1>(rb, slot + A_BYTES, uK, (uint32_t)t * BK, i * NW + wave, lane);
+    }
+  };
+
+  // The epilogue's bias for this lane's columns, loaded before the first
+  // copies: the step waits cover it, and no output store is in flight when
+  // the epilogue reads it. The plain form (EPI 0) loads and holds nothing.
+  constexpr int NBJ = G == 128 ? WTN / 16 : WTN / 32;
+  const bool hb = EPI != 0 && bias != nullptr;
+  float bj[NBJ];
+#pragma unroll
+  for (int j = 0; j < NBJ; ++j) {
+    const int col = wc0 + (G == 128 ? j * 16 + (lane & 15) : j * 32 + (lane & 31));
+    bj[j] = hb && col < N ? bias[col] : 0.0f;
+  }
+
+  issue_step(0);
+
+  for (int s = 0; s < nsteps; ++s) {
+    DG_WAIT_VMCNT(0);  // this wave's part of step s has landed
+    __syncthreads();   // all of step s visible; the other slot is free
+    auto issue_next = [&](int who) {
+      if (s + 1 < nsteps && grp == who) issue_step(s + 1);
+    };
+    const uint8_t* As = smem + (s & 1) * SLOT + wm * WTM * BK;
+    const uint8_t* Bs = smem + (s & 1) * SLOT + A_BYTES + wn * WTN * BK;
+    const uint8_t* At = smem + (s & 1) * SLOT;            // transposed tiles: K rows of the whole tile
+    const uint8_t* Bt = smem + (s & 1) * SLOT + A_BYTES;
+    // this lane's 16x16x128 fragment of A row block i / B column block j
+    auto fa16 = [&](int i, int r16, int q) {
+      if constexpr ((LAYOUT & 2) != 0) return frag_tr16<BM>(At, wm * WTM + i * 16, 0, lane);
+      else return frag(As, i * 16 + r16, 2 * q);
+    };
+    auto fb16 = [&](int j, int r16, int q) {
+      if constexpr ((LAYOUT & 1) != 0) return frag_tr16<BN>(Bt, wn * WTN + j * 16, 0, lane);
+      else return frag(Bs, j * 16 + r16, 2 * q);
+    };
+    // ... and 32x32x64 fragment of the 64-byte K chunk h
+    auto fa32 = [&](int i, int r32, int h, int h2) {
+      if constexpr ((LAYOUT & 2) != 0) return frag_tr<BM>(At, wm * WTM + i * 32, 64 * h, lane);
+      else return frag(As, i * 32 + r32, 4 * h + 2 * h2);
+    };
+    auto fb32 = [&](int j, int r32, int h, int h2) {
+      if constexpr ((LAYOUT & 1) != 0) return frag_tr<BN>(Bt, wn * WTN + j * 32, 64 * h, lane);
+      else return frag(Bs, j * 32 + r32, 4 * h + 2 * h2);
+    };
+    const float* scl = reinterpret_cast<const float*>(smem + (s & 1) * SLOT + STAGE);  // [SEGS][BM] (ROWA)
+
+    if constexpr (G == 128) {
+      // Slots t = (row block i, column block j). Slot t issues MFMA t and the
+      // promotion of slot t - LAG, whose result has had LAG MFMAs' time to
+      // land. Left alone, the scheduler puts each FMA right behind its own
+      // MFMA and waits out the MFMA latency.
+      constexpr int LAG = 3;
+      constexpr int NJ = WTN / 16, SLOTS = (WTM / 16) * NJ, DSLOT = SLOTS / 4;
+      const int r16 = lane & 15, q = lane >> 4;
+      const int ksc = s >> sshift;
+      const float a_s = ROWA ? 0.0f : sa0[ksc];
+      const float sbv0 = sb0[ksc], sbv1 = sb1[ksc];
+      const float sc0 = a_s * sbv0, sc1 = a_s * sbv1;
+      // ROWA: factors of rows 16i + 4q .. +3 of the wave tile, read one row block ahead
+      const float* const srow = scl + wm * WTM + 4 * q;
+      v4f sr[WTM / 16], fr;
+      if constexpr (ROWA) sr[0] = *reinterpret_cast<const v4f*>(srow);
+      v8i bf[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bf[j] = fb16(j, r16, q);
+      v8i a_cur = fa16(0, r16, q), a_nxt = a_cur;
+      v4f pr[LAG + 1];
+#pragma unroll
+      for (int t = 0; t < SLOTS + LAG; ++t) {
+        const int i = t / NJ, j = t % NJ;
+        if (t == 0) issue_next(0);
+        if (t == DSLOT) issue_next(1);
+        if (t < SLOTS) {
+          if (j == 0 && i + 1 < WTM / 16) {
+            a_nxt = fa16(i + 1, r16, q);
+            if constexpr (ROWA) sr[i + 1] = *reinterpret_cast<const v4f*>(srow + (i + 1) * 16);
+          }
+          pr[t % (LAG + 1)] = mfma16<FMT>(a_cur, bf[j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (t >= LAG) {
+          const int u = t - LAG, ui = u / NJ, uj = u % NJ;
+          if constexpr (ROWA) {
+            // the row block's products, shared by its column blocks; formed
+            // again where the wave's columns enter the second B block
+            // (jsplit >= 1 is wave-uniform)
+            if (uj == 0) fr = sr[ui] * sbv0;
+            if constexpr (!ONE_B) {
+              if (uj == jsplit) fr = sr[ui] * sbv1;
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], fr[v], acc.t[ui][uj][v]);
+          } else {
+            const float sc = uj < jsplit ? sc0 : sc1;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], sc, acc.t[ui][uj][v]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (t < SLOTS && j == NJ - 1) a_cur = a_nxt;
+      }
+    } else {
+      // The same schedule over the 32 x 32 blocks of each segment; waves 4-7
+      // issue their copies at the second segment. With per-row factors on the
+      // 256-wide tile (16 more registers per row block in flight) the
+      // promotion runs one MFMA behind instead of two, which keeps the kernel
+      // inside 256 registers.
+      constexpr int LAG = ROWA && BN == 256 ? 1 : 2;
+      constexpr int NJ = WTN / 32, SLOTS = (WTM / 32) * NJ;
+      const int r32 = lane & 31, h2 = lane >> 5;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kb = 2 * s + h;
+        issue_next(h);
+        if (kb < nkb) {  // K % 128 == 64: the last step holds one segment
+          const float sbv = sb0[kb];
+          const float f0 = ROWA ? 0.0f : sa0[kb] * sbv, f1 = ROWA ? 0.0f : sa1[kb] * sbv;
+          // ROWA: factors of rows 32i + 8(v/4) + 4*h2 + v%4, read with the row
+          // block's first MFMA
+          const float* const srow = scl + h * BM + wm * WTM + 4 * h2;
+          v4f sr[WTM / 32][4];
+          float fr[16];
+          v8i bf[NJ];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) bf[j] = fb32(j, r32, h, h2);
+          v8i a_cur = fa32(0, r32, h, h2), a_nxt = a_cur;
+          v16f pr[LAG + 1];
+#pragma unroll
+          for (int t = 0; t < SLOTS + LAG; ++t) {
+            const int i = t / NJ, j = t % NJ;
+            if (t < SLOTS) {
+              if (j == 0 && i + 1 < WTM / 32) a_nxt = fa32(i + 1, r32, h, h2);
+              if (ROWA && j == 0) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) sr[i][c] = *reinterpret_cast<const v4f*>(srow + i * 32 + 8 * c);
+              }
+              pr[t % (LAG + 1)] = mfma32<FMT>(a_cur, bf[j]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (t >= LAG) {
+              const int u = t - LAG, ui = u / NJ, uj = u % NJ;
+              if constexpr (ROWA) {
+                if (uj == 0) {  // the row block's products, shared by its column blocks (one B block per wave)
+#pragma unroll
+                  for (int v = 0; v < 16; ++v) fr[v] = sr[ui][v >> 2][v & 3] * sbv;
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                  acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], fr[v], acc.t[ui][uj][v]);
+              } else {
+                const float f = ui < 2 ? f0 : f1;  // rows 64.. of a 128-row wave tile use the next A block
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                  acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], f, acc.t[ui][uj][v]);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (t < SLOTS && j == NJ - 1) a_cur = a_nxt;
+          }
+        }
+      }
+    }
+  }
+  DG_WAIT_VMCNT(0);
+  // Bias and activation in place, by all eight waves at once (the passes
+  // below keep half of them idle).
+  if constexpr (EPI != 0) {
+    if constexpr (G == 128) {
+#pragma unroll
+      for (int j = 0; j < WTN / 16; ++j)
+#pragma unroll
+        for (int i = 0; i < WTM / 16; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc.t[i][j][v] = epilogue_fn<EPI>(acc.t[i][j][v], hb, bj[j], relu);
+    } else {
+#pragma unroll
+      for (int j = 0; j < WTN / 32; ++j)
+#pragma unroll
+        for (int i = 0; i < WTM / 32; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc.t[i][j][v] = epilogue_fn<EPI>(acc.t[i][j][v], hb, bj[j], relu);
+    }
+  }
+
+  // Epilogue, two passes of 128 rows: the waves whose rows lie in the pass
+  // write their BF16 sub-tiles to LDS, then all threads store the pass.
+  uint16_t* cs = reinterpret_cast<uint16_t*>(smem);
+  const int prow = wm * WTM % 128;  // first row of this wave inside its pass
+
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+    if (wm * WTM / 128 == pass) {
+      if constexpr (G == 128) {
+        const int r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < WTN / 16; ++j)
+#pragma unroll
+          for (int i = 0; i < WTM / 16; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              cs[(prow + i * 16 + 4 * q + v) * LDC + wn * WTN + j * 16 + r16] =
+                  bf16_bits(acc.t[i][j][v]);
+      } else {
+        const int r32 = lane & 31, h2 = lane >> 5;
+#pragma unroll
+        for (int j = 0; j < WTN / 32; ++j)
+#pragma unroll
+          for (int i = 0; i < WTM / 32; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              cs[(prow + i * 32 + 8 * (v >> 2) + 4 * h2 + (v & 3)) * LDC + wn * WTN + j * 32 + r32] =
+                  bf16_bits(acc.t[i][j][v]);
+      }
+    }
+    __syncthreads();
+    constexpr int CHUNKS = 128 * BN / 8;
+    static_assert(CHUNKS % NT == 0, "epilogue chunks split evenly over the threads");
+#pragma unroll
+    for (int it = 0; it < CHUNKS / NT; ++it) {
+      const int idx = it * NT + threadIdx.x;
+      const int r = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
+      const int gr = m0 + pass * 128 + r, gc = n0 + c;
+      if (gr >= M || gc >= N) continue;
+      const v4i val = *reinterpret_cast<const v4i*>(cs + r * LDC + c);
+      uint16_t* dst = out + (int64_t)gr * N + gc;
+      if (vec_store && gc + 8 <= N) {
+        *reinterpret_cast<v4i*>(dst) = val;
+      } else {
+        for (int t = 0; t < 8 && gc + t < N; ++t) dst[t] = (uint16_t)((uint32_t)val[t >> 1] >> (16 * (t & 1)));
+      }
+    }
+  }
+}
+
+template <int G, int BN, int WM, int FMT, int EPI, bool ROWA, int LAYOUT>
+hipError_t launch_fa(const GemmArgs& p, hipStream_t stream) {
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_fp8_nt_big<G, BN, WM, 4, FMT, EPI, ROWA, LAYOUT>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, p.a,
+                     p.b, p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.sshift,
+                     p.bias, p.act == 1 ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Per-row A factors are compiled for the NT layout only.
+template <int G, int BN, int WM, int FMT, int EPI, int LAYOUT>
+hipError_t launch_sa(const GemmArgs& p, hipStream_t stream) {
+  if constexpr (LAYOUT != 0) {
+    return p.rowa ? hipErrorInvalidValue : launch_fa<G, BN, WM, FMT, EPI, false, LAYOUT>(p, stream);
+  } else {
+    return p.rowa ? launch_fa<G, BN, WM, FMT, EPI, true, 0>(p, stream)
+                  : launch_fa<G, BN, WM, FMT, EPI, false, 0>(p, stream);
+  }
+}
+
+template <int G, int BN, int WM, int FMT, int LAYOUT>
+hipError_t launch_fmt(const GemmArgs& p, hipStream_t stream) {
+  switch (epilogue_form(p.bias, p.act)) {
+    case 0: return launch_sa<G, BN, WM, FMT, 0, LAYOUT>(p, stream);
+    case 1: return launch_sa<G, BN, WM, FMT, 1, LAYOUT>(p, stream);
+    case 2: return launch_sa<G, BN, WM, FMT, 2, LAYOUT>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int G, int BN, int WM, int LAYOUT>
+hipError_t launch_l(const GemmArgs& p, hipStream_t stream) {
+  if (p.ksplit != 1 || p.sshift < 0 || p.sshift > 1) return hipErrorInvalidValue;
+  switch (p.fmt) {
+    case 0: return launch_fmt<G, BN, WM, 0, LAYOUT>(p, stream);
+    case 1: return launch_fmt<G, BN, WM, 1, LAYOUT>(p, stream);
+    case 2: return launch_fmt<G, BN, WM, 2, LAYOUT>(p, stream);
+    case 3: return launch_fmt<G, BN, WM, 3, LAYOUT>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The NT table entries.
+template <int G, int BN, int WM>
+hipError_t launch(const GemmArgs& p, hipStream_t stream) {
+  return p.layout == 0 ? launch_l<G, BN, WM, 0>(p, stream) : hipErrorInvalidValue;
+}
+
+// The transposed layouts on the same tile (instantiated in gemm_fp8_big_layouts.hip).
+template <int G, int BN, int WM>
+hipError_t launch_layout(const GemmArgs& p, hipStream_t stream) {
+  switch (p.layout) {
+    case 1: return launch_l<G, BN, WM, 1>(p, stream);
+    case 2: return launch_l<G, BN, WM, 2>(p, stream);
+    case 3: return launch_l<G, BN, WM, 3>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace big
+
+}  // namespace dg

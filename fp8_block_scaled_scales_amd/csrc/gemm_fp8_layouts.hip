@@ -18,7 +18,7 @@ hipError_t launch_layout(int id, const GemmArgs& p, hipStream_t stream) {
     case 1: return launch_tiled_layout<128, 128, 2, 2, 2, 64, 4, false>(p, stream);
     case 2: return launch_tiled_layout<64, 64, 2, 2, 8, 128, 4, true>(p, stream);
     case 3: return launch_tiled_layout<64, 64, 2, 2, 8, 64, 4, true>(p, stream);
-    default: return hipErrorInvalidValue;
+    default: return launch_big_layout(id, p, stream);
   }
 }
 

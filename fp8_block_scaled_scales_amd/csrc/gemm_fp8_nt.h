@@ -53,9 +53,11 @@ hipError_t launch_big224_g128(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_big128_g128(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_big128_g64(const GemmArgs& p, hipStream_t stream);
 
-// The transposed layouts (GemmArgs::layout != 0) of tiled / split-K table
-// entry `id` (0-3).
+// The transposed layouts (GemmArgs::layout != 0) of table entry `id`: the
+// tiled and split-K entries (0-3) and the 256- and 128-wide 256-row entries
+// (4, 5, 9, 10).
 hipError_t launch_layout(int id, const GemmArgs& p, hipStream_t stream);
+hipError_t launch_big_layout(int id, const GemmArgs& p, hipStream_t stream);
 
 extern KernelEntry kTable[];
 extern const int kTableSize;

@@ -22,58 +22,6 @@ __device__ __forceinline__ v8i frag32(const uint8_t* slab, int row, int c0) {
   return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-// Transposed operands (DeepGEMM实战 §3.3: A stored [K,M] or B stored [K,N]).
-// A step's tile of such an operand is staged as its 128 K rows of W bytes
-// (the tile's M or N extent, 64 or 128), 16-byte chunks XOR-swizzled by row,
-// and read into the MFMA fragment with the transposing LDS read.
-//
-// Swizzle key of row r: the eight consecutive rows one transposing read
-// touches at one logical chunk land on distinct banks (128-byte rows: all
-// eight chunks differ; 64-byte rows: rows four apart, which share a bank
-// offset, get different chunks).
-template <int W>
-__device__ __forceinline__ int tkey(int row) {
-  return W == 128 ? (row & 7) : ((row >> 2) & 3);
-}
-
-// One instruction of a transposed tile's copy: rows RPI*grp .. RPI*grp+RPI-1
-// (RPI = 1024/W) of the step's K rows, all W bytes, into LDS at
-// lds + 1024*grp. Lane L writes physical chunk L % (W/16) of its row, so it
-// fetches the logical chunk that belongs there. rsrc's base is the step's first
-// K row at the tile's first column; pitch is the stored row length (M or N).
-template <int W>
-__device__ __forceinline__ void stage_group_t(v4i rsrc, uint8_t* lds, uint32_t pitch, int grp, int lane) {
-  constexpr int CPR = W / 16, RPI = 64 / CPR;
-  const int r_in = lane / CPR, p = lane % CPR;
-  const uint32_t c = (uint32_t)(p ^ tkey<W>(grp * RPI + r_in));
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
-  lds_dma16(rsrc, __builtin_amdgcn_readfirstlane(lds_base + grp * 1024), (uint32_t)r_in * pitch + c * 16,
-            __builtin_amdgcn_readfirstlane((uint32_t)grp * RPI * pitch));
-}
-
-// The 32 K bytes of this lane's 32x32x64 fragment from a transposed tile:
-// lane l needs column col0 + l%32 (its row of A, or of B) at K bytes
-// kofs + 32*(l/32) .. +31. ds_read_b64_tr_b8 works on 16-lane groups: lane
-// 16G + 8h + j receives byte j of the eight 8-byte rows addressed by lanes
-// 16G + h, 16G + 2 + h, ..., 16G + 14 + h, in that order (measured on gfx950
-// with an address-coded LDS pattern). So lane x addresses row
-// kofs + 32*(x/32) + 8q + (x%16)/2 at column col0 + 16*((x/16)%2) + 8*(x%2),
-// and read q = 0..3 brings K bytes 8q .. 8q+7 of the lane's own column.
-template <int W>
-__device__ __forceinline__ v8i frag_tr(const uint8_t* slab, int col0, int kofs, int lane) {
-  typedef __attribute__((address_space(3))) v2i lds_v2i;
-  const int col = col0 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-  const int row0 = kofs + 32 * (lane >> 5) + ((lane & 15) >> 1);
-  v2i r[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = row0 + 8 * q;
-    const int off = row * W + (((col >> 4) ^ tkey<W>(row)) << 4) + (col & 15);
-    r[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(lds_void_t*)(const_cast<uint8_t*>(slab) + off));
-  }
-  return (v8i){r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
-}
-
 // FMT bit 0: A is E5M2 (else E4M3), bit 1: B is E5M2 -- the instruction's
 // operand-format fields (0 = E4M3, 1 = E5M2); no block-exponent scaling.
 template <int FMT>

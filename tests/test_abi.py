@@ -130,11 +130,13 @@ def test_layout_rejects(dg, layout, M, N, want):
     assert dg.lib.dg_query_tile_layout(M, N, 256, 128, layout, ctypes.byref(info)) == getattr(dg, want)
 
 
-@pytest.mark.parametrize("M,N,K,g,layout,cls_bm", [(64, 4096, 7168, 128, 1, 64), (4096, 7168, 2048, 128, 3, 128),
-                                                   (1008, 3008, 512, 64, 2, 128), (128, 512, 1024, 256, 3, 64)])
-def test_layout_tile_choice(dg, M, N, K, g, layout, cls_bm):
+@pytest.mark.parametrize("M,N,K,g,layout,tile", [(64, 4096, 7168, 128, 1, (64, 64)), (4096, 7168, 2048, 128, 3, (256, 256)),
+                                                 (1008, 3008, 512, 64, 2, (128, 128)), (128, 512, 1024, 256, 3, (64, 64)),
+                                                 (2000, 4000, 1024, 128, 1, (256, 128)), (3584, 3584, 512, 256, 2, (256, 256))])
+def test_layout_tile_choice(dg, M, N, K, g, layout, tile):
+    # transposed layouts: split-K 64x64 for M <= 128, else the 256-row tiles 256 or 128 wide (never 224) or 128x128
     t = dg.dg_query_tile(M, N, K, g, layout)
-    assert t["bm"] == cls_bm and t["bn"] == cls_bm  # transposed layouts run the 64x64 split-K or 128x128 tiles
+    assert (t["bm"], t["bn"]) == tile
     assert dg.dg_query_tile(M, N, K, g, 0) == dg.dg_query_tile(M, N, K, g)
 
 

@@ -2,9 +2,10 @@
 CPU oracle.
 
 DeepGEMM实战 §3.3: A and B may each be stored transposed ([K,M], [K,N]) and are
-read that way. Every layout runs on shapes of both classes the transposed
-layouts use (split-K 64x64 for M <= 128, 128x128 otherwise), with ragged M
-and N (multiples of 16), K % 128 == 64 at g = 64, and g = 256. Bars: the
+read that way. Every layout runs on shapes of every class the transposed
+layouts use (split-K 64x64 for M <= 128; the 256-row tiles 256 and 128
+wide, with 16x16x128 and 32x32x64 fragments; 128x128), with ragged M and N
+(multiples of 16), K % 128 == 64 at g = 64, and g = 256. Bars: the
 elementwise tolerance against the oracle's layout reference; bit for bit
 across NN, TT and TN (one kernel family, the same K order), for all-ones
 closed forms, and for NT through the layout call against the NT call.
@@ -31,6 +32,11 @@ SHAPES = [
     (1008, 3008, 512, 128, (128, 128)),  # tiled
     (1024, 2000, 576, 64, (128, 128)),
     (512, 1040, 768, 256, (128, 128)),
+    (4000, 4000, 768, 128, (256, 256)),  # 256-row tiles: 16x16x128 fragments
+    (4000, 4000, 704, 64, (256, 256)),   # 32x32x64 fragments, K % 128 == 64
+    (3584, 3584, 512, 256, (256, 256)),
+    (2000, 4000, 1024, 128, (256, 128)),
+    (2000, 4000, 704, 64, (256, 128)),
 ]
 
 
@@ -97,7 +103,7 @@ def test_layout_parity(M, N, K, g, tile, layout):
 
 @pytest.mark.parametrize("layout,fa,fb,act,with_bias", [(NN, 1, 0, 0, False), (TN, 0, 1, 2, True),
                                                         (TT, 1, 1, 1, True)])
-@pytest.mark.parametrize("M,N,K,g,tile", [SHAPES[1], SHAPES[3]])
+@pytest.mark.parametrize("M,N,K,g,tile", [SHAPES[1], SHAPES[3], SHAPES[7], SHAPES[9]])
 def test_layout_with_formats_and_epilogue(M, N, K, g, tile, layout, fa, fb, act, with_bias):
     a8, sa, b8, sb = _operands(M, N, K, g, fa, fb, seed=12000 + M + 10 * layout)
     bias = synth.normal(12100 + N, (N,), sigma=0.5).astype(np.float32) if with_bias else None
@@ -122,7 +128,8 @@ def test_transposed_layouts_agree_bitwise(M, N, K, g, tile):
 
 
 @pytest.mark.parametrize("layout", TRANSPOSED)
-@pytest.mark.parametrize("M,N,K,g,tile", [SHAPES[0], SHAPES[1], SHAPES[3], SHAPES[5]])
+@pytest.mark.parametrize("M,N,K,g,tile", [SHAPES[0], SHAPES[1], SHAPES[3], SHAPES[5], SHAPES[6], SHAPES[7],
+                                         SHAPES[10]])
 def test_layout_closed_form_all_ones_bitwise(M, N, K, g, tile, layout):
     a8 = np.full((M, K), 0x38, np.uint8)
     b8 = np.full((N, K), 0x38, np.uint8)
@@ -141,7 +148,11 @@ def test_layout_closed_form_all_ones_bitwise(M, N, K, g, tile, layout):
 def test_layout_permutation_closed_form_bitwise():
     # A[i,k] = 1 where k = p(i): out[i,j] = sa*sb*B[j, p(i)], one element each,
     # which any transposed index or misplaced transposing read gets wrong
-    M, N, K, g = 1008, 528, 1024, 128
+    for M, N, K, g in [(1008, 528, 1024, 128), (4000, 4000, 768, 128), (2000, 4000, 704, 64)]:
+        _permutation_case(M, N, K, g)
+
+
+def _permutation_case(M, N, K, g):
     rng = np.random.default_rng(14000)
     p = rng.integers(0, K, size=M)
     a8 = np.zeros((M, K), np.uint8)
@@ -153,8 +164,9 @@ def test_layout_permutation_closed_form_bitwise():
         a_st, b_st = _store(a8, b8, layout)
         say("layout %d permutation closed form" % layout)
         _, bits = _run(a_st, b_st, sa, sb, g, layout)
-        ref = oracle.gemm_ref_layout(a_st, b_st, sa, sb, g, layout, M, N, K)
-        assert np.array_equal(bits, _common.f32_to_bf16_bits(ref.astype(np.float32))), layout
+        rows = np.unique(np.concatenate([np.arange(0, M, 13), np.arange(255, M, 256), [M - 1]]))
+        ref = oracle.gemm_ref_layout(a_st, b_st, sa, sb, g, layout, M, N, K, rows=rows)
+        assert np.array_equal(bits[rows], _common.f32_to_bf16_bits(ref.astype(np.float32))), layout
 
 
 def test_nt_through_the_layout_call_is_the_nt_call_bitwise():
