@@ -51,6 +51,7 @@ from __future__ import annotations
 import argparse
 import json
 import math
+import statistics
 import os
 import sys
 import time
@@ -214,14 +215,35 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
+    # The timed region is the K steps between start and end; events between
+    # the replays split it into up to five trials of whole replays, for the
+    # spread of the per-call time (the value is the whole region's).
+    reps = steps // L
+    cuts = sorted({round(i * reps / 5) for i in range(6)})
+    marks = [torch.cuda.Event(enable_timing=True) for _ in cuts[1:-1]]
     start.record(stream)
-    for _ in range(steps // L):
+    for r in range(reps):
+        if r in cuts[1:-1]:
+            marks[cuts.index(r) - 1].record(stream)
         graph.replay()
     end.record(stream)
     torch.cuda.synchronize(dev)
     ms = start.elapsed_time(end) / steps
+    bounds = [start] + marks + [end]
+    trials = [bounds[i].elapsed_time(bounds[i + 1]) / ((cuts[i + 1] - cuts[i]) * L) for i in range(len(bounds) - 1)]
     finite = bool(torch.isfinite(bufs[(steps - 1) % sets][4].float()).all().item())
-    return ms, sets, finite, L
+    return ms, sets, finite, L, trials
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, bias: bool = False, act: int = 0, budget_s: float = 10.0,
@@ -280,7 +302,7 @@ def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, bias: bool = False, act: i
         done = 2.0 * M * N * K * reps
         sample = "the whole %dx%d output, %d times, K=%d" % (M, N, reps, K)
     return {"value": done / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": sample + " (FP64, %.1f s)" % dt}
+            "sample": sample + " (FP64, %.1f s, %s)" % (dt, _cpu_model())}
 
 
 def main():
@@ -338,7 +360,7 @@ def main():
     layout = LAYOUTS[args.layout]
     if layout and args.sa_rows == 1:
         raise SystemExit("--sa-rows 1 runs the NT layout only")
-    ms, sets, finite, glen = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb, args.bias, act, args.sa_rows,
+    ms, sets, finite, glen, trials = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb, args.bias, act, args.sa_rows,
                                      layout)
     if not finite:
         raise SystemExit("GEMM output holds non-finite values")
@@ -349,7 +371,8 @@ def main():
         achieved, peak, unit = tflops, PEAK_FP8_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
-    default_variant = (fa, fb, g, args.bias, act, args.sa_rows, layout) == (0, 0, w["g"], False, 0, None, 0)
+    default_variant = (fa, fb, g, args.bias, act, args.sa_rows, layout, args.sets) == \
+        (0, 0, w["g"], False, 0, None, 0, None)
     tr = TRAFFIC.get(w["name"]) if default_variant else None
     traffic = tr["bytes"] if tr and tr["src"] == _kernel_source_hash() else None
 
@@ -373,6 +396,8 @@ def main():
                    "a_scales": "1x%d" % g if args.sa_rows == 1 else "%dx%d" % (g, g),
                    "layout": args.layout.upper(), "out": "bf16", "input_sets": sets,
                    "launch": "hipGraph of %d launches, replayed %d times" % (glen, args.steps // glen),
+                   "trials_us": {"n": len(trials), "median": round(statistics.median(trials) * 1e3, 3),
+                                 "min": round(min(trials) * 1e3, 3), "max": round(max(trials) * 1e3, 3)},
                    "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
                    "alg_GBps": round(nbytes / sec / 1e9, 1)},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
