@@ -32,6 +32,7 @@ DG_FMT_E5M2 = 1
 DG_ACT_NONE = 0
 DG_ACT_RELU = 1
 DG_ACT_GELU = 2
+DG_MAX_DIM = (1 << 24) - 256  # largest M, N or K (and quantiser rows, cols) the library accepts
 
 
 class dg_tile_info(ctypes.Structure):

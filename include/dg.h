@@ -44,8 +44,11 @@ extern "C" {
 
 #define DG_VERSION 100 /* 1.0.0 */
 
-/* Largest accepted dimension; keeps every in-tile byte offset in 32 bits. */
-#define DG_MAX_DIM (1LL << 24)
+/* Largest accepted dimension, 2^24 - 256: a 256-row tile of K bytes per row
+ * (256 * K) then stays below 2^32 bytes, the reach of a buffer descriptor,
+ * so every in-tile byte offset fits 32 bits; a multiple of 256, so it is a
+ * valid K for every g. */
+#define DG_MAX_DIM ((1LL << 24) - 256)
 
 /*
  * dg_gemm_fp8_nt - C[M,N] = A[M,K] * B[N,K]^T with g x g block scales.

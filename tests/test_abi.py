@@ -43,6 +43,21 @@ def test_status_codes_match_header(dg):
         m = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
         assert m and int(m.group(1)) == getattr(dg, name), name
     assert dg.dg_version() == int(re.search(r"#define DG_VERSION (\d+)", text).group(1))
+    m = re.search(r"#define DG_MAX_DIM \(\(1LL << (\d+)\) - (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) - int(m.group(2)) == dg.DG_MAX_DIM
+    # a 256-row tile of K bytes per row stays inside a 32-bit byte range, and the
+    # largest K is a multiple of every g
+    assert 256 * dg.DG_MAX_DIM < 1 << 32 and dg.DG_MAX_DIM % 256 == 0
+
+
+@pytest.mark.parametrize("g", [64, 128, 256])
+def test_max_dims_accepted(dg, g):
+    mx = dg.DG_MAX_DIM
+    for M, N, K in [(256, 256, mx), (2048, 3072, mx), (64, 4096, mx), (mx, 256, 256), (256, mx, 256)]:
+        for layout in range(4):
+            assert dg.dg_query_tile(M, N, K, g, layout)["grid"] > 0
+    with pytest.raises(ValueError):
+        dg.dg_query_tile(256, 256, mx + 256, g)
 
 
 # Fake but aligned, non-null device addresses: the checks below must fail
@@ -57,7 +72,8 @@ def _call(dg, a=A, b=B, sa=SA, sb=SB, out=OUT, M=256, N=256, K=256, g=128):
 @pytest.mark.parametrize("kw", [dict(a=0), dict(b=0), dict(sa=0), dict(sb=0), dict(out=0),
                                 dict(M=0), dict(N=0), dict(K=0), dict(M=-5), dict(K=-128),
                                 dict(K=192), dict(K=100, g=64), dict(g=96), dict(g=512), dict(K=384, g=256), dict(g=0),
-                                dict(M=(1 << 24) + 1), dict(K=1 << 25)])
+                                dict(M=(1 << 24) + 1), dict(K=1 << 25), dict(K=1 << 24),
+                                dict(N=(1 << 24) - 255)])
 def test_einval(dg, kw):
     assert _call(dg, **kw) == dg.DG_EINVAL
 
