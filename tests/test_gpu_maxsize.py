@@ -6,7 +6,9 @@ reaches, so these cases check that no tile's byte range or offset wraps:
 - K = DG_MAX_DIM on the 256x128 tiles (g = 128 and 64; NT, TN and TT), the
   32x32 streaming class and the split-K class (M = 64, N = 4096);
 - M = DG_MAX_DIM and N = DG_MAX_DIM (K = 256) on the 256x256 tiles, NT and a
-  transposed A stored [K, M].
+  transposed A stored [K, M];
+- the g x g and 1 x g quantisers with rows or cols = DG_MAX_DIM, sampled
+  blocks bitwise against the oracle's quantisers.
 
 The operands are random E4M3 codes drawn on the GPU by torch's seeded
 generator (87 GB in all; drawing them on the host would take minutes), with
@@ -142,3 +144,36 @@ def test_max_m_or_n(pool, big_m, layout):
     ok, rms = _common.within_tolerance(got, ref)
     assert ok.all(), (got[~ok][:4], ref[~ok][:4], rms)
     say("max %s layout=%d: max|err|/rms = %.3g" % ("M" if big_m else "N", layout, np.max(np.abs(got - ref)) / rms))
+
+
+@pytest.mark.parametrize("rows_max", [False, True])
+@pytest.mark.parametrize("per_row", [False, True])
+def test_max_quantizer(rows_max, per_row):
+    # block (g x g) and row (1 x g) quantisers at rows or cols = DG_MAX_DIM:
+    # sampled blocks bitwise against the oracle's quantiser on those blocks
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    g = 64
+    rows, cols = (MAX_DIM, 256) if rows_max else (64, MAX_DIM)
+    gen = torch.Generator(device="cuda:0").manual_seed(77 + rows_max + 2 * per_row)
+    x = torch.randn((rows, cols), generator=gen, device="cuda:0", dtype=torch.float32)
+    say("max quantiser: rows=%d cols=%d per_row=%d" % (rows, cols, per_row))
+    q, s = (dg.dg_quantize_fp8_rows if per_row else dg.dg_quantize_fp8_blocks)(x, gran=g)
+    torch.cuda.synchronize()
+    nrb, ncb = rows // g, cols // g
+    blocks = [(0, 0), (nrb - 1, ncb - 1), (nrb // 2, ncb // 3), (nrb - 1, 0), (0, ncb - 1)]
+    for rb, cb in blocks:
+        xb = x[rb * g:(rb + 1) * g, cb * g:(cb + 1) * g].cpu().numpy()
+        qb = q[rb * g:(rb + 1) * g, cb * g:(cb + 1) * g].cpu().numpy()
+        if per_row:
+            want_q, want_s = oracle.quantize_rows_fmt(xb, g)
+            got_s = s[rb * g:(rb + 1) * g, cb].cpu().numpy()[:, None]
+        else:
+            want_q, want_s = oracle.quantize_blocks_fmt(xb, g, 0)
+            got_s = s[rb, cb].cpu().numpy().reshape(1, 1)
+        assert np.array_equal(qb, want_q), (rb, cb)
+        assert np.array_equal(got_s.view(np.uint32), np.asarray(want_s, np.float32).view(np.uint32)), (rb, cb)
+    del x, q, s
+    torch.cuda.empty_cache()
