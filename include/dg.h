@@ -17,14 +17,26 @@
  * for a given (M, N, K, g) and device.
  *
  * All pointers are device pointers (memory the caller allocated, e.g. PyTorch
- * tensors). The library keeps no pointer after a call returns and allocates
- * nothing per call. Calls are asynchronous on `stream` (a hipStream_t; NULL is
- * the default stream); faults during execution surface at the caller's next
- * synchronisation. No call prints unless the environment sets DG_LOG=1, and
- * no call exits or throws.
+ * tensors). The library keeps no caller pointer after a call returns and
+ * allocates nothing per call. Calls are asynchronous on `stream` (a
+ * hipStream_t; NULL is the default stream); faults during execution surface
+ * at the caller's next synchronisation. No call prints unless the environment
+ * sets DG_LOG=1, and no call exits or throws.
  *
- * Thread safety: calls may come from several host threads. The one-time
- * per-device check (architecture must be gfx950) runs under std::call_once.
+ * Split-K workspace: a GEMM whose tile-table entry splits K over several
+ * workgroups (dg_query_tile reports ksplit > 1: small M with few output
+ * tiles) adds its FP32 partial tiles through a workspace the library
+ * allocates once per device, on the first such call (32 MB of partial tiles
+ * and 64 Ki arrival counters, zeroed then; each call leaves its counters at
+ * zero), and keeps until the process ends. So the first such call on a
+ * device must not be made under stream capture (later ones may), and such
+ * calls must not run concurrently on one device (on two streams, or from two
+ * threads without ordering): they share the workspace. If the allocation
+ * fails the call runs the same tile over the whole K without a workspace.
+ *
+ * Thread safety: calls may come from several host threads (subject to the
+ * split-K rule above). The one-time per-device check (architecture must be
+ * gfx950) and the workspace allocation run under std::call_once.
  */
 #ifndef DG_H
 #define DG_H
@@ -174,7 +186,7 @@ typedef struct dg_tile_info {
   int bk;        /* K bytes staged per pipeline step */
   int stages;    /* LDS ring depth */
   int waves;     /* waves per workgroup */
-  int ksplit;    /* waves splitting K inside a workgroup (1 = none) */
+  int ksplit;    /* workgroups sharing one output tile, each over a K range (1 = none) */
   int64_t grid;  /* workgroups launched */
 } dg_tile_info;
 
