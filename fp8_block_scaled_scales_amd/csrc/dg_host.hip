@@ -200,6 +200,13 @@ int validate_layout(int64_t M, int64_t N, int layout) {
   return DG_OK;
 }
 
+// Whether the byte ranges [p, p + n) and [q, q + m) share a byte (empty
+// ranges share none).
+bool overlaps(const void* p, uint64_t n, const void* q, uint64_t m) {
+  const uintptr_t x = (uintptr_t)p, y = (uintptr_t)q;
+  return n && m && x < y + m && y < x + n;
+}
+
 int gemm(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M, int64_t N, int64_t K,
          int gran, int layout, int sa_rows, int fmt_a, int fmt_b, const float* bias, int act, void* stream) {
   if (!a || !b || !sa || !sb || !out) return DG_EINVAL;
@@ -215,6 +222,19 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)sa & 3) || ((uintptr_t)sb & 3) ||
       ((uintptr_t)out & 1))
     return DG_EALIGN;
+  {
+    // out is written while the inputs are read: it may overlap none of them
+    // (the inputs may overlap each other). Sizes are the logical ones, which
+    // every layout stores in the same number of bytes.
+    const uint64_t nks = (uint64_t)(K / gran);
+    const uint64_t sa_rows_n = sa_rows == 1 ? (uint64_t)M : (uint64_t)((M + gran - 1) / gran);
+    const uint64_t ob = 2ull * (uint64_t)M * (uint64_t)N;
+    if (overlaps(out, ob, a, (uint64_t)M * (uint64_t)K) || overlaps(out, ob, b, (uint64_t)N * (uint64_t)K) ||
+        overlaps(out, ob, sa, 4ull * sa_rows_n * nks) ||
+        overlaps(out, ob, sb, 4ull * (uint64_t)((N + gran - 1) / gran) * nks) ||
+        overlaps(out, ob, bias, bias ? 4ull * (uint64_t)N : 0))
+      return DG_EINVAL;
+  }
   Plan pl = plan(M, N, K, gran, layout);
   if (!pl.e || pl.tiles * pl.ksplit > 0x7fffffff) return DG_EINVAL;
 
@@ -269,6 +289,11 @@ int quantize(const float* x, int64_t rows, int64_t cols, int gran, int block_row
   if (block_rows != gran && block_rows != 1) return DG_EINVAL;
   if (((rows + block_rows - 1) / block_rows) * (cols / gran) > 0x7fffffff) return DG_EINVAL;
   if (((uintptr_t)x & 15) || ((uintptr_t)q & 3) || ((uintptr_t)scales & 3)) return DG_EALIGN;
+  {
+    const uint64_t xb = 4ull * (uint64_t)rows * (uint64_t)cols, qb = (uint64_t)rows * (uint64_t)cols;
+    const uint64_t sbytes = 4ull * (uint64_t)((rows + block_rows - 1) / block_rows) * (uint64_t)(cols / gran);
+    if (overlaps(x, xb, q, qb) || overlaps(x, xb, scales, sbytes) || overlaps(q, qb, scales, sbytes)) return DG_EINVAL;
+  }
   const int rc = device_ready();
   if (rc != DG_OK) return rc;
   dg::QuantArgs p;
@@ -299,7 +324,8 @@ const char* dg_strerror(int code) {
     case DG_EINVAL:
       return "invalid argument (null pointer, bad dimension, K not a multiple of gran, gran not 64/128/256, "
              "sa_rows neither gran nor 1, a format code other than DG_FMT_E4M3/DG_FMT_E5M2, an unknown "
-             "activation or layout, or a transposed operand whose stored row length is not a multiple of 16)";
+             "activation or layout, a transposed operand whose stored row length is not a multiple of 16, or an "
+             "output that overlaps an input)";
     case DG_EALIGN: return "misaligned pointer (a, b need 16 bytes; sa, sb 4 bytes; out 2 bytes)";
     case DG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
     case DG_ELAUNCH:

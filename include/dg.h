@@ -70,7 +70,8 @@ extern "C" {
  *   sa   FP32 scales of A, [ceil(M/g)][K/g] row-major. 4-byte aligned.
  *   sb   FP32 scales of B, [ceil(N/g)][K/g] row-major. 4-byte aligned.
  *   out  BF16 result, [M,N] row-major (ldc = N), fully overwritten. 2-byte
- *        aligned; must not overlap the inputs.
+ *        aligned; must not overlap a, b, sa or sb (DG_EINVAL if it does;
+ *        the inputs may overlap each other, e.g. a == b for A*A^T).
  *   M, N, K  > 0 and <= DG_MAX_DIM; K a multiple of gran.
  *   gran block granularity g: 64, 128 or 256 (the pages' 64x64, 128x128 and
  *        256x256 choices, DeepGEMM实战 §3.1). For 256 the kernels promote
@@ -213,7 +214,7 @@ int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, 
  *   q       E4M3FN codes out, [rows][cols] row-major, 4-byte aligned.
  *   scales  FP32 out, [ceil(rows/gran)][cols/gran] row-major, 4-byte aligned.
  *   rows, cols > 0 and <= DG_MAX_DIM; cols a multiple of gran; gran 64, 128
- *   or 256.
+ *   or 256. x, q and scales must not overlap one another (DG_EINVAL).
  *
  * Per gran x gran block (rows past the end make edge blocks partial):
  * amax = max |x| over present elements, scale = amax / 448 in FP32 (1.0 for

@@ -223,3 +223,22 @@ def test_python_binding_rejects_bad_tensors(dg):
 def test_query_tile_choice(dg, M, N, K, g, cls):
     t = dg.dg_query_tile(M, N, K, g)
     assert (t["bm"], t["bn"], t["ksplit"]) == cls, t
+
+
+# The output may overlap no input (the inputs may overlap each other): each
+# case is rejected before any HIP call.
+@pytest.mark.parametrize("kw", [dict(out=A + 0x1000), dict(out=B), dict(sa=OUT + 0x200), dict(sb=OUT + 0x1fff0),
+                                dict(out=SB - 0x100)])
+def test_output_overlapping_an_input(dg, kw):
+    assert _call(dg, **kw) == dg.DG_EINVAL
+
+
+def test_bias_overlapping_the_output(dg):
+    assert dg.lib.dg_gemm_fp8_nt_epi(A, B, SA, SB, OUT, 256, 256, 256, 128, 0, 0, OUT + 0x100, 1, None) == dg.DG_EINVAL
+
+
+@pytest.mark.parametrize("x,q,s", [(A, A + 0x100, SA), (A, B, B + 0x10), (A, B, A + 0xff00), (A, A, SA)])
+def test_quantize_overlaps(dg, x, q, s):
+    # x [64][256] FP32 is 64 KB from A, q 16 KB, the factors 2 x 2 (or 64 x 2 per row) FP32
+    assert dg.lib.dg_quantize_fp8_blocks(x, 64, 256, 128, 0, q, s, None) == dg.DG_EINVAL
+    assert dg.lib.dg_quantize_fp8_rows(x, 64, 256, 128, 0, q, s, None) == dg.DG_EINVAL
