@@ -104,8 +104,7 @@ int64_t splits_for(const dg::KernelEntry* e, int64_t tiles, int64_t nsteps) {
 }
 
 // Transposed layouts (layout != NT) take split-K 64x64 tiles for M <= 128, and
-// otherwise the 256-row tiles 256 or 128 wide (not 224) or 128x128 tiles by the
-// rule below.
+// otherwise the 256-row tiles or 128x128 tiles by the rule below.
 Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout = DG_LAYOUT_NT) {
   Plan p{nullptr, 1, 0};
   const int gran = kernel_gran(sgran);
@@ -148,10 +147,9 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout = DG_LAYOUT_NT)
   for (int i = 0; i < dg::kTableSize; ++i) {
     const dg::KernelEntry* e = &dg::kTable[i];
     if (e->cls != dg::kClassBig || e->gran != gran) continue;
-    if (layout != DG_LAYOUT_NT && e->bn == 224) continue;  // transposed tiles are 256 or 128 wide
     const int64_t t = ((M + e->bm - 1) / e->bm) * ((N + e->bn - 1) / e->bn);
     const double fill = (double)t / (double)(256 * ((t + 255) / 256));
-    const double per_cu = e->bn == 256 ? 1.0 : e->bn == 224 ? 0.97 : 0.8;
+    const double per_cu = e->bn == 256 ? 1.0 : 0.8;
     if (fill * per_cu > best) {
       best = fill * per_cu;
       big = e;

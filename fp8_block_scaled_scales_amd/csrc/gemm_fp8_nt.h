@@ -30,7 +30,7 @@ typedef hipError_t (*Launcher)(const GemmArgs&, hipStream_t);
 
 // Kernel classes of the tile table: 128x128 tiles over the whole K, small
 // tiles whose K range is split over several workgroups (small M), 256-row
-// tiles (256, 224 or 128 columns) over the whole K (large M and N), and 32x32
+// tiles (256 or 128 columns) over the whole K (large M and N), and 32x32
 // tiles over the whole K whose waves split K inside the workgroup (small M,
 // many tiles).
 enum TileClass { kClassTiled = 0, kClassSplitK = 1, kClassBig = 2, kClassStream = 3 };
@@ -49,7 +49,6 @@ hipError_t launch_stream_g128(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_stream_g64(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_big_g128(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_big_g64(const GemmArgs& p, hipStream_t stream);
-hipError_t launch_big224_g128(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_big128_g128(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_big128_g64(const GemmArgs& p, hipStream_t stream);
 

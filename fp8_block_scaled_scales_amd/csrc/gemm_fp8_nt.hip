@@ -53,7 +53,6 @@ KernelEntry kTable[] = {
     {5, kClassBig, 256, 256, 2, 8, 64, &launch_big_g64},
     {6, kClassStream, 32, 32, 4, 4, 128, &launch_stream_g128},
     {7, kClassStream, 32, 32, 4, 4, 64, &launch_stream_g64},
-    {8, kClassBig, 256, 224, 2, 8, 128, &launch_big224_g128},
     {9, kClassBig, 256, 128, 2, 8, 128, &launch_big128_g128},
     {10, kClassBig, 256, 128, 2, 8, 64, &launch_big128_g64},
 };

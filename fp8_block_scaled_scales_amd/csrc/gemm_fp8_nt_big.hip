@@ -1,5 +1,5 @@
 // Large-tile block-scaled FP8 GEMM for gfx950: 256 x BN output tiles,
-// BN = 256, 224 or 128.
+// BN = 256 or 128.
 //
 // Same operation as the other kernels (DeepGEMM实战 §2.2: one FP32 scale per
 // g x g block of each operand, restored while the products are accumulated,
@@ -12,9 +12,10 @@
 // least ~170 FLOPs per staged byte to keep the matrix cores fed: 2*BM*BN/(BM+BN)
 // is 128 for 128x128 and 256 for 256x256. A 256x256x128 step stages 64 KB and
 // does 16.8 MFLOP (2048 clocks at peak); two ring slots fill 128 KB of the
-// 160 KB LDS. The narrower tiles exist for tile counts: 256x224 splits a
-// 7168-wide N into 32 tiles, and 256x128 gives a 2000 x 4000 output 256 tiles,
-// one per CU, where 256x256 would leave half the chip idle.
+// 160 KB LDS. The narrower tile exists for tile counts: 256x128 gives a
+// 2000 x 4000 output 256 tiles, one per CU, where 256x256 would leave half the
+// chip idle. (A 256x224 tile, which splits a 7168-wide N into 32 tiles, was
+// measured slower per step than 256x256, so never worth its better fill.)
 //
 // Workgroup: 8 waves (two per SIMD), laid out WM x WN, each owning a
 // WTM x WTN sub-tile with its FP32 accumulator in registers. Per 128-byte K
@@ -63,7 +64,6 @@ namespace dg {
 
 hipError_t launch_big_g128(const GemmArgs& p, hipStream_t s) { return big::launch<128, 256, 2>(p, s); }
 hipError_t launch_big_g64(const GemmArgs& p, hipStream_t s) { return big::launch<64, 256, 2>(p, s); }
-hipError_t launch_big224_g128(const GemmArgs& p, hipStream_t s) { return big::launch<128, 224, 4>(p, s); }
 hipError_t launch_big128_g128(const GemmArgs& p, hipStream_t s) { return big::launch<128, 128, 4>(p, s); }
 hipError_t launch_big128_g64(const GemmArgs& p, hipStream_t s) { return big::launch<64, 128, 4>(p, s); }
 

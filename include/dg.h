@@ -182,7 +182,7 @@ int dg_gemm_fp8_layout(const void* a, const void* b, const float* sa, const floa
 
 /* The tile-table entry a call with these sizes would use. */
 typedef struct dg_tile_info {
-  int kernel_id; /* index in the precompiled table */
+  int kernel_id; /* identifier of the precompiled table entry */
   int bm, bn;    /* workgroup output tile */
   int bk;        /* K bytes staged per pipeline step */
   int stages;    /* LDS ring depth */

@@ -150,7 +150,7 @@ def test_layout_rejects(dg, layout, M, N, want):
                                                  (1008, 3008, 512, 64, 2, (128, 128)), (128, 512, 1024, 256, 3, (64, 64)),
                                                  (2000, 4000, 1024, 128, 1, (256, 128)), (3584, 3584, 512, 256, 2, (256, 256))])
 def test_layout_tile_choice(dg, M, N, K, g, layout, tile):
-    # transposed layouts: split-K 64x64 for M <= 128, else the 256-row tiles 256 or 128 wide (never 224) or 128x128
+    # transposed layouts: split-K 64x64 for M <= 128, else the 256-row tiles 256 or 128 wide or 128x128
     t = dg.dg_query_tile(M, N, K, g, layout)
     assert (t["bm"], t["bn"]) == tile
     assert dg.dg_query_tile(M, N, K, g, 0) == dg.dg_query_tile(M, N, K, g)
@@ -214,7 +214,7 @@ def test_python_binding_rejects_bad_tensors(dg):
     (256, 256, 256, 128, (128, 128, 1)),      # too few tiles for 256-row tiles
     (64, 4096, 7168, 128, (32, 32, 1)),       # small M, 256 streaming tiles
     (64, 512, 7168, 128, (64, 64, 14)),       # small M, few tiles: split-K
-    (4096, 7168, 2048, 128, (256, 224, 1)),   # 512 tiles of 256x224 vs 448 of 256x256
+    (4096, 7168, 2048, 128, (256, 256, 1)),   # 448 tiles of 256x256 (1.75 rounds) over 512 of 256x128
     (8192, 8192, 8192, 128, (256, 256, 1)),   # 1024 tiles of 256x256
     (2000, 4000, 16384, 64, (256, 128, 1)),   # 256 tiles of 256x128 vs 128 of 256x256
     (8192, 8192, 8192, 256, (256, 256, 1)),   # g = 256 runs the 128-segment kernels

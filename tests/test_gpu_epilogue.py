@@ -25,7 +25,7 @@ SHAPES = [
     (64, 520, 2048, 128, (64, 64)),      # split-K
     (1000, 3000, 512, 64, (128, 128)),   # tiled
     (4000, 4000, 768, 128, (256, 256)),  # 256-row tiles
-    (3583, 3585, 512, 128, (256, 224)),
+    (3583, 3585, 512, 128, (256, 256)),
     (2000, 4000, 1024, 64, (256, 128)),
 ]
 

@@ -59,7 +59,7 @@ SHAPES = [
     (100, 520, 1088, 64, (64, 64)),
     (1000, 3000, 512, 256, (128, 128)),  # tiled
     (4000, 4000, 768, 256, (256, 256)),  # 256-row tiles
-    (3583, 3585, 512, 256, (256, 224)),
+    (3583, 3585, 512, 256, (256, 256)),
     (2000, 4000, 1024, 256, (256, 128)),
     (3841, 4100, 704, 64, (256, 128)),
 ]

@@ -253,10 +253,10 @@ def test_splitk_determinism_and_interleaving():
 
 
 # Large M and N take the 256-row-tile class (kernel ids 4, 5: 256 columns;
-# 8: 224 columns; 9, 10: 128 columns), the width chosen by tile count.
-# Ragged edges at both granularities, K % 128 == 64 at g = 64 (a half step),
-# and 224-wide tiles whose waves straddle two 128-column scale blocks.
-BIG = [(3583, 3585, 512, 128, 224), (4096, 3328, 1024, 128, 224), (4000, 4000, 256, 128, 256),
+# 9, 10: 128 columns), the width chosen by tile count. Ragged edges at both
+# granularities (M and N one short of, or just past, a tile or scale block),
+# and K % 128 == 64 at g = 64 (a half step).
+BIG = [(3583, 3585, 512, 128, 256), (4096, 3328, 1024, 128, 256), (4000, 4000, 256, 128, 256),
        (2000, 4000, 1024, 128, 128), (3600, 4000, 320, 64, 256), (3841, 4100, 704, 64, 128),
        (2000, 4000, 1088, 64, 128)]
 
@@ -282,7 +282,7 @@ def test_big_tile_parity(M, N, K, g, bn):
     _assert_parity(got[np.ix_(rows, cols)], ref, "big %dx%dx%d g=%d bn=%d" % (M, N, K, g, bn))
 
 
-@pytest.mark.parametrize("M,N,K,g,bn", [(3600, 3500, 1024, 128, 224), (3600, 3500, 1024, 64, 256),
+@pytest.mark.parametrize("M,N,K,g,bn", [(3600, 3500, 1024, 128, 256), (3600, 3500, 1024, 64, 256),
                                         (4000, 4000, 512, 128, 256), (2000, 4000, 1024, 128, 128),
                                         (2000, 4000, 1024, 64, 128)])
 def test_big_tile_all_ones_bitwise(M, N, K, g, bn):

@@ -33,7 +33,7 @@ SHAPES = [
     (1000, 3000, 576, 64, (128, 128)),
     (4000, 4000, 768, 128, (256, 256)),  # 256-row tiles
     (4000, 4000, 704, 64, (256, 256)),
-    (3583, 3585, 512, 256, (256, 224)),
+    (3583, 3585, 512, 256, (256, 256)),
     (2000, 4000, 1024, 128, (256, 128)),
     (3841, 4100, 704, 64, (256, 128)),
 ]
