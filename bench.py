@@ -235,6 +235,61 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
     return ms, sets, finite, L, trials
 
 
+def quant_leg(c: int, operand: str, steps: int, warmup: int, sets: int | None, g: int, fmt: int, per_row: bool):
+    """The GPU quantiser on workload c's FP32 A or B: per-call time over rotating input sets."""
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = torch.from_numpy(synth.make_a(c) if operand == "a" else synth.make_b(c)).to(dev)
+    rows, cols = x.shape
+    nblocks = (rows if per_row else math.ceil(rows / g)) * (cols // g)
+    set_bytes = 5 * rows * cols + 4 * nblocks  # FP32 in, FP8 codes and FP32 factors out
+    if sets is None:
+        sets = max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes) + 1))
+    bufs = [(x if i == 0 else x.clone(), torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+             torch.empty(nblocks, dtype=torch.float32, device=dev)) for i in range(sets)]
+    fn = dg.dg_quantize_fp8_rows if per_row else dg.dg_quantize_fp8_blocks
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(i, st):
+        xx, q, sc = bufs[i % sets]
+        fn(xx, gran=g, fmt=fmt, q=q, scales=sc.view(-1, cols // g), stream=st)
+
+    for i in range(max(1, warmup)):
+        launch(i, stream)
+    torch.cuda.synchronize(dev)
+    eager = (bufs[0][1].clone(), bufs[0][2].clone())
+    L = max(d for d in range(1, min(steps, 100) + 1) if steps % d == 0)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(L):
+                launch(i, cap)
+    torch.cuda.synchronize(dev)
+    for _, q, sc in bufs:
+        q.zero_()
+        sc.zero_()
+    graph.replay()
+    torch.cuda.synchronize(dev)
+    for i in range(min(sets, L)):  # every set holds the same input
+        if not (torch.equal(bufs[i][1], eager[0]) and torch.equal(bufs[i][2].view(torch.int32), eager[1].view(torch.int32))):
+            raise SystemExit("graph replay output differs from the eager call's")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps // L):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = start.elapsed_time(end) / steps
+    return ms, sets, L, rows, cols, nblocks
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -324,6 +379,9 @@ def main():
                     help="operand storage: A [M,K] or [K,M] (first letter n / t), B [N,K] or [K,N] (t / n)")
     ap.add_argument("--sa-rows", type=int, default=None, choices=(1,),
                     help="1: per-row A factors (1 x g blocks) instead of g x g blocks")
+    ap.add_argument("--quant", default=None, choices=("a", "b"),
+                    help="time the GPU quantiser on the workload's FP32 A or B instead of the GEMM (g x g "
+                         "blocks, or 1 x g with --sa-rows 1; format from the first letter pair of --fmt)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes three times (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -355,6 +413,25 @@ def main():
     if w["K"] % g:
         raise SystemExit("--gran %d does not divide K = %d" % (g, w["K"]))
     fa, fb = FORMATS[args.fmt]
+    if args.quant:
+        fmt = fa if args.quant == "a" else fb
+        ms, sets, glen, rows, cols, nblocks = quant_leg(c, args.quant, args.steps, args.warmup, args.sets, g, fmt,
+                                                        args.sa_rows == 1)
+        qbytes = 5.0 * rows * cols + 4.0 * nblocks
+        gbs = qbytes / (ms * 1e-3) / 1e9
+        print(json.dumps({
+            "metric": "FP8 block quantiser throughput (FP32 in, FP8 codes and FP32 factors out; 1 GPU)",
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": w["name"], "operand": args.quant.upper(), "rows": rows, "cols": cols, "gran": g,
+                       "blocks": "1x%d" % g if args.sa_rows == 1 else "%dx%d" % (g, g),
+                       "fmt": "e5m2" if fmt else "e4m3", "input_sets": sets,
+                       "launch": "hipGraph of %d launches, replayed %d times" % (glen, args.steps // glen)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+            "cpu_baseline": None}), flush=True)
+        return
     flops, nbytes = algorithmic(w, g, args.sa_rows)
     act = ACTS[args.act]
     layout = LAYOUTS[args.layout]

@@ -88,47 +88,63 @@ __global__ __launch_bounds__(G == 256 ? 1024 : 256) void quant_fp8_blocks(const 
 
 // 1 x g blocks (one factor per row and g-wide column segment; the per-row A
 // factors of the template article's per-channel choice, §3.4): the same rule
-// per segment. G/4 lanes own a segment, four elements each, so a wave covers
-// 256 / G segments, 256 consecutive floats when a row has that many; amax is
-// a butterfly over the segment's lanes. Segments are numbered row-major
+// per segment. G/4 lanes own a segment, four elements each, so one load
+// instruction of a wave covers 256 / G segments, 256 consecutive floats when a
+// row has that many; amax is a butterfly over the segment's lanes. Each wave
+// takes U such groups, all loads issued before any is used, so a thread has
+// U x 16 bytes in flight. Segments are numbered row-major
 // (row * cols/G + column block), which is also the factor's index in the
-// [rows][cols/G] scale tensor.
-template <int G, int FMT>
+// [rows][cols/G] scale tensor; the host keeps their count below 2^31.
+template <int G, int FMT, int U>
 __global__ __launch_bounds__(256) void quant_fp8_rows(const float* __restrict__ x, uint8_t* __restrict__ q,
-                                                      float* __restrict__ scales, int64_t nseg, int cols) {
+                                                      float* __restrict__ scales, unsigned nseg, int cols) {
   constexpr float FMAX = FMT == 1 ? 57344.0f : 448.0f;
-  constexpr int LPS = G / 4;  // lanes per segment
+  constexpr int LPS = G / 4;        // lanes per segment
+  constexpr int SPW = 64 / LPS;     // segments per wave-wide load
   const int lane = threadIdx.x & 63;
-  const int64_t seg = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / LPS) + lane / LPS;
   const int c4 = lane % LPS;
-  const bool live = seg < nseg;  // whole segments are live or not, so the butterfly stays inside live lanes
-  const int ncb = cols / G;
-  const int64_t row = live ? seg / ncb : 0;
-  const int col = live ? (int)(seg % ncb) * G + c4 * 4 : 0;
-  const v4f v = live ? *reinterpret_cast<const v4f*>(x + row * cols + col) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  const unsigned ncb = (unsigned)(cols / G);
+  // unsigned: the last workgroup's segments may pass 2^31 - 1 (and are not live)
+  const unsigned seg0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (unsigned)(SPW * U) + (unsigned)(lane / LPS);
+  v4f v[U];
+  int64_t off[U];
 #pragma unroll
-  for (int off = LPS / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  if (!live) return;
-  const float scale = amax > 0.0f ? amax / FMAX : 1.0f;
-  if (c4 == 0) scales[seg] = scale;
-  int packed;
-  if constexpr (FMT == 1) {
-    packed = __builtin_amdgcn_cvt_pk_bf8_f32(v.x / scale, v.y / scale, 0, false);
-    packed = __builtin_amdgcn_cvt_pk_bf8_f32(v.z / scale, v.w / scale, packed, true);
-  } else {
-    packed = __builtin_amdgcn_cvt_pk_fp8_f32(v.x / scale, v.y / scale, 0, false);
-    packed = __builtin_amdgcn_cvt_pk_fp8_f32(v.z / scale, v.w / scale, packed, true);
+  for (int u = 0; u < U; ++u) {
+    const unsigned seg = seg0 + (unsigned)(u * SPW);
+    // whole segments are live or not, so each butterfly stays inside live lanes
+    const unsigned row = seg < nseg ? seg / ncb : 0u;
+    const unsigned cb = seg < nseg ? seg - row * ncb : 0u;
+    off[u] = (int64_t)row * cols + cb * G + c4 * 4;
+    v[u] = seg < nseg ? *reinterpret_cast<const v4f*>(x + off[u]) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
   }
-  *reinterpret_cast<int*>(q + row * cols + col) = packed;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const unsigned seg = seg0 + (unsigned)(u * SPW);
+    float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
+#pragma unroll
+    for (int o = LPS / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    if (seg >= nseg) continue;
+    const float scale = amax > 0.0f ? amax / FMAX : 1.0f;
+    if (c4 == 0) scales[seg] = scale;
+    int packed;
+    if constexpr (FMT == 1) {
+      packed = __builtin_amdgcn_cvt_pk_bf8_f32(v[u].x / scale, v[u].y / scale, 0, false);
+      packed = __builtin_amdgcn_cvt_pk_bf8_f32(v[u].z / scale, v[u].w / scale, packed, true);
+    } else {
+      packed = __builtin_amdgcn_cvt_pk_fp8_f32(v[u].x / scale, v[u].y / scale, 0, false);
+      packed = __builtin_amdgcn_cvt_pk_fp8_f32(v[u].z / scale, v[u].w / scale, packed, true);
+    }
+    *reinterpret_cast<int*>(q + off[u]) = packed;
+  }
 }
 
 template <int G, int FMT>
 static hipError_t launch_rows_g(const QuantArgs& p, hipStream_t stream) {
+  constexpr int U = 8;
   const int64_t nseg = p.rows * (p.cols / G);
-  const int64_t per_wg = 4 * (256 / G);  // segments per workgroup of four waves
-  hipLaunchKernelGGL((quant_fp8_rows<G, FMT>), dim3((unsigned)((nseg + per_wg - 1) / per_wg)), dim3(256), 0, stream,
-                     p.x, p.q, p.scales, nseg, (int)p.cols);
+  const int64_t per_wg = 4 * (256 / G) * U;  // segments per workgroup of four waves
+  hipLaunchKernelGGL((quant_fp8_rows<G, FMT, U>), dim3((unsigned)((nseg + per_wg - 1) / per_wg)), dim3(256), 0,
+                     stream, p.x, p.q, p.scales, (unsigned)nseg, (int)p.cols);
   return hipGetLastError();
 }
 
