@@ -73,16 +73,15 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   constexpr int SLOT = STAGE + SCL;
   constexpr int LDC = BN + 8;  // bf16 pitch of an epilogue pass
   static_assert(WTM == 64 || WTM == 128, "a wave's rows lie in one 128-row scale block");
-  static_assert(WTN % 16 == 0 && WTN <= 128, "a wave's columns touch at most two 128-column scale blocks");
+  // Every wave's columns lie in one 128- (or 256-) column scale block: the
+  // tile width is a multiple of 128 and the wave width divides 128.
+  static_assert(BN % 128 == 0 && WTN % 16 == 0 && 128 % WTN == 0, "a wave's columns lie in one scale block");
   static_assert(G == 128 || WTN == 64, "g = 64: one 64-column scale block per wave");
   static_assert(BN % 8 == 0 && BN / 8 <= 4 * NW, "B copies: at most four row groups per wave");
   static_assert(128 * LDC * 2 <= 2 * STAGE, "an epilogue pass must fit in the ring");
   static_assert(BM * SEGS <= NW * 64, "a step's row factors: one 64-entry piece per wave");
   static_assert((LAYOUT & 1) == 0 || BN == 256 || BN == 128, "transposed B: 256- or 128-byte K rows");
   static_assert(LAYOUT == 0 || !ROWA, "per-row A factors: NT only");
-  // Every wave's columns lie in one 128- (or 256-) column scale block when the
-  // tile width is a multiple of 128 and the wave width divides 128.
-  constexpr bool ONE_B = BN % 128 == 0 && 128 % WTN == 0;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOT];
 
   const int lane = threadIdx.x & 63;
@@ -104,17 +103,14 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   const v4i rsa = ROWA ? rsrc_words(sa + (int64_t)m0 * nks, (uint32_t)min(BM, M - m0) * (uint32_t)nks * 4u) : (v4i){};
 
   // Scale rows of this wave. Blocks past the edge clamp to the last block
-  // (their data is zero). g >= 128: one A block; the wave's columns may cross
-  // into a second B block after jsplit 16-column blocks. g = 64: A blocks of
-  // rows wr0 and wr0 + 64, one B block.
+  // (their data is zero). g >= 128: one A block and one B block. g = 64: A
+  // blocks of rows wr0 and wr0 + 64, one B block.
   const int wr0 = m0 + wm * WTM, wc0 = n0 + wn * WTN;
   const int lastm = (M - 1) / sg, lastn = (N - 1) / sg;
   const float* const sa0 = sa + (int64_t)min(wr0 / sg, lastm) * nks;
   const float* const sa1 = sa + (int64_t)min((wr0 + 64) / sg, lastm) * nks;
   const int bn0 = wc0 / sg;
   const float* const sb0 = sb + (int64_t)min(bn0, lastn) * nks;
-  const float* const sb1 = sb + (int64_t)min(bn0 + 1, lastn) * nks;
-  const int jsplit = ((bn0 + 1) * sg - wc0) / 16;  // g >= 128: column blocks in the first B block
 
   Acc<G, WTM, WTN> acc;
   if constexpr (G == 128) {
@@ -211,8 +207,8 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       const int r16 = lane & 15, q = lane >> 4;
       const int ksc = s >> sshift;
       const float a_s = ROWA ? 0.0f : sa0[ksc];
-      const float sbv0 = sb0[ksc], sbv1 = sb1[ksc];
-      const float sc0 = a_s * sbv0, sc1 = a_s * sbv1;
+      const float sbv0 = sb0[ksc];
+      const float sc0 = a_s * sbv0;
       // ROWA: factors of rows 16i + 4q .. +3 of the wave tile, read one row block ahead
       const float* const srow = scl + wm * WTM + 4 * q;
       v4f sr[WTM / 16], fr;
@@ -238,19 +234,13 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
         if (t >= LAG) {
           const int u = t - LAG, ui = u / NJ, uj = u % NJ;
           if constexpr (ROWA) {
-            // the row block's products, shared by its column blocks; formed
-            // again where the wave's columns enter the second B block
-            // (jsplit >= 1 is wave-uniform)
+            // the row block's products, shared by its column blocks
             if (uj == 0) fr = sr[ui] * sbv0;
-            if constexpr (!ONE_B) {
-              if (uj == jsplit) fr = sr[ui] * sbv1;
-            }
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], fr[v], acc.t[ui][uj][v]);
           } else {
-            const float sc = uj < jsplit ? sc0 : sc1;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], sc, acc.t[ui][uj][v]);
+            for (int v = 0; v < 4; ++v) acc.t[ui][uj][v] = __builtin_fmaf(pr[u % (LAG + 1)][v], sc0, acc.t[ui][uj][v]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
