@@ -116,7 +116,8 @@ int dg_gemm_fp8_nt_fmt(const void* a, const void* b, const float* sa, const floa
  * BF16 store:  out[i,j] = bf16( act( C[i,j] + bias[j] ) )  with C the FP32
  * block-scaled product and everything in FP32.
  *
- *   bias  FP32 [N] device pointer, 4-byte aligned, or NULL for no bias.
+ *   bias  FP32 [N] device pointer, 4-byte aligned, or NULL for no bias; it
+ *         must not overlap out (DG_EINVAL).
  *   act   DG_ACT_NONE, DG_ACT_RELU or DG_ACT_GELU.
  *
  * With bias NULL and DG_ACT_NONE this is dg_gemm_fp8_nt_fmt, bit for bit.
