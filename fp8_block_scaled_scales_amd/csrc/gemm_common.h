@@ -100,9 +100,13 @@ __device__ __forceinline__ void stage_row_scales(v4i rsa, uint8_t* lds, uint32_t
 // slab starting at column byte k0 of the rows the descriptor covers, into
 // LDS at lds + 1024*grp (64 lanes x 16 B, written lane-contiguously from the
 // wave-uniform LDS address). Lane L writes physical chunk L%8 of row L/8, so
-// it fetches logical chunk (L%8) ^ ((row >> SW) % 8): the XOR swizzle is
-// applied on the global-address side. SW = 0 makes 8 consecutive rows
-// conflict free, SW = 1 makes 16 consecutive rows conflict free.
+// it fetches logical chunk (L%8) ^ key(row): the XOR swizzle is applied on
+// the global-address side. SW = 0: key = row % 8, so 8 consecutive rows read
+// at one logical chunk hit 8 distinct 16-byte bank groups of a 128-byte bank
+// row; SW = 1: key = (row / 2) % 8, distinct 16-byte positions over 16
+// consecutive rows of a 256-byte bank row; SW = 2: key = (row % 8) ^
+// ((row / 8) % 2), which is both (conflict free whether a 16-byte read is
+// served 8 lanes per clock over 128 bytes or 16 lanes over 256).
 // The wave-uniform part of the offset (row group and K position) goes in the
 // instruction's scalar offset, so a wave's copies share one or two per-lane
 // offset registers.
@@ -112,10 +116,12 @@ __device__ __forceinline__ void stage_row_scales(v4i rsa, uint8_t* lds, uint32_t
 template <int SW>
 __device__ __forceinline__ void stage_group(v4i rsrc, uint8_t* lds, uint32_t K, uint32_t k0, int grp, int lane,
                                             bool valid = true) {
-  static_assert(SW == 0 || SW == 1, "swizzle");
+  static_assert(SW >= 0 && SW <= 2, "swizzle");
   const uint32_t r_in = (uint32_t)lane >> 3;
-  // (row >> SW) & 7 with row = 8*grp + r_in
-  const uint32_t key = SW == 0 ? r_in : ((((uint32_t)grp & 1) << 2) + (r_in >> 1)) & 7;
+  // key(row) with row = 8*grp + r_in
+  const uint32_t key = SW == 0   ? r_in
+                       : SW == 1 ? ((((uint32_t)grp & 1) << 2) + (r_in >> 1)) & 7
+                                 : r_in ^ ((uint32_t)grp & 1);
   const uint32_t chunk = ((uint32_t)lane & 7) ^ key;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
   lds_dma16(rsrc, __builtin_amdgcn_readfirstlane(lds_base + grp * 1024), r_in * K + chunk * 16,

@@ -18,9 +18,10 @@ constexpr int BM = 256, BK = 128, NW = 8, NT = 64 * NW;
 constexpr int A_BYTES = BM * BK;
 
 // 32 K bytes (logical 16-byte chunks c0, c0+1) of staged row `row` under the
-// SW = 1 swizzle.
+// SW = 2 swizzle of stage_group (key (row % 8) ^ ((row / 8) % 2); the slab
+// offsets of the wave tiles are multiples of 64 rows, which keep it).
 __device__ __forceinline__ v8i frag(const uint8_t* slab, int row, int c0) {
-  const int sw = (row >> 1) & 7;
+  const int sw = (row & 7) ^ ((row >> 3) & 1);
   const v4i lo = *reinterpret_cast<const v4i*>(slab + row * BK + ((c0 ^ sw) << 4));
   const v4i hi = *reinterpret_cast<const v4i*>(slab + row * BK + (((c0 + 1) ^ sw) << 4));
   return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       for (int i = 0; i < 4; ++i) stage_group_t<BM>(rat, slot, (uint32_t)M, i * NW + wave, lane);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) stage_group<1>(ra, slot, uK, (uint32_t)t * BK, i * NW + wave, lane);
+      for (int i = 0; i < 4; ++i) stage_group<2>(ra, slot, uK, (uint32_t)t * BK, i * NW + wave, lane);
     }
     if constexpr ((LAYOUT & 1) != 0) {
       const v4i rbt = rsrc_words(b + k0 * N + n0, (uint32_t)(min((int64_t)BK, (int64_t)K - k0) * N - n0));
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (i * NW + wave < BN / 8) stage_group<1>(rb, slot + A_BYTES, uK, (uint32_t)t * BK, i * NW + wave, lane);
+        if (i * NW + wave < BN / 8) stage_group<2>(rb, slot + A_BYTES, uK, (uint32_t)t * BK, i * NW + wave, lane);
     }
   };
 

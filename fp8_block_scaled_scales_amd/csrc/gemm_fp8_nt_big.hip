@@ -34,7 +34,7 @@
 // by waves 4-7 a quarter of the way in: the memory pipeline takes one 1 KB
 // copy per ~14 clocks and a wave stalls until its copy is taken, so this way
 // one wave per SIMD is always free to issue MFMAs.
-// The tiles' LDS slabs use the SW = 1 swizzle: the 16 (or 32) rows a fragment
+// The tiles' LDS slabs use the SW = 2 swizzle: the 16 (or 32) rows a fragment
 // read touches together hit distinct banks.
 //
 // Epilogue: the BF16 tile goes through LDS in two 128-row passes so every
