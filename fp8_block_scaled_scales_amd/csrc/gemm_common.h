@@ -142,14 +142,24 @@ __device__ __forceinline__ void stage_slab(v4i rsrc, uint8_t* lds, uint32_t K, u
 // (the tile's M or N extent: 64, 128 or 256), 16-byte chunks XOR-swizzled by
 // row, and read into the MFMA fragment with the transposing LDS read.
 //
-// Swizzle key of row r: the eight consecutive rows one transposing read
-// touches at one logical chunk land on distinct banks (128- and 256-byte
-// rows: all eight chunks differ; 64-byte rows: rows four apart, which share a
-// bank offset, get different chunks).
+// Swizzle key of row r. A transposing read is served 32 lanes (256 bytes,
+// all 64 banks) per clock: two 16-lane groups, each eight consecutive rows
+// at one or two adjacent logical chunks, and the two groups either 32 rows
+// apart at the same chunk (16x16 fragment) or at the same rows one chunk apart
+// (32x32 fragment). The key spreads all of that over distinct banks:
+//   256-byte rows (one row = all banks): 2*(r%8) puts the eight rows on even
+//     chunk offsets, and bit 0 flips every 32 rows, so the neighbouring chunk
+//     or the group 32 rows on lands on the odd ones;
+//   128-byte rows (two rows = all banks): r%8 already separates the eight
+//     rows (odd rows sit in the other half of the banks), and bit 0 flips
+//     every 32 rows;
+//   64-byte rows (four rows = all banks): rows four apart share bank offsets,
+//     so bit 1 flips with (r/4)%2 and bit 0 every 32 rows.
 template <int W>
 __device__ __forceinline__ int tkey(int row) {
   static_assert(W == 64 || W == 128 || W == 256, "transposed tile width");
-  return W == 64 ? ((row >> 2) & 3) : (row & 7);
+  const int far = (row >> 5) & 1;
+  return W == 64 ? ((((row >> 2) & 1) << 1) | far) : W == 128 ? ((row & 7) ^ far) : ((2 * (row & 7)) ^ far);
 }
 
 // One instruction of a transposed tile's copy: rows RPI*grp .. RPI*grp+RPI-1
