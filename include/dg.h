@@ -215,7 +215,8 @@ int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, 
  *   q       E4M3FN codes out, [rows][cols] row-major, 4-byte aligned.
  *   scales  FP32 out, [ceil(rows/gran)][cols/gran] row-major, 4-byte aligned.
  *   rows, cols > 0 and <= DG_MAX_DIM; cols a multiple of gran; gran 64, 128
- *   or 256. x, q and scales must not overlap one another (DG_EINVAL).
+ *   or 256; at most 2^31 - 1 scale factors (DG_EINVAL beyond). x, q and
+ *   scales must not overlap one another (DG_EINVAL).
  *
  * Per gran x gran block (rows past the end make edge blocks partial):
  * amax = max |x| over present elements, scale = amax / 448 in FP32 (1.0 for

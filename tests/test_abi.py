@@ -242,3 +242,15 @@ def test_quantize_overlaps(dg, x, q, s):
     # x [64][256] FP32 is 64 KB from A, q 16 KB, the factors 2 x 2 (or 64 x 2 per row) FP32
     assert dg.lib.dg_quantize_fp8_blocks(x, 64, 256, 128, 0, q, s, None) == dg.DG_EINVAL
     assert dg.lib.dg_quantize_fp8_rows(x, 64, 256, 128, 0, q, s, None) == dg.DG_EINVAL
+
+def test_quantize_scale_count_cap(dg):
+    """More than 2^31 - 1 scale factors is rejected before any device work.
+    rows = 2^24 - 256 with 129 segments per row is 2,164,227,840 factors, and
+    2^24 - 256 square in 64 x 64 blocks is 262,140^2. The fake addresses sit
+    2^52 apart, beyond the 1.13e15 bytes of the largest x, so no overlap rule
+    applies."""
+    rows, g = (1 << 24) - 256, 64
+    x, q, s = 1 << 52, 1 << 53, 1 << 54
+    assert 4 * rows * rows < (1 << 52)
+    assert dg.lib.dg_quantize_fp8_rows(x, rows, 129 * g, g, 0, q, s, None) == dg.DG_EINVAL
+    assert dg.lib.dg_quantize_fp8_blocks(x, rows, rows, g, 0, q, s, None) == dg.DG_EINVAL
