@@ -14,9 +14,12 @@ namespace dg {
 
 constexpr int BK = 128;  // K bytes per pipeline step (row pitch of a staged slab)
 
-// 32 bytes of K (logical 16-byte chunks c0 and c0+1) of one staged row.
+// 32 bytes of K (logical 16-byte chunks c0 and c0+1) of one staged row. The
+// slabs use the SW = 2 swizzle of stage_group: key (row % 8) ^ ((row / 8) % 2),
+// so the rows one 16-byte read touches together hit distinct banks whether
+// the read is served 8 lanes per clock or 16.
 __device__ __forceinline__ v8i frag32(const uint8_t* slab, int row, int c0) {
-  const int sw = row & 7;
+  const int sw = (row & 7) ^ ((row >> 3) & 1);
   const v4i lo = *reinterpret_cast<const v4i*>(slab + row * BK + ((c0 ^ sw) << 4));
   const v4i hi = *reinterpret_cast<const v4i*>(slab + row * BK + (((c0 + 1) ^ sw) << 4));
   return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
 #pragma unroll
       for (int i = 0; i < BM / 8 / NWAVES; ++i) stage_group_t<BM>(rat, slot, (uint32_t)M, i * NWAVES + wave, lane);
     } else {
-      stage_slab<BM, NWAVES>(ra, slot, uK, st * BK, wave, lane);
+      stage_slab<BM, NWAVES, 2>(ra, slot, uK, st * BK, wave, lane);
     }
     if constexpr ((LAYOUT & 1) != 0) {
       const v4i rbt = rsrc_words(b + k0 * N + n0, (uint32_t)(min((int64_t)BK, (int64_t)K - k0) * N - n0));
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
       for (int i = 0; i < BN / 8 / NWAVES; ++i)
         stage_group_t<BN>(rbt, slot + A_BYTES, (uint32_t)N, i * NWAVES + wave, lane);
     } else {
-      stage_slab<BN, NWAVES>(rb, slot + A_BYTES, uK, st * BK, wave, lane);
+      stage_slab<BN, NWAVES, 2>(rb, slot + A_BYTES, uK, st * BK, wave, lane);
     }
   };
   const float* sa_row[TM];
