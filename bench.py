@@ -65,23 +65,36 @@ import synth  # noqa: E402  (seeded inputs only; no GEMM arithmetic)
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (published)
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E (published)
 MALL_BYTES = 256 << 20    # Infinity Cache
-DEFAULT_WORKLOAD = 2      # small-M decode shape, M=64 N=4096 K=7168, g=128
+DEFAULT_WORKLOAD = 4      # large square M=N=K=8192, g=128: the largest shape, MFMA-bound
 
 # HBM traffic of the GEMM kernel per launch, from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (each scaled by the copy-kernel calibration factor), keyed by
-# workload and tagged with the hash of the kernel source the counters were
-# taken on. A different hash means the kernel changed since: traffic is null.
+# workload and tagged with the hash of the sources of the kernel class that
+# workload runs (KERNEL_SOURCES) as they were when the counters were taken. A
+# different hash means the kernel changed since: traffic is null.
 TRAFFIC = {
     "decode_m64_n4096_k7168": {"src": "806112c55f3d193d", "bytes": 33667900},
 }
 
+# Sources that make up each workload's kernel: its class's device code, the
+# shared device header, the argument header and the host dispatch.
+_COMMON_SOURCES = ("gemm_common.h", "gemm_fp8_nt.h", "dg_host.hip")
+KERNEL_SOURCES = {
+    "decode_m64_n4096_k7168": ("gemm_fp8_nt_stream.hip",) + _COMMON_SOURCES,
+    "square8192": ("gemm_fp8_big.h", "gemm_fp8_nt_big.hip") + _COMMON_SOURCES,
+    "prefill_m4096_n7168_k2048": ("gemm_fp8_big.h", "gemm_fp8_nt_big.hip") + _COMMON_SOURCES,
+    "longk_m2000_n4000_k16384_g64": ("gemm_fp8_big.h", "gemm_fp8_nt_big.hip") + _COMMON_SOURCES,
+}
 
-def _kernel_source_hash() -> str:
+
+def kernel_source_hash(workload: str) -> str | None:
     import hashlib
 
-    # the sources of the default workload's kernel (the streaming class) and of its dispatch
+    names = KERNEL_SOURCES.get(workload)
+    if names is None:
+        return None
     h = hashlib.sha256()
-    for name in ("gemm_fp8_nt_stream.hip", "gemm_common.h", "gemm_fp8_nt.h", "dg_host.hip"):
+    for name in names:
         with open(os.path.join(ROOT, "fp8_block_scaled_scales_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -366,7 +379,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=str(DEFAULT_WORKLOAD),
-                    help="workload number or name (default: the small-M decode shape)")
+                    help="workload number or name (default: the large square M=N=K=8192)")
     ap.add_argument("--sets", type=int, default=None, help="input sets rotated over (default: defeat the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fmt", default="e4m3", choices=sorted(FORMATS),
@@ -451,7 +464,7 @@ def main():
     default_variant = (fa, fb, g, args.bias, act, args.sa_rows, layout, args.sets) == \
         (0, 0, w["g"], False, 0, None, 0, None)
     tr = TRAFFIC.get(w["name"]) if default_variant else None
-    traffic = tr["bytes"] if tr and tr["src"] == _kernel_source_hash() else None
+    traffic = tr["bytes"] if tr and tr["src"] == kernel_source_hash(w["name"]) else None
 
     cpu = None if args.no_cpu_baseline else cpu_leg(c, g, fa, fb, args.bias, act, sa_rows=args.sa_rows, layout=layout)
 

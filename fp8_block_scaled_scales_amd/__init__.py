@@ -38,7 +38,7 @@ DG_MAX_DIM = (1 << 24) - 256  # largest M, N or K (and quantiser rows, cols) the
 class dg_tile_info(ctypes.Structure):
     _fields_ = [("kernel_id", ctypes.c_int), ("bm", ctypes.c_int), ("bn", ctypes.c_int),
                 ("bk", ctypes.c_int), ("stages", ctypes.c_int), ("waves", ctypes.c_int),
-                ("ksplit", ctypes.c_int), ("grid", ctypes.c_int64)]
+                ("ksplit", ctypes.c_int), ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
 
 def _load():
@@ -65,6 +65,11 @@ def _load():
                                        ctypes.c_int, vp, ctypes.c_int, vp]
     lib.dg_query_tile_layout.restype = ctypes.c_int
     lib.dg_query_tile_layout.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(dg_tile_info)]
+    lib.dg_query_tile_ws.restype = ctypes.c_int
+    lib.dg_query_tile_ws.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(dg_tile_info)]
+    lib.dg_gemm_fp8_ws.restype = ctypes.c_int
+    lib.dg_gemm_fp8_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, i64, vp]
     lib.dg_quantize_fp8_rows.restype = ctypes.c_int
     lib.dg_quantize_fp8_rows.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.dg_quantize_e4m3_blocks.restype = ctypes.c_int
@@ -106,9 +111,11 @@ def dg_version() -> int:
     return _lib.dg_version()
 
 
-def dg_query_tile(M: int, N: int, K: int, gran: int = 128, layout: int = 0) -> dict:
+def dg_query_tile(M: int, N: int, K: int, gran: int = 128, layout: int = 0, workspace: bool = False) -> dict:
+    """The tile-table plan of a call: dg_gemm_fp8_layout's (workspace=False) or dg_gemm_fp8_ws's."""
     info = dg_tile_info()
-    rc = _lib.dg_query_tile_layout(M, N, K, gran, layout, ctypes.byref(info))
+    fn = _lib.dg_query_tile_ws if workspace else _lib.dg_query_tile_layout
+    rc = fn(M, N, K, gran, layout, ctypes.byref(info))
     if rc != DG_OK:
         _raise(rc, "dg_query_tile")
     return {name: getattr(info, name) for name, _ in dg_tile_info._fields_}
@@ -267,6 +274,64 @@ def dg_gemm_fp8_layout(a, b, sa, sb, out=None, gran: int = 128, layout: int = DG
     return out
 
 
+def dg_workspace(M: int, N: int, K: int, gran: int = 128, layout: int = DG_LAYOUT_NT, device="cuda"):
+    """A workspace for dg_gemm_fp8_ws of this shape (uint8 tensor), or None when its plan needs none."""
+    n = dg_query_tile(M, N, K, gran, layout, workspace=True)["workspace_bytes"]
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def dg_gemm_fp8_ws(a, b, sa, sb, out=None, gran: int = 128, layout: int = DG_LAYOUT_NT, sa_rows: int | None = None,
+                   fmt_a: int = DG_FMT_E4M3, fmt_b: int = DG_FMT_E4M3, bias=None, act: int = DG_ACT_NONE,
+                   workspace=None, stream=None):
+    """dg_gemm_fp8_layout (with dg_gemm_fp8_nt_ex's sa_rows) plus a caller-owned workspace.
+
+    With a workspace (a contiguous uint8 GPU tensor of at least
+    dg_query_tile(..., workspace=True)["workspace_bytes"] bytes, 256-byte
+    aligned; see ``dg_workspace``) small-M shapes with few output tiles split
+    K over several workgroups; every other shape runs what the call without a
+    workspace runs. Concurrent calls need distinct workspaces.
+    """
+    if layout not in (DG_LAYOUT_NT, DG_LAYOUT_NN, DG_LAYOUT_TT, DG_LAYOUT_TN):
+        raise ValueError("layout must be DG_LAYOUT_NT, _NN, _TT or _TN")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    K, M = a.shape if layout & 2 else a.shape[::-1]
+    N = b.shape[1] if layout & 1 else b.shape[0]
+    dev = a.device
+    if gran not in _GRANS or K % gran:
+        raise ValueError("gran must be 64, 128 or 256 and divide K")
+    if fmt_a not in _FP8_OF or fmt_b not in _FP8_OF:
+        raise ValueError("formats must be DG_FMT_E4M3 or DG_FMT_E5M2")
+    sa_rows = gran if sa_rows is None else sa_rows
+    if sa_rows not in (gran, 1):
+        raise ValueError("sa_rows must be gran (g x g blocks) or 1 (per-row factors)")
+    _check(a, "a", _FP8_OF[fmt_a], (K, M) if layout & 2 else (M, K), dev)
+    _check(b, "b", _FP8_OF[fmt_b], (K, N) if layout & 1 else (N, K), dev)
+    _check(sa, "sa", (torch.float32,), ((M + sa_rows - 1) // sa_rows, K // gran), dev)
+    _check(sb, "sb", (torch.float32,), ((N + gran - 1) // gran, K // gran), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", (torch.bfloat16,), (M, N), dev)
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), (N,), dev)
+    if act not in (DG_ACT_NONE, DG_ACT_RELU, DG_ACT_GELU):
+        raise ValueError("act must be DG_ACT_NONE, DG_ACT_RELU or DG_ACT_GELU")
+    if dev.type != "cuda":
+        raise ValueError("a must be a GPU tensor")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _check(workspace, "workspace", (torch.uint8,), (workspace.numel(),), dev)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = _lib.dg_gemm_fp8_ws(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
+                                 M, N, K, gran, layout, sa_rows, fmt_a, fmt_b,
+                                 None if bias is None else bias.data_ptr(), act, ws_ptr, ws_bytes, s.cuda_stream)
+    if rc != DG_OK:
+        _raise(rc, "dg_gemm_fp8_ws")
+    return out
+
+
 def _quantize(x, gran, fmt, q, scales, stream, where):
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError("x must be a 2-D tensor")
@@ -325,6 +390,7 @@ def dg_quantize_fp8_rows(x, gran: int = 128, fmt: int = DG_FMT_E4M3, q=None, sca
 
 
 __all__ = ["dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "dg_gemm_fp8_nt_epi", "dg_gemm_fp8_nt_ex", "dg_gemm_fp8_layout",
+           "dg_gemm_fp8_ws", "dg_workspace",
            "DG_LAYOUT_NT", "DG_LAYOUT_NN", "DG_LAYOUT_TT", "DG_LAYOUT_TN", "DG_ACT_NONE",
            "DG_ACT_RELU", "DG_ACT_GELU", "dg_quantize_e4m3_blocks", "dg_quantize_fp8_blocks", "dg_quantize_fp8_rows",
            "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError", "DG_OK", "DG_EINVAL",

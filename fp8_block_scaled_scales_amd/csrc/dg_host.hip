@@ -8,6 +8,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstdio>
 #include <cstdlib>
 #include <algorithm>
@@ -24,14 +26,34 @@ constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_status[kMaxDevices];  // DG_OK or DG_EUNSUPPORTED, set once per device
 
-// Split-K workspace, allocated once per device on first need and kept until
-// the process ends: FP32 partial tiles plus one arrival counter per tile
-// (zeroed once here; the kernel returns each counter to zero).
-constexpr int64_t kWsFloats = 8ll << 20;  // 32 MB of partial tiles
+// Split-K plans (dg_gemm_fp8_ws only) are capped at this many FP32 partial
+// floats and arrival counters, which bounds the workspace a caller provides.
+constexpr int64_t kWsFloats = 4ll << 20;  // 16 MB of partial tiles
 constexpr int64_t kWsCounters = 1 << 16;
-std::once_flag g_ws_once[kMaxDevices];
-float* g_ws[kMaxDevices];
-uint32_t* g_counters[kMaxDevices];
+
+// Per-call tags of the split-K arrival counters (48 bits, never 0): the
+// kernel treats a counter whose tag is not its own call's as zero, so a
+// workspace needs no clearing and a launch that never finished leaves
+// nothing a later call counts. Seeded from the clock so that a fresh
+// workspace's contents are unlikely to carry a matching tag.
+std::atomic<uint64_t> g_epoch{0};
+std::once_flag g_epoch_once;
+
+uint64_t next_epoch() {
+  std::call_once(g_epoch_once, [] {
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    g_epoch.store((t * 0x9E3779B97F4A7C15ull) >> 20);
+  });
+  uint64_t e;
+  do {
+    e = g_epoch.fetch_add(1) & ((1ull << 48) - 1);
+  } while (e == 0);
+  return e;
+}
+
+// Workspace layout of a split-K plan: the arrival counters (8 bytes per
+// tile) first, then the partial tiles from the next 256-byte boundary.
+int64_t counter_bytes(int64_t tiles) { return (tiles * 8 + 255) / 256 * 256; }
 
 thread_local hipError_t t_last_hip = hipSuccess;
 thread_local char t_msg[256];
@@ -79,15 +101,18 @@ struct Plan {
 };
 
 // Tile-table choice (pure host arithmetic, no HIP call).
-// Small M streams B. When 32x32 tiles give at least 3/4 of a workgroup per CU,
-// each takes the whole K and its waves split K inside the workgroup. With
-// fewer tiles, the K range of each 64x64 tile is split over several
-// workgroups until about one workgroup per CU (256) runs, keeping at least 4
-// pipeline steps per split. Large M and N take
-// 256x256 tiles when they give at least 3/4 of a tile per CU; the rest takes
-// 128x128 tiles over the whole K.
+// Small M streams B. Without a workspace (every call but dg_gemm_fp8_ws) a
+// small-M NT shape takes 32x32 tiles over the whole K, whose waves split K
+// inside the workgroup, whatever the tile count; a transposed layout takes
+// 64x64 tiles over the whole K. With a workspace, shapes with fewer than 192
+// tiles of 32x32 (or any transposed small-M shape) split the K range of each
+// 64x64 tile over several workgroups until about one workgroup per CU (256)
+// runs, keeping at least 4 pipeline steps per split.
+// Large M and N take the 256-row tiles (256 or 128 wide) when they give at
+// least 3/4 of a tile per CU; the rest takes 128x128 tiles over the whole K.
 // DG_FORCE_TILE=<kernel id> overrides the choice when that entry has the
-// call's granularity (tuning and benchmarking only).
+// call's granularity (tuning and benchmarking only; a split-K entry then runs
+// with one split unless the call has a workspace).
 int forced_tile() {
   static const int id = [] {
     const char* e = std::getenv("DG_FORCE_TILE");
@@ -103,40 +128,40 @@ int64_t splits_for(const dg::KernelEntry* e, int64_t tiles, int64_t nsteps) {
   return std::max<int64_t>(ks, 1);
 }
 
-// Transposed layouts (layout != NT) take split-K 64x64 tiles for M <= 128, and
-// otherwise the 256-row tiles or 128x128 tiles by the rule below.
-Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout = DG_LAYOUT_NT) {
+int64_t tiles_of(const dg::KernelEntry* e, int64_t M, int64_t N) {
+  return ((M + e->bm - 1) / e->bm) * ((N + e->bn - 1) / e->bn);
+}
+
+Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout, bool split_ok) {
   Plan p{nullptr, 1, 0};
   const int gran = kernel_gran(sgran);
   const int64_t nsteps = (K + 127) / 128;
-  if (layout != DG_LAYOUT_NT && M <= 128) {
+  auto split_k = [&]() {
     p.e = find(dg::kClassSplitK, gran);
-    p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
-    p.ksplit = (int)splits_for(p.e, p.tiles, nsteps);
+    p.tiles = tiles_of(p.e, M, N);
+    p.ksplit = split_ok ? (int)splits_for(p.e, p.tiles, nsteps) : 1;
     return p;
-  }
+  };
+  if (layout != DG_LAYOUT_NT && M <= 128) return split_k();
   const int force = layout == DG_LAYOUT_NT ? forced_tile() : -1;
   if (force >= 0) {
     for (int i = 0; i < dg::kTableSize; ++i)
       if (dg::kTable[i].id == force && dg::kTable[i].gran == gran) p.e = &dg::kTable[i];
     if (p.e) {
-      p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
-      if (p.e->cls == dg::kClassSplitK) p.ksplit = (int)splits_for(p.e, p.tiles, nsteps);
+      p.tiles = tiles_of(p.e, M, N);
+      if (p.e->cls == dg::kClassSplitK && split_ok) p.ksplit = (int)splits_for(p.e, p.tiles, nsteps);
       return p;
     }
   }
   if (M <= 128) {
     const dg::KernelEntry* st = find(dg::kClassStream, gran);
-    const int64_t st_tiles = ((M + st->bm - 1) / st->bm) * ((N + st->bn - 1) / st->bn);
-    if (st_tiles >= 192) {
+    const int64_t st_tiles = tiles_of(st, M, N);
+    if (st_tiles >= 192 || !split_ok) {
       p.e = st;
       p.tiles = st_tiles;
       return p;
     }
-    p.e = find(dg::kClassSplitK, gran);
-    p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
-    p.ksplit = (int)splits_for(p.e, p.tiles, nsteps);
-    return p;
+    return split_k();
   }
   // 256-row tiles: the width whose tile count fills the 256 CUs best, weighed
   // by the width's own speed per CU (narrower tiles stage more bytes per
@@ -147,7 +172,7 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout = DG_LAYOUT_NT)
   for (int i = 0; i < dg::kTableSize; ++i) {
     const dg::KernelEntry* e = &dg::kTable[i];
     if (e->cls != dg::kClassBig || e->gran != gran) continue;
-    const int64_t t = ((M + e->bm - 1) / e->bm) * ((N + e->bn - 1) / e->bn);
+    const int64_t t = tiles_of(e, M, N);
     const double fill = (double)t / (double)(256 * ((t + 255) / 256));
     const double per_cu = e->bn == 256 ? 1.0 : 0.8;
     if (fill * per_cu > best) {
@@ -157,22 +182,14 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout = DG_LAYOUT_NT)
     }
   }
   p.e = big && big_tiles >= 192 ? big : find(dg::kClassTiled, gran);
-  p.tiles = ((M + p.e->bm - 1) / p.e->bm) * ((N + p.e->bn - 1) / p.e->bn);
+  p.tiles = tiles_of(p.e, M, N);
   return p;
 }
 
-void alloc_workspace(int dev) {
-  if (hipMalloc(&g_ws[dev], kWsFloats * sizeof(float)) != hipSuccess) {
-    g_ws[dev] = nullptr;
-    return;
-  }
-  if (hipMalloc(&g_counters[dev], kWsCounters * sizeof(uint32_t)) != hipSuccess ||
-      hipMemset(g_counters[dev], 0, kWsCounters * sizeof(uint32_t)) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess) {
-    (void)hipFree(g_ws[dev]);
-    g_ws[dev] = nullptr;
-    g_counters[dev] = nullptr;
-  }
+// Workspace bytes of a plan: none without a K split.
+int64_t workspace_bytes(const Plan& p) {
+  if (p.ksplit <= 1) return 0;
+  return counter_bytes(p.tiles) + p.tiles * p.ksplit * p.e->bm * p.e->bn * (int64_t)sizeof(float);
 }
 
 // One-time per-device check; returns DG_OK, DG_EUNSUPPORTED or DG_ELAUNCH.
@@ -206,7 +223,8 @@ bool overlaps(const void* p, uint64_t n, const void* q, uint64_t m) {
 }
 
 int gemm(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M, int64_t N, int64_t K,
-         int gran, int layout, int sa_rows, int fmt_a, int fmt_b, const float* bias, int act, void* stream) {
+         int gran, int layout, int sa_rows, int fmt_a, int fmt_b, const float* bias, int act, void* stream,
+         bool split_ok = false, void* ws = nullptr, int64_t ws_bytes = 0) {
   if (!a || !b || !sa || !sb || !out) return DG_EINVAL;
   if (sa_rows != gran && sa_rows != 1) return DG_EINVAL;
   if (validate_layout(M, N, layout) != DG_OK) return DG_EINVAL;
@@ -215,34 +233,39 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
     return DG_EINVAL;
   if (act != DG_ACT_NONE && act != DG_ACT_RELU && act != DG_ACT_GELU) return DG_EINVAL;
   if ((uintptr_t)bias & 3) return DG_EALIGN;
+  if (ws_bytes < 0 || (ws_bytes > 0 && !ws) || (ws && ws_bytes == 0)) return DG_EINVAL;
+  if ((uintptr_t)ws & 255) return DG_EALIGN;
   int rc = validate(M, N, K, gran);
   if (rc != DG_OK) return rc;
   if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)sa & 3) || ((uintptr_t)sb & 3) ||
       ((uintptr_t)out & 1))
     return DG_EALIGN;
+  // A workspace lets small-M shapes split K; without one nothing does.
+  Plan pl = plan(M, N, K, gran, layout, split_ok && ws_bytes > 0);
+  if (!pl.e || pl.tiles * pl.ksplit > 0x7fffffff) return DG_EINVAL;
+  const int64_t need = workspace_bytes(pl);
+  if (ws_bytes > 0 && ws_bytes < need) return DG_EINVAL;
   {
     // out is written while the inputs are read: it may overlap none of them
-    // (the inputs may overlap each other). Sizes are the logical ones, which
-    // every layout stores in the same number of bytes.
+    // (the inputs may overlap each other), nor the workspace. Sizes are the
+    // logical ones, which every layout stores in the same number of bytes.
     const uint64_t nks = (uint64_t)(K / gran);
     const uint64_t sa_rows_n = sa_rows == 1 ? (uint64_t)M : (uint64_t)((M + gran - 1) / gran);
     const uint64_t ob = 2ull * (uint64_t)M * (uint64_t)N;
-    if (overlaps(out, ob, a, (uint64_t)M * (uint64_t)K) || overlaps(out, ob, b, (uint64_t)N * (uint64_t)K) ||
-        overlaps(out, ob, sa, 4ull * sa_rows_n * nks) ||
-        overlaps(out, ob, sb, 4ull * (uint64_t)((N + gran - 1) / gran) * nks) ||
-        overlaps(out, ob, bias, bias ? 4ull * (uint64_t)N : 0))
+    const uint64_t ab = (uint64_t)M * (uint64_t)K, bb = (uint64_t)N * (uint64_t)K;
+    const uint64_t sab = 4ull * sa_rows_n * nks, sbb = 4ull * (uint64_t)((N + gran - 1) / gran) * nks;
+    const uint64_t biasb = bias ? 4ull * (uint64_t)N : 0, wsb = (uint64_t)ws_bytes;
+    if (overlaps(out, ob, a, ab) || overlaps(out, ob, b, bb) || overlaps(out, ob, sa, sab) ||
+        overlaps(out, ob, sb, sbb) || overlaps(out, ob, bias, biasb))
+      return DG_EINVAL;
+    if (overlaps(ws, wsb, a, ab) || overlaps(ws, wsb, b, bb) || overlaps(ws, wsb, sa, sab) ||
+        overlaps(ws, wsb, sb, sbb) || overlaps(ws, wsb, bias, biasb) || overlaps(ws, wsb, out, ob))
       return DG_EINVAL;
   }
-  Plan pl = plan(M, N, K, gran, layout);
-  if (!pl.e || pl.tiles * pl.ksplit > 0x7fffffff) return DG_EINVAL;
 
   int dev = 0;
   rc = device_ready(&dev);
   if (rc != DG_OK) return rc;
-  if (pl.ksplit > 1) {
-    std::call_once(g_ws_once[dev], alloc_workspace, dev);
-    if (!g_ws[dev]) pl.ksplit = 1;  // no workspace: the same kernel over the whole K
-  }
   const dg::KernelEntry* e = pl.e;
 
   dg::GemmArgs p;
@@ -261,17 +284,17 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   p.layout = layout;
   p.vec_store = (((uintptr_t)out & 15) == 0 && N % 8 == 0) ? 1 : 0;
   p.ksplit = pl.ksplit;
-  p.ws = pl.ksplit > 1 ? g_ws[dev] : nullptr;
-  p.counters = pl.ksplit > 1 ? g_counters[dev] : nullptr;
+  p.counters = pl.ksplit > 1 ? static_cast<unsigned long long*>(ws) : nullptr;
+  p.ws = pl.ksplit > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counter_bytes(pl.tiles)) : nullptr;
+  p.epoch = pl.ksplit > 1 ? next_epoch() : 0;
   p.bias = bias;
   p.act = act;
   if (log_enabled())
     std::fprintf(stderr,
                  "dg_gemm_fp8 M=%lld N=%lld K=%lld g=%d layout=%d sa_rows=%d fmt=%d,%d bias=%d act=%d -> kernel %d "
-                 "(%dx%d, %d stages, %d waves) ksplit %d grid %lld\n",
+                 "(%dx%d, %d stages, %d waves) ksplit %d grid %lld workspace %lld\n",
                  (long long)M, (long long)N, (long long)K, gran, layout, sa_rows, fmt_a, fmt_b, bias ? 1 : 0, act, e->id,
-                 e->bm,
-                 e->bn, e->stages, e->waves, pl.ksplit, (long long)(pl.tiles * pl.ksplit));
+                 e->bm, e->bn, e->stages, e->waves, pl.ksplit, (long long)(pl.tiles * pl.ksplit), (long long)need);
   t_last_hip = layout == DG_LAYOUT_NT ? e->launch(p, static_cast<hipStream_t>(stream))
                                       : dg::launch_layout(e->id, p, static_cast<hipStream_t>(stream));
   return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
@@ -322,9 +345,10 @@ const char* dg_strerror(int code) {
     case DG_EINVAL:
       return "invalid argument (null pointer, bad dimension, K not a multiple of gran, gran not 64/128/256, "
              "sa_rows neither gran nor 1, a format code other than DG_FMT_E4M3/DG_FMT_E5M2, an unknown "
-             "activation or layout, a transposed operand whose stored row length is not a multiple of 16, or an "
-             "output that overlaps an input)";
-    case DG_EALIGN: return "misaligned pointer (a, b need 16 bytes; sa, sb 4 bytes; out 2 bytes)";
+             "activation or layout, a transposed operand whose stored row length is not a multiple of 16, an "
+             "output or workspace that overlaps another argument, or a workspace smaller than the plan needs)";
+    case DG_EALIGN:
+      return "misaligned pointer (a, b need 16 bytes; sa, sb, bias 4 bytes; out 2 bytes; workspace 256 bytes)";
     case DG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
     case DG_ELAUNCH:
       std::snprintf(t_msg, sizeof t_msg, "HIP error %d: %s", (int)t_last_hip, hipGetErrorString(t_last_hip));
@@ -333,12 +357,16 @@ const char* dg_strerror(int code) {
   }
 }
 
-int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, dg_tile_info* info) {
+}  // extern "C"
+
+namespace {
+
+int query(int64_t M, int64_t N, int64_t K, int gran, int layout, bool split_ok, dg_tile_info* info) {
   if (!info) return DG_EINVAL;
   int rc = validate(M, N, K, gran);
   if (rc != DG_OK) return rc;
   if ((rc = validate_layout(M, N, layout)) != DG_OK) return rc;
-  const Plan p = plan(M, N, K, gran, layout);
+  const Plan p = plan(M, N, K, gran, layout, split_ok);
   if (!p.e || p.tiles * p.ksplit > 0x7fffffff) return DG_EINVAL;
   info->kernel_id = p.e->id;
   info->bm = p.e->bm;
@@ -348,11 +376,31 @@ int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, 
   info->waves = p.e->waves;
   info->ksplit = p.ksplit;
   info->grid = p.tiles * p.ksplit;
+  info->workspace_bytes = workspace_bytes(p);
   return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, dg_tile_info* info) {
+  return query(M, N, K, gran, layout, false, info);
+}
+
+int dg_query_tile_ws(int64_t M, int64_t N, int64_t K, int gran, int layout, dg_tile_info* info) {
+  return query(M, N, K, gran, layout, true, info);
 }
 
 int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info) {
   return dg_query_tile_layout(M, N, K, gran, DG_LAYOUT_NT, info);
+}
+
+int dg_gemm_fp8_ws(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M, int64_t N,
+                   int64_t K, int gran, int layout, int sa_rows, int fmt_a, int fmt_b, const float* bias, int act,
+                   void* workspace, int64_t workspace_bytes, void* stream) {
+  return gemm(a, b, sa, sb, out, M, N, K, gran, layout, sa_rows, fmt_a, fmt_b, bias, act, stream, true, workspace,
+              workspace_bytes);
 }
 
 int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,

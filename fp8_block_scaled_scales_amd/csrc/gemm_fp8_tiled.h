@@ -48,10 +48,11 @@ __device__ __forceinline__ void wait_steps(int steps) {
 }
 
 // Split-K: ksplit workgroups share one output tile, each covering a contiguous
-// range of 128-byte K steps. Each writes its FP32 partial tile to ws; the
-// last to arrive (per-tile arrival counter) adds the partials in split order
-// (so the result does not depend on which arrives last), resets the counter
-// and writes the BF16 tile. ksplit == 1 skips all of this.
+// range of 128-byte K steps. Each writes its FP32 partial tile to ws (the
+// caller's workspace); the last to arrive (per-tile arrival counter, tagged
+// with the call's epoch) adds the partials in split order (so the result does
+// not depend on which arrives last) and writes the BF16 tile. ksplit == 1
+// skips all of this.
 //
 // G is the K segment contracted before each promotion; the scale blocks are
 // sg x sg with sg = G << sshift (g = 256 runs G = 128 with one factor per two
@@ -62,8 +63,8 @@ template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool S
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ b, const float* __restrict__ sa,
     const float* __restrict__ sb, uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
-    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, uint32_t* __restrict__ counters, int sshift,
-    const float* __restrict__ bias, int relu) {
+    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, unsigned long long* __restrict__ counters,
+    unsigned long long epoch, int sshift, const float* __restrict__ bias, int relu) {
   constexpr int NWAVES = WM * WN;
   constexpr int NT = 64 * NWAVES;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
@@ -233,13 +234,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     // the tile's slice of ws, so each store and load below moves 1 KB
     // contiguous per wave.
     //
-    // Publication without cache-wide write-back or invalidate: the partials
-    // are written and read with device-scope (sc1) buffer stores and loads,
-    // which go to the point of coherence shared by all XCDs (the per-XCD L2s
-    // are not coherent with each other). The stores are waited for before
-    // the workgroup arrives at the tile's counter, and the last arrival's
-    // loads are issued only after its arrival returned, so it reads every
-    // split's finished partial.
+    // Publication (HIP memory model, agent scope): every wave stores its part
+    // of the partial, then a release fence at agent scope orders those stores
+    // before the workgroup's arrival; the arrival is a read-modify-write of
+    // the tile's counter, and the workgroup that completes the count takes an
+    // acquire fence at agent scope before reading the other partials. The
+    // per-XCD L2s are not coherent with each other; the fences write back and
+    // invalidate what these need. The stores and loads also carry the
+    // device-scope cache policy (sc1), so the partials go to and come from the
+    // coherence point instead of sitting dirty in one XCD's L2.
+    //
+    // The counter holds (epoch << 16) | arrivals. An arrival that finds
+    // another call's tag counts from zero, so a workspace needs no clearing
+    // and a launch that never finished leaves nothing a later call counts.
     constexpr int CPOL_SC1 = 16;  // device-scope coherence bit of the buffer instructions
     constexpr int TILE_F = BM * BN, WAVE_F = TM * TN * 16 * 64;
     const int tile = tmi * tiles_n + tni;
@@ -257,12 +264,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
                                                  lane_off + (uint32_t)(((i * TN + j) * 4 + c) * 256 * 4),
                                                  (uint32_t)ks * TILE_F * 4, CPOL_SC1);
         }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores have completed
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's partial stores, before the arrival
     __syncthreads();
     __shared__ int last;
-    if (threadIdx.x == 0)
-      last = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (uint32_t)(ksplit - 1);
+    if (threadIdx.x == 0) {
+      unsigned long long old = __hip_atomic_load(&counters[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned long long now;
+      do {
+        now = (old >> 16) == epoch ? old + 1 : ((epoch << 16) | 1ull);
+      } while (!__hip_atomic_compare_exchange_weak(&counters[tile], &old, now, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT));
+      const bool done = (now & 0xFFFFull) == (unsigned long long)ksplit;
+      if (done) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every split's stores are visible
+      last = done;
+    }
     __syncthreads();
     if (!last) return;
     // Sum in split order 0, 1, ..., ksplit-1 (this split's own partial from
@@ -348,11 +363,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
       for (int t = 0; t < 8 && gc + t < N; ++t) dst[t] = (uint16_t)((uint32_t)val[t >> 1] >> (16 * (t & 1)));
     }
   }
-  // The reducer returns the tile's arrival counter to zero for the next call.
-  // It is issued last: a device-coherent store ahead of the output stores
-  // holds them up.
-  if (SPLIT && ksplit > 1 && threadIdx.x == 0)
-    __hip_atomic_store(&counters[tmi * tiles_n + tni], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- launch table -------------------------------------------------------------
@@ -364,7 +374,7 @@ static hipError_t launch_tiled_fa(const GemmArgs& p, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, ROWA, LAYOUT>),
                      dim3(tiles_m * tiles_n * p.ksplit), dim3(64 * WM * WN), 0, stream, p.a, p.b, p.sa, p.sb, p.out,
                      (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.ksplit, p.ws, p.counters,
-                     p.sshift, p.bias, p.act == 1 ? 1 : 0);
+                     p.epoch, p.sshift, p.bias, p.act == 1 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -17,26 +17,20 @@
  * for a given (M, N, K, g) and device.
  *
  * All pointers are device pointers (memory the caller allocated, e.g. PyTorch
- * tensors). The library keeps no caller pointer after a call returns and
- * allocates nothing per call. Calls are asynchronous on `stream` (a
- * hipStream_t; NULL is the default stream); faults during execution surface
- * at the caller's next synchronisation. No call prints unless the environment
- * sets DG_LOG=1, and no call exits or throws.
+ * tensors). The library keeps no caller pointer after a call returns,
+ * allocates no device memory at all, and the GEMM calls below need no
+ * workspace: every K reduction of the default tile choice, small M included,
+ * happens inside one workgroup. dg_gemm_fp8_ws is the one call that splits K
+ * over several workgroups, through a workspace the caller passes in. Calls
+ * are asynchronous on `stream` (a hipStream_t; NULL is the default stream);
+ * faults during execution surface at the caller's next synchronisation. No
+ * call prints unless the environment sets DG_LOG=1, and no call exits or
+ * throws.
  *
- * Split-K workspace: a GEMM whose tile-table entry splits K over several
- * workgroups (dg_query_tile reports ksplit > 1: small M with few output
- * tiles) adds its FP32 partial tiles through a workspace the library
- * allocates once per device, on the first such call (32 MB of partial tiles
- * and 64 Ki arrival counters, zeroed then; each call leaves its counters at
- * zero), and keeps until the process ends. So the first such call on a
- * device must not be made under stream capture (later ones may), and such
- * calls must not run concurrently on one device (on two streams, or from two
- * threads without ordering): they share the workspace. If the allocation
- * fails the call runs the same tile over the whole K without a workspace.
- *
- * Thread safety: calls may come from several host threads (subject to the
- * split-K rule above). The one-time per-device check (architecture must be
- * gfx950) and the workspace allocation run under std::call_once.
+ * Thread safety: calls may come from several host threads and run
+ * concurrently on any streams (dg_gemm_fp8_ws: each concurrent call with its
+ * own workspace). The one-time per-device check (the architecture must be
+ * gfx950) runs under std::call_once.
  */
 #ifndef DG_H
 #define DG_H
@@ -47,14 +41,23 @@
 extern "C" {
 #endif
 
-/* Status codes. */
+/* Status codes. The split follows the pitfalls article (GPU GEMM history and
+ * pitfalls, §5.4), which separates failures a caller can recover from (an
+ * argument to fix and retry) from those it cannot (a failed launch or a
+ * device fault, after which the caller should stop using the device): the
+ * first three are the former, reported before any HIP call with nothing
+ * launched; DG_ELAUNCH is the latter, with the HIP error kept for
+ * dg_strerror. */
 #define DG_OK 0
 #define DG_EINVAL (-1)       /* bad argument; nothing was launched (recoverable) */
-#define DG_EALIGN (-2)       /* misaligned pointer; nothing was launched */
-#define DG_EUNSUPPORTED (-3) /* device is not gfx950, or an unsupported option */
-#define DG_ELAUNCH (-4)      /* a HIP call failed; dg_strerror() gives its text */
+#define DG_EALIGN (-2)       /* misaligned pointer; nothing was launched (recoverable) */
+#define DG_EUNSUPPORTED (-3) /* device is not gfx950; nothing was launched */
+#define DG_ELAUNCH (-4)      /* a HIP call failed (not recoverable); dg_strerror() gives its text */
 
-#define DG_VERSION 100 /* 1.0.0 */
+/* Version of this header and library: 2.0.0 (dg_tile_info gained
+ * workspace_bytes; dg_gemm_fp8_ws and dg_query_tile_ws were added; no call
+ * but dg_gemm_fp8_ws splits K over workgroups). */
+#define DG_VERSION 200
 
 /* Largest accepted dimension, 2^24 - 256: a 256-row tile of K bytes per row
  * (256 * K) then stays below 2^32 bytes, the reach of a buffer descriptor,
@@ -172,16 +175,17 @@ int dg_gemm_fp8_nt_ex(const void* a, const void* b, const float* sa, const float
  * The result is the same product, out[i,j] as in dg_gemm_fp8_nt_epi. A stored
  * [K,M] needs M % 16 == 0 and B stored [K,N] needs N % 16 == 0 (DG_EINVAL
  * otherwise); a and b 16-byte aligned as before. DG_LAYOUT_NT is
- * dg_gemm_fp8_nt_epi bit for bit. The other layouts run the tiled classes
- * (split-K 64x64 tiles for M <= 128, 128x128 tiles otherwise; see
- * dg_query_tile_layout), which the pages' remark that NT is the fastest layout
- * holds for here too. Per-row A factors are NT only (dg_gemm_fp8_nt_ex).
+ * dg_gemm_fp8_nt_epi bit for bit. dg_query_tile_layout names the tile a
+ * layout runs. Per-row A factors are NT only (dg_gemm_fp8_nt_ex).
  */
 int dg_gemm_fp8_layout(const void* a, const void* b, const float* sa, const float* sb, void* out,
                        int64_t M, int64_t N, int64_t K, int gran, int layout, int fmt_a, int fmt_b,
                        const float* bias, int act, void* stream);
 
-/* The tile-table entry a call with these sizes would use. */
+/* The tile-table entry a call with these sizes would use. DeepGEMM实战 §6
+ * advises keeping a record of which configuration ran for which shape; this
+ * is that record, from the same host logic the calls use, so a caller can log
+ * it next to its timings (DG_LOG=1 prints it per call). */
 typedef struct dg_tile_info {
   int kernel_id; /* identifier of the precompiled table entry */
   int bm, bn;    /* workgroup output tile */
@@ -190,12 +194,14 @@ typedef struct dg_tile_info {
   int waves;     /* waves per workgroup */
   int ksplit;    /* workgroups sharing one output tile, each over a K range (1 = none) */
   int64_t grid;  /* workgroups launched */
+  int64_t workspace_bytes; /* workspace dg_gemm_fp8_ws needs for this plan (0: none) */
 } dg_tile_info;
 
 /*
  * dg_query_tile - fill *info with the tile-table entry dg_gemm_fp8_nt would
  * launch for (M, N, K, gran). Pure host logic, no HIP call. Returns DG_OK or
- * DG_EINVAL for arguments dg_gemm_fp8_nt would reject.
+ * DG_EINVAL for arguments dg_gemm_fp8_nt would reject. ksplit is always 1
+ * and workspace_bytes 0: this call never splits K over workgroups.
  */
 int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info);
 
@@ -203,6 +209,49 @@ int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info)
  * would use (DG_EINVAL for a layout or a transposed row length that call
  * would reject). */
 int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, dg_tile_info* info);
+
+/*
+ * dg_gemm_fp8_ws - the GEMM with a caller-owned workspace that lets small-M
+ * shapes with few output tiles split K over several workgroups.
+ *
+ * DeepGEMM实战 §3.2 accumulates K in segments that are summed separately and
+ * then added; §5.3 names too little parallelism as what holds back small
+ * shapes. With M <= 128 and too few output tiles to occupy the GPU, this call
+ * gives each 64x64 tile ksplit workgroups, each over a contiguous range of K
+ * segments; each writes its FP32 partial tile to the workspace, and the last
+ * to arrive adds all ksplit partials in split order (so the result does not
+ * depend on arrival order) and writes the BF16 tile. Every other shape runs
+ * exactly what dg_gemm_fp8_layout / dg_gemm_fp8_nt_ex runs, bit for bit, and
+ * leaves the workspace untouched.
+ *
+ *   a, b, sa, sb, out, M, N, K, gran, layout, fmt_a, fmt_b, bias, act
+ *        as dg_gemm_fp8_layout (sa_rows = 1 with DG_LAYOUT_NT only, as
+ *        dg_gemm_fp8_nt_ex).
+ *   sa_rows   gran or 1, as dg_gemm_fp8_nt_ex.
+ *   workspace device memory of at least workspace_bytes bytes, 256-byte
+ *        aligned, owned by the caller, or NULL with workspace_bytes 0 (then no
+ *        shape splits K). It must not overlap any other argument. Its
+ *        contents need no initialisation and are scratch between calls: every
+ *        call tags its arrival counters with a fresh per-call value, so a
+ *        launch that never finished leaves nothing a later call reads.
+ *   workspace_bytes  size of workspace; must be 0 or at least the
+ *        workspace_bytes dg_query_tile_ws reports for the shape (DG_EINVAL
+ *        otherwise).
+ *
+ * Concurrency: two calls that may run at the same time (different streams,
+ * or a graph replay beside an eager call) must use different workspaces;
+ * calls on one stream may share one. The partials are published with
+ * agent-scope release/acquire ordering (HIP memory model), so any split may
+ * run on any XCD. Returns the status codes of dg_gemm_fp8_layout.
+ */
+int dg_gemm_fp8_ws(const void* a, const void* b, const float* sa, const float* sb, void* out,
+                   int64_t M, int64_t N, int64_t K, int gran, int layout, int sa_rows, int fmt_a, int fmt_b,
+                   const float* bias, int act, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* The plan dg_gemm_fp8_ws runs for these sizes, with the workspace it needs
+ * (info->workspace_bytes; 0 when the plan does not split K). Pure host
+ * logic; DG_EINVAL for arguments dg_gemm_fp8_ws would reject. */
+int dg_query_tile_ws(int64_t M, int64_t N, int64_t K, int gran, int layout, dg_tile_info* info);
 
 /*
  * dg_quantize_e4m3_blocks - block quantisation FP32 -> E4M3FN, the step that
@@ -249,10 +298,14 @@ int dg_quantize_fp8_blocks(const float* x, int64_t rows, int64_t cols, int gran,
 int dg_quantize_fp8_rows(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q,
                          float* scales, void* stream);
 
-/* Text for a status code (for DG_ELAUNCH: the last HIP error on this thread). */
+/* Text for a status code (for DG_ELAUNCH: the last HIP error on this
+ * thread), so a caller can log which class of failure (the pitfalls article
+ * §5.4: recoverable or not) it met. The string is static, or thread-local for
+ * DG_ELAUNCH; it stays valid until this thread's next call. */
 const char* dg_strerror(int code);
 
-/* DG_VERSION of the loaded library. */
+/* DG_VERSION of the loaded library, for the same per-run record as
+ * dg_query_tile (DeepGEMM实战 §6: log which build and configuration ran). */
 int dg_version(void);
 
 #ifdef __cplusplus

@@ -37,3 +37,35 @@ def sample_indices(n: int, count: int, seed: int) -> np.ndarray:
     edge = list(range(min(8, n))) + list(range(max(0, n - 8), n))
     rest = rng.choice(n, size=min(n, count), replace=False).tolist()
     return np.array(sorted(set(edge + rest)), dtype=np.int64)
+
+
+def fp32_promotion_emulation(a_dec, b_dec, sa, sb, g: int, rows, cols) -> np.ndarray:
+    """What an ideal FP32 implementation of the method gives on outputs rows x
+    cols: each g-segment partial exact (a float64 product of decoded operands;
+    every such sum is exact in float64) then rounded to FP32, the factor
+    product sa*sb rounded to FP32, and acc = fma(P, s, acc) in FP32 over the
+    segments in order. The single rounding of the FMA is emulated in float64
+    (P*s is exact there; the add then rounds once in float64 and once to FP32).
+
+    Diagnostic only: it bounds how close to the FP64 reference an FP32
+    accumulator can be expected to stay, which is what the GPU's share of
+    outputs within one BF16 ulp is compared with."""
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    A = np.asarray(a_dec, np.float64)[rows]
+    B = np.asarray(b_dec, np.float64)[cols]
+    K = A.shape[1]
+    acc = np.zeros((rows.size, cols.size), np.float32)
+    for kb in range(K // g):
+        seg = slice(kb * g, (kb + 1) * g)
+        P = (A[:, seg] @ B[:, seg].T).astype(np.float32)
+        s = (np.asarray(sa, np.float32)[rows // g, kb][:, None] * np.asarray(sb, np.float32)[cols // g, kb][None, :])
+        acc = (P.astype(np.float64) * s.astype(np.float64) + acc.astype(np.float64)).astype(np.float32)
+    return acc.astype(np.float64)
+
+
+def within_one_ulp(got, ref) -> float:
+    """Share of outputs within one BF16 ulp of bf16(ref) (ulp = |bf16(ref)| * 2^-8)."""
+    bf_ref = bf16_bits_to_f64(f32_to_bf16_bits(np.asarray(ref, np.float64).astype(np.float32)))
+    ulp = np.abs(bf_ref) * 2.0 ** -8 + 1e-30
+    return float(np.mean(np.abs(np.asarray(got, np.float64) - bf_ref) <= ulp))

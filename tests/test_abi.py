@@ -27,8 +27,25 @@ def _declared_functions():
 
 def test_header_declares_the_api():
     names = _declared_functions()
-    for f in ("dg_gemm_fp8_nt", "dg_query_tile", "dg_strerror", "dg_version"):
+    for f in ("dg_gemm_fp8_nt", "dg_query_tile", "dg_strerror", "dg_version", "dg_gemm_fp8_ws", "dg_query_tile_ws"):
         assert f in names
+
+
+def test_tile_info_layout_matches_header(dg):
+    # the ctypes mirror of dg_tile_info: same fields, same order, same size as the C struct
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct dg_tile_info \{(.*?)\} dg_tile_info;", text, flags=re.S).group(1)
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        ctype, names = decl.split(None, 1)
+        fields += [(n.strip(), ctype) for n in names.split(",")]
+    assert [f for f, _ in fields] == [f for f, _ in dg.dg_tile_info._fields_]
+    size = {"int": 4, "int64_t": 8}
+    assert all(ctypes.sizeof(t) == size[c] for (_, c), (_, t) in zip(fields, dg.dg_tile_info._fields_))
+    assert ctypes.sizeof(dg.dg_tile_info) == 48
 
 
 def test_library_exports_every_declared_symbol(dg):
@@ -150,9 +167,11 @@ def test_layout_rejects(dg, layout, M, N, want):
                                                  (1008, 3008, 512, 64, 2, (128, 128)), (128, 512, 1024, 256, 3, (64, 64)),
                                                  (2000, 4000, 1024, 128, 1, (256, 128)), (3584, 3584, 512, 256, 2, (256, 256))])
 def test_layout_tile_choice(dg, M, N, K, g, layout, tile):
-    # transposed layouts: split-K 64x64 for M <= 128, else the 256-row tiles 256 or 128 wide or 128x128
+    # transposed layouts: 64x64 tiles over the whole K for M <= 128, else the 256-row tiles 256 or 128 wide or
+    # 128x128; without a workspace nothing splits K
     t = dg.dg_query_tile(M, N, K, g, layout)
     assert (t["bm"], t["bn"]) == tile
+    assert t["ksplit"] == 1 and t["workspace_bytes"] == 0
     assert dg.dg_query_tile(M, N, K, g, 0) == dg.dg_query_tile(M, N, K, g)
 
 
@@ -213,7 +232,8 @@ def test_python_binding_rejects_bad_tensors(dg):
 @pytest.mark.parametrize("M,N,K,g,cls", [
     (256, 256, 256, 128, (128, 128, 1)),      # too few tiles for 256-row tiles
     (64, 4096, 7168, 128, (32, 32, 1)),       # small M, 256 streaming tiles
-    (64, 512, 7168, 128, (64, 64, 14)),       # small M, few tiles: split-K
+    (64, 512, 7168, 128, (32, 32, 1)),        # small M, few tiles: still 32x32 over the whole K (no workspace)
+    (8, 300, 2048, 128, (32, 32, 1)),
     (4096, 7168, 2048, 128, (256, 256, 1)),   # 448 tiles of 256x256 (1.75 rounds) over 512 of 256x128
     (8192, 8192, 8192, 128, (256, 256, 1)),   # 1024 tiles of 256x256
     (2000, 4000, 16384, 64, (256, 128, 1)),   # 256 tiles of 256x128 vs 128 of 256x256
@@ -223,6 +243,64 @@ def test_python_binding_rejects_bad_tensors(dg):
 def test_query_tile_choice(dg, M, N, K, g, cls):
     t = dg.dg_query_tile(M, N, K, g)
     assert (t["bm"], t["bn"], t["ksplit"]) == cls, t
+    assert t["workspace_bytes"] == 0
+
+
+# dg_gemm_fp8_ws's plan: small M with fewer than 192 tiles of 32x32 (or any
+# transposed small-M shape) splits K over 64x64 tiles; everything else is the
+# plan without a workspace, which needs no workspace.
+@pytest.mark.parametrize("M,N,K,g,layout,cls", [
+    (64, 512, 7168, 128, 0, (64, 64, 14)),     # 8 tiles x 14 splits (steps/4 caps at 14)
+    (8, 300, 2048, 128, 0, (64, 64, 4)),       # 5 tiles, 16 steps: 4 splits of 4 steps
+    (64, 4096, 7168, 128, 0, (32, 32, 1)),     # 256 streaming tiles: no split
+    (64, 4096, 7168, 128, 1, (64, 64, 4)),     # transposed B: 64 tiles x 4
+    (8192, 8192, 8192, 128, 0, (256, 256, 1)),
+])
+def test_query_tile_ws_choice(dg, M, N, K, g, layout, cls):
+    t = dg.dg_query_tile(M, N, K, g, layout, workspace=True)
+    assert (t["bm"], t["bn"], t["ksplit"]) == cls, t
+    tiles = -(-M // t["bm"]) * -(-N // t["bn"])
+    assert t["grid"] == tiles * t["ksplit"]
+    if t["ksplit"] == 1:
+        assert t["workspace_bytes"] == 0
+        assert t == dg.dg_query_tile(M, N, K, g, layout)
+    else:
+        # 8-byte counters per tile rounded up to 256 bytes, then FP32 partial tiles
+        assert t["workspace_bytes"] == -(-8 * tiles // 256) * 256 + 4 * tiles * t["ksplit"] * 64 * 64
+
+
+# Fake addresses 2^40 apart for the workspace call, so that only the
+# overlap a case plants can trigger the overlap rule.
+WA, WB, WSA, WSB, WOUT, WS = (i << 40 for i in range(1, 7))
+
+
+def _ws_call(dg, ws=WS, ws_bytes=4 << 20, M=64, N=512, K=7168, g=128, layout=0, sa_rows=None, out=WOUT, a=WA):
+    return dg.lib.dg_gemm_fp8_ws(a, WB, WSA, WSB, out, M, N, K, g, layout, g if sa_rows is None else sa_rows, 0, 0,
+                                 None, 0, ws, ws_bytes, None)
+
+
+def test_ws_fake_addresses_do_not_overlap(dg):
+    # the baseline case passes every argument check; it would then need a GPU,
+    # so only its query is made here
+    need = dg.dg_query_tile(64, 512, 7168, 128, 0, workspace=True)["workspace_bytes"]
+    assert 0 < need <= 4 << 20
+    assert max(64 * 7168, 512 * 7168, 2 * 64 * 512, 4 << 20) < 1 << 40
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(ws=None, ws_bytes=4096), "DG_EINVAL"),            # a size without a buffer
+    (dict(ws_bytes=0), "DG_EINVAL"),                        # a buffer without a size
+    (dict(ws_bytes=-256), "DG_EINVAL"),
+    (dict(ws=WS + 16), "DG_EALIGN"),                        # 256-byte alignment
+    (dict(ws_bytes=4096), "DG_EINVAL"),                     # smaller than the 64x512x7168 plan needs
+    (dict(ws=WOUT - 0x1000), "DG_EINVAL"),                  # overlaps out
+    (dict(ws=WA + 0x1000), "DG_EINVAL"),                    # overlaps a
+    (dict(out=WS + (1 << 19)), "DG_EINVAL"),                # out inside the workspace
+    (dict(layout=1, sa_rows=1), "DG_EINVAL"),               # per-row A factors are NT only
+    (dict(a=WA + 8), "DG_EALIGN"),
+])
+def test_ws_rejects(dg, kw, want):
+    assert _ws_call(dg, **kw) == getattr(dg, want)
 
 
 # The output may overlap no input (the inputs may overlap each other): each

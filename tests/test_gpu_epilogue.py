@@ -22,7 +22,7 @@ NONE, RELU, GELU = 0, 1, 2
 
 SHAPES = [
     (64, 4096, 1024, 128, (32, 32)),     # streaming
-    (64, 520, 2048, 128, (64, 64)),      # split-K
+    (64, 520, 2048, 128, (32, 32)),      # streaming, few tiles
     (1000, 3000, 512, 64, (128, 128)),   # tiled
     (4000, 4000, 768, 128, (256, 256)),  # 256-row tiles
     (3583, 3585, 512, 128, (256, 256)),

@@ -55,8 +55,8 @@ def _operands(M, N, K, g, fa, fb, seed):
 SHAPES = [
     (64, 4096, 1024, 128, (32, 32)),     # streaming
     (64, 4096, 1536, 256, (32, 32)),
-    (64, 520, 2048, 256, (64, 64)),      # split-K
-    (100, 520, 1088, 64, (64, 64)),
+    (64, 520, 2048, 256, (32, 32)),      # streaming, few tiles
+    (100, 520, 1088, 64, (32, 32)),
     (1000, 3000, 512, 256, (128, 128)),  # tiled
     (4000, 4000, 768, 256, (256, 256)),  # 256-row tiles
     (3583, 3585, 512, 256, (256, 256)),

@@ -3,7 +3,7 @@ CPU oracle.
 
 DeepGEMM实战 §3.3: A and B may each be stored transposed ([K,M], [K,N]) and are
 read that way. Every layout runs on shapes of every class the transposed
-layouts use (split-K 64x64 for M <= 128; the 256-row tiles 256 and 128
+layouts use (64x64 over the whole K for M <= 128; the 256-row tiles 256 and 128
 wide, with 16x16x128 and 32x32x64 fragments; 128x128), with ragged M and N
 (multiples of 16), K % 128 == 64 at g = 64, and g = 256. Bars: the
 elementwise tolerance against the oracle's layout reference; bit for bit
@@ -26,7 +26,7 @@ TRANSPOSED = [NN, TT, TN]
 
 # (M, N, K, g, expected tile): ragged M, N (multiples of 16)
 SHAPES = [
-    (64, 4096, 1024, 128, (64, 64)),    # split-K
+    (64, 4096, 1024, 128, (64, 64)),    # 64x64 over the whole K
     (96, 528, 1088, 64, (64, 64)),
     (128, 512, 1024, 256, (64, 64)),
     (1008, 3008, 512, 128, (128, 128)),  # tiled

@@ -4,7 +4,8 @@ DG_MAX_DIM = 2^24 - 256 bounds M, N and K. At K = DG_MAX_DIM a 256-row tile
 covers 256 * K = 2^32 - 65536 bytes, the edge of what a buffer descriptor
 reaches, so these cases check that no tile's byte range or offset wraps:
 - K = DG_MAX_DIM on the 256x128 tiles (g = 128 and 64; NT, TN and TT), the
-  32x32 streaming class and the split-K class (M = 64, N = 4096);
+  32x32 streaming class, the 64x64 class over the whole K, and the split-K
+  class of dg_gemm_fp8_ws (M = 64, N = 4096);
 - M = DG_MAX_DIM and N = DG_MAX_DIM (K = 256) on the 256x256 tiles, NT and a
   transposed A stored [K, M];
 - the g x g and 1 x g quantisers with rows or cols = DG_MAX_DIM, sampled
@@ -72,21 +73,26 @@ def _logical_rows(stored, idx, transposed):
     return stored.index_select(0, t).cpu().numpy()
 
 
-def _check_long_k(pool, M, N, g, layout, tile):
+def _check_long_k(pool, M, N, g, layout, tile, ws=False):
     import torch
 
     import fp8_block_scaled_scales_amd as dg
 
     K = K_MAX
-    t = dg.dg_query_tile(M, N, K, g, layout)
+    t = dg.dg_query_tile(M, N, K, g, layout, workspace=ws)
     assert (t["bm"], t["bn"]) == tile, t
+    assert (t["ksplit"] > 1) == ws, t
     a_st = pool[:M * K].view(K, M) if layout & 2 else pool[:M * K].view(M, K)
     b_st = pool[M * K:(M + N) * K].view(K, N) if layout & 1 else pool[M * K:(M + N) * K].view(N, K)
     fa, fb = _kfactors(40 + g + layout, K // g), _kfactors(41 + g + layout, K // g)
     sa = torch.from_numpy(np.tile(fa, ((M + g - 1) // g, 1))).to("cuda:0")
     sb = torch.from_numpy(np.tile(fb, ((N + g - 1) // g, 1))).to("cuda:0")
-    say("max K: M=%d N=%d K=%d g=%d layout=%d tile=%s" % (M, N, K, g, layout, tile))
-    out = dg.dg_gemm_fp8_layout(a_st, b_st, sa, sb, gran=g, layout=layout)
+    say("max K: M=%d N=%d K=%d g=%d layout=%d tile=%s ksplit=%d" % (M, N, K, g, layout, tile, t["ksplit"]))
+    if ws:
+        out = dg.dg_gemm_fp8_ws(a_st, b_st, sa, sb, gran=g, layout=layout,
+                                workspace=dg.dg_workspace(M, N, K, g, layout))
+    else:
+        out = dg.dg_gemm_fp8_layout(a_st, b_st, sa, sb, gran=g, layout=layout)
     torch.cuda.synchronize()
     rows = np.unique(np.array([0, 1, tile[0] - 1, min(tile[0], M - 1), M // 2 + 3, M - 2, M - 1]))
     cols = np.unique(np.array([0, 1, tile[1] - 1, min(tile[1], N - 1), N // 2 + 5, N - 2, N - 1]))
@@ -105,9 +111,9 @@ def test_max_k_256x128_tiles(pool, g, layout):
     _check_long_k(pool, 2048, 3072, g, layout, (256, 128))
 
 
-@pytest.mark.parametrize("layout,tile", [(0, (32, 32)), (3, (64, 64))])
-def test_max_k_small_m(pool, layout, tile):
-    _check_long_k(pool, 64, 4096, 128, layout, tile)
+@pytest.mark.parametrize("layout,tile,ws", [(0, (32, 32), False), (3, (64, 64), False), (3, (64, 64), True)])
+def test_max_k_small_m(pool, layout, tile, ws):
+    _check_long_k(pool, 64, 4096, 128, layout, tile, ws)
 
 
 @pytest.mark.parametrize("big_m,layout", [(True, 0), (True, 2), (False, 0)])

@@ -27,8 +27,8 @@ SHAPES = [
     (64, 4096, 1024, 128, (32, 32)),     # streaming
     (100, 4096, 1088, 64, (32, 32)),
     (64, 4096, 1536, 256, (32, 32)),
-    (64, 520, 2048, 128, (64, 64)),      # split-K
-    (100, 520, 1088, 64, (64, 64)),
+    (64, 520, 2048, 128, (32, 32)),      # streaming, few tiles
+    (100, 520, 1088, 64, (32, 32)),
     (1000, 3000, 512, 128, (128, 128)),  # tiled
     (1000, 3000, 576, 64, (128, 128)),
     (4000, 4000, 768, 128, (256, 256)),  # 256-row tiles
