@@ -247,6 +247,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     // The counter holds (epoch << 16) | arrivals. An arrival that finds
     // another call's tag counts from zero, so a workspace needs no clearing
     // and a launch that never finished leaves nothing a later call counts.
+    // The last arrival puts the count back to zero under the same tag: a
+    // captured graph replays the call with the same epoch, and each replay
+    // then counts from zero too.
     constexpr int CPOL_SC1 = 16;  // device-scope coherence bit of the buffer instructions
     constexpr int TILE_F = BM * BN, WAVE_F = TM * TN * 16 * 64;
     const int tile = tmi * tiles_n + tni;
@@ -275,7 +278,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
       } while (!__hip_atomic_compare_exchange_weak(&counters[tile], &old, now, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT));
       const bool done = (now & 0xFFFFull) == (unsigned long long)ksplit;
-      if (done) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every split's stores are visible
+      if (done) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every split's stores are visible
+        __hip_atomic_store(&counters[tile], epoch << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       last = done;
     }
     __syncthreads();

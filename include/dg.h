@@ -233,7 +233,9 @@ int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, 
  *        shape splits K). It must not overlap any other argument. Its
  *        contents need no initialisation and are scratch between calls: every
  *        call tags its arrival counters with a fresh per-call value, so a
- *        launch that never finished leaves nothing a later call reads.
+ *        launch that never finished leaves nothing a later call reads. A call
+ *        captured into a graph keeps its tag; each replay that completes
+ *        leaves the counters at zero under it, so replays may repeat.
  *   workspace_bytes  size of workspace; must be 0 or at least the
  *        workspace_bytes dg_query_tile_ws reports for the shape (DG_EINVAL
  *        otherwise).
