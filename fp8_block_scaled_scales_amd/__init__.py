@@ -27,6 +27,7 @@ DG_EINVAL = -1
 DG_EALIGN = -2
 DG_EUNSUPPORTED = -3
 DG_ELAUNCH = -4
+DG_ESCRATCH = -5
 DG_FMT_E4M3 = 0
 DG_FMT_E5M2 = 1
 DG_ACT_NONE = 0
@@ -70,6 +71,11 @@ def _load():
     lib.dg_gemm_fp8_ws.restype = ctypes.c_int
     lib.dg_gemm_fp8_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp, i64, vp]
+    lib.dg_gemm_fp8_noalloc.restype = ctypes.c_int
+    lib.dg_gemm_fp8_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.dg_noalloc_scratch_bytes.restype = ctypes.c_int64
+    lib.dg_noalloc_scratch_bytes.argtypes = []
     lib.dg_quantize_fp8_rows.restype = ctypes.c_int
     lib.dg_quantize_fp8_rows.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.dg_quantize_e4m3_blocks.restype = ctypes.c_int
@@ -280,17 +286,8 @@ def dg_workspace(M: int, N: int, K: int, gran: int = 128, layout: int = DG_LAYOU
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
-def dg_gemm_fp8_ws(a, b, sa, sb, out=None, gran: int = 128, layout: int = DG_LAYOUT_NT, sa_rows: int | None = None,
-                   fmt_a: int = DG_FMT_E4M3, fmt_b: int = DG_FMT_E4M3, bias=None, act: int = DG_ACT_NONE,
-                   workspace=None, stream=None):
-    """dg_gemm_fp8_layout (with dg_gemm_fp8_nt_ex's sa_rows) plus a caller-owned workspace.
-
-    With a workspace (a contiguous uint8 GPU tensor of at least
-    dg_query_tile(..., workspace=True)["workspace_bytes"] bytes, 256-byte
-    aligned; see ``dg_workspace``) small-M shapes with few output tiles split
-    K over several workgroups; every other shape runs what the call without a
-    workspace runs. Concurrent calls need distinct workspaces.
-    """
+def _ws_args(a, b, sa, sb, out, gran, layout, sa_rows, fmt_a, fmt_b, bias, act):
+    """Checks shared by dg_gemm_fp8_ws and dg_gemm_fp8_noalloc; returns (M, N, K, sa_rows, dev)."""
     if layout not in (DG_LAYOUT_NT, DG_LAYOUT_NN, DG_LAYOUT_TT, DG_LAYOUT_TN):
         raise ValueError("layout must be DG_LAYOUT_NT, _NN, _TT or _TN")
     if a.dim() != 2 or b.dim() != 2:
@@ -309,15 +306,31 @@ def dg_gemm_fp8_ws(a, b, sa, sb, out=None, gran: int = 128, layout: int = DG_LAY
     _check(b, "b", _FP8_OF[fmt_b], (K, N) if layout & 1 else (N, K), dev)
     _check(sa, "sa", (torch.float32,), ((M + sa_rows - 1) // sa_rows, K // gran), dev)
     _check(sb, "sb", (torch.float32,), ((N + gran - 1) // gran, K // gran), dev)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    _check(out, "out", (torch.bfloat16,), (M, N), dev)
+    if out is not None:
+        _check(out, "out", (torch.bfloat16,), (M, N), dev)
     if bias is not None:
         _check(bias, "bias", (torch.float32,), (N,), dev)
     if act not in (DG_ACT_NONE, DG_ACT_RELU, DG_ACT_GELU):
         raise ValueError("act must be DG_ACT_NONE, DG_ACT_RELU or DG_ACT_GELU")
     if dev.type != "cuda":
         raise ValueError("a must be a GPU tensor")
+    return M, N, K, sa_rows, dev
+
+
+def dg_gemm_fp8_ws(a, b, sa, sb, out=None, gran: int = 128, layout: int = DG_LAYOUT_NT, sa_rows: int | None = None,
+                   fmt_a: int = DG_FMT_E4M3, fmt_b: int = DG_FMT_E4M3, bias=None, act: int = DG_ACT_NONE,
+                   workspace=None, stream=None):
+    """dg_gemm_fp8_layout (with dg_gemm_fp8_nt_ex's sa_rows) plus a caller-owned workspace.
+
+    With a workspace (a contiguous uint8 GPU tensor of at least
+    dg_query_tile(..., workspace=True)["workspace_bytes"] bytes, 256-byte
+    aligned; see ``dg_workspace``) small-M shapes with few output tiles split
+    K over several workgroups; every other shape runs what the call without a
+    workspace runs. Concurrent calls need distinct workspaces.
+    """
+    M, N, K, sa_rows, dev = _ws_args(a, b, sa, sb, out, gran, layout, sa_rows, fmt_a, fmt_b, bias, act)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         _check(workspace, "workspace", (torch.uint8,), (workspace.numel(),), dev)
@@ -330,6 +343,32 @@ def dg_gemm_fp8_ws(a, b, sa, sb, out=None, gran: int = 128, layout: int = DG_LAY
     if rc != DG_OK:
         _raise(rc, "dg_gemm_fp8_ws")
     return out
+
+
+def dg_gemm_fp8_noalloc(a, b, sa, sb, out, gran: int = 128, layout: int = DG_LAYOUT_NT, sa_rows: int | None = None,
+                        fmt_a: int = DG_FMT_E4M3, fmt_b: int = DG_FMT_E4M3, bias=None, act: int = DG_ACT_NONE,
+                        stream=None):
+    """dg_gemm_fp8_ws with the library's fixed scratch array as the workspace: nothing is allocated.
+
+    ``out`` must be given (this wrapper allocates nothing either). Calls that
+    may overlap in time on one GPU race on the shared scratch; a plan that
+    needs more than dg_noalloc_scratch_bytes() raises (DG_ESCRATCH).
+    """
+    if out is None:
+        raise ValueError("dg_gemm_fp8_noalloc needs a preallocated out")
+    M, N, K, sa_rows, dev = _ws_args(a, b, sa, sb, out, gran, layout, sa_rows, fmt_a, fmt_b, bias, act)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = _lib.dg_gemm_fp8_noalloc(a.data_ptr(), b.data_ptr(), sa.data_ptr(), sb.data_ptr(), out.data_ptr(),
+                                      M, N, K, gran, layout, sa_rows, fmt_a, fmt_b,
+                                      None if bias is None else bias.data_ptr(), act, s.cuda_stream)
+    if rc != DG_OK:
+        _raise(rc, "dg_gemm_fp8_noalloc")
+    return out
+
+
+def dg_noalloc_scratch_bytes() -> int:
+    return _lib.dg_noalloc_scratch_bytes()
 
 
 def _quantize(x, gran, fmt, q, scales, stream, where):
@@ -390,7 +429,7 @@ def dg_quantize_fp8_rows(x, gran: int = 128, fmt: int = DG_FMT_E4M3, q=None, sca
 
 
 __all__ = ["dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "dg_gemm_fp8_nt_epi", "dg_gemm_fp8_nt_ex", "dg_gemm_fp8_layout",
-           "dg_gemm_fp8_ws", "dg_workspace",
+           "dg_gemm_fp8_ws", "dg_workspace", "dg_gemm_fp8_noalloc", "dg_noalloc_scratch_bytes", "DG_ESCRATCH",
            "DG_LAYOUT_NT", "DG_LAYOUT_NN", "DG_LAYOUT_TT", "DG_LAYOUT_TN", "DG_ACT_NONE",
            "DG_ACT_RELU", "DG_ACT_GELU", "dg_quantize_e4m3_blocks", "dg_quantize_fp8_blocks", "dg_quantize_fp8_rows",
            "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError", "DG_OK", "DG_EINVAL",

@@ -55,6 +55,25 @@ uint64_t next_epoch() {
 // tile) first, then the partial tiles from the next 256-byte boundary.
 int64_t counter_bytes(int64_t tiles) { return (tiles * 8 + 255) / 256 * 256; }
 
+// The workspace of dg_gemm_fp8_noalloc, for callers that cannot allocate
+// device memory: a fixed array in the library's code object, one copy per GPU
+// the library runs on, held until the process ends. Its host-side name is a
+// stand-in, not a device address: the device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// address is passed to kernels. Static device memory starts zeroed; the
+// split-K counters need nothing else (their per-call tags are never zero).
+constexpr int64_t kScratchBytes = 4ll << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+void find_scratch(int dev) {
+  void* p = nullptr;
+  g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  g_scratch[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+}
+
 thread_local hipError_t t_last_hip = hipSuccess;
 thread_local char t_msg[256];
 
@@ -222,9 +241,12 @@ bool overlaps(const void* p, uint64_t n, const void* q, uint64_t m) {
   return n && m && x < y + m && y < x + n;
 }
 
+// split_ok: small-M shapes may split K over workgroups, through ws (the
+// caller's, ws_bytes long; none when ws_bytes is 0) or, with use_scratch,
+// through the library's static scratch array.
 int gemm(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M, int64_t N, int64_t K,
          int gran, int layout, int sa_rows, int fmt_a, int fmt_b, const float* bias, int act, void* stream,
-         bool split_ok = false, void* ws = nullptr, int64_t ws_bytes = 0) {
+         bool split_ok = false, void* ws = nullptr, int64_t ws_bytes = 0, bool use_scratch = false) {
   if (!a || !b || !sa || !sb || !out) return DG_EINVAL;
   if (sa_rows != gran && sa_rows != 1) return DG_EINVAL;
   if (validate_layout(M, N, layout) != DG_OK) return DG_EINVAL;
@@ -241,10 +263,11 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
       ((uintptr_t)out & 1))
     return DG_EALIGN;
   // A workspace lets small-M shapes split K; without one nothing does.
-  Plan pl = plan(M, N, K, gran, layout, split_ok && ws_bytes > 0);
+  Plan pl = plan(M, N, K, gran, layout, split_ok && (ws_bytes > 0 || use_scratch));
   if (!pl.e || pl.tiles * pl.ksplit > 0x7fffffff) return DG_EINVAL;
   const int64_t need = workspace_bytes(pl);
   if (ws_bytes > 0 && ws_bytes < need) return DG_EINVAL;
+  if (use_scratch && need > kScratchBytes) return DG_ESCRATCH;
   {
     // out is written while the inputs are read: it may overlap none of them
     // (the inputs may overlap each other), nor the workspace. Sizes are the
@@ -267,6 +290,14 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   rc = device_ready(&dev);
   if (rc != DG_OK) return rc;
   const dg::KernelEntry* e = pl.e;
+  if (use_scratch && pl.ksplit > 1) {
+    std::call_once(g_scratch_once[dev], find_scratch, dev);
+    if (!g_scratch[dev]) {
+      t_last_hip = g_scratch_err[dev];
+      return DG_ELAUNCH;
+    }
+    ws = g_scratch[dev];
+  }
 
   dg::GemmArgs p;
   p.a = static_cast<const uint8_t*>(a);
@@ -350,6 +381,9 @@ const char* dg_strerror(int code) {
     case DG_EALIGN:
       return "misaligned pointer (a, b need 16 bytes; sa, sb, bias 4 bytes; out 2 bytes; workspace 256 bytes)";
     case DG_EUNSUPPORTED: return "unsupported device (gfx950 required)";
+    case DG_ESCRATCH:
+      return "the call's K split needs more workspace than dg_gemm_fp8_noalloc's fixed scratch "
+             "(dg_noalloc_scratch_bytes()); use dg_gemm_fp8_ws with a workspace of dg_query_tile_ws's size";
     case DG_ELAUNCH:
       std::snprintf(t_msg, sizeof t_msg, "HIP error %d: %s", (int)t_last_hip, hipGetErrorString(t_last_hip));
       return t_msg;
@@ -391,6 +425,15 @@ int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, 
 int dg_query_tile_ws(int64_t M, int64_t N, int64_t K, int gran, int layout, dg_tile_info* info) {
   return query(M, N, K, gran, layout, true, info);
 }
+
+int dg_gemm_fp8_noalloc(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M,
+                        int64_t N, int64_t K, int gran, int layout, int sa_rows, int fmt_a, int fmt_b,
+                        const float* bias, int act, void* stream) {
+  return gemm(a, b, sa, sb, out, M, N, K, gran, layout, sa_rows, fmt_a, fmt_b, bias, act, stream, true, nullptr, 0,
+              true);
+}
+
+int64_t dg_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info) {
   return dg_query_tile_layout(M, N, K, gran, DG_LAYOUT_NT, info);

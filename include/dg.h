@@ -53,6 +53,7 @@ extern "C" {
 #define DG_EALIGN (-2)       /* misaligned pointer; nothing was launched (recoverable) */
 #define DG_EUNSUPPORTED (-3) /* device is not gfx950; nothing was launched */
 #define DG_ELAUNCH (-4)      /* a HIP call failed (not recoverable); dg_strerror() gives its text */
+#define DG_ESCRATCH (-5)     /* dg_gemm_fp8_noalloc: the plan needs more than its fixed scratch; nothing launched */
 
 /* Version of this header and library: 2.0.0 (dg_tile_info gained
  * workspace_bytes; dg_gemm_fp8_ws and dg_query_tile_ws were added; no call
@@ -249,6 +250,31 @@ int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, 
 int dg_gemm_fp8_ws(const void* a, const void* b, const float* sa, const float* sb, void* out,
                    int64_t M, int64_t N, int64_t K, int gran, int layout, int sa_rows, int fmt_a, int fmt_b,
                    const float* bias, int act, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * dg_gemm_fp8_noalloc - dg_gemm_fp8_ws for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same plans and the same results, bit for bit,
+ * with the workspace taken from a fixed array inside the library instead of
+ * an argument. The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine).
+ *
+ * The array is dg_noalloc_scratch_bytes() bytes (4 MiB) of device memory per
+ * GPU the library runs on, held until the process ends; its device address
+ * is looked up on the first call on each device. A shape whose plan needs a
+ * larger workspace (dg_query_tile_ws) is rejected with DG_ESCRATCH before
+ * anything is launched. Every call on one GPU shares that GPU's array: calls
+ * that may overlap in time on one GPU (different streams, graph replays
+ * beside eager calls) race and must not be made; calls on one stream may
+ * follow each other freely. Arguments and other status codes as
+ * dg_gemm_fp8_ws.
+ */
+int dg_gemm_fp8_noalloc(const void* a, const void* b, const float* sa, const float* sb, void* out,
+                        int64_t M, int64_t N, int64_t K, int gran, int layout, int sa_rows, int fmt_a, int fmt_b,
+                        const float* bias, int act, void* stream);
+
+/* Bytes of the fixed scratch array dg_gemm_fp8_noalloc uses on each GPU. */
+int64_t dg_noalloc_scratch_bytes(void);
 
 /* The plan dg_gemm_fp8_ws runs for these sizes, with the workspace it needs
  * (info->workspace_bytes; 0 when the plan does not split K). Pure host

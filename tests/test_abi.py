@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(dg):
 
 def test_status_codes_match_header(dg):
     text = open(HEADER).read()
-    for name in ("DG_OK", "DG_EINVAL", "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH"):
+    for name in ("DG_OK", "DG_EINVAL", "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH", "DG_ESCRATCH"):
         m = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
         assert m and int(m.group(1)) == getattr(dg, name), name
     assert dg.dg_version() == int(re.search(r"#define DG_VERSION (\d+)", text).group(1))
@@ -204,7 +204,7 @@ def test_format_codes_match_header(dg):
 
 
 def test_strerror(dg):
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(dg.dg_strerror(code), str) and dg.dg_strerror(code)
 
 
@@ -332,3 +332,14 @@ def test_quantize_scale_count_cap(dg):
     assert 4 * rows * rows < (1 << 52)
     assert dg.lib.dg_quantize_fp8_rows(x, rows, 129 * g, g, 0, q, s, None) == dg.DG_EINVAL
     assert dg.lib.dg_quantize_fp8_blocks(x, rows, rows, g, 0, q, s, None) == dg.DG_EINVAL
+
+
+def test_noalloc_scratch_limit(dg):
+    # the fixed scratch is 4 MiB; a plan needing more is refused before any HIP call
+    assert dg.dg_noalloc_scratch_bytes() == 4 << 20
+    M, N, K, g = 32, 6080, 2048, 128  # 190 tiles of 32x32 -> 95 tiles of 64x64 x 3 splits
+    need = dg.dg_query_tile(M, N, K, g, workspace=True)["workspace_bytes"]
+    assert need > dg.dg_noalloc_scratch_bytes()
+    assert dg.lib.dg_gemm_fp8_noalloc(WA, WB, WSA, WSB, WOUT, M, N, K, g, 0, g, 0, 0, None, 0, None) == dg.DG_ESCRATCH
+    # argument errors still come first
+    assert dg.lib.dg_gemm_fp8_noalloc(0, WB, WSA, WSB, WOUT, M, N, K, g, 0, g, 0, 0, None, 0, None) == dg.DG_EINVAL
