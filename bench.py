@@ -73,7 +73,10 @@ DEFAULT_WORKLOAD = 4      # large square M=N=K=8192, g=128: the largest shape, M
 # workload runs (KERNEL_SOURCES) as they were when the counters were taken. A
 # different hash means the kernel changed since: traffic is null.
 TRAFFIC = {
-    "decode_m64_n4096_k7168": {"src": "806112c55f3d193d", "bytes": 33667900},
+    "square8192": {"src": "93e9bb54ad47e1cb", "bytes": 941172143},
+    "prefill_m4096_n7168_k2048": {"src": "93e9bb54ad47e1cb", "bytes": 151255113},
+    "longk_m2000_n4000_k16384_g64": {"src": "93e9bb54ad47e1cb", "bytes": 278794639},
+    "decode_m64_n4096_k7168": {"src": "3e721c10e3904d6b", "bytes": 33667556},
 }
 
 # Sources that make up each workload's kernel: its class's device code, the
@@ -370,7 +373,9 @@ def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, bias: bool = False, act: i
         done = 2.0 * M * N * K * reps
         sample = "the whole %dx%d output, %d times, K=%d" % (M, N, reps, K)
     return {"value": done / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": sample + " (FP64, %.1f s, %s)" % (dt, _cpu_model())}
+            "sample": sample + " (FP64, %.1f s; %d threads of the host's %d hardware threads, within its CPU "
+                               "quota of %s and one GPU's CPU share of %d; %s)" % (
+                dt, threads, oracle.host_threads(), oracle.cpu_quota(), oracle.CPU_SHARE, _cpu_model())}
 
 
 def main():

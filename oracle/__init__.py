@@ -119,9 +119,36 @@ def _ptr(arr: np.ndarray, ctype):
     return arr.ctypes.data_as(ctypes.POINTER(ctype))
 
 
+# CPU share of one GPU on the hosts this runs on: worker pools stay within it
+# whatever the host's hardware thread count.
+CPU_SHARE = 16
+
+
+def host_threads() -> int:
+    """std::thread::hardware_concurrency() of this host."""
+    return max(1, _load().dgo_hardware_threads())
+
+
+def cpu_quota() -> int | None:
+    """CPUs this process may use: its affinity mask, capped by a cgroup v2 cpu.max quota when one is set."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            q = max(1, -(-int(quota) // int(period)))
+            n = q if n is None else min(n, q)
+    except (OSError, ValueError):
+        pass
+    return n
+
+
 def default_threads() -> int:
-    """Host threads the oracle uses: all hardware threads, at most 16."""
-    return max(1, min(16, _load().dgo_hardware_threads()))
+    """Host threads the oracle uses: the hardware threads, within the process's
+    CPU quota and the CPU share of one GPU (CPU_SHARE)."""
+    n = min(host_threads(), CPU_SHARE)
+    q = cpu_quota()
+    return max(1, min(n, q) if q else n)
 
 
 def e4m3_decode(codes) -> np.ndarray:
