@@ -243,8 +243,9 @@ def dg_gemm_fp8_layout(a, b, sa, sb, out=None, gran: int = 128, layout: int = DG
     """dg_gemm_fp8_nt_epi with A stored [M,K] or [K,M] and B stored [N,K] or [K,N] per ``layout``.
 
     a: [M,K] (NT, NN) or [K,M] (TT, TN); b: [N,K] (NT, TT) or [K,N] (NN, TN); sa and
-    sb keep their logical shapes [ceil(M/g), K/g] and [ceil(N/g), K/g]. A stored
-    [K,M] needs M % 16 == 0, B stored [K,N] needs N % 16 == 0.
+    sb keep their logical shapes [ceil(M/g), K/g] and [ceil(N/g), K/g]. M and N may
+    be any length (ragged edges included) in every layout. Per-row A factors with
+    a layout: dg_gemm_fp8_ws (workspace=None) takes both.
     """
     if layout not in (DG_LAYOUT_NT, DG_LAYOUT_NN, DG_LAYOUT_TT, DG_LAYOUT_TN):
         raise ValueError("layout must be DG_LAYOUT_NT, _NN, _TT or _TN")

@@ -225,12 +225,15 @@ int device_ready(int* dev_out = nullptr) {
 
 namespace {
 
-// Layout checks shared by the GEMM and the tile query: a known code, and the
-// stored row length of a transposed operand (M for A [K,M], N for B [K,N]) a
-// multiple of 16 bytes, the granule its tiles are copied in.
+// Layout check shared by the GEMM and the tile query: a known code. A
+// transposed operand's stored rows (M bytes for A [K,M], N for B [K,N]) may
+// have any length: its tiles are copied in 16-byte pieces along those rows
+// whatever their alignment, and the bytes a piece takes past a row's end
+// belong to rows of A or B past M or N, whose outputs are never stored.
 int validate_layout(int64_t M, int64_t N, int layout) {
+  (void)M;
+  (void)N;
   if (layout < DG_LAYOUT_NT || layout > DG_LAYOUT_TN) return DG_EINVAL;
-  if (((layout & 2) && M % 16 != 0) || ((layout & 1) && N % 16 != 0)) return DG_EINVAL;
   return DG_OK;
 }
 
@@ -250,7 +253,6 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   if (!a || !b || !sa || !sb || !out) return DG_EINVAL;
   if (sa_rows != gran && sa_rows != 1) return DG_EINVAL;
   if (validate_layout(M, N, layout) != DG_OK) return DG_EINVAL;
-  if (layout != DG_LAYOUT_NT && sa_rows == 1) return DG_EINVAL;  // per-row factors are compiled for NT only
   if ((fmt_a != DG_FMT_E4M3 && fmt_a != DG_FMT_E5M2) || (fmt_b != DG_FMT_E4M3 && fmt_b != DG_FMT_E5M2))
     return DG_EINVAL;
   if (act != DG_ACT_NONE && act != DG_ACT_RELU && act != DG_ACT_GELU) return DG_EINVAL;
@@ -376,7 +378,7 @@ const char* dg_strerror(int code) {
     case DG_EINVAL:
       return "invalid argument (null pointer, bad dimension, K not a multiple of gran, gran not 64/128/256, "
              "sa_rows neither gran nor 1, a format code other than DG_FMT_E4M3/DG_FMT_E5M2, an unknown "
-             "activation or layout, a transposed operand whose stored row length is not a multiple of 16, an "
+             "activation or layout, an "
              "output or workspace that overlaps another argument, or a workspace smaller than the plan needs)";
     case DG_EALIGN:
       return "misaligned pointer (a, b need 16 bytes; sa, sb, bias 4 bytes; out 2 bytes; workspace 256 bytes)";

@@ -177,6 +177,34 @@ __device__ __forceinline__ void stage_group_t(v4i rsrc, uint8_t* lds, uint32_t p
             __builtin_amdgcn_readfirstlane((uint32_t)grp * RPI * pitch));
 }
 
+// Byte range of the descriptor a transposed tile's step copies read through:
+// the step's K rows (k0 .. k0 + rows - 1) of a stored [K, len] operand from
+// column col0 on. A 16-byte piece of the tile's last column chunk may reach
+// past a stored row's end when len is not a multiple of 16; the range check
+// drops a 4-byte word that reaches past the range whole, so the range runs 16
+// bytes into the next K row when there is one (past the last row see
+// patch_tail_t).
+__device__ __forceinline__ uint32_t tile_range_t(int64_t k0, int K, int len, int col0, int BKr) {
+  const int64_t rows = min((int64_t)BKr, (int64_t)K - k0);
+  return (uint32_t)(rows * len - col0 + (k0 + rows < K ? 16 : 0));
+}
+
+// The tensor's last K row has no row after it, and the copy of a tile's last
+// column chunk of it loses the 1 to 3 bytes of its last 4-byte word that lie
+// inside the tensor when len % 4 != 0. Lanes 0-2 write those bytes (stored
+// columns [len & ~3, len) that fall in the W-wide tile from col0) from memory
+// into slab row `row`, at their swizzled places. src is the stored last row.
+// Called between two barriers: after every wave's copies of the step have
+// landed, before any wave reads the slab.
+template <int W>
+__device__ __forceinline__ void patch_tail_t(uint8_t* slab, const uint8_t* src, int row, int len, int col0, int lane) {
+  const int c = (len & ~3) + lane;
+  if (lane < (len & 3) && c >= col0 && c < col0 + W) {
+    const int t = c - col0;
+    slab[row * W + (((t >> 4) ^ tkey<W>(row)) << 4) + (t & 15)] = src[c];
+  }
+}
+
 // The 32 K bytes of this lane's 32x32x64 fragment from a transposed tile:
 // lane l needs column col0 + l%32 (its row of A, or of B) at K bytes
 // kofs + 32*(l/32) .. +31. ds_read_b64_tr_b8 works on 16-lane groups: lane

@@ -82,7 +82,6 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   static_assert(128 * LDC * 2 <= 2 * STAGE, "an epilogue pass must fit in the ring");
   static_assert(BM * SEGS <= NW * 64, "a step's row factors: one 64-entry piece per wave");
   static_assert((LAYOUT & 1) == 0 || BN == 256 || BN == 128, "transposed B: 256- or 128-byte K rows");
-  static_assert(LAYOUT == 0 || !ROWA, "per-row A factors: NT only");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOT];
 
   const int lane = threadIdx.x & 63;
@@ -135,7 +134,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
     const int64_t k0 = (int64_t)t * BK;
     if constexpr ((LAYOUT & 2) != 0) {
       // the step's K rows of A^T from column m0; past the tensor reads zero
-      const v4i rat = rsrc_words(a + k0 * M + m0, (uint32_t)(min((int64_t)BK, (int64_t)K - k0) * M - m0));
+      const v4i rat = rsrc_words(a + k0 * M + m0, tile_range_t(k0, K, M, m0, BK));
 #pragma unroll
       for (int i = 0; i < 4; ++i) stage_group_t<BM>(rat, slot, (uint32_t)M, i * NW + wave, lane);
     } else {
@@ -143,7 +142,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       for (int i = 0; i < 4; ++i) stage_group<2>(ra, slot, uK, (uint32_t)t * BK, i * NW + wave, lane);
     }
     if constexpr ((LAYOUT & 1) != 0) {
-      const v4i rbt = rsrc_words(b + k0 * N + n0, (uint32_t)(min((int64_t)BK, (int64_t)K - k0) * N - n0));
+      const v4i rbt = rsrc_words(b + k0 * N + n0, tile_range_t(k0, K, N, n0, BK));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (i * NW + wave < BN / 8) stage_group_t<BN>(rbt, slot + A_BYTES, (uint32_t)N, i * NW + wave, lane);
@@ -171,6 +170,19 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
   for (int s = 0; s < nsteps; ++s) {
     DG_WAIT_VMCNT(0);  // this wave's part of step s has landed
     __syncthreads();   // all of step s visible; the other slot is free
+    if constexpr (LAYOUT != 0) {
+      // the tensor's last K row of a transposed operand whose stored row
+      // length is not a multiple of 4 (see patch_tail_t)
+      if (s == nsteps - 1 && (((LAYOUT & 2) && (M & 3)) || ((LAYOUT & 1) && (N & 3)))) {
+        if (wave == 0) {
+          uint8_t* slot = smem + (s & 1) * SLOT;
+          const int row = K - 1 - s * BK;
+          if ((LAYOUT & 2) && (M & 3)) patch_tail_t<BM>(slot, a + (int64_t)(K - 1) * M, row, M, m0, lane);
+          if ((LAYOUT & 1) && (N & 3)) patch_tail_t<BN>(slot + A_BYTES, b + (int64_t)(K - 1) * N, row, N, n0, lane);
+        }
+        __syncthreads();
+      }
+    }
     auto issue_next = [&](int who) {
       if (s + 1 < nsteps && grp == who) issue_step(s + 1);
     };
@@ -393,35 +405,39 @@ hipError_t launch_fa(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Per-row A factors are compiled for the NT layout only.
-template <int G, int BN, int WM, int FMT, int EPI, int LAYOUT>
+// RS selects the A factor forms compiled: 0 both, chosen by p.rowa (the NT
+// entries); 1 g x g blocks only; 2 per-row factors only (the transposed
+// layouts compile the two forms in separate translation units).
+template <int G, int BN, int WM, int FMT, int EPI, int LAYOUT, int RS>
 hipError_t launch_sa(const GemmArgs& p, hipStream_t stream) {
-  if constexpr (LAYOUT != 0) {
+  if constexpr (RS == 1) {
     return p.rowa ? hipErrorInvalidValue : launch_fa<G, BN, WM, FMT, EPI, false, LAYOUT>(p, stream);
+  } else if constexpr (RS == 2) {
+    return p.rowa ? launch_fa<G, BN, WM, FMT, EPI, true, LAYOUT>(p, stream) : hipErrorInvalidValue;
   } else {
-    return p.rowa ? launch_fa<G, BN, WM, FMT, EPI, true, 0>(p, stream)
-                  : launch_fa<G, BN, WM, FMT, EPI, false, 0>(p, stream);
+    return p.rowa ? launch_fa<G, BN, WM, FMT, EPI, true, LAYOUT>(p, stream)
+                  : launch_fa<G, BN, WM, FMT, EPI, false, LAYOUT>(p, stream);
   }
 }
 
-template <int G, int BN, int WM, int FMT, int LAYOUT>
+template <int G, int BN, int WM, int FMT, int LAYOUT, int RS>
 hipError_t launch_fmt(const GemmArgs& p, hipStream_t stream) {
   switch (epilogue_form(p.bias, p.act)) {
-    case 0: return launch_sa<G, BN, WM, FMT, 0, LAYOUT>(p, stream);
-    case 1: return launch_sa<G, BN, WM, FMT, 1, LAYOUT>(p, stream);
-    case 2: return launch_sa<G, BN, WM, FMT, 2, LAYOUT>(p, stream);
+    case 0: return launch_sa<G, BN, WM, FMT, 0, LAYOUT, RS>(p, stream);
+    case 1: return launch_sa<G, BN, WM, FMT, 1, LAYOUT, RS>(p, stream);
+    case 2: return launch_sa<G, BN, WM, FMT, 2, LAYOUT, RS>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int G, int BN, int WM, int LAYOUT>
+template <int G, int BN, int WM, int LAYOUT, int RS>
 hipError_t launch_l(const GemmArgs& p, hipStream_t stream) {
   if (p.ksplit != 1 || p.sshift < 0 || p.sshift > 1) return hipErrorInvalidValue;
   switch (p.fmt) {
-    case 0: return launch_fmt<G, BN, WM, 0, LAYOUT>(p, stream);
-    case 1: return launch_fmt<G, BN, WM, 1, LAYOUT>(p, stream);
-    case 2: return launch_fmt<G, BN, WM, 2, LAYOUT>(p, stream);
-    case 3: return launch_fmt<G, BN, WM, 3, LAYOUT>(p, stream);
+    case 0: return launch_fmt<G, BN, WM, 0, LAYOUT, RS>(p, stream);
+    case 1: return launch_fmt<G, BN, WM, 1, LAYOUT, RS>(p, stream);
+    case 2: return launch_fmt<G, BN, WM, 2, LAYOUT, RS>(p, stream);
+    case 3: return launch_fmt<G, BN, WM, 3, LAYOUT, RS>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -429,16 +445,17 @@ hipError_t launch_l(const GemmArgs& p, hipStream_t stream) {
 // The NT table entries.
 template <int G, int BN, int WM>
 hipError_t launch(const GemmArgs& p, hipStream_t stream) {
-  return p.layout == 0 ? launch_l<G, BN, WM, 0>(p, stream) : hipErrorInvalidValue;
+  return p.layout == 0 ? launch_l<G, BN, WM, 0, 0>(p, stream) : hipErrorInvalidValue;
 }
 
-// The transposed layouts on the same tile (instantiated in gemm_fp8_big_layouts.hip).
-template <int G, int BN, int WM>
+// The transposed layouts on the same tile, with the A factor form RS
+// (instantiated in gemm_fp8_big_layouts.hip and gemm_fp8_big_layouts_rowa.hip).
+template <int G, int BN, int WM, int RS>
 hipError_t launch_layout(const GemmArgs& p, hipStream_t stream) {
   switch (p.layout) {
-    case 1: return launch_l<G, BN, WM, 1>(p, stream);
-    case 2: return launch_l<G, BN, WM, 2>(p, stream);
-    case 3: return launch_l<G, BN, WM, 3>(p, stream);
+    case 1: return launch_l<G, BN, WM, 1, RS>(p, stream);
+    case 2: return launch_l<G, BN, WM, 2, RS>(p, stream);
+    case 3: return launch_l<G, BN, WM, 3, RS>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

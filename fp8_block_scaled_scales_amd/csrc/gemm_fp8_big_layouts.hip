@@ -10,12 +10,13 @@
 
 namespace dg {
 
+// g x g A factors here; per-row A factors in gemm_fp8_big_layouts_rowa.hip.
 hipError_t launch_big_layout(int id, const GemmArgs& p, hipStream_t stream) {
   switch (id) {
-    case 4: return big::launch_layout<128, 256, 2>(p, stream);
-    case 5: return big::launch_layout<64, 256, 2>(p, stream);
-    case 9: return big::launch_layout<128, 128, 4>(p, stream);
-    case 10: return big::launch_layout<64, 128, 4>(p, stream);
+    case 4: return big::launch_layout<128, 256, 2, 1>(p, stream);
+    case 5: return big::launch_layout<64, 256, 2, 1>(p, stream);
+    case 9: return big::launch_layout<128, 128, 4, 1>(p, stream);
+    case 10: return big::launch_layout<64, 128, 4, 1>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,12 +12,14 @@
 
 namespace dg {
 
+// g x g A factors here; per-row A factors in gemm_fp8_layouts_rowa.hip.
 hipError_t launch_layout(int id, const GemmArgs& p, hipStream_t stream) {
+  if (p.rowa) return launch_layout_rowa(id, p, stream);
   switch (id) {
-    case 0: return launch_tiled_layout<128, 128, 2, 2, 2, 128, 4, false>(p, stream);
-    case 1: return launch_tiled_layout<128, 128, 2, 2, 2, 64, 4, false>(p, stream);
-    case 2: return launch_tiled_layout<64, 64, 2, 2, 8, 128, 4, true>(p, stream);
-    case 3: return launch_tiled_layout<64, 64, 2, 2, 8, 64, 4, true>(p, stream);
+    case 0: return launch_tiled_layout<128, 128, 2, 2, 2, 128, 4, false, 1>(p, stream);
+    case 1: return launch_tiled_layout<128, 128, 2, 2, 2, 64, 4, false, 1>(p, stream);
+    case 2: return launch_tiled_layout<64, 64, 2, 2, 8, 128, 4, true, 1>(p, stream);
+    case 3: return launch_tiled_layout<64, 64, 2, 2, 8, 64, 4, true, 1>(p, stream);
     default: return launch_big_layout(id, p, stream);
   }
 }

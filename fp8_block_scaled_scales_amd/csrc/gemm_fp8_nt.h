@@ -55,9 +55,11 @@ hipError_t launch_big128_g64(const GemmArgs& p, hipStream_t stream);
 
 // The transposed layouts (GemmArgs::layout != 0) of table entry `id`: the
 // tiled and split-K entries (0-3) and the 256- and 128-wide 256-row entries
-// (4, 5, 9, 10).
+// (4, 5, 9, 10); the _rowa forms take per-row A factors.
 hipError_t launch_layout(int id, const GemmArgs& p, hipStream_t stream);
 hipError_t launch_big_layout(int id, const GemmArgs& p, hipStream_t stream);
+hipError_t launch_layout_rowa(int id, const GemmArgs& p, hipStream_t stream);
+hipError_t launch_big_layout_rowa(int id, const GemmArgs& p, hipStream_t stream);
 
 extern KernelEntry kTable[];
 extern const int kTableSize;

@@ -57,7 +57,7 @@ __device__ __forceinline__ void wait_steps(int steps) {
 // G is the K segment contracted before each promotion; the scale blocks are
 // sg x sg with sg = G << sshift (g = 256 runs G = 128 with one factor per two
 // segments). ROWA: A's factors are per row, sa is [M][K/sg]. LAYOUT bit 1: A
-// stored [K,M]; bit 0: B stored [K,N] (M resp. N a multiple of 16).
+// stored [K,M]; bit 0: B stored [K,N] (M resp. N any length).
 template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, bool ROWA,
           int LAYOUT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
@@ -114,14 +114,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     const int64_t k0 = (int64_t)st * BK;
     if constexpr ((LAYOUT & 2) != 0) {
       // the step's K rows of A^T from column m0; past the tensor reads zero
-      const v4i rat = rsrc_words(a + k0 * M + m0, (uint32_t)(min((int64_t)BK, (int64_t)K - k0) * M - m0));
+      const v4i rat = rsrc_words(a + k0 * M + m0, tile_range_t(k0, K, M, m0, BK));
 #pragma unroll
       for (int i = 0; i < BM / 8 / NWAVES; ++i) stage_group_t<BM>(rat, slot, (uint32_t)M, i * NWAVES + wave, lane);
     } else {
       stage_slab<BM, NWAVES, 2>(ra, slot, uK, st * BK, wave, lane);
     }
     if constexpr ((LAYOUT & 1) != 0) {
-      const v4i rbt = rsrc_words(b + k0 * N + n0, (uint32_t)(min((int64_t)BK, (int64_t)K - k0) * N - n0));
+      const v4i rbt = rsrc_words(b + k0 * N + n0, tile_range_t(k0, K, N, n0, BK));
 #pragma unroll
       for (int i = 0; i < BN / 8 / NWAVES; ++i)
         stage_group_t<BN>(rbt, slot + A_BYTES, (uint32_t)N, i * NWAVES + wave, lane);
@@ -166,6 +166,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     // Step s landed once only the later steps' loads are outstanding.
     wait_steps<LOADS, STAGES - 2>(min(STAGES - 2, nsteps - 1 - s));
     __syncthreads();  // step s visible to all waves; slot (s-1)%STAGES free
+    if constexpr (LAYOUT != 0) {
+      // the tensor's last K row of a transposed operand whose stored row
+      // length is not a multiple of 4 (see patch_tail_t)
+      if (st0 + s == nsteps_all - 1 && (((LAYOUT & 2) && (M & 3)) || ((LAYOUT & 1) && (N & 3)))) {
+        if (wave == 0) {
+          uint8_t* slot = smem + (s % STAGES) * STAGE_BYTES;
+          const int row = K - 1 - (st0 + s) * BK;
+          if ((LAYOUT & 2) && (M & 3)) patch_tail_t<BM>(slot, a + (int64_t)(K - 1) * M, row, M, m0, lane);
+          if ((LAYOUT & 1) && (N & 3)) patch_tail_t<BN>(slot + A_BYTES, b + (int64_t)(K - 1) * N, row, N, n0, lane);
+        }
+        __syncthreads();
+      }
+    }
 
     if (s + STAGES - 1 < nsteps) stage_step(s + STAGES - 1);
 
@@ -384,36 +397,42 @@ static hipError_t launch_tiled_fa(const GemmArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Per-row A factors are compiled for the NT layout only.
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, int LAYOUT>
+// RS selects the A factor forms compiled: 0 both, chosen by p.rowa (the NT
+// entries); 1 g x g blocks only; 2 per-row factors only (the transposed
+// layouts compile the two forms in separate translation units).
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, int LAYOUT,
+          int RS>
 static hipError_t launch_tiled_sa(const GemmArgs& p, hipStream_t stream) {
-  if constexpr (LAYOUT != 0) {
+  if constexpr (RS == 1) {
     return p.rowa ? hipErrorInvalidValue
                   : launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, false, LAYOUT>(p, stream);
+  } else if constexpr (RS == 2) {
+    return p.rowa ? launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, true, LAYOUT>(p, stream)
+                  : hipErrorInvalidValue;
   } else {
-    return p.rowa ? launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, true, 0>(p, stream)
-                  : launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, false, 0>(p, stream);
+    return p.rowa ? launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, true, LAYOUT>(p, stream)
+                  : launch_tiled_fa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, false, LAYOUT>(p, stream);
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int LAYOUT>
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int LAYOUT, int RS>
 static hipError_t launch_tiled_fmt(const GemmArgs& p, hipStream_t stream) {
   switch (epilogue_form(p.bias, p.act)) {
-    case 0: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 0, LAYOUT>(p, stream);
-    case 1: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 1, LAYOUT>(p, stream);
-    case 2: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 2, LAYOUT>(p, stream);
+    case 0: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 0, LAYOUT, RS>(p, stream);
+    case 1: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 1, LAYOUT, RS>(p, stream);
+    case 2: return launch_tiled_sa<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, 2, LAYOUT, RS>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int LAYOUT>
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int LAYOUT, int RS>
 static hipError_t launch_tiled_l(const GemmArgs& p, hipStream_t stream) {
   if ((!SPLIT && p.ksplit != 1) || p.sshift < 0 || p.sshift > 1) return hipErrorInvalidValue;
   switch (p.fmt) {
-    case 0: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 0, LAYOUT>(p, stream);
-    case 1: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 1, LAYOUT>(p, stream);
-    case 2: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 2, LAYOUT>(p, stream);
-    case 3: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 3, LAYOUT>(p, stream);
+    case 0: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 0, LAYOUT, RS>(p, stream);
+    case 1: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 1, LAYOUT, RS>(p, stream);
+    case 2: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 2, LAYOUT, RS>(p, stream);
+    case 3: return launch_tiled_fmt<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 3, LAYOUT, RS>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -421,16 +440,18 @@ static hipError_t launch_tiled_l(const GemmArgs& p, hipStream_t stream) {
 // The NT table entries.
 template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT>
 static hipError_t launch_tiled(const GemmArgs& p, hipStream_t stream) {
-  return p.layout == 0 ? launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 0>(p, stream) : hipErrorInvalidValue;
+  return p.layout == 0 ? launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 0, 0>(p, stream)
+                       : hipErrorInvalidValue;
 }
 
-// The transposed layouts on the same tile (instantiated in gemm_fp8_layouts.hip).
-template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT>
+// The transposed layouts on the same tile, with the A factor form RS
+// (instantiated in gemm_fp8_layouts.hip and gemm_fp8_layouts_rowa.hip).
+template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int RS>
 static hipError_t launch_tiled_layout(const GemmArgs& p, hipStream_t stream) {
   switch (p.layout) {
-    case 1: return launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 1>(p, stream);
-    case 2: return launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 2>(p, stream);
-    case 3: return launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 3>(p, stream);
+    case 1: return launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 1, RS>(p, stream);
+    case 2: return launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 2, RS>(p, stream);
+    case 3: return launch_tiled_l<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, 3, RS>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -173,11 +173,12 @@ int dg_gemm_fp8_nt_ex(const void* a, const void* b, const float* sa, const float
  *        quantiser run on a stored [K,M] matrix gives the transpose of sa).
  *   layout  DG_LAYOUT_NT, _NN, _TT or _TN.
  *
- * The result is the same product, out[i,j] as in dg_gemm_fp8_nt_epi. A stored
- * [K,M] needs M % 16 == 0 and B stored [K,N] needs N % 16 == 0 (DG_EINVAL
- * otherwise); a and b 16-byte aligned as before. DG_LAYOUT_NT is
- * dg_gemm_fp8_nt_epi bit for bit. dg_query_tile_layout names the tile a
- * layout runs. Per-row A factors are NT only (dg_gemm_fp8_nt_ex).
+ * The result is the same product, out[i,j] as in dg_gemm_fp8_nt_epi, for any
+ * M and N (a stored row of M or N bytes need not be a multiple of 16 long);
+ * a and b 16-byte aligned as before. DG_LAYOUT_NT is dg_gemm_fp8_nt_epi bit
+ * for bit. dg_query_tile_layout names the tile a layout runs.
+ * dg_gemm_fp8_ws (with no workspace) takes a layout together with per-row A
+ * factors.
  */
 int dg_gemm_fp8_layout(const void* a, const void* b, const float* sa, const float* sb, void* out,
                        int64_t M, int64_t N, int64_t K, int gran, int layout, int fmt_a, int fmt_b,
@@ -226,9 +227,9 @@ int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, 
  * leaves the workspace untouched.
  *
  *   a, b, sa, sb, out, M, N, K, gran, layout, fmt_a, fmt_b, bias, act
- *        as dg_gemm_fp8_layout (sa_rows = 1 with DG_LAYOUT_NT only, as
- *        dg_gemm_fp8_nt_ex).
- *   sa_rows   gran or 1, as dg_gemm_fp8_nt_ex.
+ *        as dg_gemm_fp8_layout.
+ *   sa_rows   gran or 1, as dg_gemm_fp8_nt_ex, with any layout: sa is
+ *        [M][K/gran] with sa_rows = 1 whatever the storage of A's codes.
  *   workspace device memory of at least workspace_bytes bytes, 256-byte
  *        aligned, owned by the caller, or NULL with workspace_bytes 0 (then no
  *        shape splits K). It must not overlap any other argument. Its

@@ -155,12 +155,18 @@ def test_python_binding_checks_row_scale_shapes(dg):
 
 
 @pytest.mark.parametrize("layout,M,N,want", [(4, 256, 256, "DG_EINVAL"), (-1, 256, 256, "DG_EINVAL"),
-                                              (2, 1000, 256, "DG_EINVAL"), (3, 1000, 256, "DG_EINVAL"),
-                                              (1, 256, 1000, "DG_EINVAL"), (3, 256, 1000, "DG_EINVAL")])
+                                              (7, 1000, 256, "DG_EINVAL")])
 def test_layout_rejects(dg, layout, M, N, want):
     assert dg.lib.dg_gemm_fp8_layout(A, B, SA, SB, OUT, M, N, 256, 128, layout, 0, 0, None, 0, None) == getattr(dg, want)
     info = dg.dg_tile_info()
     assert dg.lib.dg_query_tile_layout(M, N, 256, 128, layout, ctypes.byref(info)) == getattr(dg, want)
+
+
+@pytest.mark.parametrize("layout,M,N", [(2, 1000, 256), (3, 1001, 257), (1, 256, 1000), (3, 7, 4095), (1, 64, 4099)])
+def test_layout_accepts_any_row_length(dg, layout, M, N):
+    # a transposed operand's stored rows (M or N bytes) need not be a multiple of 16 long
+    t = dg.dg_query_tile(M, N, 256, 128, layout)
+    assert t["grid"] > 0 and t["ksplit"] == 1
 
 
 @pytest.mark.parametrize("M,N,K,g,layout,tile", [(64, 4096, 7168, 128, 1, (64, 64)), (4096, 7168, 2048, 128, 3, (256, 256)),
@@ -296,7 +302,6 @@ def test_ws_fake_addresses_do_not_overlap(dg):
     (dict(ws=WOUT - 0x1000), "DG_EINVAL"),                  # overlaps out
     (dict(ws=WA + 0x1000), "DG_EINVAL"),                    # overlaps a
     (dict(out=WS + (1 << 19)), "DG_EINVAL"),                # out inside the workspace
-    (dict(layout=1, sa_rows=1), "DG_EINVAL"),               # per-row A factors are NT only
     (dict(a=WA + 8), "DG_EALIGN"),
 ])
 def test_ws_rejects(dg, kw, want):

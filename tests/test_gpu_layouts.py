@@ -182,3 +182,110 @@ def test_nt_through_the_layout_call_is_the_nt_call_bitwise():
                            torch.from_numpy(sa).to(dev), torch.from_numpy(sb).to(dev), gran=g)
     torch.cuda.synchronize()
     assert np.array_equal(o1, o2.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+# Ragged stored rows: M (A stored [K,M]) and N (B stored [K,N]) not multiples
+# of 16, so the transposed rows are not 16-byte aligned, on the 64x64, 128x128
+# and 256-row tiles (256 and 128 wide), K % 128 == 64 at g = 64.
+RAGGED_T = [
+    (7, 4095, 1024, 128), (97, 531, 1088, 64), (1001, 3003, 512, 128), (999, 2001, 576, 64),
+    (4001, 3999, 512, 128), (2003, 3997, 704, 64),
+]
+
+
+@pytest.mark.parametrize("layout", TRANSPOSED)
+@pytest.mark.parametrize("M,N,K,g", RAGGED_T)
+def test_layout_ragged_parity(M, N, K, g, layout):
+    import fp8_block_scaled_scales_amd as dg
+
+    t = dg.dg_query_tile(M, N, K, g, layout)
+    tile = (t["bm"], t["bn"])
+    a8, sa, b8, sb = _operands(M, N, K, g, 0, 0, seed=16000 + M + N)
+    a_st, b_st = _store(a8, b8, layout)
+    say("ragged layout %d M=%d N=%d K=%d g=%d tile %s" % (layout, M, N, K, g, tile))
+    got, bits = _run(a_st, b_st, sa, sb, g, layout)
+    assert np.all(np.isfinite(got))
+    rows, cols = _sample(M, N, tile, M + 5 * N)
+    ref = oracle.gemm_ref_layout(a_st, b_st, sa, sb, g, layout, M, N, K, rows=rows, cols=cols)
+    _assert_parity(got[np.ix_(rows, cols)], ref, "ragged layout %d %dx%dx%d g=%d" % (layout, M, N, K, g))
+
+
+@pytest.mark.parametrize("M,N,K,g", [RAGGED_T[1], RAGGED_T[2], RAGGED_T[4], RAGGED_T[5]])
+def test_layout_ragged_closed_form_and_agreement_bitwise(M, N, K, g):
+    # all-ones codes with power-of-two block factors: exact, so every layout
+    # matches bf16(ref) bit for bit, ragged edges included
+    a8 = np.full((M, K), 0x38, np.uint8)
+    b8 = np.full((N, K), 0x38, np.uint8)
+    nkb = K // g
+    sa = (2.0 ** ((np.arange((M + g - 1) // g)[:, None] - np.arange(nkb)[None, :]) % 7 - 3)).astype(np.float32)
+    sb = (2.0 ** ((2 * np.arange((N + g - 1) // g)[:, None] + np.arange(nkb)[None, :]) % 3)).astype(np.float32)
+    rows = np.unique(np.concatenate([np.arange(0, M, 7), [M - 1]]))
+    cols = np.unique(np.concatenate([np.arange(0, N, 37), [N - 1]]))
+    ref = oracle.gemm_ref(a8, b8, sa, sb, g, rows, cols)
+    for layout in TRANSPOSED:
+        a_st, b_st = _store(a8, b8, layout)
+        say("ragged closed form layout %d M=%d N=%d K=%d g=%d" % (layout, M, N, K, g))
+        _, bits = _run(a_st, b_st, sa, sb, g, layout)
+        assert np.array_equal(bits[np.ix_(rows, cols)], _common.f32_to_bf16_bits(ref.astype(np.float32))), layout
+
+
+def _run_ws(a_st, b_st, sa, sb, g, layout, sa_rows=None, fa=0, fb=0, bias=None, act=0):
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    dev = "cuda:0"
+    t = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (a_st, b_st, sa, sb)]
+    tbias = None if bias is None else torch.from_numpy(bias).to(dev)
+    out = dg.dg_gemm_fp8_ws(t[0], t[1], t[2], t[3], gran=g, layout=layout, sa_rows=sa_rows, fmt_a=fa, fmt_b=fb,
+                            bias=tbias, act=act)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# Per-row A factors (one per row and K segment) with a transposed layout, on
+# the 64x64, 128x128 and 256-row tiles; ragged M and N included.
+ROWA_T = [(64, 4096, 1024, 128), (97, 531, 1088, 64), (1008, 3008, 512, 128), (1001, 3003, 576, 64),
+          (4000, 4000, 768, 128), (2003, 3997, 704, 64), (512, 1040, 768, 256)]
+
+
+@pytest.mark.parametrize("layout", TRANSPOSED)
+@pytest.mark.parametrize("M,N,K,g", ROWA_T)
+def test_layout_rowscales_parity(M, N, K, g, layout):
+    import fp8_block_scaled_scales_amd as dg
+
+    t = dg.dg_query_tile(M, N, K, g, layout, workspace=False)
+    tile = (t["bm"], t["bn"])
+    x = synth.normal(17000 + M, (M, K)) * np.exp(np.random.default_rng(M).uniform(-4, 4, size=(M, 1)))
+    a8, sa = oracle.quantize_rows_fmt(x.astype(np.float32), g, 0)
+    b8, sb = oracle.quantize_blocks_fmt(synth.normal(17001 + N, (N, K), sigma=0.02), g, 0)
+    a_st, b_st = _store(a8, b8, layout)
+    say("per-row layout %d M=%d N=%d K=%d g=%d tile %s" % (layout, M, N, K, g, tile))
+    got, _ = _run_ws(a_st, b_st, sa, sb, g, layout, sa_rows=1)
+    rows, cols = _sample(M, N, tile, M + 7 * N)
+    ref = oracle.gemm_ref_rowa(a8, b8, sa, sb, g, rows=rows, cols=cols)
+    _assert_parity(got[np.ix_(rows, cols)], ref, "per-row layout %d %dx%dx%d g=%d" % (layout, M, N, K, g))
+
+
+@pytest.mark.parametrize("M,N,K,g", [(4000, 4000, 768, 128), (2003, 3997, 704, 64), (1008, 3008, 512, 128)])
+def test_layout_rowscales_same_bits_as_nt(M, N, K, g):
+    # the transposed tiles read the same K order as the NT tiles of the same
+    # class, so per-row results agree with the NT per-row call bit for bit
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    x = synth.normal(18000 + M, (M, K)) * np.exp(np.random.default_rng(M + 1).uniform(-4, 4, size=(M, 1)))
+    a8, sa = oracle.quantize_rows_fmt(x.astype(np.float32), g, 0)
+    b8, sb = oracle.quantize_blocks_fmt(synth.normal(18001 + N, (N, K), sigma=0.02), g, 0)
+    dev = "cuda:0"
+    nt = dg.dg_gemm_fp8_nt_ex(torch.from_numpy(a8).to(dev), torch.from_numpy(b8).to(dev), torch.from_numpy(sa).to(dev),
+                              torch.from_numpy(sb).to(dev), gran=g, sa_rows=1)
+    torch.cuda.synchronize()
+    want = nt.view(torch.int16).cpu().numpy().view(np.uint16)
+    for layout in TRANSPOSED:
+        t = dg.dg_query_tile(M, N, K, g, layout)
+        assert t["kernel_id"] == dg.dg_query_tile(M, N, K, g)["kernel_id"], (layout, t)
+        a_st, b_st = _store(a8, b8, layout)
+        say("per-row layout %d vs NT bits M=%d N=%d K=%d g=%d" % (layout, M, N, K, g))
+        assert np.array_equal(_run_ws(a_st, b_st, sa, sb, g, layout, sa_rows=1)[1], want), layout
