@@ -8,6 +8,7 @@ FP32 promotion, BF16 epilogue) runs inside that one kernel launch.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--fmt e4m3|e5m2|e4m3xe5m2|e5m2xe4m3] [--gran 64|128|256]
                   [--bias] [--act none|relu|gelu] [--sa-rows 1] [--layout nt|nn|tt|tn]
+                  [--workspace]
 
 --fmt and --gran run the same workload with the operands in another FP8
 format or with another block granularity (default: E4M3 and the workload's
@@ -15,8 +16,9 @@ own g); --bias and --act add the fused epilogue out = act(C + bias) (bias a
 seeded N(0, 0.5) vector); --sa-rows 1 scales A per row and K segment (1 x g
 blocks, quantised by dg_quantize_fp8_rows) instead of per g x g block;
 --layout stores A as [K,M] (tt, tn) and/or B as [K,N] (nn, tn), transposed
-on the GPU before timing, and calls dg_gemm_fp8_layout; the default run is
-the E4M3 NT workload as specified.
+on the GPU before timing, and calls dg_gemm_fp8_layout; --workspace calls
+dg_gemm_fp8_ws with a workspace instead (small-M shapes may then split K over
+workgroups); the default run is the E4M3 NT workload as specified.
 
 Inputs: FP32 matrices drawn from the seeded generators in ``synth`` (the
 workload's shapes and value distributions), copied to the GPU and block
@@ -83,7 +85,7 @@ TRAFFIC = {
 # shared device header, the argument header and the host dispatch.
 _COMMON_SOURCES = ("gemm_common.h", "gemm_fp8_nt.h", "dg_host.hip")
 KERNEL_SOURCES = {
-    "decode_m64_n4096_k7168": ("gemm_fp8_nt_stream.hip",) + _COMMON_SOURCES,
+    "decode_m64_n4096_k7168": ("gemm_fp8_stream.hip",) + _COMMON_SOURCES,
     "square8192": ("gemm_fp8_big.h", "gemm_fp8_nt_big.hip") + _COMMON_SOURCES,
     "prefill_m4096_n7168_k2048": ("gemm_fp8_big.h", "gemm_fp8_nt_big.hip") + _COMMON_SOURCES,
     "longk_m2000_n4000_k16384_g64": ("gemm_fp8_big.h", "gemm_fp8_nt_big.hip") + _COMMON_SOURCES,
@@ -158,7 +160,7 @@ LAYOUTS = {"nt": 0, "nn": 1, "tt": 2, "tn": 3}
 
 
 def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int = 0, fb: int = 0,
-            bias: bool = False, act: int = 0, sa_rows: int | None = None, layout: int = 0):
+            bias: bool = False, act: int = 0, sa_rows: int | None = None, layout: int = 0, ws: bool = False):
     import torch
 
     import fp8_block_scaled_scales_amd as dg
@@ -181,13 +183,23 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
                      torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
     stream = torch.cuda.current_stream(dev)
     print("bench: workload %d %s, %d input sets of %.1f MB, tile %s" % (
-        c, w["name"], sets, set_bytes / 1e6, dg.dg_query_tile(M, N, K, g, layout)), file=sys.stderr, flush=True)
+        c, w["name"], sets, set_bytes / 1e6, dg.dg_query_tile(M, N, K, g, layout, workspace=ws)), file=sys.stderr,
+        flush=True)
 
     tbias = torch.from_numpy(make_bias(N)).to(dev) if bias else None
+    # one workspace for every call: they all run on one stream
+    wsbuf = dg.dg_workspace(M, N, K, g, layout, device=dev) if ws else None
 
     def launch(i, st):
         x = bufs[i % sets]
-        if layout:
+        if ws:
+            dg.dg_gemm_fp8_ws(x[0], x[2], x[1], x[3], out=x[4], gran=g, layout=layout, sa_rows=sa_rows, fmt_a=fa,
+                              fmt_b=fb, bias=tbias, act=act, workspace=wsbuf, stream=st)
+        elif layout and sa_rows == 1:
+            # per-row A factors with a transposed layout: the workspace call, without a workspace
+            dg.dg_gemm_fp8_ws(x[0], x[2], x[1], x[3], out=x[4], gran=g, layout=layout, sa_rows=1, fmt_a=fa, fmt_b=fb,
+                              bias=tbias, act=act, stream=st)
+        elif layout:
             dg.dg_gemm_fp8_layout(x[0], x[2], x[1], x[3], out=x[4], gran=g, layout=layout, fmt_a=fa, fmt_b=fb,
                                   bias=tbias, act=act, stream=st)
         elif sa_rows == 1:
@@ -339,10 +351,11 @@ def cpu_leg(c: int, g: int, fa: int = 0, fb: int = 0, bias: bool = False, act: i
     b_st = np.ascontiguousarray(b8.T) if layout & 1 else b8
 
     def ref(rows=None):
-        if layout:
-            r = oracle.gemm_ref_layout(a_st, b_st, sa, sb, g, layout, M, N, K, fa, fb, rows=rows)
-        elif sa_rows == 1:
+        if sa_rows == 1:
+            # per-row A factors: the oracle on the logical operands (the stored layout changes no product)
             r = oracle.gemm_ref_rowa(a8, b8, sa, sb, g, fa, fb, rows=rows)
+        elif layout:
+            r = oracle.gemm_ref_layout(a_st, b_st, sa, sb, g, layout, M, N, K, fa, fb, rows=rows)
         elif fa == 0 and fb == 0:
             r = oracle.gemm_ref(a8, b8, sa, sb, g, rows=rows)
         else:
@@ -395,6 +408,8 @@ def main():
     ap.add_argument("--act", default="none", choices=sorted(ACTS), help="fused epilogue activation")
     ap.add_argument("--layout", default="nt", choices=sorted(LAYOUTS),
                     help="operand storage: A [M,K] or [K,M] (first letter n / t), B [N,K] or [K,N] (t / n)")
+    ap.add_argument("--workspace", action="store_true",
+                    help="call dg_gemm_fp8_ws with a workspace (small-M shapes may then split K over workgroups)")
     ap.add_argument("--sa-rows", type=int, default=None, choices=(1,),
                     help="1: per-row A factors (1 x g blocks) instead of g x g blocks")
     ap.add_argument("--quant", default=None, choices=("a", "b"),
@@ -453,10 +468,8 @@ def main():
     flops, nbytes = algorithmic(w, g, args.sa_rows)
     act = ACTS[args.act]
     layout = LAYOUTS[args.layout]
-    if layout and args.sa_rows == 1:
-        raise SystemExit("--sa-rows 1 runs the NT layout only")
     ms, sets, finite, glen, trials = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb, args.bias, act, args.sa_rows,
-                                     layout)
+                                             layout, args.workspace)
     if not finite:
         raise SystemExit("GEMM output holds non-finite values")
     sec = ms * 1e-3
@@ -466,8 +479,8 @@ def main():
         achieved, peak, unit = tflops, PEAK_FP8_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / sec / 1e9, PEAK_HBM_GBS, "GB/s"
-    default_variant = (fa, fb, g, args.bias, act, args.sa_rows, layout, args.sets) == \
-        (0, 0, w["g"], False, 0, None, 0, None)
+    default_variant = (fa, fb, g, args.bias, act, args.sa_rows, layout, args.sets, args.workspace) == \
+        (0, 0, w["g"], False, 0, None, 0, None, False)
     tr = TRAFFIC.get(w["name"]) if default_variant else None
     traffic = tr["bytes"] if tr and tr["src"] == kernel_source_hash(w["name"]) else None
 
@@ -490,6 +503,7 @@ def main():
                    "epilogue": ("bias+" if args.bias else "") + args.act,
                    "a_scales": "1x%d" % g if args.sa_rows == 1 else "%dx%d" % (g, g),
                    "layout": args.layout.upper(), "out": "bf16", "input_sets": sets,
+                   "entry": "dg_gemm_fp8_ws (workspace)" if args.workspace else "without workspace",
                    "launch": "hipGraph of %d launches, replayed %d times" % (glen, args.steps // glen),
                    "trials_us": {"n": len(trials), "median": round(statistics.median(trials) * 1e3, 3),
                                  "min": round(min(trials) * 1e3, 3), "max": round(max(trials) * 1e3, 3)},

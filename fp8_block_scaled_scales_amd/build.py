@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdg.so")
-SOURCES = ["dg_host.hip", "gemm_fp8_nt.hip", "gemm_fp8_nt_big.hip", "gemm_fp8_nt_stream.hip", "gemm_fp8_layouts.hip",
+SOURCES = ["dg_host.hip", "gemm_fp8_nt.hip", "gemm_fp8_nt_big.hip", "gemm_fp8_stream.hip", "gemm_fp8_layouts.hip",
            "gemm_fp8_big_layouts.hip", "gemm_fp8_layouts_rowa.hip", "gemm_fp8_big_layouts_rowa.hip", "quant_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

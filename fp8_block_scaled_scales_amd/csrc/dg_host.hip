@@ -121,12 +121,11 @@ struct Plan {
 
 // Tile-table choice (pure host arithmetic, no HIP call).
 // Small M streams B. Without a workspace (every call but dg_gemm_fp8_ws) a
-// small-M NT shape takes 32x32 tiles over the whole K, whose waves split K
-// inside the workgroup, whatever the tile count; a transposed layout takes
-// 64x64 tiles over the whole K. With a workspace, shapes with fewer than 192
-// tiles of 32x32 (or any transposed small-M shape) split the K range of each
-// 64x64 tile over several workgroups until about one workgroup per CU (256)
-// runs, keeping at least 4 pipeline steps per split.
+// small-M shape of any layout takes 32x32 tiles over the whole K, whose waves
+// split K inside the workgroup, whatever the tile count. With a workspace,
+// shapes with fewer than 192 tiles of 32x32 split the K range of each 64x64
+// tile over several workgroups until about one workgroup per CU (256) runs,
+// keeping at least 4 pipeline steps per split.
 // Large M and N take the 256-row tiles (256 or 128 wide) when they give at
 // least 3/4 of a tile per CU; the rest takes 128x128 tiles over the whole K.
 // DG_FORCE_TILE=<kernel id> overrides the choice when that entry has the
@@ -161,7 +160,6 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout, bool split_ok)
     p.ksplit = split_ok ? (int)splits_for(p.e, p.tiles, nsteps) : 1;
     return p;
   };
-  if (layout != DG_LAYOUT_NT && M <= 128) return split_k();
   const int force = layout == DG_LAYOUT_NT ? forced_tile() : -1;
   if (force >= 0) {
     for (int i = 0; i < dg::kTableSize; ++i)
@@ -175,7 +173,7 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout, bool split_ok)
   if (M <= 128) {
     const dg::KernelEntry* st = find(dg::kClassStream, gran);
     const int64_t st_tiles = tiles_of(st, M, N);
-    if (st_tiles >= 192 || !split_ok) {
+    if (!split_ok || st_tiles >= 192) {
       p.e = st;
       p.tiles = st_tiles;
       return p;
@@ -328,8 +326,10 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
                  "(%dx%d, %d stages, %d waves) ksplit %d grid %lld workspace %lld\n",
                  (long long)M, (long long)N, (long long)K, gran, layout, sa_rows, fmt_a, fmt_b, bias ? 1 : 0, act, e->id,
                  e->bm, e->bn, e->stages, e->waves, pl.ksplit, (long long)(pl.tiles * pl.ksplit), (long long)need);
-  t_last_hip = layout == DG_LAYOUT_NT ? e->launch(p, static_cast<hipStream_t>(stream))
-                                      : dg::launch_layout(e->id, p, static_cast<hipStream_t>(stream));
+  // the streaming entries take every layout themselves
+  t_last_hip = layout == DG_LAYOUT_NT || e->cls == dg::kClassStream
+                   ? e->launch(p, static_cast<hipStream_t>(stream))
+                   : dg::launch_layout(e->id, p, static_cast<hipStream_t>(stream));
   return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
 }
 

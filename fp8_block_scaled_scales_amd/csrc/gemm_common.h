@@ -155,11 +155,16 @@ __device__ __forceinline__ void stage_slab(v4i rsrc, uint8_t* lds, uint32_t K, u
 //     every 32 rows;
 //   64-byte rows (four rows = all banks): rows four apart share bank offsets,
 //     so bit 1 flips with (r/4)%2 and bit 0 every 32 rows.
+//   32-byte rows (the streaming class): the eight rows a 32-lane half reads
+//     are 256 contiguous bytes already, so no swizzle.
 template <int W>
 __device__ __forceinline__ int tkey(int row) {
-  static_assert(W == 64 || W == 128 || W == 256, "transposed tile width");
+  static_assert(W == 32 || W == 64 || W == 128 || W == 256, "transposed tile width");
   const int far = (row >> 5) & 1;
-  return W == 64 ? ((((row >> 2) & 1) << 1) | far) : W == 128 ? ((row & 7) ^ far) : ((2 * (row & 7)) ^ far);
+  return W == 32    ? 0
+         : W == 64  ? ((((row >> 2) & 1) << 1) | far)
+         : W == 128 ? ((row & 7) ^ far)
+                    : ((2 * (row & 7)) ^ far);
 }
 
 // One instruction of a transposed tile's copy: rows RPI*grp .. RPI*grp+RPI-1

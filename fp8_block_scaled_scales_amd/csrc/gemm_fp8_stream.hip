@@ -25,6 +25,14 @@
 // template article's per-channel choice, §3.4): each A slot carries the
 // step's 32 (g >= 128) or 64 (g = 64) row factors, copied ahead of the slab
 // by one 4-byte-per-lane copy; the B ring gives up a slot to make room.
+//
+// Transposed operands (LAYOUT; DeepGEMM实战 §3.3: A stored [K,M] and/or B
+// stored [K,N]): a step's tile of such an operand is its 128 K rows of 32
+// bytes, copied with the same number of 16-byte-per-lane copies as the NT
+// slab (32 K rows per copy) and read with the transposing LDS read. Eight
+// such rows are 256 contiguous bytes, all banks once, so these slabs need no
+// swizzle. The fragments hold the same K bytes in the same order as the NT
+// ones, so every layout gives the NT bits.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -63,6 +71,14 @@ struct Ring {
   static_assert(A_AHEAD * (A_LOADS + B_LOADS) + (B_AHEAD - A_AHEAD) * B_LOADS < 64, "vmcnt range");
 };
 
+// Descriptor over step st's tile of an operand stored [K, len], from column
+// col0 (see tile_range_t); steps past the end get an empty range, so their
+// copies move nothing.
+__device__ __forceinline__ v4i step_rsrc_t(const uint8_t* base, int K, int len, int col0, int st, int nsteps) {
+  const int64_t k0 = (int64_t)st * BK;
+  return st < nsteps ? rsrc_words(base + k0 * len + col0, tile_range_t(k0, K, len, col0, BK)) : rsrc_words(base, 0);
+}
+
 __device__ __forceinline__ v8i frag(const uint8_t* slab, int row, int c0) {
   const int sw = (row >> 1) & 7;
   const v4i lo = *reinterpret_cast<const v4i*>(slab + row * BK + ((c0 ^ sw) << 4));
@@ -73,9 +89,9 @@ __device__ __forceinline__ v8i frag(const uint8_t* slab, int row, int c0) {
 // G: K segment contracted before each promotion; scale blocks sg = G << sshift
 // (g = 256 runs the G = 128 kernel with one factor per two segments). FMT bit
 // 0: A is E5M2 (else E4M3), bit 1: B is E5M2. ROWA: A's factors are per row,
-// sa is [M][K/sg].
-template <int G, int FMT, int EPI, bool ROWA>
-__global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __restrict__ a,
+// sa is [M][K/sg]. LAYOUT bit 1: A stored [K,M]; bit 0: B stored [K,N].
+template <int G, int FMT, int EPI, bool ROWA, int LAYOUT>
+__global__ __launch_bounds__(64 * NW) void gemm_fp8_stream(const uint8_t* __restrict__ a,
                                                               const uint8_t* __restrict__ b,
                                                               const float* __restrict__ sa,
                                                               const float* __restrict__ sb,
@@ -83,6 +99,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
                                                               int tiles_m, int tiles_n, int sshift,
                                                               const float* __restrict__ bias, int relu) {
   static_assert(G == 64 || G == 128, "granularity");
+  constexpr bool TA = (LAYOUT & 2) != 0, TB = (LAYOUT & 1) != 0;
   using R = Ring<ROWA>;
   constexpr int SEGS = BK / G;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NW * R::WAVE_LDS];
@@ -93,8 +110,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
   map_tile<2>(tiles_m, tiles_n, ks, tmi, tni);
   const int m0 = tmi * BM, n0 = tni * BN;
   const uint32_t uK = (uint32_t)K;
-  const v4i ra = rsrc_words(a + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * uK);
-  const v4i rb = rsrc_words(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
+  // NT operands: one descriptor over the tile's rows for the whole K
+  // (transposed ones take one per step, step_rsrc_t)
+  const v4i ra = TA ? (v4i){} : rsrc_words(a + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * uK);
+  const v4i rb = TB ? (v4i){} : rsrc_words(b + (int64_t)n0 * K, (uint32_t)min(BN, N - n0) * uK);
 
   const int nkb = K / G;
   const int sg = G << sshift, nks = K / sg;
@@ -121,14 +140,36 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
     if constexpr (ROWA)
       stage_row_scales<BM, SEGS>(rsa, slot + A_SLAB, (uint32_t)nks, (uint32_t)((st * SEGS) >> sshift), 0, lane,
                                  st < nsteps);
+    if constexpr (TA) {
+      const v4i rat = step_rsrc_t(a, K, M, m0, st, nsteps);
 #pragma unroll
-    for (int g = 0; g < BM / 8; ++g) stage_group<1>(ra, slot, uK, (uint32_t)st * BK, g, lane, st < nsteps);
+      for (int g = 0; g < BK / 32; ++g) stage_group_t<BM>(rat, slot, (uint32_t)M, g, lane);
+    } else {
+#pragma unroll
+      for (int g = 0; g < BM / 8; ++g) stage_group<1>(ra, slot, uK, (uint32_t)st * BK, g, lane, st < nsteps);
+    }
   };
   auto issue_b = [&](int t) {
     const int st = wave + NW * t;
+    uint8_t* const slot = b_ring + (t % R::B_SLOTS) * B_SLAB;
+    if constexpr (TB) {
+      const v4i rbt = step_rsrc_t(b, K, N, n0, st, nsteps);
 #pragma unroll
-    for (int g = 0; g < BN / 8; ++g)
-      stage_group<1>(rb, b_ring + (t % R::B_SLOTS) * B_SLAB, uK, (uint32_t)st * BK, g, lane, st < nsteps);
+      for (int g = 0; g < BK / 32; ++g) stage_group_t<BN>(rbt, slot, (uint32_t)N, g, lane);
+    } else {
+#pragma unroll
+      for (int g = 0; g < BN / 8; ++g) stage_group<1>(rb, slot, uK, (uint32_t)st * BK, g, lane, st < nsteps);
+    }
+  };
+  // The lane's 32x32x64 fragment of K half q (K bytes 64q + 32*(lane/32) ..
+  // +31 of the step) from a slab, NT or transposed.
+  auto frag_a = [&](const uint8_t* s, int q) {
+    if constexpr (TA) return frag_tr<BM>(s, 0, 64 * q, lane);
+    else return frag(s, lane & 31, 4 * q + 2 * (lane >> 5));
+  };
+  auto frag_b = [&](const uint8_t* s, int q) {
+    if constexpr (TB) return frag_tr<BN>(s, 0, 64 * q, lane);
+    else return frag(s, lane & 31, 4 * q + 2 * (lane >> 5));
   };
 
   v16f acc = {};
@@ -158,26 +199,35 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
     issue_b(R::B_AHEAD - R::A_AHEAD + j);
   }
 
-  const int r32 = lane & 31, h2 = lane >> 5;
+  const int h2 = lane >> 5;
   for (int t = 0; t < my_steps; ++t) {
     DG_WAIT_VMCNT(R::WAIT_AFTER_A);  // A(t) and the earlier-issued B(t) have landed
     const int st = wave + NW * t;
-    const uint8_t* As = a_ring + (t % R::A_SLOTS) * R::A_PITCH;
-    const uint8_t* Bs = b_ring + (t % R::B_SLOTS) * B_SLAB;
+    uint8_t* const As = a_ring + (t % R::A_SLOTS) * R::A_PITCH;
+    uint8_t* const Bs = b_ring + (t % R::B_SLOTS) * B_SLAB;
+    if constexpr (LAYOUT != 0) {
+      // the tensor's last K row of a transposed operand whose stored row
+      // length is not a multiple of 4 (see patch_tail_t); the slots are this
+      // wave's own, so its own copies having landed is enough
+      if (st == nsteps - 1) {
+        const int row = K - 1 - st * BK;
+        if (TA && (M & 3)) patch_tail_t<BM>(As, a + (int64_t)(K - 1) * M, row, M, m0, lane);
+        if (TB && (N & 3)) patch_tail_t<BN>(Bs, b + (int64_t)(K - 1) * N, row, N, n0, lane);
+      }
+    }
     // ROWA: factors [SEGS][32] of the step; this lane's rows 8c + 4*h2 .. +3
     const float* const srow = reinterpret_cast<const float*>(As + A_SLAB) + 4 * h2;
 #pragma unroll
     for (int h = 0; h < BK / 64; ++h) {
       const int kb = G == 128 ? st : 2 * st + h;
       if (G == 64 && kb >= nkb) break;  // K % 128 == 64: the last step holds one segment
-      const int c0 = 4 * h + 2 * h2;
-      const v8i af = frag(As, r32, c0);
-      const v8i bf = frag(Bs, r32, c0);
+      const v8i af = frag_a(As, h);
+      const v8i bf = frag_b(Bs, h);
       if (G == 128) {
         if (h == 0) {
           // the segment is the whole step: chain both halves, then promote once
-          const v8i af1 = frag(As, r32, c0 + 4);
-          const v8i bf1 = frag(Bs, r32, c0 + 4);
+          const v8i af1 = frag_a(As, 1);
+          const v8i bf1 = frag_b(Bs, 1);
           v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, (v16f){}, FMT & 1, FMT >> 1, 0, 0, 0, 0);
           p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af1, bf1, p, FMT & 1, FMT >> 1, 0, 0, 0, 0);
           promote(p, srow, sb_row[kb >> sshift], sa_row[kb >> sshift]);
@@ -216,25 +266,37 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_nt_stream(const uint8_t* __r
   }
 }
 
-template <int G, int FMT, int EPI, bool ROWA>
+template <int G, int FMT, int EPI, bool ROWA, int LAYOUT>
 hipError_t launch_fa(const GemmArgs& p, hipStream_t stream) {
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_fp8_nt_stream<G, FMT, EPI, ROWA>), dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream, p.a,
-                     p.b, p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.sshift, p.bias, p.act == 1 ? 1 : 0);
+  hipLaunchKernelGGL((gemm_fp8_stream<G, FMT, EPI, ROWA, LAYOUT>), dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream,
+                     p.a, p.b, p.sa, p.sb, p.out, (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.sshift, p.bias,
+                     p.act == 1 ? 1 : 0);
   return hipGetLastError();
 }
 
-template <int G, int FMT, int EPI>
+template <int G, int FMT, int EPI, int LAYOUT>
 hipError_t launch_sa(const GemmArgs& p, hipStream_t stream) {
-  return p.rowa ? launch_fa<G, FMT, EPI, true>(p, stream) : launch_fa<G, FMT, EPI, false>(p, stream);
+  return p.rowa ? launch_fa<G, FMT, EPI, true, LAYOUT>(p, stream) : launch_fa<G, FMT, EPI, false, LAYOUT>(p, stream);
 }
 
-template <int G, int FMT>
+template <int G, int FMT, int LAYOUT>
 hipError_t launch_fmt(const GemmArgs& p, hipStream_t stream) {
   switch (epilogue_form(p.bias, p.act)) {
-    case 0: return launch_sa<G, FMT, 0>(p, stream);
-    case 1: return launch_sa<G, FMT, 1>(p, stream);
-    case 2: return launch_sa<G, FMT, 2>(p, stream);
+    case 0: return launch_sa<G, FMT, 0, LAYOUT>(p, stream);
+    case 1: return launch_sa<G, FMT, 1, LAYOUT>(p, stream);
+    case 2: return launch_sa<G, FMT, 2, LAYOUT>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int G, int LAYOUT>
+hipError_t launch_l(const GemmArgs& p, hipStream_t stream) {
+  switch (p.fmt) {
+    case 0: return launch_fmt<G, 0, LAYOUT>(p, stream);
+    case 1: return launch_fmt<G, 1, LAYOUT>(p, stream);
+    case 2: return launch_fmt<G, 2, LAYOUT>(p, stream);
+    case 3: return launch_fmt<G, 3, LAYOUT>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -242,17 +304,18 @@ hipError_t launch_fmt(const GemmArgs& p, hipStream_t stream) {
 template <int G>
 hipError_t launch(const GemmArgs& p, hipStream_t stream) {
   if (p.ksplit != 1 || p.sshift < 0 || p.sshift > 1) return hipErrorInvalidValue;
-  switch (p.fmt) {
-    case 0: return launch_fmt<G, 0>(p, stream);
-    case 1: return launch_fmt<G, 1>(p, stream);
-    case 2: return launch_fmt<G, 2>(p, stream);
-    case 3: return launch_fmt<G, 3>(p, stream);
+  switch (p.layout) {
+    case 0: return launch_l<G, 0>(p, stream);
+    case 1: return launch_l<G, 1>(p, stream);
+    case 2: return launch_l<G, 2>(p, stream);
+    case 3: return launch_l<G, 3>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace stream
 
+// Every layout: the NT table entries (6, 7) and their transposed forms.
 hipError_t launch_stream_g128(const GemmArgs& p, hipStream_t s) { return stream::launch<128>(p, s); }
 hipError_t launch_stream_g64(const GemmArgs& p, hipStream_t s) { return stream::launch<64>(p, s); }
 

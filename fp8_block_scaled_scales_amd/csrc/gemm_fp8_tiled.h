@@ -248,14 +248,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     // contiguous per wave.
     //
     // Publication (HIP memory model, agent scope): every wave stores its part
-    // of the partial, then a release fence at agent scope orders those stores
-    // before the workgroup's arrival; the arrival is a read-modify-write of
-    // the tile's counter, and the workgroup that completes the count takes an
-    // acquire fence at agent scope before reading the other partials. The
-    // per-XCD L2s are not coherent with each other; the fences write back and
-    // invalidate what these need. The stores and loads also carry the
-    // device-scope cache policy (sc1), so the partials go to and come from the
-    // coherence point instead of sitting dirty in one XCD's L2.
+    // of the partial and waits for those stores; the workgroup barrier (a
+    // workgroup-scope release and acquire) orders them before thread 0's
+    // arrival, a read-modify-write of the tile's counter with release
+    // semantics at agent scope, and the thread that completes the count takes
+    // an acquire fence at agent scope before the barrier after which every
+    // wave reads the other partials. The per-XCD L2s are not coherent with
+    // each other; the agent-scope release and acquire write back and
+    // invalidate what these need, once per workgroup (one such fence per wave
+    // would sweep the L2 four times per workgroup). The stores and loads also
+    // carry the device-scope cache policy (sc1), so the partials go to and
+    // come from the coherence point instead of sitting dirty in one XCD's L2.
     //
     // The counter holds (epoch << 16) | arrivals. An arrival that finds
     // another call's tag counts from zero, so a workspace needs no clearing
@@ -280,7 +283,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
                                                  lane_off + (uint32_t)(((i * TN + j) * 4 + c) * 256 * 4),
                                                  (uint32_t)ks * TILE_F * 4, CPOL_SC1);
         }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's partial stores, before the arrival
+    DG_WAIT_VMCNT(0);  // this wave's partial stores have completed
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     __shared__ int last;
     if (threadIdx.x == 0) {

@@ -175,8 +175,9 @@ int dg_gemm_fp8_nt_ex(const void* a, const void* b, const float* sa, const float
  *
  * The result is the same product, out[i,j] as in dg_gemm_fp8_nt_epi, for any
  * M and N (a stored row of M or N bytes need not be a multiple of 16 long);
- * a and b 16-byte aligned as before. DG_LAYOUT_NT is dg_gemm_fp8_nt_epi bit
- * for bit. dg_query_tile_layout names the tile a layout runs.
+ * a and b 16-byte aligned as before. Every layout gives dg_gemm_fp8_nt_epi's
+ * result bit for bit (the same K order inside every product).
+ * dg_query_tile_layout names the tile a layout runs: the NT choice.
  * dg_gemm_fp8_ws (with no workspace) takes a layout together with per-row A
  * factors.
  */

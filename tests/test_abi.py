@@ -169,12 +169,12 @@ def test_layout_accepts_any_row_length(dg, layout, M, N):
     assert t["grid"] > 0 and t["ksplit"] == 1
 
 
-@pytest.mark.parametrize("M,N,K,g,layout,tile", [(64, 4096, 7168, 128, 1, (64, 64)), (4096, 7168, 2048, 128, 3, (256, 256)),
-                                                 (1008, 3008, 512, 64, 2, (128, 128)), (128, 512, 1024, 256, 3, (64, 64)),
+@pytest.mark.parametrize("M,N,K,g,layout,tile", [(64, 4096, 7168, 128, 1, (32, 32)), (4096, 7168, 2048, 128, 3, (256, 256)),
+                                                 (1008, 3008, 512, 64, 2, (128, 128)), (128, 512, 1024, 256, 3, (32, 32)),
                                                  (2000, 4000, 1024, 128, 1, (256, 128)), (3584, 3584, 512, 256, 2, (256, 256))])
 def test_layout_tile_choice(dg, M, N, K, g, layout, tile):
-    # transposed layouts: 64x64 tiles over the whole K for M <= 128, else the 256-row tiles 256 or 128 wide or
-    # 128x128; without a workspace nothing splits K
+    # transposed layouts: the NT choice, streaming 32x32 tiles for M <= 128, else the 256-row tiles 256 or 128
+    # wide or 128x128; without a workspace nothing splits K
     t = dg.dg_query_tile(M, N, K, g, layout)
     assert (t["bm"], t["bn"]) == tile
     assert t["ksplit"] == 1 and t["workspace_bytes"] == 0
@@ -252,14 +252,16 @@ def test_query_tile_choice(dg, M, N, K, g, cls):
     assert t["workspace_bytes"] == 0
 
 
-# dg_gemm_fp8_ws's plan: small M with fewer than 192 tiles of 32x32 (or any
-# transposed small-M shape) splits K over 64x64 tiles; everything else is the
-# plan without a workspace, which needs no workspace.
+# dg_gemm_fp8_ws's plan: small M with fewer than 192 tiles of 32x32 (any
+# layout) splits K over 64x64 tiles; everything else is the plan without a
+# workspace, which needs no workspace.
 @pytest.mark.parametrize("M,N,K,g,layout,cls", [
     (64, 512, 7168, 128, 0, (64, 64, 14)),     # 8 tiles x 14 splits (steps/4 caps at 14)
     (8, 300, 2048, 128, 0, (64, 64, 4)),       # 5 tiles, 16 steps: 4 splits of 4 steps
     (64, 4096, 7168, 128, 0, (32, 32, 1)),     # 256 streaming tiles: no split
-    (64, 4096, 7168, 128, 1, (64, 64, 4)),     # transposed B: 64 tiles x 4
+    (64, 4096, 7168, 128, 1, (32, 32, 1)),     # B stored [K,N]: 256 streaming tiles, no split
+    (64, 4096, 7168, 128, 2, (32, 32, 1)),     # A stored [K,M]: the same
+    (64, 1024, 7168, 128, 3, (64, 64, 14)),    # 16 tiles x 14 splits (steps/4 caps at 14)
     (8192, 8192, 8192, 128, 0, (256, 256, 1)),
 ])
 def test_query_tile_ws_choice(dg, M, N, K, g, layout, cls):

@@ -26,9 +26,10 @@ TRANSPOSED = [NN, TT, TN]
 
 # (M, N, K, g, expected tile): ragged M, N (multiples of 16)
 SHAPES = [
-    (64, 4096, 1024, 128, (64, 64)),    # 64x64 over the whole K
-    (96, 528, 1088, 64, (64, 64)),
-    (128, 512, 1024, 256, (64, 64)),
+    (64, 4096, 1024, 128, (32, 32)),    # streaming 32x32 over the whole K
+    (96, 528, 1088, 64, (32, 32)),
+    (128, 512, 1024, 256, (32, 32)),
+    (64, 4096, 7168, 128, (32, 32)),    # the decode shape
     (1008, 3008, 512, 128, (128, 128)),  # tiled
     (1024, 2000, 576, 64, (128, 128)),
     (512, 1040, 768, 256, (128, 128)),
@@ -119,12 +120,14 @@ def test_layout_with_formats_and_epilogue(M, N, K, g, tile, layout, fa, fb, act,
 @pytest.mark.parametrize("M,N,K,g,tile", SHAPES)
 def test_transposed_layouts_agree_bitwise(M, N, K, g, tile):
     a8, sa, b8, sb = _operands(M, N, K, g, 0, 0, seed=13000 + M + K)
+    # every layout's fragments hold the NT K order, so all four give the same bits
     bits = {}
-    for layout in TRANSPOSED:
+    for layout in [NT] + TRANSPOSED:
         a_st, b_st = _store(a8, b8, layout)
         say("layout %d bits M=%d N=%d K=%d g=%d" % (layout, M, N, K, g))
         bits[layout] = _run(a_st, b_st, sa, sb, g, layout)[1]
-    assert np.array_equal(bits[NN], bits[TT]) and np.array_equal(bits[NN], bits[TN])
+    for layout in TRANSPOSED:
+        assert np.array_equal(bits[layout], bits[NT]), layout
 
 
 @pytest.mark.parametrize("layout", TRANSPOSED)

@@ -111,9 +111,10 @@ def test_max_k_256x128_tiles(pool, g, layout):
     _check_long_k(pool, 2048, 3072, g, layout, (256, 128))
 
 
-@pytest.mark.parametrize("layout,tile,ws", [(0, (32, 32), False), (3, (64, 64), False), (3, (64, 64), True)])
-def test_max_k_small_m(pool, layout, tile, ws):
-    _check_long_k(pool, 64, 4096, 128, layout, tile, ws)
+@pytest.mark.parametrize("layout,N,tile,ws", [(0, 4096, (32, 32), False), (3, 4096, (32, 32), False),
+                                              (3, 1024, (64, 64), True)])
+def test_max_k_small_m(pool, layout, N, tile, ws):
+    _check_long_k(pool, 64, N, 128, layout, tile, ws)
 
 
 @pytest.mark.parametrize("big_m,layout", [(True, 0), (True, 2), (False, 0)])
