@@ -21,6 +21,9 @@ import torch  # loads the HIP runtime libdg.so binds to
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdg.so")
+# The same sources built with an extra full wait and workgroup barrier after
+# every pipeline step (race check build; see load_library).
+SYNC_LIB_PATH = os.path.join(_HERE, "libdg_sync.so")
 
 DG_OK = 0
 DG_EINVAL = -1
@@ -42,11 +45,15 @@ class dg_tile_info(ctypes.Structure):
                 ("ksplit", ctypes.c_int), ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError("libdg.so is not built (run fp8_block_scaled_scales_amd.build.build()); "
-                          "there is no non-HIP fallback")
-    lib = ctypes.CDLL(LIB_PATH)
+def load_library(path: str):
+    """Open a build of the C ABI at ``path`` (ctypes handle with every
+    signature declared). The package itself uses libdg.so; the race check
+    build libdg_sync.so is opened this way beside it (its own symbols, bound
+    within itself) to compare the two builds' results."""
+    if not os.path.exists(path):
+        raise ImportError("%s is not built (run fp8_block_scaled_scales_amd.build.build()); "
+                          "there is no non-HIP fallback" % os.path.basename(path))
+    lib = ctypes.CDLL(path)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.dg_gemm_fp8_nt.restype = ctypes.c_int
     lib.dg_gemm_fp8_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
@@ -89,7 +96,7 @@ def _load():
     return lib
 
 
-_lib = _load()
+_lib = load_library(LIB_PATH)
 lib = _lib  # raw ctypes handle, for tests that exercise the C ABI directly
 
 

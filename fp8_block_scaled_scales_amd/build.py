@@ -6,6 +6,7 @@ fp8_block_scaled_scales_amd.build``. Always recompiles.
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -13,8 +14,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdg.so")
-SOURCES = ["dg_host.hip", "gemm_fp8_nt.hip", "gemm_fp8_nt_big.hip", "gemm_fp8_stream.hip", "gemm_fp8_layouts.hip",
-           "gemm_fp8_big_layouts.hip", "gemm_fp8_layouts_rowa.hip", "gemm_fp8_big_layouts_rowa.hip", "quant_fp8.hip"]
+# Longest compiles first, so the parallel build's slowest jobs start at once.
+SOURCES = ["gemm_fp8_big_layouts_rowa.hip", "gemm_fp8_big_layouts.hip", "gemm_fp8_stream.hip",
+           "gemm_fp8_layouts_rowa.hip", "gemm_fp8_layouts.hip", "gemm_fp8_nt_big.hip", "gemm_fp8_nt.hip",
+           "quant_fp8.hip", "dg_host.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -32,37 +35,55 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source to an object at once (one hipcc per source), then link."""
+# Libraries built from the same sources: the release build, and the race
+# check build with an extra full wait and workgroup barrier after every
+# pipeline step (DG_EXTRA_SYNC in gemm_common.h), whose results must equal the
+# release build's bit for bit.
+VARIANTS = {"libdg.so": [], "libdg_sync.so": ["-DDG_EXTRA_SYNC"]}
+LINK = ["--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-Bsymbolic"]
+
+
+def build(verbose: bool = False, variants=None) -> str:
+    """Compile every source of every variant to an object (at most one hipcc
+    per CPU at a time), then link each library. Returns the release library's
+    path."""
+    names = list(VARIANTS) if variants is None else list(variants)
     tag = "%d" % os.getpid()
-    objs, procs = [], []
+    jobs = []
     for src in SOURCES:
-        obj = os.path.join(CSRC, src + ".tmp%s.o" % tag)
-        cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + ["-c", os.path.join(CSRC, src), "-o", obj]
+        for name in names:
+            obj = os.path.join(CSRC, "%s.%s.tmp%s.o" % (src, name.split(".")[0], tag))
+            cmd = [HIPCC] + [f for f in FLAGS if f != "-shared"] + VARIANTS[name] + \
+                ["-c", os.path.join(CSRC, src), "-o", obj]
+            jobs.append((name, obj, cmd))
+
+    def compile_one(cmd):
         if verbose:
             print(" ".join(cmd), flush=True)
-        objs.append(obj)
-        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
-    failed = False
-    for p in procs:
-        out, err = p.communicate()
-        if p.returncode != 0:
-            sys.stderr.write(out + err)
-            failed = True
+        return subprocess.run(cmd, capture_output=True, text=True)
+
+    width = max(1, min(len(jobs), os.cpu_count() or 1))
     try:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=width) as pool:
+            results = list(pool.map(compile_one, [cmd for _, _, cmd in jobs]))
+        failed = [r for r in results if r.returncode != 0]
+        for r in failed:
+            sys.stderr.write(r.stdout + r.stderr)
         if failed:
-            raise RuntimeError("hipcc failed compiling libdg.so's sources")
-        tmp = LIB + ".tmp" + tag
-        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            sys.stderr.write(res.stdout + res.stderr)
-            raise RuntimeError("hipcc failed linking libdg.so")
-        os.replace(tmp, LIB)
+            raise RuntimeError("hipcc failed compiling the library sources")
+        for name in names:
+            lib = os.path.join(HERE, name)
+            tmp = lib + ".tmp" + tag
+            cmd = [HIPCC] + LINK + [obj for n, obj, _ in jobs if n == name] + ["-o", tmp]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError("hipcc failed linking " + name)
+            os.replace(tmp, lib)
     finally:
-        for obj in objs:
+        for _, obj, _ in jobs:
             if os.path.exists(obj):
                 os.remove(obj)
     return LIB

@@ -19,6 +19,31 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #define DG_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
 
+// Race check build (compiled with -DDG_EXTRA_SYNC into libdg_sync.so): every
+// pipeline step ends with all of the wave's memory operations drained (every
+// copy in flight landed, every LDS read done) and, in the kernels whose waves
+// share the LDS ring, a workgroup barrier (the extra barrier per buffer switch
+// of the template article, §5.5). The ring's own waits and barriers are meant
+// to make these redundant, so this build must give the release build's bits:
+// a difference means a slot was read before its copy landed or refilled
+// while still being read. DG_STEP_SYNC_WAVE is for the per-wave rings, whose
+// waves run different step counts and so cannot meet at extra barriers.
+#ifdef DG_EXTRA_SYNC
+#define DG_STEP_SYNC_WG()            \
+  do {                               \
+    __builtin_amdgcn_s_waitcnt(0);   \
+    __syncthreads();                 \
+  } while (0)
+#define DG_STEP_SYNC_WAVE() __builtin_amdgcn_s_waitcnt(0)
+#else
+#define DG_STEP_SYNC_WG() \
+  do {                    \
+  } while (0)
+#define DG_STEP_SYNC_WAVE() \
+  do {                      \
+  } while (0)
+#endif
+
 // Workgroup id -> (split, tile row, tile col).
 // The dispatcher hands workgroup i to XCD i % 8. Renumber so that each XCD
 // owns a contiguous run of the logical order. The logical order runs over the

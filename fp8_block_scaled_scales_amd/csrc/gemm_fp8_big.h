@@ -379,6 +379,7 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
         }
       }
     }
+    DG_STEP_SYNC_WG();
   }
   DG_WAIT_VMCNT(0);
   // Bias and activation in place, by all eight waves at once (the passes

@@ -237,6 +237,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_stream(const uint8_t* __rest
         promote(p, srow + 32 * h, sb_row[kb], sa_row[kb]);
       }
     }
+    DG_STEP_SYNC_WAVE();
     // Refill the slots of step t-1, read by this wave only and done with one
     // iteration ago.
     issue_a(t + R::A_AHEAD);

@@ -240,6 +240,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
         }
       }
     }
+    DG_STEP_SYNC_WG();
   }
 
   if (SPLIT && ksplit > 1) {

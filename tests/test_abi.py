@@ -54,6 +54,20 @@ def test_library_exports_every_declared_symbol(dg):
         assert hasattr(lib, name), name
 
 
+def test_race_check_build_exports_every_declared_symbol(dg):
+    # the build with extra waits and barriers per pipeline step answers the
+    # same host-side calls the same way
+    lib = dg.load_library(dg.SYNC_LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.dg_version() == dg.dg_version()
+    for M, N, K, g, layout in [(64, 4096, 7168, 128, 0), (64, 512, 7168, 128, 1), (8192, 8192, 8192, 128, 3)]:
+        a, b = dg.dg_tile_info(), dg.dg_tile_info()
+        assert lib.dg_query_tile_ws(M, N, K, g, layout, ctypes.byref(a)) == 0
+        assert dg.lib.dg_query_tile_ws(M, N, K, g, layout, ctypes.byref(b)) == 0
+        assert [getattr(a, f) for f, _ in a._fields_] == [getattr(b, f) for f, _ in b._fields_]
+
+
 def test_status_codes_match_header(dg):
     text = open(HEADER).read()
     for name in ("DG_OK", "DG_EINVAL", "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH", "DG_ESCRATCH"):
