@@ -7,10 +7,14 @@
 //
 // Per block: amax = max |x| over the elements present (edge blocks past the
 // last row are partial), scale = amax / fmax (FP32, correctly rounded; 1.0
-// for an all-zero block; fmax = 448 for E4M3, 57344 for E5M2), code =
+// where that is zero: an all-zero block, or amax so small the quotient
+// underflows; fmax = 448 for E4M3, 57344 for E5M2), code =
 // FP8(x / scale) with a correctly rounded FP32 divide and the hardware's
-// round-to-nearest-even conversion. Because |x / scale| <= fmax up to one
-// rounding, which still rounds to fmax, no value can overflow the format.
+// round-to-nearest-even conversion, saturating at +-fmax (reached only where
+// scale is subnormal and so coarsely rounded; otherwise |x / scale| <= fmax
+// up to one rounding, which still rounds to fmax).
+// The divide is taken as a reciprocal and two FMA corrections, which give the
+// correctly rounded quotient (div_by_scale).
 //
 // One workgroup per block, 256 threads (1024 for g = 256). The block (64 KB
 // for g = 128) stays in registers between the amax pass and the encode pass,
@@ -25,6 +29,67 @@
 namespace dg {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Division by a block's scale s, rounded as the correctly rounded FP32 divide
+// rounds it, without a divide per element. inv = RN(1/s) is computed once per
+// block (a correctly rounded divide); per element q0 = RN(x * inv) lies within
+// 1.5 ulp of x/s, one correction q1 = RN(q0 + RN(x - q0*s) * inv) (the
+// remainder exact under the FMA) brings it within one ulp, and a second
+// correction then gives RN(x/s) by Markstein's theorem on FMA-based division
+// (P. Markstein, "IA-64 and Elementary Functions", 2000; also the chapter on
+// division with an FMA in the Handbook of Floating-Point Arithmetic): with a
+// correctly rounded reciprocal and a quotient within one ulp, the corrected
+// quotient is the correctly rounded one. The theorem asks that nothing
+// overflows or underflows: s and 1/s normal (the caller's uniform test,
+// recip_ok; blocks outside it divide per element) and x/s at most the
+// format's largest value. A quotient in FP32's subnormal range may come out
+// wrong in its last bits, but every such value is far below half the smallest
+// FP8 subnormal and encodes to a signed zero either way; the sign is x's (an
+// input -0 gives -0, where the corrections alone would give +0).
+// A block's factor: amax / fmax (correctly rounded), or 1.0 where that is
+// zero: an all-zero block, or one whose amax is so small that the quotient
+// underflows (no factor of zero to divide by; 1.0 encodes its values, all
+// below fmax * 2^-150, under 2^-134, as zeros).
+__device__ __forceinline__ float block_scale(float amax, float fmax) {
+  const float s = amax / fmax;
+  return s > 0.0f ? s : 1.0f;
+}
+
+__device__ __forceinline__ bool recip_ok(float s) { return s >= 0x1p-120f && s <= 0x1p120f; }
+
+__device__ __forceinline__ float div_by_scale(float x, float s, float inv) {
+  float q = x * inv;
+  q = __builtin_fmaf(__builtin_fmaf(-q, s, x), inv, q);
+  q = __builtin_fmaf(__builtin_fmaf(-q, s, x), inv, q);
+  return __builtin_copysignf(q, x);
+}
+
+// Two FP8 codes of (x0, x1) packed into the low (HI = false) or high half of
+// `old`: FMT 0 E4M3FN, 1 E5M2 (hardware round-to-nearest-even).
+template <int FMT, bool HI>
+__device__ __forceinline__ int cvt2(float x0, float x1, int old) {
+  if constexpr (FMT == 1) return __builtin_amdgcn_cvt_pk_bf8_f32(x0, x1, old, HI);
+  else return __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, old, HI);
+}
+
+// Four codes of v / s in one 32-bit word (bytes in element order). FAST (s
+// and 1/s normal): |v / s| rounds to at most fmax, since s carries a relative
+// error of at most 2^-24. Otherwise s is subnormal or tiny, its own rounding
+// can be coarse enough that |v / s| passes fmax, and the quotient saturates
+// to +-fmax as FP8's round-to-nearest with saturation takes it (the
+// conversion instruction alone does not saturate).
+template <int FMT, bool FAST>
+__device__ __forceinline__ int encode4(v4f v, float s, float inv) {
+  if constexpr (FAST) {
+    const int lo = cvt2<FMT, false>(div_by_scale(v.x, s, inv), div_by_scale(v.y, s, inv), 0);
+    return cvt2<FMT, true>(div_by_scale(v.z, s, inv), div_by_scale(v.w, s, inv), lo);
+  } else {
+    constexpr float FMAX = FMT == 1 ? 57344.0f : 448.0f;
+    auto sat = [](float y) { return fminf(fmaxf(y, -FMAX), FMAX); };
+    const int lo = cvt2<FMT, false>(sat(v.x / s), sat(v.y / s), 0);
+    return cvt2<FMT, true>(sat(v.z / s), sat(v.w / s), lo);
+  }
+}
 
 template <int G, int FMT>
 __global__ __launch_bounds__(G == 256 ? 1024 : 256) void quant_fp8_blocks(const float* __restrict__ x,
@@ -64,23 +129,16 @@ __global__ __launch_bounds__(G == 256 ? 1024 : 256) void quant_fp8_blocks(const 
   amax = red[0];
 #pragma unroll
   for (int w = 1; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
-  const float scale = amax > 0.0f ? amax / FMAX : 1.0f;
+  const float scale = block_scale(amax, FMAX);
   if (t == 0) scales[blockIdx.x] = scale;
 
+  const float inv = 1.0f / scale;
+  const bool fast = recip_ok(scale);
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int r = rb * G + p * ROWS_PER_PASS + rsub;
     if (r < rows) {
-      // v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 pack two E4M3 / E5M2 codes into
-      // the low or high 16 bits.
-      int packed;
-      if constexpr (FMT == 1) {
-        packed = __builtin_amdgcn_cvt_pk_bf8_f32(v[p].x / scale, v[p].y / scale, 0, false);
-        packed = __builtin_amdgcn_cvt_pk_bf8_f32(v[p].z / scale, v[p].w / scale, packed, true);
-      } else {
-        packed = __builtin_amdgcn_cvt_pk_fp8_f32(v[p].x / scale, v[p].y / scale, 0, false);
-        packed = __builtin_amdgcn_cvt_pk_fp8_f32(v[p].z / scale, v[p].w / scale, packed, true);
-      }
+      const int packed = fast ? encode4<FMT, true>(v[p], scale, inv) : encode4<FMT, false>(v[p], scale, inv);
       *reinterpret_cast<int*>(q + (int64_t)r * cols + col) = packed;
     }
   }
@@ -124,16 +182,12 @@ __global__ __launch_bounds__(256) void quant_fp8_rows(const float* __restrict__ 
 #pragma unroll
     for (int o = LPS / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     if (seg >= nseg) continue;
-    const float scale = amax > 0.0f ? amax / FMAX : 1.0f;
+    const float scale = block_scale(amax, FMAX);
     if (c4 == 0) scales[seg] = scale;
-    int packed;
-    if constexpr (FMT == 1) {
-      packed = __builtin_amdgcn_cvt_pk_bf8_f32(v[u].x / scale, v[u].y / scale, 0, false);
-      packed = __builtin_amdgcn_cvt_pk_bf8_f32(v[u].z / scale, v[u].w / scale, packed, true);
-    } else {
-      packed = __builtin_amdgcn_cvt_pk_fp8_f32(v[u].x / scale, v[u].y / scale, 0, false);
-      packed = __builtin_amdgcn_cvt_pk_fp8_f32(v[u].z / scale, v[u].w / scale, packed, true);
-    }
+    // the segment's lanes agree on scale, so a divergent choice splits
+    // whole segments
+    const int packed = recip_ok(scale) ? encode4<FMT, true>(v[u], scale, 1.0f / scale)
+                                       : encode4<FMT, false>(v[u], scale, 0.0f);
     *reinterpret_cast<int*>(q + off[u]) = packed;
   }
 }

@@ -298,9 +298,11 @@ int dg_query_tile_ws(int64_t M, int64_t N, int64_t K, int gran, int layout, dg_t
  *   scales must not overlap one another (DG_EINVAL).
  *
  * Per gran x gran block (rows past the end make edge blocks partial):
- * amax = max |x| over present elements, scale = amax / 448 in FP32 (1.0 for
- * an all-zero block), q = E4M3(x / scale) with an FP32 divide and
- * round-to-nearest-even. Inputs must be finite. Same status codes and
+ * amax = max |x| over present elements, scale = amax / 448 in FP32 (1.0
+ * where that is zero: an all-zero block, or a block so small that the
+ * quotient underflows, whose values then encode as zeros), q = E4M3(x /
+ * scale) with the correctly rounded FP32 quotient and round-to-nearest-even.
+ * Inputs must be finite. Same status codes and
  * asynchrony as dg_gemm_fp8_nt.
  */
 int dg_quantize_e4m3_blocks(const float* x, int64_t rows, int64_t cols, int gran, void* q, float* scales,
@@ -322,7 +324,7 @@ int dg_quantize_fp8_blocks(const float* x, int64_t rows, int64_t cols, int gran,
  *   scales  FP32 out, [rows][cols/gran] row-major, 4-byte aligned.
  *
  * Per segment: amax = max |x| over its gran elements, scale = amax / fmax
- * (448 or 57344) in FP32 (1.0 for an all-zero segment), codes as
+ * (448 or 57344) in FP32 (1.0 where that is zero, as above), codes as
  * dg_quantize_fp8_blocks. Same arguments and status codes otherwise.
  */
 int dg_quantize_fp8_rows(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q,

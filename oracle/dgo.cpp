@@ -19,7 +19,8 @@
 //    §4.4: quantisation happens outside the GEMM and must use the GEMM's
 //    granularity; §5.2: divide when quantising, multiply when dequantising).
 //    Per g x g block: amax over the elements present (edge blocks are
-//    partial), scale = amax / 448 in FP32 (1.0 for an all-zero block), and
+//    partial), scale = amax / 448 in FP32 (1.0 for an all-zero block, and
+//    for a block so small that amax / 448 underflows to zero), and
 //    each element becomes E4M3(x / scale), an FP32 divide followed by
 //    round-to-nearest-even with saturation to +-448.
 //
@@ -181,6 +182,16 @@ uint8_t dgo_e5m2_encode(float y) {
 }
 
 // Format codes shared with the Python side: 0 = E4M3FN, 1 = E5M2.
+// A block's factor: amax / fmax in FP32, or 1.0 where that is zero: for an
+// all-zero block, and for a block whose amax is so small (below fmax times
+// half the smallest FP32 subnormal) that the quotient underflows to zero; a
+// zero factor would divide by zero, while 1.0 encodes such a block's values
+// (all below fmax * 2^-150, under 2^-134 in magnitude) as zeros.
+static float block_scale(float amax, float fmax) {
+  const float s = amax / fmax;
+  return s > 0.0f ? s : 1.0f;
+}
+
 static double decode_fmt(int fmt, uint8_t code) { return fmt == 1 ? dgo_e5m2_decode(code) : dgo_e4m3_decode(code); }
 static uint8_t encode_fmt(int fmt, float y) { return fmt == 1 ? dgo_e5m2_encode(y) : dgo_e4m3_encode(y); }
 
@@ -219,7 +230,7 @@ int dgo_quantize_blocks(const float* x, int64_t rows, int64_t cols, int g, uint8
             const float a = std::fabs(x[r * cols + c]);
             if (a > amax) amax = a;
           }
-        const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+        const float scale = block_scale(amax, 448.0f);
         scales[rb * ncb + cb] = scale;
         for (int64_t r = r0; r < r1; ++r)
           for (int64_t c = c0; c < c1; ++c) q[r * cols + c] = dgo_e4m3_encode(x[r * cols + c] / scale);
@@ -302,7 +313,7 @@ int dgo_quantize_blocks_fmt(const float* x, int64_t rows, int64_t cols, int g, i
             const float a = std::fabs(x[r * cols + c]);
             if (a > amax) amax = a;
           }
-        const float scale = amax > 0.0f ? amax / fmax : 1.0f;
+        const float scale = block_scale(amax, fmax);
         scales[rb * ncb + cb] = scale;
         for (int64_t r = r0; r < r1; ++r)
           for (int64_t c = c0; c < c1; ++c) q[r * cols + c] = encode_fmt(fmt, x[r * cols + c] / scale);
@@ -370,7 +381,7 @@ int dgo_quantize_rows_fmt(const float* x, int64_t rows, int64_t cols, int g, int
         float amax = 0.0f;
         for (int64_t c = 0; c < g; ++c)
           if (std::fabs(seg[c]) > amax) amax = std::fabs(seg[c]);
-        const float scale = amax > 0.0f ? amax / fmax : 1.0f;
+        const float scale = block_scale(amax, fmax);
         scales[r * ncb + cb] = scale;
         for (int64_t c = 0; c < g; ++c) q[r * cols + cb * g + c] = encode_fmt(fmt, seg[c] / scale);
       }

@@ -79,3 +79,26 @@ def test_dequantisation_error_bound():
     # every block's largest element lands on +-448
     for rb, cb, rs, cs in _blocks(*x.shape, g):
         assert np.max(np.abs(deq[rs, cs])) == 448.0
+
+
+@pytest.mark.parametrize("fmt,mag", [(0, 1e-44), (1, 1e-42), (1, 3e-41)])
+def test_underflowing_scale_is_one(fmt, mag):
+    # amax / fmax rounds to zero in FP32 for these blocks (fmax 448 or 57344):
+    # the factor is then 1.0, as for an all-zero block, and every value (far
+    # below the smallest FP8 subnormal) encodes as a zero of its own sign
+    fmax = np.float32(448.0 if fmt == 0 else 57344.0)
+    x = (np.random.default_rng(7).uniform(-1.0, 1.0, (64, 64)) * mag).astype(np.float32)
+    x[0, 0] = np.float32(-mag)
+    assert np.float32(np.abs(x).max()) / fmax == np.float32(0.0)
+    for q, s in (oracle.quantize_blocks_fmt(x, 64, fmt), oracle.quantize_rows_fmt(x, 64, fmt)):
+        assert np.all(s == np.float32(1.0))
+        assert np.array_equal(q, np.where(np.signbit(x), 0x80, 0x00).astype(np.uint8))
+
+
+def test_scale_just_above_underflow():
+    # the smallest amax whose quotient does not underflow keeps amax / 448
+    x = np.zeros((64, 64), np.float32)
+    x[3, 5] = np.float32(448.0) * np.float32(2.0 ** -149)  # amax / 448 = 2^-149, the smallest subnormal
+    q, s = oracle.quantize_blocks(x, 64)
+    assert s[0, 0] == np.float32(2.0 ** -149)
+    assert q[3, 5] == 0x7E  # 448
