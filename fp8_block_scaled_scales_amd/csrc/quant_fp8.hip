@@ -64,6 +64,30 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float inv) {
   return __builtin_copysignf(q, x);
 }
 
+// One DPP move of v across the wave (row_mask, bank_mask all on; every
+// source lane exists for the patterns used here).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over each aligned group of L lanes (L = 16, 32 or 64), in every lane of
+// the group: within quads by two swaps (DPP quad_perm [1,0,3,2], [2,3,0,1]),
+// then each lane against its mirror in the 8-lane half row and in the 16-lane
+// row (DPP row_half_mirror, row_mirror), which leaves the row's max in every
+// lane; beyond 16 lanes, cross-lane shuffles. max is exact and order-free.
+template <int L>
+__device__ __forceinline__ float group_max(float m) {
+  static_assert(L == 16 || L == 32 || L == 64, "group");
+  m = fmaxf(m, dpp_f<0xB1>(m));
+  m = fmaxf(m, dpp_f<0x4E>(m));
+  m = fmaxf(m, dpp_f<0x141>(m));
+  m = fmaxf(m, dpp_f<0x140>(m));
+  if constexpr (L >= 32) m = fmaxf(m, __shfl_xor(m, 16, 64));
+  if constexpr (L >= 64) m = fmaxf(m, __shfl_xor(m, 32, 64));
+  return m;
+}
+
 // Two FP8 codes of (x0, x1) packed into the low (HI = false) or high half of
 // `old`: FMT 0 E4M3FN, 1 E5M2 (hardware round-to-nearest-even).
 template <int FMT, bool HI>
@@ -121,9 +145,8 @@ __global__ __launch_bounds__(G == 256 ? 1024 : 256) void quant_fp8_blocks(const 
     }
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w))));
   }
-  // max is exact and order-free: wave butterfly, then across the waves
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  // max is exact and order-free: over the wave, then across the waves
+  amax = group_max<64>(amax);
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
   amax = red[0];
@@ -163,24 +186,31 @@ __global__ __launch_bounds__(256) void quant_fp8_rows(const float* __restrict__ 
   const int c4 = lane % LPS;
   const unsigned ncb = (unsigned)(cols / G);
   // unsigned: the last workgroup's segments may pass 2^31 - 1 (and are not live)
-  const unsigned seg0 = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (unsigned)(SPW * U) + (unsigned)(lane / LPS);
+  const unsigned wseg = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (unsigned)(SPW * U);  // the wave's first segment
+  const unsigned seg0 = wseg + (unsigned)(lane / LPS);
+  // (row, column block) of the wave's first segment from one division; the
+  // lane's segments follow it by at most SPW * U - 1, a few row wraps at most
+  const unsigned wrow = wseg / ncb, wcb = wseg - wrow * ncb;
   v4f v[U];
   int64_t off[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const unsigned seg = seg0 + (unsigned)(u * SPW);
-    // whole segments are live or not, so each butterfly stays inside live lanes
-    const unsigned row = seg < nseg ? seg / ncb : 0u;
-    const unsigned cb = seg < nseg ? seg - row * ncb : 0u;
-    off[u] = (int64_t)row * cols + cb * G + c4 * 4;
+    unsigned row = wrow, cb = wcb + (seg - wseg);
+    if (cb >= ncb) {
+      const unsigned k = cb < 2 * ncb ? 1u : cb / ncb;
+      row += k;
+      cb -= k * ncb;
+    }
+    // whole segments are live or not, so each reduction stays inside live lanes
+    off[u] = seg < nseg ? (int64_t)row * cols + cb * G + c4 * 4 : 0;
     v[u] = seg < nseg ? *reinterpret_cast<const v4f*>(x + off[u]) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const unsigned seg = seg0 + (unsigned)(u * SPW);
-    float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
-#pragma unroll
-    for (int o = LPS / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float amax =
+        group_max<LPS>(fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
     if (seg >= nseg) continue;
     const float scale = block_scale(amax, FMAX);
     if (c4 == 0) scales[seg] = scale;
