@@ -75,10 +75,10 @@ DEFAULT_WORKLOAD = 4      # large square M=N=K=8192, g=128: the largest shape, M
 # workload runs (KERNEL_SOURCES) as they were when the counters were taken. A
 # different hash means the kernel changed since: traffic is null.
 TRAFFIC = {
-    "square8192": {"src": "93e9bb54ad47e1cb", "bytes": 941172143},
-    "prefill_m4096_n7168_k2048": {"src": "93e9bb54ad47e1cb", "bytes": 151255113},
-    "longk_m2000_n4000_k16384_g64": {"src": "93e9bb54ad47e1cb", "bytes": 278794639},
-    "decode_m64_n4096_k7168": {"src": "3e721c10e3904d6b", "bytes": 33667556},
+    "square8192": {"src": "fa1d097fb6d5cff3", "bytes": 941103541},
+    "prefill_m4096_n7168_k2048": {"src": "fa1d097fb6d5cff3", "bytes": 151255113},
+    "longk_m2000_n4000_k16384_g64": {"src": "fa1d097fb6d5cff3", "bytes": 278792047},
+    "decode_m64_n4096_k7168": {"src": "54352dcee8148392", "bytes": 33667236},
 }
 
 # Sources that make up each workload's kernel: its class's device code, the
