@@ -219,19 +219,30 @@ __device__ __forceinline__ uint32_t tile_range_t(int64_t k0, int K, int len, int
   return (uint32_t)(rows * len - col0 + (k0 + rows < K ? 16 : 0));
 }
 
-// The tensor's last K row has no row after it, and the copy of a tile's last
-// column chunk of it loses the 1 to 3 bytes of its last 4-byte word that lie
-// inside the tensor when len % 4 != 0. Lanes 0-2 write those bytes (stored
-// columns [len & ~3, len) that fall in the W-wide tile from col0) from memory
-// into slab row `row`, at their swizzled places. src is the stored last row.
+// The tensor's last step has no row after it to run into. There the range
+// check drops the 4-byte words that reach past the tensor's end, and every
+// byte such a word holds lies in the tensor's last 3 bytes (a dropped word
+// starts less than 4 bytes before the end). With rows of 4 bytes or more
+// those are the last len % 4 bytes of the last K row; with rows of 1 to 3
+// bytes they reach back over up to 3 rows. Lanes 0-2 each take one of the
+// last 3 bytes (global offset total - 1 - lane, total = K * len) and, when it
+// lies in this step's rows (from k0) and the W-wide tile from col0, write it
+// from memory into the slab at its swizzled place. Writing a byte that was
+// not dropped writes the value already there. src is the tensor's base.
 // Called between two barriers: after every wave's copies of the step have
-// landed, before any wave reads the slab.
+// landed, before any wave reads the slab (or, for a wave's private ring, after
+// that wave's own copies have landed).
 template <int W>
-__device__ __forceinline__ void patch_tail_t(uint8_t* slab, const uint8_t* src, int row, int len, int col0, int lane) {
-  const int c = (len & ~3) + lane;
-  if (lane < (len & 3) && c >= col0 && c < col0 + W) {
-    const int t = c - col0;
-    slab[row * W + (((t >> 4) ^ tkey<W>(row)) << 4) + (t & 15)] = src[c];
+__device__ __forceinline__ void patch_tail_t(uint8_t* slab, const uint8_t* src, int64_t total, int len, int64_t k0,
+                                             int col0, int lane) {
+  const int64_t e = total - 1 - lane;
+  if (lane < 3 && e >= 0) {
+    const int64_t row = e / len;
+    const int col = (int)(e - row * len);
+    if (row >= k0 && col >= col0 && col < col0 + W) {
+      const int r = (int)(row - k0), t = col - col0;
+      slab[r * W + (((t >> 4) ^ tkey<W>(r)) << 4) + (t & 15)] = src[e];
+    }
   }
 }
 

@@ -232,9 +232,9 @@ __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict_
       if (s == nsteps - 1 && (((LAYOUT & 2) && (M & 3)) || ((LAYOUT & 1) && (N & 3)))) {
         if (wave == 0) {
           uint8_t* slot = smem + (s & 1) * SLOT;
-          const int row = K - 1 - s * BK;
-          if ((LAYOUT & 2) && (M & 3)) patch_tail_t<BM>(slot, a + (int64_t)(K - 1) * M, row, M, m0, lane);
-          if ((LAYOUT & 1) && (N & 3)) patch_tail_t<BN>(slot + A_BYTES, b + (int64_t)(K - 1) * N, row, N, n0, lane);
+          const int64_t k0 = (int64_t)s * BK;
+          if ((LAYOUT & 2) && (M & 3)) patch_tail_t<BM>(slot, a, (int64_t)K * M, M, k0, m0, lane);
+          if ((LAYOUT & 1) && (N & 3)) patch_tail_t<BN>(slot + A_BYTES, b, (int64_t)K * N, N, k0, n0, lane);
         }
         __syncthreads();
       }

@@ -210,9 +210,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_fp8_stream(const uint8_t* __rest
       // length is not a multiple of 4 (see patch_tail_t); the slots are this
       // wave's own, so its own copies having landed is enough
       if (st == nsteps - 1) {
-        const int row = K - 1 - st * BK;
-        if (TA && (M & 3)) patch_tail_t<BM>(As, a + (int64_t)(K - 1) * M, row, M, m0, lane);
-        if (TB && (N & 3)) patch_tail_t<BN>(Bs, b + (int64_t)(K - 1) * N, row, N, n0, lane);
+        const int64_t k0 = (int64_t)st * BK;
+        if (TA && (M & 3)) patch_tail_t<BM>(As, a, (int64_t)K * M, M, k0, m0, lane);
+        if (TB && (N & 3)) patch_tail_t<BN>(Bs, b, (int64_t)K * N, N, k0, n0, lane);
       }
     }
     // ROWA: factors [SEGS][32] of the step; this lane's rows 8c + 4*h2 .. +3

@@ -172,9 +172,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
       if (st0 + s == nsteps_all - 1 && (((LAYOUT & 2) && (M & 3)) || ((LAYOUT & 1) && (N & 3)))) {
         if (wave == 0) {
           uint8_t* slot = smem + (s % STAGES) * STAGE_BYTES;
-          const int row = K - 1 - (st0 + s) * BK;
-          if ((LAYOUT & 2) && (M & 3)) patch_tail_t<BM>(slot, a + (int64_t)(K - 1) * M, row, M, m0, lane);
-          if ((LAYOUT & 1) && (N & 3)) patch_tail_t<BN>(slot + A_BYTES, b + (int64_t)(K - 1) * N, row, N, n0, lane);
+          const int64_t k0 = (int64_t)(st0 + s) * BK;
+          if ((LAYOUT & 2) && (M & 3)) patch_tail_t<BM>(slot, a, (int64_t)K * M, M, k0, m0, lane);
+          if ((LAYOUT & 1) && (N & 3)) patch_tail_t<BN>(slot + A_BYTES, b, (int64_t)K * N, N, k0, n0, lane);
         }
         __syncthreads();
       }

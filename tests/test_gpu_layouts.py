@@ -292,3 +292,32 @@ def test_layout_rowscales_same_bits_as_nt(M, N, K, g):
         a_st, b_st = _store(a8, b8, layout)
         say("per-row layout %d vs NT bits M=%d N=%d K=%d g=%d" % (layout, M, N, K, g))
         assert np.array_equal(_run_ws(a_st, b_st, sa, sb, g, layout, sa_rows=1)[1], want), layout
+
+
+# The smallest shapes: stored rows of 1-3 bytes (shorter than one 4-byte word,
+# so the tensor's last K row comes entirely from the tail patch), one-row and
+# one-column outputs, K of a single segment, and a few tile-edge sizes; every
+# layout against the oracle and bit for bit against NT, g x g and per-row
+# factors. The whole output is compared.
+TINY = [(1, 1, 64, 64), (1, 17, 128, 128), (3, 2, 192, 64), (2, 130, 256, 128), (33, 3, 128, 64),
+        (5, 7, 256, 256), (130, 129, 128, 128), (259, 6, 192, 64)]
+
+
+@pytest.mark.parametrize("rowa", [False, True])
+@pytest.mark.parametrize("M,N,K,g", TINY)
+def test_tiny_shapes_every_layout(M, N, K, g, rowa):
+    x = synth.normal(19000 + M + N, (M, K))
+    if rowa:
+        a8, sa = oracle.quantize_rows_fmt(x, g, 0)
+    else:
+        a8, sa = oracle.quantize_blocks_fmt(x, g, 0)
+    b8, sb = oracle.quantize_blocks_fmt(synth.normal(19001 + N, (N, K), sigma=0.02), g, 0)
+    ref = oracle.gemm_ref_rowa(a8, b8, sa, sb, g) if rowa else oracle.gemm_ref_fmt(a8, b8, sa, sb, g, 0, 0)
+    bits = {}
+    for layout in [NT] + TRANSPOSED:
+        a_st, b_st = _store(a8, b8, layout)
+        say("tiny layout %d M=%d N=%d K=%d g=%d rowa=%d" % (layout, M, N, K, g, rowa))
+        got, bits[layout] = _run_ws(a_st, b_st, sa, sb, g, layout, sa_rows=1 if rowa else None)
+        _assert_parity(got, ref, "tiny layout %d %dx%dx%d g=%d" % (layout, M, N, K, g))
+    for layout in TRANSPOSED:
+        assert np.array_equal(bits[layout], bits[NT]), layout
