@@ -232,7 +232,7 @@ def test_layout_ragged_closed_form_and_agreement_bitwise(M, N, K, g):
         assert np.array_equal(bits[np.ix_(rows, cols)], _common.f32_to_bf16_bits(ref.astype(np.float32))), layout
 
 
-def _run_ws(a_st, b_st, sa, sb, g, layout, sa_rows=None, fa=0, fb=0, bias=None, act=0):
+def _run_ws(a_st, b_st, sa, sb, g, layout, sa_rows=None, fa=0, fb=0, bias=None, act=0, workspace=False):
     import torch
 
     import fp8_block_scaled_scales_amd as dg
@@ -240,8 +240,13 @@ def _run_ws(a_st, b_st, sa, sb, g, layout, sa_rows=None, fa=0, fb=0, bias=None, 
     dev = "cuda:0"
     t = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (a_st, b_st, sa, sb)]
     tbias = None if bias is None else torch.from_numpy(bias).to(dev)
+    ws = None
+    if workspace:
+        K, M = a_st.shape if layout & 2 else a_st.shape[::-1]
+        N = b_st.shape[1] if layout & 1 else b_st.shape[0]
+        ws = dg.dg_workspace(M, N, K, g, layout, device=dev)
     out = dg.dg_gemm_fp8_ws(t[0], t[1], t[2], t[3], gran=g, layout=layout, sa_rows=sa_rows, fmt_a=fa, fmt_b=fb,
-                            bias=tbias, act=act)
+                            bias=tbias, act=act, workspace=ws)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), out.view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -319,5 +324,31 @@ def test_tiny_shapes_every_layout(M, N, K, g, rowa):
         say("tiny layout %d M=%d N=%d K=%d g=%d rowa=%d" % (layout, M, N, K, g, rowa))
         got, bits[layout] = _run_ws(a_st, b_st, sa, sb, g, layout, sa_rows=1 if rowa else None)
         _assert_parity(got, ref, "tiny layout %d %dx%dx%d g=%d" % (layout, M, N, K, g))
+    for layout in TRANSPOSED:
+        assert np.array_equal(bits[layout], bits[NT]), layout
+
+
+@pytest.mark.parametrize("rowa", [False, True])
+@pytest.mark.parametrize("M,N,K,g", [(1, 1, 2048, 128), (3, 2, 1088, 64), (2, 130, 1024, 128), (33, 3, 2048, 64),
+                                     (5, 7, 1536, 256), (97, 5, 1088, 64)])
+def test_tiny_shapes_every_layout_split_k(M, N, K, g, rowa):
+    # the same with a workspace: these few tiles split K over workgroups, and
+    # only the last split's final step holds the tensor's last bytes
+    import fp8_block_scaled_scales_amd as dg
+
+    assert all(dg.dg_query_tile(M, N, K, g, layout, workspace=True)["ksplit"] > 1 for layout in range(4))
+    x = synth.normal(19500 + M + N, (M, K))
+    if rowa:
+        a8, sa = oracle.quantize_rows_fmt(x, g, 0)
+    else:
+        a8, sa = oracle.quantize_blocks_fmt(x, g, 0)
+    b8, sb = oracle.quantize_blocks_fmt(synth.normal(19501 + N, (N, K), sigma=0.02), g, 0)
+    ref = oracle.gemm_ref_rowa(a8, b8, sa, sb, g) if rowa else oracle.gemm_ref_fmt(a8, b8, sa, sb, g, 0, 0)
+    bits = {}
+    for layout in [NT] + TRANSPOSED:
+        a_st, b_st = _store(a8, b8, layout)
+        say("tiny split-K layout %d M=%d N=%d K=%d g=%d rowa=%d" % (layout, M, N, K, g, rowa))
+        got, bits[layout] = _run_ws(a_st, b_st, sa, sb, g, layout, sa_rows=1 if rowa else None, workspace=True)
+        _assert_parity(got, ref, "tiny split-K layout %d %dx%dx%d g=%d" % (layout, M, N, K, g))
     for layout in TRANSPOSED:
         assert np.array_equal(bits[layout], bits[NT]), layout
