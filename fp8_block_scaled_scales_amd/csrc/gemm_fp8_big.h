@@ -110,11 +110,10 @@ struct Acc<64, WTM, WTN> {
 // 128). The scale blocks are sg x sg with sg = G << sshift: for g = 256 the
 // G = 128 kernel promotes every 128 K with its 256-block's factor. ROWA: A's
 // factors are per row, sa is [M][K/sg].
-// LAYOUT bit 1: A stored [K,M]; bit 0: B stored [K,N] (M resp. N a multiple
-// of 16; B transposed on the 256- and 128-wide tiles only). A transposed tile
-// is staged as its 128 K rows and read with the transposing LDS read
-// (frag_tr16 / frag_tr in gemm_common.h); the K order inside a fragment is
-// the NT order.
+// LAYOUT bit 1: A stored [K,M]; bit 0: B stored [K,N] (M resp. N any
+// length; B transposed on the 256- and 128-wide tiles). A transposed tile is
+// staged as its 128 K rows and read with the transposing LDS read (frag_tr16
+// / frag_tr in gemm_common.h); the K order inside a fragment is the NT order.
 template <int G, int BN, int WM, int GROUP_M, int FMT, int EPI, bool ROWA, int LAYOUT>
 __global__ __launch_bounds__(NT) void gemm_fp8_nt_big(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
                                                       const float* __restrict__ sa, const float* __restrict__ sb,
