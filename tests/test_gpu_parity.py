@@ -326,3 +326,43 @@ def test_stream_all_ones_bitwise():
     got, bits = gemm(a8, sa, b8, sb, g)
     ref = oracle.gemm_ref(a8, b8, sa, sb, g)
     assert np.array_equal(bits, _common.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+def test_default_calls_two_streams_concurrently():
+    """The calls without a workspace keep every K reduction inside a
+    workgroup and use no memory beyond their arguments, so they may run at
+    the same time on any streams: a streaming-class shape, a 256-row shape and
+    a 128x128 shape enqueued alternately on three streams, 8 times each with
+    no synchronisation between; every output equals its first, which matches
+    the oracle."""
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+    from tests._gpu import device_inputs
+
+    shapes = [(64, 4096, 2048, 128), (4096, 4096, 512, 128), (1008, 1000, 512, 64)]
+    assert [dg.dg_query_tile(*s)["bm"] for s in shapes] == [32, 256, 128]
+    ops, ts = [], []
+    for i, (M, N, K, g) in enumerate(shapes):
+        a8, sa = oracle.quantize_blocks(synth.normal(8800 + i, (M, K)), g)
+        b8, sb = oracle.quantize_blocks(synth.normal(8810 + i, (N, K), sigma=0.02), g)
+        ops.append((a8, sa, b8, sb))
+        ts.append(device_inputs(a8, sa, b8, sb))
+    streams = [torch.cuda.Stream() for _ in shapes]
+    outs = [[torch.empty((s[0], s[1]), dtype=torch.bfloat16, device="cuda:0") for _ in range(8)] for s in shapes]
+    torch.cuda.synchronize()
+    say("default calls on three streams")
+    for r in range(8):
+        for i, (M, N, K, g) in enumerate(shapes):
+            ta, tsa, tb, tsb = ts[i]
+            dg.dg_gemm_fp8_nt(ta, tb, tsa, tsb, out=outs[i][r], gran=g, stream=streams[i])
+    torch.cuda.synchronize()
+    for i, (M, N, K, g) in enumerate(shapes):
+        a8, sa, b8, sb = ops[i]
+        first = outs[i][0].view(torch.int16).cpu().numpy()
+        rows = _common.sample_indices(M, 64, seed=i)
+        got = _common.bf16_bits_to_f64(first.view(np.uint16))[rows]
+        ok, _ = _common.within_tolerance(got, oracle.gemm_ref(a8, b8, sa, sb, g, rows=rows))
+        assert ok.all(), (M, N, K)
+        for r in range(1, 8):
+            assert np.array_equal(outs[i][r].view(torch.int16).cpu().numpy(), first), (i, r)

@@ -63,3 +63,31 @@ def test_noalloc_rejects_a_plan_beyond_the_scratch():
     with pytest.raises(dg.DGError) as e:
         dg.dg_gemm_fp8_noalloc(ta, tb, tsa, tsb, out, gran=g)
     assert e.value.code == dg.DG_ESCRATCH
+
+
+def test_noalloc_layout_and_row_factors():
+    # a transposed layout with per-row A factors through the split path, the
+    # scratch holding the previous test's contents: bit for bit the workspace call
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    M, N, K, g, layout = 96, 528, 2048, 128, 3
+    plan = dg.dg_query_tile(M, N, K, g, layout, workspace=True)
+    assert plan["ksplit"] > 1 and plan["workspace_bytes"] <= dg.dg_noalloc_scratch_bytes()
+    x = synth.normal(9300, (M, K)) * np.exp(np.random.default_rng(9300).uniform(-3, 3, size=(M, 1)))
+    a8, sa = oracle.quantize_rows_fmt(x.astype(np.float32), g, 0)
+    b8, sb = oracle.quantize_blocks(synth.normal(9301, (N, K), sigma=0.02), g)
+    dev = "cuda:0"
+    ta = torch.from_numpy(np.ascontiguousarray(a8.T)).to(dev)  # A stored [K, M]
+    tb = torch.from_numpy(np.ascontiguousarray(b8.T)).to(dev)  # B stored [K, N]
+    tsa, tsb = torch.from_numpy(sa).to(dev), torch.from_numpy(sb).to(dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    say("noalloc TN per-row %dx%dx%d ksplit=%d" % (M, N, K, plan["ksplit"]))
+    dg.dg_gemm_fp8_noalloc(ta, tb, tsa, tsb, out, gran=g, layout=layout, sa_rows=1)
+    got = _bits(out)
+    want = _bits(dg.dg_gemm_fp8_ws(ta, tb, tsa, tsb, gran=g, layout=layout, sa_rows=1,
+                                   workspace=dg.dg_workspace(M, N, K, g, layout)))
+    assert np.array_equal(got, want)
+    ok, _ = _common.within_tolerance(_common.bf16_bits_to_f64(got), oracle.gemm_ref_rowa(a8, b8, sa, sb, g))
+    assert ok.all()
