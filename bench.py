@@ -75,10 +75,10 @@ DEFAULT_WORKLOAD = 4      # large square M=N=K=8192, g=128: the largest shape, M
 # workload runs (KERNEL_SOURCES) as they were when the counters were taken. A
 # different hash means the kernel changed since: traffic is null.
 TRAFFIC = {
-    "square8192": {"src": "fa1d097fb6d5cff3", "bytes": 941103541},
-    "prefill_m4096_n7168_k2048": {"src": "fa1d097fb6d5cff3", "bytes": 151255113},
-    "longk_m2000_n4000_k16384_g64": {"src": "fa1d097fb6d5cff3", "bytes": 278792047},
-    "decode_m64_n4096_k7168": {"src": "54352dcee8148392", "bytes": 33667236},
+    "square8192": {"src": "7738ea92222c4788", "bytes": 940717399},
+    "prefill_m4096_n7168_k2048": {"src": "7738ea92222c4788", "bytes": 151255113},
+    "longk_m2000_n4000_k16384_g64": {"src": "7738ea92222c4788", "bytes": 278793359},
+    "decode_m64_n4096_k7168": {"src": "fbbfe466c6166c58", "bytes": 33667620},
 }
 
 # Sources that make up each workload's kernel: its class's device code, the
