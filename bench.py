@@ -36,6 +36,12 @@ graph is replayed once untimed first, and its outputs are checked bit for bit
 against the eager calls'), so the host's per-call cost does not sit between
 kernels of a few microseconds. value = 2*M*N*K / (time per step) in TFLOP/s.
 
+Sustained clock: after the timed steps the same graph replays for
+--clock-window seconds (default 3, untimed) while a host thread samples
+`amd-smi metric --clock --power`; config.sustained_clock gives the median of
+the samples' mean gfx clock over the XCDs and of the socket power (null
+without amd-smi). It says at what clock the measured rate was reached.
+
 roofline: the GEMM kernel is the only kernel of a step. Its average launch
 duration is the timed region / K. achieved = algorithmic FLOPs (MFMA-bound
 shapes) or algorithmic bytes (HBM-bound shapes) per launch / that duration,
@@ -55,6 +61,7 @@ import json
 import math
 import statistics
 import os
+import subprocess
 import sys
 import time
 
@@ -260,7 +267,66 @@ def gpu_leg(c: int, steps: int, warmup: int, sets: int | None, g: int, fa: int =
     bounds = [start] + marks + [end]
     trials = [bounds[i].elapsed_time(bounds[i + 1]) / ((cuts[i + 1] - cuts[i]) * L) for i in range(len(bounds) - 1)]
     finite = bool(torch.isfinite(bufs[(steps - 1) % sets][4].float()).all().item())
-    return ms, sets, finite, L, trials
+    clock = clock_window(graph, dev, ms * L) if clock_s > 0 else None
+    return ms, sets, finite, L, trials, clock
+
+
+def _smi_sample():
+    """One amd-smi reading of GPU 0: (mean gfx clock over the XCDs in MHz,
+    socket power in W), or None when amd-smi is missing or says nothing."""
+    try:
+        res = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True,
+                             text=True, timeout=20)
+        txt = res.stdout
+        starts = [i for i in (txt.find("{"), txt.find("[")) if i >= 0]
+        d = json.loads(txt[min(starts):])
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clks = [v["clk"]["value"] for k, v in g["clock"].items()
+                if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        pw = g.get("power", {}).get("socket_power", {})
+        return (sum(clks) / len(clks) if clks else None), (pw.get("value") if isinstance(pw, dict) else None)
+    except Exception:
+        return None
+
+
+clock_s = 3.0  # length of the untimed clock window after the timed steps (0: none)
+
+
+def clock_window(graph, dev, graph_ms: float):
+    """The sustained gfx clock under this load: after the timed steps, the
+    same graph replays for about clock_s seconds (untimed) while a host thread
+    samples amd-smi; returns the median of the samples' mean gfx clock over
+    the XCDs and of the socket power, or None without amd-smi."""
+    import threading
+
+    import torch
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            r = _smi_sample()
+            if r is None:
+                return
+            samples.append(r)
+
+    reps = max(1, int(clock_s * 1e3 / max(graph_ms, 1e-3)))
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    for r in range(reps):
+        graph.replay()
+        if r % 16 == 15:
+            torch.cuda.synchronize(dev)  # keep the queue short, so the window lasts as long as the replays
+    torch.cuda.synchronize(dev)
+    stop.set()
+    th.join(timeout=30)
+    clk = [c for c, _ in samples if c]
+    pw = [p for _, p in samples if p]
+    if not clk:
+        return None
+    return {"gfx_mhz_median": round(statistics.median(clk), 1), "socket_power_w_median": statistics.median(pw) if pw else None,
+            "samples": len(clk), "source": "amd-smi metric --clock --power, sampled while the graph replayed for %.1f s "
+                                            "after the timed steps (untimed)" % clock_s}
 
 
 def quant_leg(c: int, operand: str, steps: int, warmup: int, sets: int | None, g: int, fmt: int, per_row: bool):
@@ -408,6 +474,9 @@ def main():
     ap.add_argument("--act", default="none", choices=sorted(ACTS), help="fused epilogue activation")
     ap.add_argument("--layout", default="nt", choices=sorted(LAYOUTS),
                     help="operand storage: A [M,K] or [K,M] (first letter n / t), B [N,K] or [K,N] (t / n)")
+    ap.add_argument("--clock-window", type=float, default=3.0, metavar="S",
+                    help="after the timed steps, keep replaying for S seconds (untimed) while sampling the gfx "
+                         "clock and power with amd-smi (0: skip)")
     ap.add_argument("--workspace", action="store_true",
                     help="call dg_gemm_fp8_ws with a workspace (small-M shapes may then split K over workgroups)")
     ap.add_argument("--sa-rows", type=int, default=None, choices=(1,),
@@ -419,6 +488,8 @@ def main():
                     help="only run a plain device copy of MB megabytes three times (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
     args = ap.parse_args()
+    global clock_s
+    clock_s = max(0.0, args.clock_window)
 
     if args.copy_probe:
         import torch
@@ -468,8 +539,8 @@ def main():
     flops, nbytes = algorithmic(w, g, args.sa_rows)
     act = ACTS[args.act]
     layout = LAYOUTS[args.layout]
-    ms, sets, finite, glen, trials = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb, args.bias, act, args.sa_rows,
-                                             layout, args.workspace)
+    ms, sets, finite, glen, trials, clock = gpu_leg(c, args.steps, args.warmup, args.sets, g, fa, fb, args.bias, act,
+                                                    args.sa_rows, layout, args.workspace)
     if not finite:
         raise SystemExit("GEMM output holds non-finite values")
     sec = ms * 1e-3
@@ -508,6 +579,7 @@ def main():
                    "trials_us": {"n": len(trials), "median": round(statistics.median(trials) * 1e3, 3),
                                  "min": round(min(trials) * 1e3, 3), "max": round(max(trials) * 1e3, 3)},
                    "pct_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
+                   "sustained_clock": clock,
                    "alg_GBps": round(nbytes / sec / 1e9, 1)},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic},
