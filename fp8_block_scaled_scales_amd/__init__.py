@@ -332,9 +332,10 @@ def dg_gemm_fp8_ws(a, b, sa, sb, out=None, gran: int = 128, layout: int = DG_LAY
 
     With a workspace (a contiguous uint8 GPU tensor of at least
     dg_query_tile(..., workspace=True)["workspace_bytes"] bytes, 256-byte
-    aligned; see ``dg_workspace``) small-M shapes with few output tiles split
-    K over several workgroups; every other shape runs what the call without a
-    workspace runs. Concurrent calls need distinct workspaces.
+    aligned; see ``dg_workspace``) small-M shapes with few output tiles and a
+    long K (16384 and up, cut at least 8 ways) split K over several
+    workgroups; every other shape runs what the call without a workspace
+    runs. Concurrent calls need distinct workspaces.
     """
     M, N, K, sa_rows, dev = _ws_args(a, b, sa, sb, out, gran, layout, sa_rows, fmt_a, fmt_b, bias, act)
     if out is None:

@@ -8,8 +8,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
-#include <chrono>
 #include <cstdio>
 #include <cstdlib>
 #include <algorithm>
@@ -27,41 +25,34 @@ std::once_flag g_dev_once[kMaxDevices];
 int g_dev_status[kMaxDevices];  // DG_OK or DG_EUNSUPPORTED, set once per device
 
 // Split-K plans (dg_gemm_fp8_ws only) are capped at this many FP32 partial
-// floats and arrival counters, which bounds the workspace a caller provides.
+// floats, which bounds the workspace a caller provides.
 constexpr int64_t kWsFloats = 4ll << 20;  // 16 MB of partial tiles
-constexpr int64_t kWsCounters = 1 << 16;
 
-// Per-call tags of the split-K arrival counters (48 bits, never 0): the
-// kernel treats a counter whose tag is not its own call's as zero, so a
-// workspace needs no clearing and a launch that never finished leaves
-// nothing a later call counts. Seeded from the clock so that a fresh
-// workspace's contents are unlikely to carry a matching tag.
-std::atomic<uint64_t> g_epoch{0};
-std::once_flag g_epoch_once;
+// When a workspace plan splits K. A split costs about 2 us beyond the
+// streaming kernel's time for the same K range (the FP32 partials' trip
+// through memory and the second kernel), and its 64x64 tiles move fewer
+// bytes per CU only when there are few of them, so it pays where it cuts a
+// long K range several times: at least kSplitMinSteps 128-byte K steps and
+// at least kSplitMin splits. Graph-timed on small M (8, 64, 128 rows, N 256
+// to 4096, g = 128, K 1024 to 32768): K >= 16384 with 8 to 16 splits took
+// 0.46 to 0.81 of the streaming time; K = 7168 with 8 to 14 splits 0.91 to
+// 1.15; K <= 4096 1.05 to 1.6; 4 splits 0.95 to 1.57 at any K; 2 splits
+// (M = 128, N = 4096, whose streaming tiles take two rounds) 0.87 to 1.10.
+// kMaxSplit bounds the second kernel's sum per output.
+constexpr int64_t kSplitMinSteps = 128;
+constexpr int64_t kSplitMin = 8;
+constexpr int64_t kMaxSplit = 16;
 
-uint64_t next_epoch() {
-  std::call_once(g_epoch_once, [] {
-    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
-    g_epoch.store((t * 0x9E3779B97F4A7C15ull) >> 20);
-  });
-  uint64_t e;
-  do {
-    e = g_epoch.fetch_add(1) & ((1ull << 48) - 1);
-  } while (e == 0);
-  return e;
-}
-
-// Workspace layout of a split-K plan: the arrival counters (8 bytes per
-// tile) first, then the partial tiles from the next 256-byte boundary.
-int64_t counter_bytes(int64_t tiles) { return (tiles * 8 + 255) / 256 * 256; }
+// Workspace layout of a split-K plan: the FP32 partial tiles,
+// [tile][split][bm][bn], row-major inside a tile.
 
 // The workspace of dg_gemm_fp8_noalloc, for callers that cannot allocate
 // device memory: a fixed array in the library's code object, one copy per GPU
 // the library runs on, held until the process ends. Its host-side name is a
 // stand-in, not a device address: the device address is looked up once per
 // device (hipGetSymbolAddress, with that device current) and only that
-// address is passed to kernels. Static device memory starts zeroed; the
-// split-K counters need nothing else (their per-call tags are never zero).
+// address is passed to kernels. A split-K call writes every partial it
+// reads, so the array's contents never matter.
 constexpr int64_t kScratchBytes = 4ll << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 std::once_flag g_scratch_once[kMaxDevices];
@@ -120,29 +111,26 @@ struct Plan {
 };
 
 // Tile-table choice (pure host arithmetic, no HIP call).
-// Small M streams B. Without a workspace (every call but dg_gemm_fp8_ws) a
-// small-M shape of any layout takes 32x32 tiles over the whole K, whose waves
-// split K inside the workgroup, whatever the tile count. With a workspace,
-// shapes with fewer than 192 tiles of 32x32 split the K range of each 64x64
-// tile over several workgroups until about one workgroup per CU (256) runs,
-// keeping at least 4 pipeline steps per split.
+// Small M streams B. A small-M shape of any layout takes 32x32 tiles over the
+// whole K, whose waves split K inside the workgroup, whatever the tile count;
+// with a workspace, a long K (kSplitMinSteps) that gives at least kSplitMin
+// splits instead splits the K range of each 64x64 tile over several
+// workgroups, until about one workgroup per CU (256) runs, at most kMaxSplit
+// per tile and at least 4 pipeline steps per split.
 // Large M and N take the 256-row tiles (256 or 128 wide) when they give at
 // least 3/4 of a tile per CU; the rest takes 128x128 tiles over the whole K.
-// DG_FORCE_TILE=<kernel id> overrides the choice when that entry has the
-// call's granularity (tuning and benchmarking only; a split-K entry then runs
-// with one split unless the call has a workspace).
+// DG_FORCE_TILE=<kernel id>, read at every call, replaces the choice when
+// that entry has the call's granularity (tuning, benchmarking and tests; a
+// split-K entry then runs with one split unless the call has a workspace).
 int forced_tile() {
-  static const int id = [] {
-    const char* e = std::getenv("DG_FORCE_TILE");
-    return e ? std::atoi(e) : -1;
-  }();
-  return id;
+  const char* e = std::getenv("DG_FORCE_TILE");
+  return e ? std::atoi(e) : -1;
 }
 
 int64_t splits_for(const dg::KernelEntry* e, int64_t tiles, int64_t nsteps) {
   int64_t ks = (256 + tiles / 2) / tiles;
-  ks = std::min<int64_t>(ks, nsteps / 4);
-  while (ks > 1 && (tiles * ks * e->bm * e->bn > kWsFloats || tiles > kWsCounters)) --ks;
+  ks = std::min<int64_t>(std::min<int64_t>(ks, kMaxSplit), nsteps / 4);
+  while (ks > 1 && tiles * ks * e->bm * e->bn > kWsFloats) --ks;
   return std::max<int64_t>(ks, 1);
 }
 
@@ -150,7 +138,7 @@ int64_t tiles_of(const dg::KernelEntry* e, int64_t M, int64_t N) {
   return ((M + e->bm - 1) / e->bm) * ((N + e->bn - 1) / e->bn);
 }
 
-Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout, bool split_ok) {
+Plan plan(int64_t M, int64_t N, int64_t K, int sgran, bool split_ok) {
   Plan p{nullptr, 1, 0};
   const int gran = kernel_gran(sgran);
   const int64_t nsteps = (K + 127) / 128;
@@ -160,7 +148,7 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout, bool split_ok)
     p.ksplit = split_ok ? (int)splits_for(p.e, p.tiles, nsteps) : 1;
     return p;
   };
-  const int force = layout == DG_LAYOUT_NT ? forced_tile() : -1;
+  const int force = forced_tile();
   if (force >= 0) {
     for (int i = 0; i < dg::kTableSize; ++i)
       if (dg::kTable[i].id == force && dg::kTable[i].gran == gran) p.e = &dg::kTable[i];
@@ -171,14 +159,11 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout, bool split_ok)
     }
   }
   if (M <= 128) {
-    const dg::KernelEntry* st = find(dg::kClassStream, gran);
-    const int64_t st_tiles = tiles_of(st, M, N);
-    if (!split_ok || st_tiles >= 192) {
-      p.e = st;
-      p.tiles = st_tiles;
-      return p;
-    }
-    return split_k();
+    if (split_ok && nsteps >= kSplitMinSteps && split_k().ksplit >= kSplitMin) return p;
+    p.e = find(dg::kClassStream, gran);
+    p.tiles = tiles_of(p.e, M, N);
+    p.ksplit = 1;
+    return p;
   }
   // 256-row tiles: the width whose tile count fills the 256 CUs best, weighed
   // by the width's own speed per CU (narrower tiles stage more bytes per
@@ -206,7 +191,7 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, int layout, bool split_ok)
 // Workspace bytes of a plan: none without a K split.
 int64_t workspace_bytes(const Plan& p) {
   if (p.ksplit <= 1) return 0;
-  return counter_bytes(p.tiles) + p.tiles * p.ksplit * p.e->bm * p.e->bn * (int64_t)sizeof(float);
+  return p.tiles * p.ksplit * p.e->bm * p.e->bn * (int64_t)sizeof(float);
 }
 
 // One-time per-device check; returns DG_OK, DG_EUNSUPPORTED or DG_ELAUNCH.
@@ -263,7 +248,7 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
       ((uintptr_t)out & 1))
     return DG_EALIGN;
   // A workspace lets small-M shapes split K; without one nothing does.
-  Plan pl = plan(M, N, K, gran, layout, split_ok && (ws_bytes > 0 || use_scratch));
+  Plan pl = plan(M, N, K, gran, split_ok && (ws_bytes > 0 || use_scratch));
   if (!pl.e || pl.tiles * pl.ksplit > 0x7fffffff) return DG_EINVAL;
   const int64_t need = workspace_bytes(pl);
   if (ws_bytes > 0 && ws_bytes < need) return DG_EINVAL;
@@ -315,9 +300,7 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   p.layout = layout;
   p.vec_store = (((uintptr_t)out & 15) == 0 && N % 8 == 0) ? 1 : 0;
   p.ksplit = pl.ksplit;
-  p.counters = pl.ksplit > 1 ? static_cast<unsigned long long*>(ws) : nullptr;
-  p.ws = pl.ksplit > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counter_bytes(pl.tiles)) : nullptr;
-  p.epoch = pl.ksplit > 1 ? next_epoch() : 0;
+  p.ws = pl.ksplit > 1 ? static_cast<float*>(ws) : nullptr;
   p.bias = bias;
   p.act = act;
   if (log_enabled())
@@ -402,7 +385,7 @@ int query(int64_t M, int64_t N, int64_t K, int gran, int layout, bool split_ok, 
   int rc = validate(M, N, K, gran);
   if (rc != DG_OK) return rc;
   if ((rc = validate_layout(M, N, layout)) != DG_OK) return rc;
-  const Plan p = plan(M, N, K, gran, layout, split_ok);
+  const Plan p = plan(M, N, K, gran, split_ok);
   if (!p.e || p.tiles * p.ksplit > 0x7fffffff) return DG_EINVAL;
   info->kernel_id = p.e->id;
   info->bm = p.e->bm;

@@ -21,8 +21,6 @@ struct GemmArgs {
   int vec_store;  // out is 16-byte aligned and N % 8 == 0: full-row chunks use 16-byte stores
   int ksplit;     // workgroups per output tile along K (1 = no split)
   float* ws;      // split-K partial tiles, tiles * ksplit * bm * bn floats (ksplit > 1; caller's workspace)
-  unsigned long long* counters;  // split-K arrival counters, one per tile (caller's workspace)
-  unsigned long long epoch;      // this call's counter tag (48 bits, nonzero; ksplit > 1)
   const float* bias;   // FP32 [N] added before the activation, or null
   int act;             // epilogue activation: 0 none, 1 ReLU, 2 GELU
 };

@@ -48,11 +48,13 @@ __device__ __forceinline__ void wait_steps(int steps) {
 }
 
 // Split-K: ksplit workgroups share one output tile, each covering a contiguous
-// range of 128-byte K steps. Each writes its FP32 partial tile to ws (the
-// caller's workspace); the last to arrive (per-tile arrival counter, tagged
-// with the call's epoch) adds the partials in split order (so the result does
-// not depend on which arrives last) and writes the BF16 tile. ksplit == 1
-// skips all of this.
+// range of 128-byte K steps, and each writes its FP32 partial tile to ws (the
+// caller's workspace) with plain stores. A second kernel on the same stream,
+// splitk_reduce, adds the partials in split order (so the result does not
+// depend on which split ran when) and writes the BF16 tile with the
+// epilogue: the kernel boundary orders the two, so no workgroup waits for or
+// signals another and nothing in the workspace is read before this call
+// wrote it. ksplit == 1 skips all of this.
 //
 // G is the K segment contracted before each promotion; the scale blocks are
 // sg x sg with sg = G << sshift (g = 256 runs G = 128 with one factor per two
@@ -63,8 +65,8 @@ template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool S
 __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ b, const float* __restrict__ sa,
     const float* __restrict__ sb, uint16_t* __restrict__ out, int M, int N, int K, int tiles_m,
-    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, unsigned long long* __restrict__ counters,
-    unsigned long long epoch, int sshift, const float* __restrict__ bias, int relu) {
+    int tiles_n, int vec_store, int ksplit, float* __restrict__ ws, int sshift, const float* __restrict__ bias,
+    int relu) {
   constexpr int NWAVES = WM * WN;
   constexpr int NT = 64 * NWAVES;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
@@ -244,119 +246,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
   }
 
   if (SPLIT && ksplit > 1) {
-    // Partial tile layout: [split][wave][i][j][quarter][lane] of float4 within
-    // the tile's slice of ws, so each store and load below moves 1 KB
-    // contiguous per wave.
-    //
-    // Publication (HIP memory model, agent scope): every wave stores its part
-    // of the partial and waits for those stores; the workgroup barrier (a
-    // workgroup-scope release and acquire) orders them before thread 0's
-    // arrival, a read-modify-write of the tile's counter with release
-    // semantics at agent scope, and the thread that completes the count takes
-    // an acquire fence at agent scope before the barrier after which every
-    // wave reads the other partials. The per-XCD L2s are not coherent with
-    // each other; the agent-scope release and acquire write back and
-    // invalidate what these need, once per workgroup (one such fence per wave
-    // would sweep the L2 four times per workgroup). The stores and loads also
-    // carry the device-scope cache policy (sc1), so the partials go to and
-    // come from the coherence point instead of sitting dirty in one XCD's L2.
-    //
-    // The counter holds (epoch << 16) | arrivals. An arrival that finds
-    // another call's tag counts from zero, so a workspace needs no clearing
-    // and a launch that never finished leaves nothing a later call counts.
-    // The last arrival puts the count back to zero under the same tag: a
-    // captured graph replays the call with the same epoch, and each replay
-    // then counts from zero too.
-    constexpr int CPOL_SC1 = 16;  // device-scope coherence bit of the buffer instructions
-    constexpr int TILE_F = BM * BN, WAVE_F = TM * TN * 16 * 64;
-    const int tile = tmi * tiles_n + tni;
-    const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
-        ws + (int64_t)tile * ksplit * TILE_F, (short)0, ksplit * TILE_F * 4, 0x00020000);
-    const uint32_t lane_off = (uint32_t)(wave * WAVE_F + lane * 4) * 4;  // bytes
+    // This split's FP32 partial tile, row-major, to its slot of the
+    // workspace; splitk_reduce (launched next on the same stream) adds the
+    // splits and writes the output. Each store covers two tile rows of 32
+    // columns (128 contiguous bytes each).
+    float* part = ws + ((int64_t)(tmi * tiles_n + tni) * ksplit + ks) * (BM * BN);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const v4f v = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rws,
-                                                 lane_off + (uint32_t)(((i * TN + j) * 4 + c) * 256 * 4),
-                                                 (uint32_t)ks * TILE_F * 4, CPOL_SC1);
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WTM + i * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
+          const int c = wn * WTN + j * 32 + (lane & 31);
+          part[r * BN + c] = acc[i][j][v];
         }
-    DG_WAIT_VMCNT(0);  // this wave's partial stores have completed
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    __shared__ int last;
-    if (threadIdx.x == 0) {
-      unsigned long long old = __hip_atomic_load(&counters[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      unsigned long long now;
-      do {
-        now = (old >> 16) == epoch ? old + 1 : ((epoch << 16) | 1ull);
-      } while (!__hip_atomic_compare_exchange_weak(&counters[tile], &old, now, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT));
-      const bool done = (now & 0xFFFFull) == (unsigned long long)ksplit;
-      if (done) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every split's stores are visible
-        __hip_atomic_store(&counters[tile], epoch << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      last = done;
-    }
-    __syncthreads();
-    if (!last) return;
-    // Sum in split order 0, 1, ..., ksplit-1 (this split's own partial from
-    // registers): the same additions whichever split arrived last. The other
-    // splits' partials are fetched four splits at a time, all loads of a
-    // batch in flight together.
-    v4f tot[TM][TN][4];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) tot[i][j][c] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-    for (int sp0 = 0; sp0 < ksplit; sp0 += 4) {
-      v4f got[4][TM][TN][4];
-#pragma unroll
-      for (int bsp = 0; bsp < 4; ++bsp) {
-        // splits past the end and this split's own slot read nothing (an
-        // offset past the range reads zero) and are not added
-        const int sp = sp0 + bsp;
-        const uint32_t soff = (sp < ksplit && sp != ks) ? (uint32_t)sp * TILE_F * 4 : 0x80000000u;
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              got[bsp][i][j][c] = __builtin_bit_cast(
-                  v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                           rws, lane_off + (uint32_t)(((i * TN + j) * 4 + c) * 256 * 4), soff, CPOL_SC1));
-      }
-#pragma unroll
-      for (int bsp = 0; bsp < 4; ++bsp) {
-        const int sp = sp0 + bsp;
-        if (sp < ksplit) {
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                tot[i][j][c] += sp == ks ? (v4f){acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
-                                                 acc[i][j][4 * c + 3]}
-                                         : got[bsp][i][j][c];
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * c + e] = tot[i][j][c][e];
+    return;
   }
 
   // Epilogue: BF16 tile through LDS, then 16-byte row-contiguous stores.
@@ -389,6 +294,45 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_fp8_nt_tiled(
   }
 }
 
+// Second kernel of a K split: out = epilogue(sum over splits 0, 1, ...,
+// ksplit-1 of the partial tiles), the additions in split order, in FP32, then
+// rounded to BF16. One thread per four consecutive columns of a tile row; the
+// grid covers every tile (tiles * BM * BN / 4 threads, 256 per workgroup),
+// and threads past M or N store nothing.
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ ws, uint16_t* __restrict__ out, int M,
+                                                     int N, int tiles_n, int ksplit, int vec_store,
+                                                     const float* __restrict__ bias, int relu) {
+  constexpr int Q = BN / 4;  // float4 per tile row
+  static_assert((BM * Q) % 256 == 0, "whole workgroups per tile");
+  const int tile = (int)(blockIdx.x / ((BM * Q) / 256));
+  const int e = (int)(blockIdx.x % ((BM * Q) / 256)) * 256 + (int)threadIdx.x;
+  const int r = e / Q, c = (e % Q) * 4;
+  const int gr = (tile / tiles_n) * BM + r, gc = (tile % tiles_n) * BN + c;
+  if (gr >= M || gc >= N) return;
+  const float* p = ws + (int64_t)tile * ksplit * (BM * BN) + r * BN + c;
+  v4f sum = {0.0f, 0.0f, 0.0f, 0.0f};
+  int sp = 0;
+  for (; sp + 8 <= ksplit; sp += 8) {  // eight loads in flight, added in order
+    v4f q[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) q[t] = *reinterpret_cast<const v4f*>(p + (int64_t)(sp + t) * (BM * BN));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sum += q[t];
+  }
+  for (; sp < ksplit; ++sp) sum += *reinterpret_cast<const v4f*>(p + (int64_t)sp * (BM * BN));
+  const bool hb = EPI != 0 && bias != nullptr;
+  uint16_t h[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) h[t] = bf16_bits(epilogue_fn<EPI>(sum[t], hb, hb && gc + t < N ? bias[gc + t] : 0.0f, relu));
+  uint16_t* dst = out + (int64_t)gr * N + gc;
+  if (vec_store && gc + 4 <= N) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+  } else {
+    for (int t = 0; t < 4 && gc + t < N; ++t) dst[t] = h[t];
+  }
+}
+
 // ---- launch table -------------------------------------------------------------
 
 template <int BM, int BN, int WM, int WN, int STAGES, int G, int GROUP_M, bool SPLIT, int FMT, int EPI, bool ROWA,
@@ -397,9 +341,16 @@ static hipError_t launch_tiled_fa(const GemmArgs& p, hipStream_t stream) {
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
   hipLaunchKernelGGL((gemm_fp8_nt_tiled<BM, BN, WM, WN, STAGES, G, GROUP_M, SPLIT, FMT, EPI, ROWA, LAYOUT>),
                      dim3(tiles_m * tiles_n * p.ksplit), dim3(64 * WM * WN), 0, stream, p.a, p.b, p.sa, p.sb, p.out,
-                     (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.ksplit, p.ws, p.counters,
-                     p.epoch, p.sshift, p.bias, p.act == 1 ? 1 : 0);
-  return hipGetLastError();
+                     (int)p.M, (int)p.N, (int)p.K, tiles_m, tiles_n, p.vec_store, p.ksplit, p.ws, p.sshift, p.bias,
+                     p.act == 1 ? 1 : 0);
+  hipError_t err = hipGetLastError();
+  if (SPLIT && p.ksplit > 1 && err == hipSuccess) {
+    hipLaunchKernelGGL((splitk_reduce<BM, BN, EPI>), dim3(tiles_m * tiles_n * (BM * BN / 4 / 256)), dim3(256), 0,
+                       stream, p.ws, p.out, (int)p.M, (int)p.N, tiles_n, p.ksplit, p.vec_store, p.bias,
+                       p.act == 1 ? 1 : 0);
+    err = hipGetLastError();
+  }
+  return err;
 }
 
 // RS selects the A factor forms compiled: 0 both, chosen by p.rowa (the NT

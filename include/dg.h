@@ -25,7 +25,10 @@
  * are asynchronous on `stream` (a hipStream_t; NULL is the default stream);
  * faults during execution surface at the caller's next synchronisation. No
  * call prints unless the environment sets DG_LOG=1, and no call exits or
- * throws.
+ * throws. DG_FORCE_TILE=<kernel id> in the environment, read at every call,
+ * replaces the tile choice with that table entry where it has the call's
+ * granularity (tuning and tests; results stay within the same tolerance,
+ * with other bits).
  *
  * Thread safety: calls may come from several host threads and run
  * concurrently on any streams (dg_gemm_fp8_ws: each concurrent call with its
@@ -215,17 +218,21 @@ int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, 
 
 /*
  * dg_gemm_fp8_ws - the GEMM with a caller-owned workspace that lets small-M
- * shapes with few output tiles split K over several workgroups.
+ * shapes with few output tiles and a long K split K over several workgroups.
  *
  * DeepGEMM实战 §3.2 accumulates K in segments that are summed separately and
  * then added; §5.3 names too little parallelism as what holds back small
- * shapes. With M <= 128 and too few output tiles to occupy the GPU, this call
- * gives each 64x64 tile ksplit workgroups, each over a contiguous range of K
- * segments; each writes its FP32 partial tile to the workspace, and the last
- * to arrive adds all ksplit partials in split order (so the result does not
- * depend on arrival order) and writes the BF16 tile. Every other shape runs
- * exactly what dg_gemm_fp8_layout / dg_gemm_fp8_nt_ex runs, bit for bit, and
- * leaves the workspace untouched.
+ * shapes. With M <= 128, K >= 16384 (128 steps of 128) and few enough output
+ * tiles that each 64x64 tile gets at least 8 workgroups (at most 16, about
+ * 256 in all), this call gives each tile ksplit workgroups, each over a
+ * contiguous range of K segments, which write their FP32 partial tiles to the
+ * workspace; a second kernel on the same stream adds each tile's partials in
+ * split order (so the result does not depend on which split ran when),
+ * applies the epilogue and writes the BF16 tile. The split costs about 2 us
+ * of its own, which shorter K ranges do not win back against the default
+ * plan's split of K inside the workgroup. Every other shape runs exactly what
+ * dg_gemm_fp8_layout / dg_gemm_fp8_nt_ex runs, bit for bit, and leaves the
+ * workspace untouched.
  *
  *   a, b, sa, sb, out, M, N, K, gran, layout, fmt_a, fmt_b, bias, act
  *        as dg_gemm_fp8_layout.
@@ -234,20 +241,17 @@ int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, 
  *   workspace device memory of at least workspace_bytes bytes, 256-byte
  *        aligned, owned by the caller, or NULL with workspace_bytes 0 (then no
  *        shape splits K). It must not overlap any other argument. Its
- *        contents need no initialisation and are scratch between calls: every
- *        call tags its arrival counters with a fresh per-call value, so a
- *        launch that never finished leaves nothing a later call reads. A call
- *        captured into a graph keeps its tag; each replay that completes
- *        leaves the counters at zero under it, so replays may repeat.
+ *        contents need no initialisation and are scratch between calls: a
+ *        call writes every partial it reads, within the same call.
  *   workspace_bytes  size of workspace; must be 0 or at least the
  *        workspace_bytes dg_query_tile_ws reports for the shape (DG_EINVAL
  *        otherwise).
  *
  * Concurrency: two calls that may run at the same time (different streams,
  * or a graph replay beside an eager call) must use different workspaces;
- * calls on one stream may share one. The partials are published with
- * agent-scope release/acquire ordering (HIP memory model), so any split may
- * run on any XCD. Returns the status codes of dg_gemm_fp8_layout.
+ * calls on one stream may share one. The two kernels of a split call are
+ * ordered by the stream (or by the graph's edge when captured); no workgroup
+ * waits for another. Returns the status codes of dg_gemm_fp8_layout.
  */
 int dg_gemm_fp8_ws(const void* a, const void* b, const float* sa, const float* sb, void* out,
                    int64_t M, int64_t N, int64_t K, int gran, int layout, int sa_rows, int fmt_a, int fmt_b,

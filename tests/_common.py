@@ -2,7 +2,31 @@
 
 from __future__ import annotations
 
+import contextlib
+import os
+
 import numpy as np
+
+# Table ids of the split-K class (64x64 tiles) for K segments of 128 and 64.
+SPLIT_TILE = {128: 2, 256: 2, 64: 3}
+
+
+@contextlib.contextmanager
+def forced_split(g: int):
+    """Inside, every call runs the split-K class (DG_FORCE_TILE, which the
+    library reads at each call), splitting K over workgroups when a workspace
+    is given, whatever the shape. The plan itself splits only long K ranges
+    (16384 and up); this reaches the split path on shapes the oracle finishes
+    in moments."""
+    old = os.environ.get("DG_FORCE_TILE")
+    os.environ["DG_FORCE_TILE"] = str(SPLIT_TILE[g])
+    try:
+        yield
+    finally:
+        if old is None:
+            del os.environ["DG_FORCE_TILE"]
+        else:
+            os.environ["DG_FORCE_TILE"] = old
 
 
 def within_tolerance(got, ref, rms=None):

@@ -112,28 +112,28 @@ void gemm_rejects() {
          "layout -1");
   // the workspace call: size, alignment, presence and overlap rules
   dg_tile_info t;
-  expect(dg_query_tile_ws(64, 512, 7168, 128, 0, &t), DG_OK, "ws plan");
+  expect(dg_query_tile_ws(64, 512, 32768, 128, 0, &t), DG_OK, "ws plan");
   const int64_t need = t.workspace_bytes;
   expect(need > 0, 1, "a split plan needs a workspace");
-  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 7168, 128, 0, 128, 0, 0, nullptr, 0, ws, need - 1, nullptr),
+  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 32768, 128, 0, 128, 0, 0, nullptr, 0, ws, need - 1, nullptr),
          DG_EINVAL, "workspace too small");
-  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 7168, 128, 0, 128, 0, 0, nullptr, 0, shift(ws, 128), need,
+  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 32768, 128, 0, 128, 0, 0, nullptr, 0, shift(ws, 128), need,
                         nullptr),
          DG_EALIGN, "workspace misaligned");
-  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 7168, 128, 0, 128, 0, 0, nullptr, 0, nullptr, need, nullptr),
+  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 32768, 128, 0, 128, 0, 0, nullptr, 0, nullptr, need, nullptr),
          DG_EINVAL, "size without a workspace");
-  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 7168, 128, 0, 128, 0, 0, nullptr, 0, ws, -1, nullptr), DG_EINVAL,
+  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 32768, 128, 0, 128, 0, 0, nullptr, 0, ws, -1, nullptr), DG_EINVAL,
          "negative workspace size");
-  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 7168, 128, 0, 128, 0, 0, nullptr, 0, ws, 0, nullptr), DG_EINVAL,
+  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 32768, 128, 0, 128, 0, 0, nullptr, 0, ws, 0, nullptr), DG_EINVAL,
          "workspace without a size");
-  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 7168, 128, 0, 128, 0, 0, nullptr, 0, out, need, nullptr),
+  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 32768, 128, 0, 128, 0, 0, nullptr, 0, out, need, nullptr),
          DG_EINVAL, "workspace overlaps out");
-  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 7168, 128, 0, 128, 0, 0, nullptr, 0, shift(a, 256), need,
+  expect(dg_gemm_fp8_ws(a, b, sa, sb, out, 64, 512, 32768, 128, 0, 128, 0, 0, nullptr, 0, shift(a, 256), need,
                         nullptr),
          DG_EINVAL, "workspace overlaps a");
-  expect(dg_gemm_fp8_noalloc(a, b, sa, sb, out, 64, 512, 7168, 96, 0, 96, 0, 0, nullptr, 0, nullptr), DG_EINVAL,
+  expect(dg_gemm_fp8_noalloc(a, b, sa, sb, out, 64, 512, 32768, 96, 0, 96, 0, 0, nullptr, 0, nullptr), DG_EINVAL,
          "noalloc gran 96");
-  expect(dg_gemm_fp8_noalloc(a, b, sa, sb, shift(out, 1), 64, 512, 7168, 128, 0, 128, 0, 0, nullptr, 0, nullptr),
+  expect(dg_gemm_fp8_noalloc(a, b, sa, sb, shift(out, 1), 64, 512, 32768, 128, 0, 128, 0, 0, nullptr, 0, nullptr),
          DG_EALIGN, "noalloc out misaligned");
 }
 

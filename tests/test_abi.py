@@ -266,16 +266,24 @@ def test_query_tile_choice(dg, M, N, K, g, cls):
     assert t["workspace_bytes"] == 0
 
 
-# dg_gemm_fp8_ws's plan: small M with fewer than 192 tiles of 32x32 (any
-# layout) splits K over 64x64 tiles; everything else is the plan without a
-# workspace, which needs no workspace.
+# dg_gemm_fp8_ws's plan: small M (any layout) with K of at least 16384 (128
+# steps) that the 64x64 tiles split at least 8 ways (round(256 / tiles), at
+# most 16, at least 4 steps each) splits K over workgroups; everything else is
+# the plan without a workspace, which needs no workspace.
 @pytest.mark.parametrize("M,N,K,g,layout,cls", [
-    (64, 512, 7168, 128, 0, (64, 64, 14)),     # 8 tiles x 14 splits (steps/4 caps at 14)
-    (8, 300, 2048, 128, 0, (64, 64, 4)),       # 5 tiles, 16 steps: 4 splits of 4 steps
-    (64, 4096, 7168, 128, 0, (32, 32, 1)),     # 256 streaming tiles: no split
-    (64, 4096, 7168, 128, 1, (32, 32, 1)),     # B stored [K,N]: 256 streaming tiles, no split
-    (64, 4096, 7168, 128, 2, (32, 32, 1)),     # A stored [K,M]: the same
-    (64, 1024, 7168, 128, 3, (64, 64, 14)),    # 16 tiles x 14 splits (steps/4 caps at 14)
+    (64, 512, 7168, 128, 0, (32, 32, 1)),      # K below 16384: streams, workspace or not
+    (8, 300, 2048, 128, 0, (32, 32, 1)),
+    (64, 512, 8192, 128, 0, (32, 32, 1)),      # 64 steps: streams
+    (64, 512, 16384, 128, 0, (64, 64, 16)),    # 128 steps: 8 tiles, 32 splits capped at 16
+    (64, 512, 24576, 128, 0, (64, 64, 16)),    # 8 tiles: 32 splits capped at 16
+    (8, 256, 32768, 128, 0, (64, 64, 16)),     # 4 tiles: 64 capped at 16
+    (64, 2048, 32768, 128, 1, (64, 64, 8)),    # B stored [K,N]: 32 tiles x 8 splits
+    (64, 1024, 24576, 128, 3, (64, 64, 16)),   # 16 tiles x 16
+    (96, 528, 24576, 256, 2, (64, 64, 14)),    # 18 tiles x 14 (g = 256 runs 128-segment steps)
+    (128, 1024, 65536, 64, 0, (64, 64, 8)),    # g = 64: 32 tiles x 8
+    (8, 4096, 32768, 128, 0, (32, 32, 1)),     # 64 tiles would give 4 splits: streams
+    (64, 4096, 32768, 128, 2, (32, 32, 1)),    # the same, A stored [K,M]
+    (64, 4096, 7168, 128, 0, (32, 32, 1)),
     (8192, 8192, 8192, 128, 0, (256, 256, 1)),
 ])
 def test_query_tile_ws_choice(dg, M, N, K, g, layout, cls):
@@ -287,8 +295,24 @@ def test_query_tile_ws_choice(dg, M, N, K, g, layout, cls):
         assert t["workspace_bytes"] == 0
         assert t == dg.dg_query_tile(M, N, K, g, layout)
     else:
-        # 8-byte counters per tile rounded up to 256 bytes, then FP32 partial tiles
-        assert t["workspace_bytes"] == -(-8 * tiles // 256) * 256 + 4 * tiles * t["ksplit"] * 64 * 64
+        # the FP32 partial tiles
+        assert t["workspace_bytes"] == 4 * tiles * t["ksplit"] * 64 * 64
+
+
+@pytest.mark.parametrize("M,N,K,g,layout,ksplit", [(64, 512, 7168, 128, 0, 14), (8, 300, 2048, 128, 3, 4),
+                                                   (97, 531, 1088, 64, 1, 2), (64, 4096, 7168, 128, 2, 4)])
+def test_forced_split_plan(dg, M, N, K, g, layout, ksplit):
+    # DG_FORCE_TILE, read at every call: the split class on any shape, split
+    # with a workspace, one split without; unset again, the plan is back
+    from tests._common import forced_split
+
+    free = dg.dg_query_tile(M, N, K, g, layout, workspace=True)
+    with forced_split(g):
+        t = dg.dg_query_tile(M, N, K, g, layout, workspace=True)
+        assert (t["bm"], t["bn"], t["ksplit"]) == (64, 64, ksplit), t
+        t1 = dg.dg_query_tile(M, N, K, g, layout)
+        assert (t1["bm"], t1["bn"], t1["ksplit"], t1["workspace_bytes"]) == (64, 64, 1, 0), t1
+    assert dg.dg_query_tile(M, N, K, g, layout, workspace=True) == free
 
 
 # Fake addresses 2^40 apart for the workspace call, so that only the
@@ -296,7 +320,7 @@ def test_query_tile_ws_choice(dg, M, N, K, g, layout, cls):
 WA, WB, WSA, WSB, WOUT, WS = (i << 40 for i in range(1, 7))
 
 
-def _ws_call(dg, ws=WS, ws_bytes=4 << 20, M=64, N=512, K=7168, g=128, layout=0, sa_rows=None, out=WOUT, a=WA):
+def _ws_call(dg, ws=WS, ws_bytes=4 << 20, M=64, N=512, K=32768, g=128, layout=0, sa_rows=None, out=WOUT, a=WA):
     return dg.lib.dg_gemm_fp8_ws(a, WB, WSA, WSB, out, M, N, K, g, layout, g if sa_rows is None else sa_rows, 0, 0,
                                  None, 0, ws, ws_bytes, None)
 
@@ -304,9 +328,9 @@ def _ws_call(dg, ws=WS, ws_bytes=4 << 20, M=64, N=512, K=7168, g=128, layout=0, 
 def test_ws_fake_addresses_do_not_overlap(dg):
     # the baseline case passes every argument check; it would then need a GPU,
     # so only its query is made here
-    need = dg.dg_query_tile(64, 512, 7168, 128, 0, workspace=True)["workspace_bytes"]
+    need = dg.dg_query_tile(64, 512, 32768, 128, 0, workspace=True)["workspace_bytes"]
     assert 0 < need <= 4 << 20
-    assert max(64 * 7168, 512 * 7168, 2 * 64 * 512, 4 << 20) < 1 << 40
+    assert max(64 * 32768, 512 * 32768, 2 * 64 * 512, 4 << 20) < 1 << 40
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -314,7 +338,7 @@ def test_ws_fake_addresses_do_not_overlap(dg):
     (dict(ws_bytes=0), "DG_EINVAL"),                        # a buffer without a size
     (dict(ws_bytes=-256), "DG_EINVAL"),
     (dict(ws=WS + 16), "DG_EALIGN"),                        # 256-byte alignment
-    (dict(ws_bytes=4096), "DG_EINVAL"),                     # smaller than the 64x512x7168 plan needs
+    (dict(ws_bytes=4096), "DG_EINVAL"),                     # smaller than the 64x512x32768 plan needs
     (dict(ws=WOUT - 0x1000), "DG_EINVAL"),                  # overlaps out
     (dict(ws=WA + 0x1000), "DG_EINVAL"),                    # overlaps a
     (dict(out=WS + (1 << 19)), "DG_EINVAL"),                # out inside the workspace
@@ -358,7 +382,7 @@ def test_quantize_scale_count_cap(dg):
 def test_noalloc_scratch_limit(dg):
     # the fixed scratch is 4 MiB; a plan needing more is refused before any HIP call
     assert dg.dg_noalloc_scratch_bytes() == 4 << 20
-    M, N, K, g = 32, 6080, 2048, 128  # 190 tiles of 32x32 -> 95 tiles of 64x64 x 3 splits
+    M, N, K, g = 128, 1088, 32768, 128  # 34 tiles of 64x64 x 8 splits: 4.25 MiB of partials
     need = dg.dg_query_tile(M, N, K, g, workspace=True)["workspace_bytes"]
     assert need > dg.dg_noalloc_scratch_bytes()
     assert dg.lib.dg_gemm_fp8_noalloc(WA, WB, WSA, WSB, WOUT, M, N, K, g, 0, g, 0, 0, None, 0, None) == dg.DG_ESCRATCH

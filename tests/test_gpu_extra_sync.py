@@ -28,8 +28,8 @@ CASES = [
     (64, 4096, 1024, 128, 0, False, 0, 0, 0, False, False, (32, 32, False)),
     (64, 4095, 1024, 128, 1, False, 0, 0, 1, True, False, (32, 32, False)),
     (97, 531, 1088, 64, 2, True, 0, 0, 0, False, False, (32, 32, False)),
-    (96, 528, 2048, 128, 0, False, 0, 1, 0, False, True, (64, 64, True)),
-    (96, 528, 2048, 128, 3, True, 0, 0, 2, True, True, (64, 64, True)),
+    (96, 528, 24576, 128, 0, False, 0, 1, 0, False, True, (64, 64, True)),
+    (96, 528, 24576, 128, 3, True, 0, 0, 2, True, True, (64, 64, True)),
     (1008, 3008, 512, 128, 0, False, 0, 0, 0, False, False, (128, 128, False)),
     (1024, 2000, 576, 64, 1, False, 1, 1, 0, False, False, (128, 128, False)),
     (4000, 4000, 768, 128, 0, False, 0, 0, 2, True, False, (256, 256, False)),

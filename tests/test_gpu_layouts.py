@@ -332,8 +332,15 @@ def test_tiny_shapes_every_layout(M, N, K, g, rowa):
 @pytest.mark.parametrize("M,N,K,g", [(1, 1, 2048, 128), (3, 2, 1088, 64), (2, 130, 1024, 128), (33, 3, 2048, 64),
                                      (5, 7, 1536, 256), (97, 5, 1088, 64)])
 def test_tiny_shapes_every_layout_split_k(M, N, K, g, rowa):
-    # the same with a workspace: these few tiles split K over workgroups, and
-    # only the last split's final step holds the tensor's last bytes
+    # the same through the split-K class with a workspace (the tile override:
+    # the plan itself streams K ranges this short): these few tiles split K
+    # over workgroups, and only the last split's final step holds the
+    # tensor's last bytes
+    with _common.forced_split(g):
+        _tiny_split_k(M, N, K, g, rowa)
+
+
+def _tiny_split_k(M, N, K, g, rowa):
     import fp8_block_scaled_scales_amd as dg
 
     assert all(dg.dg_query_tile(M, N, K, g, layout, workspace=True)["ksplit"] > 1 for layout in range(4))

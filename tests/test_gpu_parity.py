@@ -205,8 +205,9 @@ def test_non_default_stream_and_unaligned_out():
 
 # Small M with few 32x32 tiles: without a workspace the streaming class still
 # takes them (whole K per workgroup, waves splitting K, partials added in wave
-# order inside the workgroup); the cross-workgroup split of these shapes
-# (dg_gemm_fp8_ws) is covered in test_gpu_workspace.py.
+# order inside the workgroup); the cross-workgroup split (dg_gemm_fp8_ws on
+# long K ranges, and on these short ones through the tile override) is
+# covered in test_gpu_workspace.py.
 FEW_TILES = [
     (1, 4096, 7168, 128), (64, 1000, 4096, 64), (100, 520, 2048, 128), (33, 700, 64 * 37, 64),
     (128, 512, 8192, 128), (7, 64, 16384, 64), (96, 2000, 1024, 128), (8, 300, 2048, 128),

@@ -3,14 +3,17 @@
 The other GPU tests take the options one or two at a time on chosen shapes.
 Here each case draws, from a fixed seed, a shape from edge sizes (1-3, one
 under/over a tile edge, ragged), a granularity, formats for A and B, block or
-per-row A factors, an epilogue, and whether a workspace is given (few tiles
-then split K), and runs it in all four layouts. Every output element is
+per-row A factors, an epilogue, and whether a workspace is given (then the
+split-K class runs, through the tile override, and splits K over
+workgroups), and runs it in all four layouts. Every output element is
 compared with the oracle (tolerance as everywhere), and the three transposed
 layouts must give the NT layout's bits (the same K order inside every
 product).
 """
 
 from __future__ import annotations
+
+import contextlib
 
 import numpy as np
 import pytest
@@ -64,21 +67,22 @@ def test_option_sweep(i):
     tsa, tsb = torch.from_numpy(sa).to(dev), torch.from_numpy(sb).to(dev)
     tbias = None if bias is None else torch.from_numpy(bias).to(dev)
     bits = {}
-    for layout in range(4):
-        a_st = np.ascontiguousarray(a8.T) if layout & 2 else a8
-        b_st = np.ascontiguousarray(b8.T) if layout & 1 else b8
-        plan = dg.dg_query_tile(M, N, K, g, layout, workspace=ws)
-        say("sweep %d: %dx%dx%d g=%d fmt %d,%d rowa=%d epi=%d ws=%d layout %d -> %dx%d ksplit %d" % (
-            i, M, N, K, g, fa, fb, rowa, epi, ws, layout, plan["bm"], plan["bn"], plan["ksplit"]))
-        out = dg.dg_gemm_fp8_ws(torch.from_numpy(a_st).to(dev), torch.from_numpy(b_st).to(dev), tsa, tsb, gran=g,
-                                layout=layout, sa_rows=1 if rowa else None, fmt_a=fa, fmt_b=fb, bias=tbias, act=act,
-                                workspace=dg.dg_workspace(M, N, K, g, layout, device=dev) if ws else None)
-        torch.cuda.synchronize()
-        bits[layout] = out.view(torch.int16).cpu().numpy().view(np.uint16)
-        got = _common.bf16_bits_to_f64(bits[layout])
-        ok, rms = _common.within_tolerance(got, ref)
-        assert ok.all(), "case %d layout %d: %d of %d outside tolerance (first at %s)" % (
-            i, layout, int((~ok).sum()), ok.size, np.argwhere(~ok)[0])
+    with _common.forced_split(g) if ws else contextlib.nullcontext():
+        for layout in range(4):
+            a_st = np.ascontiguousarray(a8.T) if layout & 2 else a8
+            b_st = np.ascontiguousarray(b8.T) if layout & 1 else b8
+            plan = dg.dg_query_tile(M, N, K, g, layout, workspace=ws)
+            say("sweep %d: %dx%dx%d g=%d fmt %d,%d rowa=%d epi=%d ws=%d layout %d -> %dx%d ksplit %d" % (
+                i, M, N, K, g, fa, fb, rowa, epi, ws, layout, plan["bm"], plan["bn"], plan["ksplit"]))
+            out = dg.dg_gemm_fp8_ws(torch.from_numpy(a_st).to(dev), torch.from_numpy(b_st).to(dev), tsa, tsb, gran=g,
+                                    layout=layout, sa_rows=1 if rowa else None, fmt_a=fa, fmt_b=fb, bias=tbias, act=act,
+                                    workspace=dg.dg_workspace(M, N, K, g, layout, device=dev) if ws else None)
+            torch.cuda.synchronize()
+            bits[layout] = out.view(torch.int16).cpu().numpy().view(np.uint16)
+            got = _common.bf16_bits_to_f64(bits[layout])
+            ok, rms = _common.within_tolerance(got, ref)
+            assert ok.all(), "case %d layout %d: %d of %d outside tolerance (first at %s)" % (
+                i, layout, int((~ok).sum()), ok.size, np.argwhere(~ok)[0])
     for layout in (1, 2, 3):
         assert np.array_equal(bits[layout], bits[0]), "case %d: layout %d differs from NT" % (i, layout)
 

@@ -4,13 +4,18 @@ separately, then added; §5.3: small shapes lack parallelism), with the FP32
 partial tiles in a workspace the caller owns.
 
 Bars: the elementwise tolerance against the oracle; bit for bit between
-repeated calls (the partials are added in split order, whichever workgroup
-arrives last), for all-ones closed forms, and against the call without a
+repeated calls (the partials are added in split order, whichever split ran
+when), for all-ones closed forms, and against the call without a
 workspace wherever the workspace plan does not split. The workspace needs no
 initialisation and keeps nothing a later call reads: calls on garbage or on
-another call's leftovers (counters tagged by earlier calls, partials of other
-shapes) give the same bits as calls on a fresh workspace. Two calls on two
-streams at once, each with its own workspace, both match the oracle.
+another call's partials give the same bits as calls on a fresh workspace.
+Two calls on two streams at once, each with its own workspace, both match
+the oracle.
+
+The plan splits only long K ranges (K >= 16384 cut at least 8 ways); the
+split kernel is also run on short ones through the tile override, so its
+edges (ragged M and N, few steps per split) are covered where the oracle is
+quick.
 """
 
 import numpy as np
@@ -23,11 +28,14 @@ from tests._gpu import device_inputs, say
 
 pytestmark = pytest.mark.gpu
 
-# Small M with few 32x32 tiles: the workspace plan splits K over 64x64 tiles.
+# Small M, few tiles, long K: the workspace plan splits K over 64x64 tiles.
 SPLITK = [
-    (1, 4096, 7168, 128), (64, 1000, 4096, 64), (100, 520, 2048, 128), (33, 700, 64 * 37, 64),
-    (128, 512, 8192, 128), (7, 64, 16384, 64), (96, 2000, 1024, 128), (64, 512, 7168, 128), (8, 300, 2048, 256),
+    (1, 2048, 32768, 128), (64, 1000, 24576, 64), (100, 520, 24576, 128), (33, 700, 64 * 400, 64),
+    (128, 512, 32768, 128), (7, 64, 65536, 64), (96, 1000, 24576, 128), (64, 512, 24576, 128), (8, 300, 24576, 256),
 ]
+# Short K ranges the plan streams, split through the tile override.
+SPLITK_FORCED = [(64, 512, 7168, 128), (8, 300, 2048, 256), (100, 520, 2048, 128), (33, 700, 64 * 37, 64),
+                 (96, 2000, 1024, 128), (1, 4096, 7168, 128)]
 
 
 def _operands(M, N, K, g, seed, fa=0, fb=0):
@@ -69,34 +77,39 @@ def _assert_parity(got, ref, label):
     say("%s: max|err|/rms = %.3g" % (label, np.max(np.abs(got - ref)) / rms))
 
 
-@pytest.mark.parametrize("M,N,K,g", SPLITK)
-def test_ws_splitk_parity(M, N, K, g):
+@pytest.mark.parametrize("M,N,K,g,forced", [s + (False,) for s in SPLITK] + [s + (True,) for s in SPLITK_FORCED])
+def test_ws_splitk_parity(M, N, K, g, forced):
+    import contextlib
+
     import torch
 
     import fp8_block_scaled_scales_amd as dg
 
-    plan = dg.dg_query_tile(M, N, K, g, workspace=True)
-    assert plan["ksplit"] > 1 and plan["workspace_bytes"] > 0, plan
     assert dg.dg_query_tile(M, N, K, g)["ksplit"] == 1
+    assert (dg.dg_query_tile(M, N, K, g, workspace=True)["ksplit"] > 1) != forced
     a8, sa, b8, sb = _operands(M, N, K, g, 5000 + M + N)
     t = device_inputs(a8, sa, b8, sb)
-    ws = dg.dg_workspace(M, N, K, g)
-    say("ws split-K M=%d N=%d K=%d g=%d ksplit=%d ws=%d" % (M, N, K, g, plan["ksplit"], ws.numel()))
-    out = _ws_call(t, g, ws)
     ref = oracle.gemm_ref_fmt(a8, b8, sa, sb, g, 0, 0)
-    _assert_parity(_vals(out), ref, "ws split-K %dx%dx%d g=%d" % (M, N, K, g))
-    bits = _bits(out)
-    # again on the same workspace, and on a larger one
-    assert np.array_equal(_bits(_ws_call(t, g, ws)), bits)
-    big = torch.empty(ws.numel() + (1 << 20), dtype=torch.uint8, device="cuda:0")
-    assert np.array_equal(_bits(_ws_call(t, g, big)), bits)
+    with _common.forced_split(g) if forced else contextlib.nullcontext():
+        plan = dg.dg_query_tile(M, N, K, g, workspace=True)
+        assert plan["ksplit"] > 1 and plan["workspace_bytes"] > 0, plan
+        ws = dg.dg_workspace(M, N, K, g)
+        say("ws split-K M=%d N=%d K=%d g=%d ksplit=%d ws=%d forced=%d" % (M, N, K, g, plan["ksplit"], ws.numel(),
+                                                                          forced))
+        out = _ws_call(t, g, ws)
+        _assert_parity(_vals(out), ref, "ws split-K %dx%dx%d g=%d" % (M, N, K, g))
+        bits = _bits(out)
+        # again on the same workspace, and on a larger one
+        assert np.array_equal(_bits(_ws_call(t, g, ws)), bits)
+        big = torch.empty(ws.numel() + (1 << 20), dtype=torch.uint8, device="cuda:0")
+        assert np.array_equal(_bits(_ws_call(t, g, big)), bits)
     # the call without a workspace (in-workgroup K split) on the same inputs is also within tolerance
     _assert_parity(_vals(dg.dg_gemm_fp8_nt_fmt(t[0], t[2], t[1], t[3], gran=g)), ref,
                    "no workspace %dx%dx%d g=%d" % (M, N, K, g))
 
 
 def test_ws_all_ones_bitwise():
-    M, N, K, g = 64, 384, 4096, 128
+    M, N, K, g = 64, 384, 24576, 128
     a8 = np.full((M, K), 0x38, np.uint8)
     b8 = np.full((N, K), 0x38, np.uint8)
     sa = np.array([[2.0 ** ((mb - kb) % 7 - 3) for kb in range(K // g)] for mb in range(-(-M // g))], np.float32)
@@ -111,34 +124,30 @@ def test_ws_all_ones_bitwise():
 
 
 def test_ws_garbage_and_stale_contents():
-    """No initialisation needed, nothing carried over: a workspace full of 0xFF
-    bytes, of random bytes, or holding counters a launch left mid-count (one
-    arrival short, tagged by an earlier call), gives the fresh-workspace bits."""
+    """No initialisation needed, nothing carried over: every call writes each
+    partial it adds before adding it, so a workspace full of 0xFF bytes (NaN
+    floats), of random bytes, or of another shape's partials gives the
+    fresh-workspace bits."""
     import torch
 
     import fp8_block_scaled_scales_amd as dg
 
-    M, N, K, g = 64, 512, 7168, 128
+    M, N, K, g = 64, 512, 24576, 128
     a8, sa, b8, sb = _operands(M, N, K, g, 8100)
     t = device_inputs(a8, sa, b8, sb)
     plan = dg.dg_query_tile(M, N, K, g, workspace=True)
+    assert plan["ksplit"] > 1
     ws = torch.zeros(plan["workspace_bytes"], dtype=torch.uint8, device="cuda:0")
     say("ws garbage/stale: fresh")
     want = _bits(_ws_call(t, g, ws))
-    tiles = plan["grid"] // plan["ksplit"]
-    counters = ws[:8 * tiles].view(torch.int64)
-    # what the last call left: every tile's counter back at zero arrivals under that call's tag
-    tag = int(counters[0].item()) >> 16
-    assert tag != 0
-    assert all((int(c) >> 16) == tag and (int(c) & 0xFFFF) == 0 for c in counters.cpu().tolist())
+    other = (8, 300, 24576, 128)
+    t_other = device_inputs(*_operands(*other, seed=8101))
     cases = {
         "ones": lambda: ws.fill_(0xFF),
         "random": lambda: ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda:0",
                                                  generator=torch.Generator(device="cuda:0").manual_seed(3))),
-        # an aborted launch of the previous call: one arrival short on every tile
-        "one short": lambda: counters.copy_(torch.full_like(counters, (tag << 16) | (plan["ksplit"] - 1))),
-        # counters of some other call mid-count, with any arrival count
-        "other tag": lambda: counters.copy_(torch.arange(tiles, device="cuda:0", dtype=torch.int64) + (12345 << 16)),
+        "another shape's partials": lambda: _ws_call(t_other, other[3], ws[:dg.dg_query_tile(
+            *other, workspace=True)["workspace_bytes"]]),
     }
     for name, plant in cases.items():
         plant()
@@ -152,7 +161,7 @@ def test_ws_interleaved_shapes_one_workspace():
     on one workspace (one stream) 20 times: every result bit for bit the same."""
     import fp8_block_scaled_scales_amd as dg
 
-    shapes = [(64, 512, 7168, 128), (8, 300, 2048, 128)]
+    shapes = [(64, 512, 24576, 128), (128, 1024, 24576, 128)]
     plans = [dg.dg_query_tile(*s, workspace=True) for s in shapes]
     assert plans[0]["ksplit"] != plans[1]["ksplit"] and all(p["ksplit"] > 1 for p in plans), plans
     ws = dg.dg_workspace(*max(shapes, key=lambda s: dg.dg_query_tile(*s, workspace=True)["workspace_bytes"]))
@@ -177,7 +186,8 @@ def test_ws_two_streams_concurrently():
 
     import fp8_block_scaled_scales_amd as dg
 
-    shapes = [(64, 512, 7168, 128), (100, 520, 2048, 128)]
+    shapes = [(64, 512, 24576, 128), (100, 520, 24576, 128)]
+    assert all(dg.dg_query_tile(*s, workspace=True)["ksplit"] > 1 for s in shapes)
     ops = [_operands(*s, seed=8300 + i) for i, s in enumerate(shapes)]
     ts = [device_inputs(*o) for o in ops]
     wss = [dg.dg_workspace(*s) for s in shapes]
@@ -206,7 +216,8 @@ def test_ws_graph_replays():
 
     import fp8_block_scaled_scales_amd as dg
 
-    M, N, K, g = 64, 512, 7168, 128
+    M, N, K, g = 64, 512, 24576, 128
+    assert dg.dg_query_tile(M, N, K, g, workspace=True)["ksplit"] > 1
     a8, sa, b8, sb = _operands(M, N, K, g, 8700)
     t = device_inputs(a8, sa, b8, sb)
     ws = dg.dg_workspace(M, N, K, g)
@@ -229,7 +240,8 @@ def test_ws_graph_replays():
 
 
 @pytest.mark.parametrize("M,N,K,g,layout", [(64, 4096, 7168, 128, 0), (2000, 4000, 1024, 128, 0),
-                                            (256, 256, 256, 128, 0), (1008, 3008, 512, 128, 2)])
+                                            (256, 256, 256, 128, 0), (1008, 3008, 512, 128, 2),
+                                            (64, 512, 7168, 128, 3), (8, 4096, 32768, 128, 0)])
 def test_ws_without_split_is_the_plain_call(M, N, K, g, layout):
     """Shapes the workspace plan does not split run the call without a
     workspace, bit for bit, and leave the workspace untouched."""
@@ -241,7 +253,8 @@ def test_ws_without_split_is_the_plain_call(M, N, K, g, layout):
     assert plan["ksplit"] == 1 and plan["workspace_bytes"] == 0
     a8, sa, b8, sb = _operands(M, N, K, g, 8400 + M)
     a_st = np.ascontiguousarray(a8.T) if layout & 2 else a8
-    t = device_inputs(a_st, sa, b8, sb)
+    b_st = np.ascontiguousarray(b8.T) if layout & 1 else b8
+    t = device_inputs(a_st, sa, b_st, sb)
     ws = torch.full((1 << 16,), 0x5A, dtype=torch.uint8, device="cuda:0")
     say("ws without split %dx%dx%d layout %d" % (M, N, K, layout))
     got = _bits(_ws_call(t, g, ws, layout=layout))
@@ -259,7 +272,7 @@ def test_ws_split_variants(case):
 
     import fp8_block_scaled_scales_amd as dg
 
-    M, N, K, g, layout, fa, fb, act, with_bias, rowa = 96, 528, 2048, 128, 0, 0, 0, 0, False, False
+    M, N, K, g, layout, fa, fb, act, with_bias, rowa = 96, 528, 24576, 128, 0, 0, 0, 0, False, False
     if case == "e5m2":
         fa = fb = 1
     elif case == "e4m3xe5m2":
@@ -270,11 +283,11 @@ def test_ws_split_variants(case):
         act, with_bias = 1, True
     elif case.startswith("rowa"):
         rowa, g = True, int(case[-3:].lstrip("g"))
-        K = 2048 if g == 128 else 1088
+        K = 24576 if g == 128 else 64 * 385
     elif case in ("nn", "tt", "tn"):
         layout = {"nn": 1, "tt": 2, "tn": 3}[case]
     elif case == "g64_half_step":
-        g, K = 64, 1088
+        g, K = 64, 64 * 385  # 192.5 steps of 128
     plan = dg.dg_query_tile(M, N, K, g, layout, workspace=True)
     assert plan["ksplit"] > 1, plan
     x = synth.normal(8500, (M, K))

@@ -33,9 +33,10 @@ def test_noalloc_matches_workspace_call():
 
     import fp8_block_scaled_scales_amd as dg
 
-    shapes = [(64, 512, 7168, 128), (8, 300, 2048, 128), (64, 4096, 1024, 128), (64, 512, 7168, 128)]
+    shapes = [(64, 512, 24576, 128), (8, 300, 24576, 128), (64, 4096, 1024, 128), (64, 512, 24576, 128)]
     for i, (M, N, K, g) in enumerate(shapes):
         plan = dg.dg_query_tile(M, N, K, g, workspace=True)
+        assert (plan["ksplit"] > 1) == (i != 2), plan
         assert plan["workspace_bytes"] <= dg.dg_noalloc_scratch_bytes()
         a8, sa, b8, sb = _case(M, N, K, g, 9100 + i)
         ta, tsa, tb, tsb = device_inputs(a8, sa, b8, sb)
@@ -55,7 +56,7 @@ def test_noalloc_rejects_a_plan_beyond_the_scratch():
 
     import fp8_block_scaled_scales_amd as dg
 
-    M, N, K, g = 32, 6080, 2048, 128
+    M, N, K, g = 128, 1088, 32768, 128  # 34 tiles x 8 splits: 4.25 MiB of partials
     assert dg.dg_query_tile(M, N, K, g, workspace=True)["workspace_bytes"] > dg.dg_noalloc_scratch_bytes()
     a8, sa, b8, sb = _case(M, N, K, g, 9200)
     ta, tsa, tb, tsb = device_inputs(a8, sa, b8, sb)
@@ -72,7 +73,7 @@ def test_noalloc_layout_and_row_factors():
 
     import fp8_block_scaled_scales_amd as dg
 
-    M, N, K, g, layout = 96, 528, 2048, 128, 3
+    M, N, K, g, layout = 96, 528, 24576, 128, 3
     plan = dg.dg_query_tile(M, N, K, g, layout, workspace=True)
     assert plan["ksplit"] > 1 and plan["workspace_bytes"] <= dg.dg_noalloc_scratch_bytes()
     x = synth.normal(9300, (M, K)) * np.exp(np.random.default_rng(9300).uniform(-3, 3, size=(M, 1)))
