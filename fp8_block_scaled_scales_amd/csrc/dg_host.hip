@@ -117,8 +117,9 @@ struct Plan {
 // splits instead splits the K range of each 64x64 tile over several
 // workgroups, until about one workgroup per CU (256) runs, at most kMaxSplit
 // per tile and at least 4 pipeline steps per split.
-// Large M and N take the 256-row tiles (256 or 128 wide) when they give at
-// least 3/4 of a tile per CU; the rest takes 128x128 tiles over the whole K.
+// Larger M takes the table entry of the call's granularity with the least
+// estimated time (estimate_us): the 32x32 streaming tiles, 64x64 tiles over
+// the whole K, 128x128, or the 256-row tiles 128 or 256 wide.
 // DG_FORCE_TILE=<kernel id>, read at every call, replaces the choice when
 // that entry has the call's granularity (tuning, benchmarking and tests; a
 // split-K entry then runs with one split unless the call has a workspace).
@@ -136,6 +137,17 @@ int64_t splits_for(const dg::KernelEntry* e, int64_t tiles, int64_t nsteps) {
 
 int64_t tiles_of(const dg::KernelEntry* e, int64_t M, int64_t N) {
   return ((M + e->bm - 1) / e->bm) * ((N + e->bn - 1) / e->bn);
+}
+
+// Estimated microseconds of one launch of e on M x N x K (whole K per
+// workgroup): the entry's fixed cost plus, per round of one workgroup per
+// CU, the larger of moving the tile's operand rows (bm + bn rows of K bytes)
+// and its arithmetic (2 bm bn K FLOP) at the entry's per-CU rates.
+double estimate_us(const dg::KernelEntry* e, int64_t M, int64_t N, int64_t K) {
+  const int64_t rounds = (tiles_of(e, M, N) + 255) / 256;
+  const double bytes = (double)(e->bm + e->bn) * (double)K;
+  const double flop = 2.0 * e->bm * e->bn * (double)K;
+  return e->cost_us + (double)rounds * std::max(bytes / (e->cu_gbps * 1e3), flop / (e->cu_tflops * 1e6));
 }
 
 Plan plan(int64_t M, int64_t N, int64_t K, int sgran, bool split_ok) {
@@ -165,26 +177,25 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, bool split_ok) {
     p.ksplit = 1;
     return p;
   }
-  // 256-row tiles: the width whose tile count fills the 256 CUs best, weighed
-  // by the width's own speed per CU (narrower tiles stage more bytes per
-  // FLOP); too few tiles of any width fall back to 128 x 128.
-  const dg::KernelEntry* big = nullptr;
+  // Larger M: the entry with the least estimated time. Every class streams
+  // its operand rows from L2 into the CU at a rate per CU that barely
+  // depends on the tile (the workgroups of one CU share it), so a launch
+  // takes about rounds x max(bytes per workgroup / that rate, FLOP per
+  // workgroup / the entry's MFMA rate) plus a fixed cost, with rounds the
+  // tiles per CU. Small tiles win when there are few of them (less per CU,
+  // more CUs busy), large ones when the arithmetic dominates.
   double best = 0.0;
-  int64_t big_tiles = 0;
   for (int i = 0; i < dg::kTableSize; ++i) {
     const dg::KernelEntry* e = &dg::kTable[i];
-    if (e->cls != dg::kClassBig || e->gran != gran) continue;
-    const int64_t t = tiles_of(e, M, N);
-    const double fill = (double)t / (double)(256 * ((t + 255) / 256));
-    const double per_cu = e->bn == 256 ? 1.0 : 0.8;
-    if (fill * per_cu > best) {
-      best = fill * per_cu;
-      big = e;
-      big_tiles = t;
+    if (e->gran != gran) continue;
+    const double t = estimate_us(e, M, N, K);
+    if (!p.e || t < best) {
+      best = t;
+      p.e = e;
     }
   }
-  p.e = big && big_tiles >= 192 ? big : find(dg::kClassTiled, gran);
   p.tiles = tiles_of(p.e, M, N);
+  p.ksplit = 1;
   return p;
 }
 

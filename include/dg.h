@@ -199,13 +199,16 @@ typedef struct dg_tile_info {
   int stages;    /* LDS ring depth */
   int waves;     /* waves per workgroup */
   int ksplit;    /* workgroups sharing one output tile, each over a K range (1 = none) */
-  int64_t grid;  /* workgroups launched */
+  int64_t grid;  /* workgroups of the GEMM kernel (a K split adds a second, smaller launch) */
   int64_t workspace_bytes; /* workspace dg_gemm_fp8_ws needs for this plan (0: none) */
 } dg_tile_info;
 
 /*
  * dg_query_tile - fill *info with the tile-table entry dg_gemm_fp8_nt would
- * launch for (M, N, K, gran). Pure host logic, no HIP call. Returns DG_OK or
+ * launch for (M, N, K, gran): for M <= 128 the 32x32 streaming tiles, for
+ * larger M the entry with the least estimated launch time (operand bytes per
+ * CU and FLOP per CU at each entry's measured rates, per round of tiles).
+ * Pure host logic, no HIP call. Returns DG_OK or
  * DG_EINVAL for arguments dg_gemm_fp8_nt would reject. ksplit is always 1
  * and workspace_bytes 0: this call never splits K over workgroups.
  */

@@ -247,10 +247,14 @@ def test_python_binding_rejects_bad_tensors(dg):
         dg.dg_gemm_fp8_nt(a, a, torch.ones(1, 1), torch.ones(1, 1))  # CPU tensors
 
 
-# Host-side tile choice for the five workloads and the 256-row widths: the
-# width whose tile count fills the 256 CUs best, weighed by per-CU speed.
+# Host-side tile choice for the five workloads and shapes between them: M up
+# to 128 streams; larger M takes the entry with the least estimated time.
 @pytest.mark.parametrize("M,N,K,g,cls", [
-    (256, 256, 256, 128, (128, 128, 1)),      # too few tiles for 256-row tiles
+    (256, 256, 256, 128, (64, 64, 1)),        # 16 tiles of 64x64
+    (250, 1000, 2048, 128, (32, 32, 1)),      # few tiles, M > 128: the 32x32 streaming tiles
+    (600, 1000, 2048, 64, (64, 64, 1)),
+    (777, 3333, 2048, 128, (128, 128, 1)),
+    (1536, 7168, 2048, 128, (256, 256, 1)),   # 168 tiles of 256x256 beat 672 of 128x128
     (64, 4096, 7168, 128, (32, 32, 1)),       # small M, 256 streaming tiles
     (64, 512, 7168, 128, (32, 32, 1)),        # small M, few tiles: still 32x32 over the whole K (no workspace)
     (8, 300, 2048, 128, (32, 32, 1)),

@@ -23,6 +23,8 @@ NONE, RELU, GELU = 0, 1, 2
 SHAPES = [
     (64, 4096, 1024, 128, (32, 32)),     # streaming
     (64, 520, 2048, 128, (32, 32)),      # streaming, few tiles
+    (250, 1000, 2048, 64, (32, 32)),     # streaming, M > 128 with few tiles
+    (300, 1031, 1024, 128, (64, 64)),    # 64x64 over the whole K
     (1000, 3000, 512, 64, (128, 128)),   # tiled
     (4000, 4000, 768, 128, (256, 256)),  # 256-row tiles
     (3583, 3585, 512, 128, (256, 256)),

@@ -57,11 +57,15 @@ SHAPES = [
     (64, 4096, 1536, 256, (32, 32)),
     (64, 520, 2048, 256, (32, 32)),      # streaming, few tiles
     (100, 520, 1088, 64, (32, 32)),
-    (1000, 3000, 512, 256, (128, 128)),  # tiled
+    (257, 1024, 7168, 256, (32, 32)),    # streaming, M > 128 with few tiles
+    (257, 3000, 1024, 256, (64, 64)),    # 64x64 over the whole K
+    (600, 1000, 2048, 64, (64, 64)),
+    (700, 4100, 1024, 256, (128, 128)),  # tiled
+    (1000, 3000, 576, 64, (128, 128)),
     (4000, 4000, 768, 256, (256, 256)),  # 256-row tiles
     (3583, 3585, 512, 256, (256, 256)),
     (2000, 4000, 1024, 256, (256, 128)),
-    (3841, 4100, 704, 64, (256, 128)),
+    (2000, 4000, 704, 64, (256, 128)),
 ]
 
 

@@ -245,11 +245,11 @@ def test_few_tiles_all_ones_bitwise():
 
 
 # Large M and N take the 256-row-tile class (kernel ids 4, 5: 256 columns;
-# 9, 10: 128 columns), the width chosen by tile count. Ragged edges at both
+# 9, 10: 128 columns), the width chosen by the launch estimate. Ragged edges at both
 # granularities (M and N one short of, or just past, a tile or scale block),
 # and K % 128 == 64 at g = 64 (a half step).
-BIG = [(3583, 3585, 512, 128, 256), (4096, 3328, 1024, 128, 256), (4000, 4000, 256, 128, 256),
-       (2000, 4000, 1024, 128, 128), (3600, 4000, 320, 64, 256), (3841, 4100, 704, 64, 128),
+BIG = [(3583, 3585, 512, 128, 256), (4096, 3328, 1024, 128, 256), (4000, 4000, 256, 128, 128),
+       (2000, 4000, 1024, 128, 128), (3600, 4000, 320, 64, 256), (2049, 4100, 704, 64, 256),
        (2000, 4000, 1088, 64, 128)]
 
 
@@ -341,7 +341,7 @@ def test_default_calls_two_streams_concurrently():
     import fp8_block_scaled_scales_amd as dg
     from tests._gpu import device_inputs
 
-    shapes = [(64, 4096, 2048, 128), (4096, 4096, 512, 128), (1008, 1000, 512, 64)]
+    shapes = [(64, 4096, 2048, 128), (4096, 4096, 512, 128), (1008, 3008, 2048, 64)]
     assert [dg.dg_query_tile(*s)["bm"] for s in shapes] == [32, 256, 128]
     ops, ts = [], []
     for i, (M, N, K, g) in enumerate(shapes):

@@ -29,13 +29,16 @@ SHAPES = [
     (64, 4096, 1536, 256, (32, 32)),
     (64, 520, 2048, 128, (32, 32)),      # streaming, few tiles
     (100, 520, 1088, 64, (32, 32)),
-    (1000, 3000, 512, 128, (128, 128)),  # tiled
+    (250, 1000, 2048, 128, (32, 32)),    # streaming, M > 128 with few tiles
+    (300, 1031, 1024, 64, (64, 64)),     # 64x64 over the whole K
+    (257, 3000, 1024, 128, (64, 64)),
+    (777, 3333, 2048, 128, (128, 128)),  # tiled
     (1000, 3000, 576, 64, (128, 128)),
     (4000, 4000, 768, 128, (256, 256)),  # 256-row tiles
     (4000, 4000, 704, 64, (256, 256)),
     (3583, 3585, 512, 256, (256, 256)),
     (2000, 4000, 1024, 128, (256, 128)),
-    (3841, 4100, 704, 64, (256, 128)),
+    (2000, 4000, 704, 64, (256, 128)),
 ]
 
 
