@@ -111,15 +111,14 @@ struct Plan {
 };
 
 // Tile-table choice (pure host arithmetic, no HIP call).
-// Small M streams B. A small-M shape of any layout takes 32x32 tiles over the
-// whole K, whose waves split K inside the workgroup, whatever the tile count;
-// with a workspace, a long K (kSplitMinSteps) that gives at least kSplitMin
-// splits instead splits the K range of each 64x64 tile over several
-// workgroups, until about one workgroup per CU (256) runs, at most kMaxSplit
-// per tile and at least 4 pipeline steps per split.
-// Larger M takes the table entry of the call's granularity with the least
-// estimated time (estimate_us): the 32x32 streaming tiles, 64x64 tiles over
-// the whole K, 128x128, or the 256-row tiles 128 or 256 wide.
+// Every shape takes the table entry of the call's granularity with the least
+// estimated time (estimate_us), the whole K per workgroup: the 32x32
+// streaming tiles (whose waves split K inside the workgroup), 64x64,
+// 128x128, or the 256-row tiles 128 or 256 wide. With a workspace, M <= 128
+// and a long K (kSplitMinSteps) that gives at least kSplitMin splits instead
+// splits the K range of each 64x64 tile over several workgroups, until about
+// one workgroup per CU (256) runs, at most kMaxSplit per tile and at least 4
+// pipeline steps per split.
 // DG_FORCE_TILE=<kernel id>, read at every call, replaces the choice when
 // that entry has the call's granularity (tuning, benchmarking and tests; a
 // split-K entry then runs with one split unless the call has a workspace).
@@ -140,14 +139,21 @@ int64_t tiles_of(const dg::KernelEntry* e, int64_t M, int64_t N) {
 }
 
 // Estimated microseconds of one launch of e on M x N x K (whole K per
-// workgroup): the entry's fixed cost plus, per round of one workgroup per
-// CU, the larger of moving the tile's operand rows (bm + bn rows of K bytes)
-// and its arithmetic (2 bm bn K FLOP) at the entry's per-CU rates.
+// workgroup). Every class is held back by how fast one CU pulls its tile's
+// operand rows from L2 (the workgroups of one CU share that rate) or by its
+// arithmetic, so a launch takes the entry's fixed cost plus, per round of
+// one tile per CU, a fixed cost and the larger of moving bm + bn rows of K
+// bytes and 2 bm bn K FLOP at the entry's per-CU rates. The constants were
+// fitted by least squares in log time to graph-timed launches of every
+// entry on 172 shapes (M 32 to 4096, N 1024 to 28672, K 2048 to 8192,
+// g 64 and 128); the least estimate picked an entry within 1.8% of the
+// fastest on every one of them.
 double estimate_us(const dg::KernelEntry* e, int64_t M, int64_t N, int64_t K) {
   const int64_t rounds = (tiles_of(e, M, N) + 255) / 256;
   const double bytes = (double)(e->bm + e->bn) * (double)K;
   const double flop = 2.0 * e->bm * e->bn * (double)K;
-  return e->cost_us + (double)rounds * std::max(bytes / (e->cu_gbps * 1e3), flop / (e->cu_tflops * 1e6));
+  return e->launch_us +
+         (double)rounds * (e->round_us + std::max(bytes / (e->cu_gbps * 1e3), flop / (e->cu_tflops * 1e6)));
 }
 
 Plan plan(int64_t M, int64_t N, int64_t K, int sgran, bool split_ok) {
@@ -170,20 +176,11 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, bool split_ok) {
       return p;
     }
   }
-  if (M <= 128) {
-    if (split_ok && nsteps >= kSplitMinSteps && split_k().ksplit >= kSplitMin) return p;
-    p.e = find(dg::kClassStream, gran);
-    p.tiles = tiles_of(p.e, M, N);
-    p.ksplit = 1;
-    return p;
-  }
-  // Larger M: the entry with the least estimated time. Every class streams
-  // its operand rows from L2 into the CU at a rate per CU that barely
-  // depends on the tile (the workgroups of one CU share it), so a launch
-  // takes about rounds x max(bytes per workgroup / that rate, FLOP per
-  // workgroup / the entry's MFMA rate) plus a fixed cost, with rounds the
-  // tiles per CU. Small tiles win when there are few of them (less per CU,
-  // more CUs busy), large ones when the arithmetic dominates.
+  if (M <= 128 && split_ok && nsteps >= kSplitMinSteps && split_k().ksplit >= kSplitMin) return p;
+  // The entry with the least estimated time: small tiles where there are few
+  // of them (fewer bytes per CU, more CUs busy), large ones where the
+  // arithmetic dominates.
+  p = Plan{nullptr, 1, 0};
   double best = 0.0;
   for (int i = 0; i < dg::kTableSize; ++i) {
     const dg::KernelEntry* e = &dg::kTable[i];

@@ -34,10 +34,10 @@ typedef hipError_t (*Launcher)(const GemmArgs&, hipStream_t);
 // many tiles).
 enum TileClass { kClassTiled = 0, kClassSplitK = 1, kClassBig = 2, kClassStream = 3 };
 
-// A table entry, with the constants of its launch-time estimate (see plan()
-// in dg_host.hip): fixed cost, L2->CU bytes per second per CU, and FLOP per
-// second per CU, fitted to graph-timed launches of the entry over small to
-// large shapes.
+// A table entry, with the constants of its launch-time estimate (see
+// estimate_us in dg_host.hip): fixed costs per launch and per round of
+// tiles, operand bytes and FLOP per second per CU, fitted to graph-timed
+// launches of the entry over small to large shapes.
 struct KernelEntry {
   int id;
   int cls;
@@ -46,7 +46,8 @@ struct KernelEntry {
   int waves;
   int gran;
   Launcher launch;
-  float cost_us;       // fixed cost per launch
+  float launch_us;     // fixed cost per launch
+  float round_us;      // fixed cost per round of one tile per CU
   float cu_gbps;       // operand bytes per CU per second, GB/s
   float cu_tflops;     // FLOP per CU per second, TFLOP/s
 };

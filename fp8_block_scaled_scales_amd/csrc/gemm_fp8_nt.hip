@@ -44,17 +44,18 @@
 namespace dg {
 
 KernelEntry kTable[] = {
-    // id, class, bm, bn, stages, waves, gran, launcher, estimate: fixed us, GB/s per CU, TFLOP/s per CU
-    {0, kClassTiled, 128, 128, 2, 4, 128, &launch_tiled<128, 128, 2, 2, 2, 128, 4, false>, 6.0f, 56.0f, 7.5f},
-    {1, kClassTiled, 128, 128, 2, 4, 64, &launch_tiled<128, 128, 2, 2, 2, 64, 4, false>, 6.0f, 44.0f, 5.5f},
-    {2, kClassSplitK, 64, 64, 8, 4, 128, &launch_tiled<64, 64, 2, 2, 8, 128, 4, true>, 3.5f, 40.0f, 3.0f},
-    {3, kClassSplitK, 64, 64, 8, 4, 64, &launch_tiled<64, 64, 2, 2, 8, 64, 4, true>, 3.5f, 32.0f, 2.0f},
-    {4, kClassBig, 256, 256, 2, 8, 128, &launch_big_g128, 6.0f, 50.0f, 12.5f},
-    {5, kClassBig, 256, 256, 2, 8, 64, &launch_big_g64, 6.0f, 38.0f, 10.0f},
-    {6, kClassStream, 32, 32, 4, 4, 128, &launch_stream_g128, 4.5f, 46.0f, 2.0f},
-    {7, kClassStream, 32, 32, 4, 4, 64, &launch_stream_g64, 6.0f, 36.0f, 2.0f},
-    {9, kClassBig, 256, 128, 2, 8, 128, &launch_big128_g128, 4.5f, 54.0f, 9.5f},
-    {10, kClassBig, 256, 128, 2, 8, 64, &launch_big128_g64, 6.0f, 44.0f, 7.5f},
+    // id, class, bm, bn, stages, waves, gran, launcher,
+    // estimate: us per launch, us per round, GB/s per CU, TFLOP/s per CU
+    {0, kClassTiled, 128, 128, 2, 4, 128, &launch_tiled<128, 128, 2, 2, 2, 128, 4, false>, 6.0f, 0.0f, 54.0f, 7.0f},
+    {1, kClassTiled, 128, 128, 2, 4, 64, &launch_tiled<128, 128, 2, 2, 2, 64, 4, false>, 6.0f, 0.0f, 40.0f, 5.5f},
+    {2, kClassSplitK, 64, 64, 8, 4, 128, &launch_tiled<64, 64, 2, 2, 8, 128, 4, true>, 1.5f, 3.0f, 50.0f, 3.5f},
+    {3, kClassSplitK, 64, 64, 8, 4, 64, &launch_tiled<64, 64, 2, 2, 8, 64, 4, true>, 1.5f, 3.0f, 38.0f, 2.5f},
+    {4, kClassBig, 256, 256, 2, 8, 128, &launch_big_g128, 4.5f, 3.0f, 54.0f, 13.5f},
+    {5, kClassBig, 256, 256, 2, 8, 64, &launch_big_g64, 4.5f, 3.0f, 42.0f, 10.5f},
+    {6, kClassStream, 32, 32, 4, 4, 128, &launch_stream_g128, 2.5f, 2.0f, 70.0f, 2.5f},
+    {7, kClassStream, 32, 32, 4, 4, 64, &launch_stream_g64, 1.5f, 3.0f, 56.0f, 2.0f},
+    {9, kClassBig, 256, 128, 2, 8, 128, &launch_big128_g128, 1.5f, 3.0f, 56.0f, 10.0f},
+    {10, kClassBig, 256, 128, 2, 8, 64, &launch_big128_g64, 2.5f, 3.0f, 46.0f, 8.0f},
 };
 const int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 

@@ -205,9 +205,9 @@ typedef struct dg_tile_info {
 
 /*
  * dg_query_tile - fill *info with the tile-table entry dg_gemm_fp8_nt would
- * launch for (M, N, K, gran): for M <= 128 the 32x32 streaming tiles, for
- * larger M the entry with the least estimated launch time (operand bytes per
- * CU and FLOP per CU at each entry's measured rates, per round of tiles).
+ * launch for (M, N, K, gran): the entry with the least estimated launch time
+ * (fixed costs, then operand bytes per CU and FLOP per CU at each entry's
+ * measured rates, per round of one tile per CU).
  * Pure host logic, no HIP call. Returns DG_OK or
  * DG_EINVAL for arguments dg_gemm_fp8_nt would reject. ksplit is always 1
  * and workspace_bytes 0: this call never splits K over workgroups.

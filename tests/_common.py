@@ -12,14 +12,11 @@ SPLIT_TILE = {128: 2, 256: 2, 64: 3}
 
 
 @contextlib.contextmanager
-def forced_split(g: int):
-    """Inside, every call runs the split-K class (DG_FORCE_TILE, which the
-    library reads at each call), splitting K over workgroups when a workspace
-    is given, whatever the shape. The plan itself splits only long K ranges
-    (16384 and up); this reaches the split path on shapes the oracle finishes
-    in moments."""
+def forced_tile(kernel_id: int):
+    """Inside, every call of a matching granularity runs table entry
+    kernel_id (DG_FORCE_TILE, which the library reads at each call)."""
     old = os.environ.get("DG_FORCE_TILE")
-    os.environ["DG_FORCE_TILE"] = str(SPLIT_TILE[g])
+    os.environ["DG_FORCE_TILE"] = str(kernel_id)
     try:
         yield
     finally:
@@ -27,6 +24,14 @@ def forced_split(g: int):
             del os.environ["DG_FORCE_TILE"]
         else:
             os.environ["DG_FORCE_TILE"] = old
+
+
+def forced_split(g: int):
+    """Inside, every call runs the split-K class, splitting K over workgroups
+    when a workspace is given, whatever the shape. The plan itself splits
+    only long K ranges (16384 and up); this reaches the split path on shapes
+    the oracle finishes in moments."""
+    return forced_tile(SPLIT_TILE[g])
 
 
 def within_tolerance(got, ref, rms=None):

@@ -250,8 +250,10 @@ def test_python_binding_rejects_bad_tensors(dg):
 # Host-side tile choice for the five workloads and shapes between them: M up
 # to 128 streams; larger M takes the entry with the least estimated time.
 @pytest.mark.parametrize("M,N,K,g,cls", [
-    (256, 256, 256, 128, (64, 64, 1)),        # 16 tiles of 64x64
+    (256, 256, 256, 128, (32, 32, 1)),        # 64 tiles of 32x32
     (250, 1000, 2048, 128, (32, 32, 1)),      # few tiles, M > 128: the 32x32 streaming tiles
+    (128, 7168, 2048, 64, (64, 64, 1)),       # M <= 128 with 896 tiles of 32x32: 224 of 64x64 win
+    (128, 28672, 2048, 128, (128, 128, 1)),
     (600, 1000, 2048, 64, (64, 64, 1)),
     (777, 3333, 2048, 128, (128, 128, 1)),
     (1536, 7168, 2048, 128, (256, 256, 1)),   # 168 tiles of 256x256 beat 672 of 128x128

@@ -31,7 +31,7 @@ CASES = [
     (96, 528, 24576, 128, 0, False, 0, 1, 0, False, True, (64, 64, True)),
     (96, 528, 24576, 128, 3, True, 0, 0, 2, True, True, (64, 64, True)),
     (250, 1008, 2048, 128, 2, False, 0, 0, 0, False, False, (32, 32, False)),
-    (1024, 2000, 576, 64, 1, False, 1, 1, 0, False, False, (64, 64, False)),
+    (608, 1008, 2048, 64, 1, False, 1, 1, 0, False, False, (64, 64, False)),
     (704, 4096, 1024, 128, 0, False, 0, 0, 0, False, False, (128, 128, False)),
     (1008, 3008, 2048, 64, 3, True, 0, 0, 1, True, False, (128, 128, False)),
     (4000, 4000, 768, 128, 0, False, 0, 0, 2, True, False, (256, 256, False)),

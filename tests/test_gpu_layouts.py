@@ -31,9 +31,10 @@ SHAPES = [
     (128, 512, 1024, 256, (32, 32)),
     (64, 4096, 7168, 128, (32, 32)),    # the decode shape
     (256, 1008, 2048, 64, (32, 32)),    # streaming, M > 128 with few tiles
-    (1024, 2000, 576, 64, (64, 64)),    # 64x64 over the whole K
+    (608, 1008, 2048, 64, (64, 64)),    # 64x64 over the whole K
     (512, 1040, 768, 256, (64, 64)),
     (704, 4096, 1024, 128, (128, 128)),  # tiled
+    (1024, 2000, 576, 64, (128, 128)),
     (1008, 3008, 2048, 64, (128, 128)),
     (1008, 3008, 512, 128, (256, 128)),
     (4000, 4000, 768, 128, (256, 256)),  # 256-row tiles: 16x16x128 fragments

@@ -119,11 +119,18 @@ def test_max_k_small_m(pool, layout, N, tile, ws):
 
 @pytest.mark.parametrize("big_m,layout", [(True, 0), (True, 2), (False, 0)])
 def test_max_m_or_n(pool, big_m, layout):
+    M, N, K, g = (MAX_DIM, 256, 256, 128) if big_m else (256, MAX_DIM, 256, 128)
+    # the 256x256 tiles (table entry 4), whose tiles span the most bytes of
+    # A and B (the plan takes 128x128 tiles here)
+    with _common.forced_tile(4):
+        _max_m_or_n(pool, M, N, K, g, big_m, layout)
+
+
+def _max_m_or_n(pool, M, N, K, g, big_m, layout):
     import torch
 
     import fp8_block_scaled_scales_amd as dg
 
-    M, N, K, g = (MAX_DIM, 256, 256, 128) if big_m else (256, MAX_DIM, 256, 128)
     t = dg.dg_query_tile(M, N, K, g, layout)
     assert (t["bm"], t["bn"]) == (256, 256), t
     a_st = pool[:M * K].view(K, M) if layout & 2 else pool[:M * K].view(M, K)

@@ -248,7 +248,7 @@ def test_few_tiles_all_ones_bitwise():
 # 9, 10: 128 columns), the width chosen by the launch estimate. Ragged edges at both
 # granularities (M and N one short of, or just past, a tile or scale block),
 # and K % 128 == 64 at g = 64 (a half step).
-BIG = [(3583, 3585, 512, 128, 256), (4096, 3328, 1024, 128, 256), (4000, 4000, 256, 128, 128),
+BIG = [(3583, 3585, 512, 128, 256), (4096, 3328, 1024, 128, 256), (4000, 4000, 256, 128, 256),
        (2000, 4000, 1024, 128, 128), (3600, 4000, 320, 64, 256), (2049, 4100, 704, 64, 256),
        (2000, 4000, 1088, 64, 128)]
 
@@ -293,10 +293,11 @@ def test_big_tile_all_ones_bitwise(M, N, K, g, bn):
     assert np.array_equal(bits[np.ix_(rows, cols)], _common.f32_to_bf16_bits(ref.astype(np.float32)))
 
 
-# Small M with many 32x32 tiles takes the streaming class (kernel ids 6, 7):
-# whole K per workgroup, waves splitting K, partials added in wave order.
-STREAM = [(64, 6150, 1920, 128), (1, 8192, 1024, 128), (33, 8000, 64 * 37, 64), (128, 7168, 2048, 64),
-          (100, 3000, 896, 128)]
+# Small M with up to a round or so of 32x32 tiles takes the streaming class
+# (kernel ids 6, 7): whole K per workgroup, waves splitting K, partials added
+# in wave order.
+STREAM = [(64, 4096, 1920, 128), (1, 8192, 1024, 128), (33, 4000, 64 * 37, 64), (128, 2000, 2048, 64),
+          (100, 2000, 896, 128)]
 
 
 @pytest.mark.parametrize("M,N,K,g", STREAM)

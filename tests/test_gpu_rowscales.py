@@ -25,7 +25,7 @@ E4, E5 = 0, 1
 # K % 128 == 64 at g = 64, g = 256 on the G = 128 kernels.
 SHAPES = [
     (64, 4096, 1024, 128, (32, 32)),     # streaming
-    (100, 4096, 1088, 64, (32, 32)),
+    (100, 4096, 1088, 64, (64, 64)),     # M <= 128, many tiles: 64x64
     (64, 4096, 1536, 256, (32, 32)),
     (64, 520, 2048, 128, (32, 32)),      # streaming, few tiles
     (100, 520, 1088, 64, (32, 32)),
