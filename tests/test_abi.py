@@ -394,3 +394,31 @@ def test_noalloc_scratch_limit(dg):
     assert dg.lib.dg_gemm_fp8_noalloc(WA, WB, WSA, WSB, WOUT, M, N, K, g, 0, g, 0, 0, None, 0, None) == dg.DG_ESCRATCH
     # argument errors still come first
     assert dg.lib.dg_gemm_fp8_noalloc(0, WB, WSA, WSB, WOUT, M, N, K, g, 0, g, 0, 0, None, 0, None) == dg.DG_EINVAL
+
+
+def test_tile_choice_is_the_same_for_every_layout(dg):
+    """Every layout runs NT's plan (so every layout returns NT's bits), with
+    and without a workspace, over a grid of shapes across all classes."""
+    import itertools
+
+    for M, N, K, g in itertools.product((1, 33, 128, 250, 777, 2000, 4096), (17, 1000, 4096, 28672),
+                                        (256, 2048, 16384), (64, 128, 256)):
+        if K % g:
+            continue
+        for ws in (False, True):
+            nt = dg.dg_query_tile(M, N, K, g, 0, workspace=ws)
+            for layout in (1, 2, 3):
+                assert dg.dg_query_tile(M, N, K, g, layout, workspace=ws) == nt, (M, N, K, g, layout, ws)
+
+
+def test_workspace_plans_stay_within_their_cap(dg):
+    # a split plan's partials never exceed 16 MB, its splits 16, and every
+    # split keeps at least 4 of the 128-byte K steps
+    import itertools
+
+    for M, N, K in itertools.product((1, 64, 128), (64, 1000, 4096, 8192), (16384, 65536, 1 << 20)):
+        t = dg.dg_query_tile(M, N, K, 128, workspace=True)
+        if t["ksplit"] > 1:
+            assert t["workspace_bytes"] <= 16 << 20 and 8 <= t["ksplit"] <= 16
+            assert K // 128 // t["ksplit"] >= 4
+
