@@ -332,8 +332,8 @@ def dg_gemm_fp8_ws(a, b, sa, sb, out=None, gran: int = 128, layout: int = DG_LAY
 
     With a workspace (a contiguous uint8 GPU tensor of at least
     dg_query_tile(..., workspace=True)["workspace_bytes"] bytes, 256-byte
-    aligned; see ``dg_workspace``) small-M shapes with few output tiles and a
-    long K (16384 and up, cut at least 8 ways) split K over several
+    aligned; see ``dg_workspace``) shapes with few output tiles and a long K
+    (16384 and up, cut at least 8 ways) split K over several
     workgroups; every other shape runs what the call without a workspace
     runs. Concurrent calls need distinct workspaces.
     """

@@ -33,9 +33,11 @@ constexpr int64_t kWsFloats = 4ll << 20;  // 16 MB of partial tiles
 // through memory and the second kernel), and its 64x64 tiles move fewer
 // bytes per CU only when there are few of them, so it pays where it cuts a
 // long K range several times: at least kSplitMinSteps 128-byte K steps and
-// at least kSplitMin splits. Graph-timed on small M (8, 64, 128 rows, N 256
-// to 4096, g = 128, K 1024 to 32768): K >= 16384 with 8 to 16 splits took
-// 0.46 to 0.81 of the streaming time; K = 7168 with 8 to 14 splits 0.91 to
+// at least kSplitMin splits (at most 32 tiles of 64x64, whatever M). Graph-timed
+// on small M (8, 64, 128 rows, N 256 to 4096, g = 128, K 1024 to 32768):
+// K >= 16384 with 8 to 16 splits took 0.46 to 0.81 of the streaming time,
+// and with M 192 to 2048 (N 64 to 640, K 16384 to 65536, g 64 and 128) 0.46
+// to 0.90 of the planned entry's; K = 7168 with 8 to 14 splits 0.91 to
 // 1.15; K <= 4096 1.05 to 1.6; 4 splits 0.95 to 1.57 at any K; 2 splits
 // (M = 128, N = 4096, whose streaming tiles take two rounds) 0.87 to 1.10.
 // kMaxSplit bounds the second kernel's sum per output.
@@ -114,9 +116,9 @@ struct Plan {
 // Every shape takes the table entry of the call's granularity with the least
 // estimated time (estimate_us), the whole K per workgroup: the 32x32
 // streaming tiles (whose waves split K inside the workgroup), 64x64,
-// 128x128, or the 256-row tiles 128 or 256 wide. With a workspace, M <= 128
-// and a long K (kSplitMinSteps) that gives at least kSplitMin splits instead
-// splits the K range of each 64x64 tile over several workgroups, until about
+// 128x128, or the 256-row tiles 128 or 256 wide. With a workspace, a long K
+// (kSplitMinSteps) that gives at least kSplitMin splits instead splits the
+// K range of each 64x64 tile over several workgroups, until about
 // one workgroup per CU (256) runs, at most kMaxSplit per tile and at least 4
 // pipeline steps per split.
 // DG_FORCE_TILE=<kernel id>, read at every call, replaces the choice when
@@ -176,7 +178,7 @@ Plan plan(int64_t M, int64_t N, int64_t K, int sgran, bool split_ok) {
       return p;
     }
   }
-  if (M <= 128 && split_ok && nsteps >= kSplitMinSteps && split_k().ksplit >= kSplitMin) return p;
+  if (split_ok && nsteps >= kSplitMinSteps && split_k().ksplit >= kSplitMin) return p;
   // The entry with the least estimated time: small tiles where there are few
   // of them (fewer bytes per CU, more CUs busy), large ones where the
   // arithmetic dominates.
@@ -235,7 +237,7 @@ bool overlaps(const void* p, uint64_t n, const void* q, uint64_t m) {
   return n && m && x < y + m && y < x + n;
 }
 
-// split_ok: small-M shapes may split K over workgroups, through ws (the
+// split_ok: few-tile long-K shapes may split K over workgroups, through ws (the
 // caller's, ws_bytes long; none when ws_bytes is 0) or, with use_scratch,
 // through the library's static scratch array.
 int gemm(const void* a, const void* b, const float* sa, const float* sb, void* out, int64_t M, int64_t N, int64_t K,
@@ -255,7 +257,7 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)sa & 3) || ((uintptr_t)sb & 3) ||
       ((uintptr_t)out & 1))
     return DG_EALIGN;
-  // A workspace lets small-M shapes split K; without one nothing does.
+  // A workspace lets few-tile long-K shapes split K; without one nothing does.
   Plan pl = plan(M, N, K, gran, split_ok && (ws_bytes > 0 || use_scratch));
   if (!pl.e || pl.tiles * pl.ksplit > 0x7fffffff) return DG_EINVAL;
   const int64_t need = workspace_bytes(pl);

@@ -220,13 +220,13 @@ int dg_query_tile(int64_t M, int64_t N, int64_t K, int gran, dg_tile_info* info)
 int dg_query_tile_layout(int64_t M, int64_t N, int64_t K, int gran, int layout, dg_tile_info* info);
 
 /*
- * dg_gemm_fp8_ws - the GEMM with a caller-owned workspace that lets small-M
+ * dg_gemm_fp8_ws - the GEMM with a caller-owned workspace that lets
  * shapes with few output tiles and a long K split K over several workgroups.
  *
  * DeepGEMM实战 §3.2 accumulates K in segments that are summed separately and
  * then added; §5.3 names too little parallelism as what holds back small
- * shapes. With M <= 128, K >= 16384 (128 steps of 128) and few enough output
- * tiles that each 64x64 tile gets at least 8 workgroups (at most 16, about
+ * shapes. With K >= 16384 (128 steps of 128) and few enough output tiles
+ * (M x N up to 32 tiles of 64x64) that each gets at least 8 workgroups (at most 16, about
  * 256 in all), this call gives each tile ksplit workgroups, each over a
  * contiguous range of K segments, which write their FP32 partial tiles to the
  * workspace; a second kernel on the same stream adds each tile's partials in

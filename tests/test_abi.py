@@ -272,8 +272,8 @@ def test_query_tile_choice(dg, M, N, K, g, cls):
     assert t["workspace_bytes"] == 0
 
 
-# dg_gemm_fp8_ws's plan: small M (any layout) with K of at least 16384 (128
-# steps) that the 64x64 tiles split at least 8 ways (round(256 / tiles), at
+# dg_gemm_fp8_ws's plan: K of at least 16384 (128 steps) that the 64x64
+# tiles split at least 8 ways (any layout, any M) (round(256 / tiles), at
 # most 16, at least 4 steps each) splits K over workgroups; everything else is
 # the plan without a workspace, which needs no workspace.
 @pytest.mark.parametrize("M,N,K,g,layout,cls", [
@@ -288,6 +288,9 @@ def test_query_tile_choice(dg, M, N, K, g, cls):
     (96, 528, 24576, 256, 2, (64, 64, 14)),    # 18 tiles x 14 (g = 256 runs 128-segment steps)
     (128, 1024, 65536, 64, 0, (64, 64, 8)),    # g = 64: 32 tiles x 8
     (8, 4096, 32768, 128, 0, (32, 32, 1)),     # 64 tiles would give 4 splits: streams
+    (256, 512, 32768, 128, 2, (64, 64, 8)),    # larger M, 32 tiles: 8 splits
+    (2048, 64, 65536, 64, 0, (64, 64, 8)),
+    (256, 1024, 32768, 128, 0, (32, 32, 1)),   # 64 tiles: 4 splits, the plan without a workspace
     (64, 4096, 32768, 128, 2, (32, 32, 1)),    # the same, A stored [K,M]
     (64, 4096, 7168, 128, 0, (32, 32, 1)),
     (8192, 8192, 8192, 128, 0, (256, 256, 1)),

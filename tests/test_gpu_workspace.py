@@ -28,10 +28,11 @@ from tests._gpu import device_inputs, say
 
 pytestmark = pytest.mark.gpu
 
-# Small M, few tiles, long K: the workspace plan splits K over 64x64 tiles.
+# Few tiles, long K: the workspace plan splits K over 64x64 tiles.
 SPLITK = [
     (1, 2048, 32768, 128), (64, 1000, 24576, 64), (100, 520, 24576, 128), (33, 700, 64 * 400, 64),
     (128, 512, 32768, 128), (7, 64, 65536, 64), (96, 1000, 24576, 128), (64, 512, 24576, 128), (8, 300, 24576, 256),
+    (256, 500, 16384, 128), (1000, 100, 16384, 64),  # larger M, few tiles
 ]
 # Short K ranges the plan streams, split through the tile override.
 SPLITK_FORCED = [(64, 512, 7168, 128), (8, 300, 2048, 256), (100, 520, 2048, 128), (33, 700, 64 * 37, 64),
