@@ -147,8 +147,8 @@ int64_t tiles_of(const dg::KernelEntry* e, int64_t M, int64_t N) {
 // one tile per CU, a fixed cost and the larger of moving bm + bn rows of K
 // bytes and 2 bm bn K FLOP at the entry's per-CU rates. The constants were
 // fitted by least squares in log time to graph-timed launches of every
-// entry on 172 shapes (M 32 to 4096, N 1024 to 28672, K 2048 to 8192,
-// g 64 and 128); the least estimate picked an entry within 1.8% of the
+// entry on 166 shapes (M 32 to 4096, N 1024 to 28672, K 2048 to 8192,
+// g 64 and 128); the least estimate picked an entry within 3% of the
 // fastest on every one of them.
 double estimate_us(const dg::KernelEntry* e, int64_t M, int64_t N, int64_t K) {
   const int64_t rounds = (tiles_of(e, M, N) + 255) / 256;

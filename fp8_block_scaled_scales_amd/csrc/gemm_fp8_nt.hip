@@ -53,9 +53,9 @@ KernelEntry kTable[] = {
     {4, kClassBig, 256, 256, 2, 8, 128, &launch_big_g128, 4.5f, 3.0f, 54.0f, 13.5f},
     {5, kClassBig, 256, 256, 2, 8, 64, &launch_big_g64, 4.5f, 3.0f, 42.0f, 10.5f},
     {6, kClassStream, 32, 32, 4, 4, 128, &launch_stream_g128, 2.5f, 2.0f, 70.0f, 2.5f},
-    {7, kClassStream, 32, 32, 4, 4, 64, &launch_stream_g64, 1.5f, 3.0f, 56.0f, 2.0f},
+    {7, kClassStream, 32, 32, 4, 4, 64, &launch_stream_g64, 1.5f, 3.0f, 64.0f, 2.5f},
     {9, kClassBig, 256, 128, 2, 8, 128, &launch_big128_g128, 1.5f, 3.0f, 56.0f, 10.0f},
-    {10, kClassBig, 256, 128, 2, 8, 64, &launch_big128_g64, 2.5f, 3.0f, 46.0f, 8.0f},
+    {10, kClassBig, 256, 128, 2, 8, 64, &launch_big128_g64, 2.5f, 3.0f, 48.0f, 8.0f},
 };
 const int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
