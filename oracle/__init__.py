@@ -28,6 +28,12 @@ computes and which passage of the pages it follows:
   template article §3.4: per-tensor or per-channel factors, per channel the
   usual choice).
 
+* ``bf16_decode``, ``f16_decode``, ``quantize_blocks_16``, ``quantize_rows_16``:
+  the quantisers on BF16 or FP16 input (DeepGEMM实战 §4.4: the weights and
+  activations to quantise come in FP16 or BF16): each input is decoded from
+  its bit fields to its exact value (FP32 holds every finite one exactly) and
+  the block rule above then applies unchanged.
+
 Parity status: every function above is pinned by the CPU tests
 (``tests/test_oracle_*.py``) against torch's float8 cast, brute force, exact
 rational arithmetic, numpy's float64 matmul, closed forms and invariants.
@@ -109,6 +115,13 @@ def _load():
                                         ctypes.c_int, ctypes.c_int, i64p, i64, i64p, i64, f64p, ctypes.c_int]
     lib.dgo_epilogue.restype = ctypes.c_int
     lib.dgo_epilogue.argtypes = [f64p, i64, i64, i64p, f32p, ctypes.c_int]
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    lib.dgo_bf16_decode.restype = ctypes.c_double
+    lib.dgo_bf16_decode.argtypes = [ctypes.c_uint16]
+    lib.dgo_f16_decode.restype = ctypes.c_double
+    lib.dgo_f16_decode.argtypes = [ctypes.c_uint16]
+    lib.dgo_decode16_n.restype = ctypes.c_int
+    lib.dgo_decode16_n.argtypes = [u16p, i64, ctypes.c_int, f32p]
     lib.dgo_hardware_threads.restype = ctypes.c_int
     lib.dgo_hardware_threads.argtypes = []
     _lib = lib
@@ -382,3 +395,37 @@ def epilogue(ref, bias=None, act: int = ACT_NONE, cols=None) -> np.ndarray:
     if rc != 0:
         raise ValueError("dgo_epilogue rejected its arguments")
     return out
+
+
+# 16-bit input kinds: 1 = BF16, 2 = FP16 (IEEE binary16).
+IN_BF16 = 1
+IN_F16 = 2
+
+
+def decode16(bits, kind: int) -> np.ndarray:
+    """16-bit patterns (uint16, any shape) of kind IN_BF16 or IN_F16 -> float32 values (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    if _load().dgo_decode16_n(_ptr(b, ctypes.c_uint16), b.size, kind, _ptr(out, ctypes.c_float)) != 0:
+        raise ValueError("kind must be IN_BF16 or IN_F16")
+    return out
+
+
+def bf16_decode(bits) -> np.ndarray:
+    """BF16 bit patterns -> float32 values."""
+    return decode16(bits, IN_BF16)
+
+
+def f16_decode(bits) -> np.ndarray:
+    """FP16 bit patterns -> float32 values."""
+    return decode16(bits, IN_F16)
+
+
+def quantize_blocks_16(bits, kind: int, g: int, fmt: int = 0, nthreads: int | None = None):
+    """g x g quantisation of a BF16 or FP16 matrix given as its bit patterns [rows, cols] (uint16)."""
+    return quantize_blocks_fmt(decode16(bits, kind), g, fmt, nthreads)
+
+
+def quantize_rows_16(bits, kind: int, g: int, fmt: int = 0, nthreads: int | None = None):
+    """1 x g quantisation of a BF16 or FP16 matrix given as its bit patterns [rows, cols] (uint16)."""
+    return quantize_rows_fmt(decode16(bits, kind), g, fmt, nthreads)

@@ -68,6 +68,14 @@
 //    with op(B) = B^T for B stored [N][K]). The scales keep their logical
 //    shapes: sa [ceil(M/g)][K/g], sb [ceil(N/g)][K/g].
 //
+//  * 16-bit inputs to the quantiser (DeepGEMM实战 §4.4: the weights and
+//    activations that are quantised to FP8 arrive in FP16 or BF16). Such an
+//    input is first decoded to its exact value, which FP32 holds exactly,
+//    and the block rule above then applies unchanged. BF16 is read as the
+//    format that keeps FP32's sign and 8-bit exponent (bias 127) and 7
+//    fraction bits, FP16 as IEEE binary16 (5-bit exponent, bias 15, 10
+//    fraction bits); both have subnormals at exponent field 0.
+//
 // Scale tensors are row-major FP32: sa is [ceil(M/g)][K/g] ([M][K/g] with
 // per-row A scales), sb is [ceil(N/g)][K/g]. K must be a multiple of g.
 //
@@ -495,6 +503,49 @@ int dgo_epilogue(double* ref, int64_t nrows, int64_t ncols, const int64_t* cols,
       if (act == 2) y = 0.5 * y * (1.0 + std::erf(y / std::sqrt(2.0)));
       ref[r * ncols + c] = y;
     }
+  return 0;
+}
+
+// BF16 decode of one bit pattern from its fields: sign, 8-bit exponent
+// (bias 127), 7-bit fraction; exponent 0 holds subnormals f/128 * 2^-126,
+// exponent 255 infinity (f = 0) or NaN.
+double dgo_bf16_decode(uint16_t bits) {
+  const int s = bits >> 15;
+  const int e = (bits >> 7) & 0xFF;
+  const int f = bits & 0x7F;
+  double mag;
+  if (e == 0xFF)
+    mag = f ? std::nan("") : HUGE_VAL;
+  else if (e == 0)
+    mag = std::ldexp((double)f / 128.0, -126);
+  else
+    mag = std::ldexp(1.0 + (double)f / 128.0, e - 127);
+  return s ? -mag : mag;
+}
+
+// IEEE binary16 decode of one bit pattern: sign, 5-bit exponent (bias 15),
+// 10-bit fraction; exponent 0 holds subnormals f/1024 * 2^-14, exponent 31
+// infinity (f = 0) or NaN.
+double dgo_f16_decode(uint16_t bits) {
+  const int s = bits >> 15;
+  const int e = (bits >> 10) & 0x1F;
+  const int f = bits & 0x3FF;
+  double mag;
+  if (e == 0x1F)
+    mag = f ? std::nan("") : HUGE_VAL;
+  else if (e == 0)
+    mag = std::ldexp((double)f / 1024.0, -14);
+  else
+    mag = std::ldexp(1.0 + (double)f / 1024.0, e - 15);
+  return s ? -mag : mag;
+}
+
+// Decode n 16-bit patterns (kind 1 = BF16, 2 = FP16) to FP32. Every finite
+// value of either format is exactly an FP32 value, so the narrowing from the
+// FP64 decode is exact. Returns 0, or -1 for an unknown kind.
+int dgo_decode16_n(const uint16_t* bits, int64_t n, int kind, float* out) {
+  if (kind != 1 && kind != 2) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = (float)(kind == 1 ? dgo_bf16_decode(bits[i]) : dgo_f16_decode(bits[i]));
   return 0;
 }
 
