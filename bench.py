@@ -329,8 +329,13 @@ def clock_window(graph, dev, graph_ms: float):
                                             "after the timed steps (untimed)" % clock_s}
 
 
-def quant_leg(c: int, operand: str, steps: int, warmup: int, sets: int | None, g: int, fmt: int, per_row: bool):
-    """The GPU quantiser on workload c's FP32 A or B: per-call time over rotating input sets."""
+QUANT_IN = {"f32": 4, "bf16": 2, "f16": 2}  # input element kinds of the quantiser and their bytes
+
+
+def quant_leg(c: int, operand: str, steps: int, warmup: int, sets: int | None, g: int, fmt: int, per_row: bool,
+              in_kind: str = "f32"):
+    """The GPU quantiser on workload c's A or B (FP32, or rounded to BF16 / FP16 before the timed region):
+    per-call time over rotating input sets."""
     import torch
 
     import fp8_block_scaled_scales_amd as dg
@@ -338,14 +343,19 @@ def quant_leg(c: int, operand: str, steps: int, warmup: int, sets: int | None, g
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = torch.from_numpy(synth.make_a(c) if operand == "a" else synth.make_b(c)).to(dev)
+    if in_kind != "f32":
+        x = x.to(torch.bfloat16 if in_kind == "bf16" else torch.float16)
     rows, cols = x.shape
     nblocks = (rows if per_row else math.ceil(rows / g)) * (cols // g)
-    set_bytes = 5 * rows * cols + 4 * nblocks  # FP32 in, FP8 codes and FP32 factors out
+    set_bytes = (QUANT_IN[in_kind] + 1) * rows * cols + 4 * nblocks  # input in, FP8 codes and FP32 factors out
     if sets is None:
         sets = max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes) + 1))
     bufs = [(x if i == 0 else x.clone(), torch.empty((rows, cols), dtype=torch.uint8, device=dev),
              torch.empty(nblocks, dtype=torch.float32, device=dev)) for i in range(sets)]
-    fn = dg.dg_quantize_fp8_rows if per_row else dg.dg_quantize_fp8_blocks
+    if in_kind == "f32":
+        fn = dg.dg_quantize_fp8_rows if per_row else dg.dg_quantize_fp8_blocks
+    else:
+        fn = dg.dg_quantize_fp8_rows_typed if per_row else dg.dg_quantize_fp8_blocks_typed
     stream = torch.cuda.current_stream(dev)
 
     def launch(i, st):
@@ -484,6 +494,8 @@ def main():
     ap.add_argument("--quant", default=None, choices=("a", "b"),
                     help="time the GPU quantiser on the workload's FP32 A or B instead of the GEMM (g x g "
                          "blocks, or 1 x g with --sa-rows 1; format from the first letter pair of --fmt)")
+    ap.add_argument("--quant-in", default="f32", choices=tuple(QUANT_IN),
+                    help="with --quant: the operand's element type as the quantiser reads it")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes three times (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -520,15 +532,17 @@ def main():
     if args.quant:
         fmt = fa if args.quant == "a" else fb
         ms, sets, glen, rows, cols, nblocks = quant_leg(c, args.quant, args.steps, args.warmup, args.sets, g, fmt,
-                                                        args.sa_rows == 1)
-        qbytes = 5.0 * rows * cols + 4.0 * nblocks
+                                                        args.sa_rows == 1, args.quant_in)
+        qbytes = (QUANT_IN[args.quant_in] + 1.0) * rows * cols + 4.0 * nblocks
         gbs = qbytes / (ms * 1e-3) / 1e9
         print(json.dumps({
-            "metric": "FP8 block quantiser throughput (FP32 in, FP8 codes and FP32 factors out; 1 GPU)",
+            "metric": "FP8 block quantiser throughput (%s in, FP8 codes and FP32 factors out; 1 GPU)"
+                      % args.quant_in.upper(),
             "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "f32", "data": "synthetic",
-            "config": {"workload": w["name"], "operand": args.quant.upper(), "rows": rows, "cols": cols, "gran": g,
+            "config": {"workload": w["name"], "operand": args.quant.upper(), "input": args.quant_in, "rows": rows,
+                       "cols": cols, "gran": g,
                        "blocks": "1x%d" % g if args.sa_rows == 1 else "%dx%d" % (g, g),
                        "fmt": "e5m2" if fmt else "e4m3", "input_sets": sets,
                        "launch": "hipGraph of %d launches, replayed %d times" % (glen, args.steps // glen)},

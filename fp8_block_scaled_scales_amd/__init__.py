@@ -33,6 +33,9 @@ DG_ELAUNCH = -4
 DG_ESCRATCH = -5
 DG_FMT_E4M3 = 0
 DG_FMT_E5M2 = 1
+DG_IN_F32 = 0
+DG_IN_BF16 = 1
+DG_IN_F16 = 2
 DG_ACT_NONE = 0
 DG_ACT_RELU = 1
 DG_ACT_GELU = 2
@@ -89,6 +92,10 @@ def load_library(path: str):
     lib.dg_quantize_e4m3_blocks.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp]
     lib.dg_quantize_fp8_blocks.restype = ctypes.c_int
     lib.dg_quantize_fp8_blocks.argtypes = [vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    for name in ("dg_quantize_fp8_blocks_typed", "dg_quantize_fp8_rows_typed"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.dg_strerror.restype = ctypes.c_char_p
     lib.dg_strerror.argtypes = [ctypes.c_int]
     lib.dg_version.restype = ctypes.c_int
@@ -137,6 +144,7 @@ def dg_query_tile(M: int, N: int, K: int, gran: int = 128, layout: int = 0, work
 _FP8 = (torch.float8_e4m3fn, torch.uint8)
 _FP8_OF = {DG_FMT_E4M3: (torch.float8_e4m3fn, torch.uint8), DG_FMT_E5M2: (torch.float8_e5m2, torch.uint8)}
 _GRANS = (64, 128, 256)
+_IN_OF = {torch.float32: DG_IN_F32, torch.bfloat16: DG_IN_BF16, torch.float16: DG_IN_F16}
 
 
 def _check(t, name, dtypes, shape, device):
@@ -391,17 +399,21 @@ def _quantize(x, gran, fmt, q, scales, stream, where):
         raise ValueError("gran must be 64, 128 or 256 and divide cols")
     if fmt not in _FP8_OF:
         raise ValueError("fmt must be DG_FMT_E4M3 or DG_FMT_E5M2")
-    _check(x, "x", (torch.float32,), (rows, cols), dev)
+    typed = where.endswith("_typed")
+    _check(x, "x", tuple(_IN_OF) if typed else (torch.float32,), (rows, cols), dev)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-    brows = 1 if where == "dg_quantize_fp8_rows" else gran  # rows per block
+    brows = 1 if where.startswith("dg_quantize_fp8_rows") else gran  # rows per block
     if scales is None:
         scales = torch.empty(((rows + brows - 1) // brows, cols // gran), dtype=torch.float32, device=dev)
     _check(q, "q", _FP8_OF[fmt], (rows, cols), dev)
     _check(scales, "scales", (torch.float32,), ((rows + brows - 1) // brows, cols // gran), dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
-        if where == "dg_quantize_fp8_rows":
+        if typed:
+            rc = getattr(_lib, where)(x.data_ptr(), _IN_OF[x.dtype], rows, cols, gran, fmt, q.data_ptr(),
+                                      scales.data_ptr(), s.cuda_stream)
+        elif where == "dg_quantize_fp8_rows":
             rc = _lib.dg_quantize_fp8_rows(x.data_ptr(), rows, cols, gran, fmt, q.data_ptr(), scales.data_ptr(),
                                            s.cuda_stream)
         elif fmt == DG_FMT_E4M3 and where == "dg_quantize_e4m3_blocks":
@@ -437,9 +449,24 @@ def dg_quantize_fp8_rows(x, gran: int = 128, fmt: int = DG_FMT_E4M3, q=None, sca
     return _quantize(x, gran, fmt, q, scales, stream, "dg_quantize_fp8_rows")
 
 
+def dg_quantize_fp8_blocks_typed(x, gran: int = 128, fmt: int = DG_FMT_E4M3, q=None, scales=None, stream=None):
+    """dg_quantize_fp8_blocks on float32, bfloat16 or float16 x (the input kind is x's dtype).
+
+    Each element is widened exactly to FP32 first, so a 16-bit x and its FP32
+    copy give identical codes and scales.
+    """
+    return _quantize(x, gran, fmt, q, scales, stream, "dg_quantize_fp8_blocks_typed")
+
+
+def dg_quantize_fp8_rows_typed(x, gran: int = 128, fmt: int = DG_FMT_E4M3, q=None, scales=None, stream=None):
+    """dg_quantize_fp8_rows on float32, bfloat16 or float16 x (the input kind is x's dtype)."""
+    return _quantize(x, gran, fmt, q, scales, stream, "dg_quantize_fp8_rows_typed")
+
+
 __all__ = ["dg_gemm_fp8_nt", "dg_gemm_fp8_nt_fmt", "dg_gemm_fp8_nt_epi", "dg_gemm_fp8_nt_ex", "dg_gemm_fp8_layout",
            "dg_gemm_fp8_ws", "dg_workspace", "dg_gemm_fp8_noalloc", "dg_noalloc_scratch_bytes", "DG_ESCRATCH",
            "DG_LAYOUT_NT", "DG_LAYOUT_NN", "DG_LAYOUT_TT", "DG_LAYOUT_TN", "DG_ACT_NONE",
            "DG_ACT_RELU", "DG_ACT_GELU", "dg_quantize_e4m3_blocks", "dg_quantize_fp8_blocks", "dg_quantize_fp8_rows",
+           "dg_quantize_fp8_blocks_typed", "dg_quantize_fp8_rows_typed", "DG_IN_F32", "DG_IN_BF16", "DG_IN_F16",
            "dg_query_tile", "dg_strerror", "dg_version", "DGError", "DGArgumentError", "DG_OK", "DG_EINVAL",
            "DG_EALIGN", "DG_EUNSUPPORTED", "DG_ELAUNCH", "DG_FMT_E4M3", "DG_FMT_E5M2", "DG_MAX_DIM", "LIB_PATH"]

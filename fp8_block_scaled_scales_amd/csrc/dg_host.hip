@@ -326,18 +326,22 @@ int gemm(const void* a, const void* b, const float* sa, const float* sb, void* o
   return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
 }
 
-// block_rows: rows per block, gran (g x g blocks) or 1 (1 x g blocks).
-int quantize(const float* x, int64_t rows, int64_t cols, int gran, int block_rows, int fmt, void* q, float* scales,
-             void* stream) {
+// block_rows: rows per block, gran (g x g blocks) or 1 (1 x g blocks); in:
+// DG_IN_F32, DG_IN_BF16 or DG_IN_F16.
+int quantize(const void* x, int in, int64_t rows, int64_t cols, int gran, int block_rows, int fmt, void* q,
+             float* scales, void* stream) {
   if (!x || !q || !scales) return DG_EINVAL;
   if (fmt != DG_FMT_E4M3 && fmt != DG_FMT_E5M2) return DG_EINVAL;
+  if (in != DG_IN_F32 && in != DG_IN_BF16 && in != DG_IN_F16) return DG_EINVAL;
+  const uint64_t esize = in == DG_IN_F32 ? 4 : 2;
   if (rows <= 0 || cols <= 0 || rows > DG_MAX_DIM || cols > DG_MAX_DIM) return DG_EINVAL;
   if ((gran != 64 && gran != 128 && gran != 256) || cols % gran != 0) return DG_EINVAL;
   if (block_rows != gran && block_rows != 1) return DG_EINVAL;
   if (((rows + block_rows - 1) / block_rows) * (cols / gran) > 0x7fffffff) return DG_EINVAL;
-  if (((uintptr_t)x & 15) || ((uintptr_t)q & 3) || ((uintptr_t)scales & 3)) return DG_EALIGN;
+  // a lane writes one code per element of its 16-byte load: 4 bytes, or 8 for 16-bit input
+  if (((uintptr_t)x & 15) || ((uintptr_t)q & (16 / esize - 1)) || ((uintptr_t)scales & 3)) return DG_EALIGN;
   {
-    const uint64_t xb = 4ull * (uint64_t)rows * (uint64_t)cols, qb = (uint64_t)rows * (uint64_t)cols;
+    const uint64_t xb = esize * (uint64_t)rows * (uint64_t)cols, qb = (uint64_t)rows * (uint64_t)cols;
     const uint64_t sbytes = 4ull * (uint64_t)((rows + block_rows - 1) / block_rows) * (uint64_t)(cols / gran);
     if (overlaps(x, xb, q, qb) || overlaps(x, xb, scales, sbytes) || overlaps(q, qb, scales, sbytes)) return DG_EINVAL;
   }
@@ -351,9 +355,10 @@ int quantize(const float* x, int64_t rows, int64_t cols, int gran, int block_row
   p.cols = cols;
   p.gran = gran;
   p.fmt = fmt;
+  p.in = in;
   if (log_enabled())
-    std::fprintf(stderr, "dg_quantize_fp8 rows=%lld cols=%lld block %dx%d fmt=%d\n", (long long)rows,
-                 (long long)cols, block_rows, gran, fmt);
+    std::fprintf(stderr, "dg_quantize_fp8 rows=%lld cols=%lld block %dx%d fmt=%d in=%d\n", (long long)rows,
+                 (long long)cols, block_rows, gran, fmt, in);
   t_last_hip = block_rows == 1 ? dg::launch_quant_rows(p, static_cast<hipStream_t>(stream))
                                : dg::launch_quant(p, static_cast<hipStream_t>(stream));
   return t_last_hip == hipSuccess ? DG_OK : DG_ELAUNCH;
@@ -472,17 +477,27 @@ int dg_gemm_fp8_layout(const void* a, const void* b, const float* sa, const floa
 
 int dg_quantize_fp8_blocks(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q, float* scales,
                            void* stream) {
-  return quantize(x, rows, cols, gran, gran, fmt, q, scales, stream);
+  return quantize(x, DG_IN_F32, rows, cols, gran, gran, fmt, q, scales, stream);
 }
 
 int dg_quantize_fp8_rows(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q, float* scales,
                          void* stream) {
-  return quantize(x, rows, cols, gran, 1, fmt, q, scales, stream);
+  return quantize(x, DG_IN_F32, rows, cols, gran, 1, fmt, q, scales, stream);
 }
 
 int dg_quantize_e4m3_blocks(const float* x, int64_t rows, int64_t cols, int gran, void* q, float* scales,
                             void* stream) {
-  return quantize(x, rows, cols, gran, gran, DG_FMT_E4M3, q, scales, stream);
+  return quantize(x, DG_IN_F32, rows, cols, gran, gran, DG_FMT_E4M3, q, scales, stream);
+}
+
+int dg_quantize_fp8_blocks_typed(const void* x, int in_type, int64_t rows, int64_t cols, int gran, int fmt, void* q,
+                                 float* scales, void* stream) {
+  return quantize(x, in_type, rows, cols, gran, gran, fmt, q, scales, stream);
+}
+
+int dg_quantize_fp8_rows_typed(const void* x, int in_type, int64_t rows, int64_t cols, int gran, int fmt, void* q,
+                               float* scales, void* stream) {
+  return quantize(x, in_type, rows, cols, gran, 1, fmt, q, scales, stream);
 }
 
 }  // extern "C"

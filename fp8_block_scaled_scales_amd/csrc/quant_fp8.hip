@@ -1,5 +1,5 @@
-// Block quantiser FP32 -> FP8 (E4M3FN or E5M2) with one FP32 scale per g x g
-// block, g = 64, 128 or 256, for gfx950. It produces the GEMM's inputs: the
+// Block quantiser FP32, BF16 or FP16 -> FP8 (E4M3FN or E5M2) with one FP32
+// scale per g x g block, g = 64, 128 or 256, for gfx950. It produces the GEMM's inputs: the
 // pages place quantisation outside the GEMM, say that activations must be
 // quantised online and that the granularity must equal the GEMM's
 // (DeepGEMM实战 §4.4), that one factor per block maps the block into FP8 range
@@ -16,10 +16,15 @@
 // The divide is taken as a reciprocal and two FMA corrections, which give the
 // correctly rounded quotient (div_by_scale).
 //
+// 16-bit inputs (the weights and activations to quantise arrive in FP16 or
+// BF16, DeepGEMM实战 §4.4) are widened exactly to FP32 as they are used; the
+// rule is then the FP32 one, on the same values.
+//
 // One workgroup per block, 256 threads (1024 for g = 256). The block (64 KB
-// for g = 128) stays in registers between the amax pass and the encode pass,
-// so x is read from HBM once: the kernel is bound by HBM bandwidth (4 bytes
-// in, 1 byte out per element).
+// of FP32 for g = 128) stays in registers, as loaded, between the amax pass
+// and the encode pass, so x is read from HBM once: the kernel is bound by HBM
+// bandwidth (4 or 2 bytes in, 1 byte out per element). Every load is 16
+// bytes: four FP32 or eight 16-bit elements per lane.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -29,6 +34,62 @@
 namespace dg {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Input element kinds: 0 FP32, 1 BF16, 2 FP16 (the library's DG_IN_* codes).
+template <int IN>
+struct InKind {
+  static constexpr int kBytes = IN == 0 ? 4 : 2;  // bytes per element
+  static constexpr int kPerLoad = 16 / kBytes;     // elements per 16-byte load
+  static constexpr int kQuads = kPerLoad / 4;      // groups of four per load
+};
+
+// Elements 4*H .. 4*H+3 of a 16-byte load, as FP32 (exact for every kind).
+// A 32-bit word holds two 16-bit elements, the first in its low half. BF16 is
+// the high half of an FP32 pattern; FP16 converts exactly.
+template <int IN, int H>
+__device__ __forceinline__ v4f widen(v4u w) {
+  if constexpr (IN == 0) {
+    return __builtin_bit_cast(v4f, w);
+  } else {
+    const unsigned a = H ? w.z : w.x, b = H ? w.w : w.y;
+    if constexpr (IN == 1) {
+      return (v4f){__uint_as_float(a << 16), __uint_as_float(a & 0xFFFF0000u), __uint_as_float(b << 16),
+                   __uint_as_float(b & 0xFFFF0000u)};
+    } else {
+      const v2h ha = __builtin_bit_cast(v2h, a), hb = __builtin_bit_cast(v2h, b);
+      return (v4f){(float)ha.x, (float)ha.y, (float)hb.x, (float)hb.y};
+    }
+  }
+}
+
+__device__ __forceinline__ float amax4(v4f v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v2u16 abs_bits2(unsigned w) { return __builtin_bit_cast(v2u16, w & 0x7FFF7FFFu); }
+
+// max |x| over the elements of one 16-byte load. For 16-bit input the max is
+// taken on the bit patterns: with the sign bit cleared, the patterns of
+// finite BF16 or FP16 values order as the magnitudes do, so a packed 16-bit
+// integer max finds the largest, which is then widened once. Nothing widened
+// here stays live until the encode pass, which widens its own copies.
+template <int IN>
+__device__ __forceinline__ float amax_load(v4u w) {
+  if constexpr (IN == 0) {
+    return amax4(widen<IN, 0>(w));
+  } else {
+    const v2u16 m = __builtin_elementwise_max(__builtin_elementwise_max(abs_bits2(w.x), abs_bits2(w.y)),
+                                              __builtin_elementwise_max(abs_bits2(w.z), abs_bits2(w.w)));
+    const unsigned top = m.x > m.y ? m.x : m.y;
+    if constexpr (IN == 1) return __uint_as_float(top << 16);
+    else return (float)__builtin_bit_cast(_Float16, (unsigned short)top);
+  }
+}
 
 // Division by a block's scale s, rounded as the correctly rounded FP32 divide
 // rounds it, without a divide per element. inv = RN(1/s) is computed once per
@@ -71,18 +132,19 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Max over each aligned group of L lanes (L = 16, 32 or 64), in every lane of
-// the group: within quads by two swaps (DPP quad_perm [1,0,3,2], [2,3,0,1]),
-// then each lane against its mirror in the 8-lane half row and in the 16-lane
-// row (DPP row_half_mirror, row_mirror), which leaves the row's max in every
-// lane; beyond 16 lanes, cross-lane shuffles. max is exact and order-free.
+// Max over each aligned group of L lanes (L = 8, 16, 32 or 64), in every lane
+// of the group: within quads by two swaps (DPP quad_perm [1,0,3,2],
+// [2,3,0,1]), then each lane against its mirror in the 8-lane half row, which
+// leaves the half row's max in every lane, and in the 16-lane row (DPP
+// row_half_mirror, row_mirror); beyond 16 lanes, cross-lane shuffles. max is
+// exact and order-free.
 template <int L>
 __device__ __forceinline__ float group_max(float m) {
-  static_assert(L == 16 || L == 32 || L == 64, "group");
+  static_assert(L == 8 || L == 16 || L == 32 || L == 64, "group");
   m = fmaxf(m, dpp_f<0xB1>(m));
   m = fmaxf(m, dpp_f<0x4E>(m));
   m = fmaxf(m, dpp_f<0x141>(m));
-  m = fmaxf(m, dpp_f<0x140>(m));
+  if constexpr (L >= 16) m = fmaxf(m, dpp_f<0x140>(m));
   if constexpr (L >= 32) m = fmaxf(m, __shfl_xor(m, 16, 64));
   if constexpr (L >= 64) m = fmaxf(m, __shfl_xor(m, 32, 64));
   return m;
@@ -115,35 +177,50 @@ __device__ __forceinline__ int encode4(v4f v, float s, float inv) {
   }
 }
 
-template <int G, int FMT>
-__global__ __launch_bounds__(G == 256 ? 1024 : 256) void quant_fp8_blocks(const float* __restrict__ x,
+// The codes of one 16-byte load's elements, divided by s, stored at q (4 or
+// 8 bytes: one code per element, in element order).
+template <int FMT, int IN, bool FAST>
+__device__ __forceinline__ void encode_store(v4u w, float s, float inv, uint8_t* q) {
+  const int c0 = encode4<FMT, FAST>(widen<IN, 0>(w), s, inv);
+  if constexpr (InKind<IN>::kQuads == 1) {
+    *reinterpret_cast<int*>(q) = c0;
+  } else {
+    *reinterpret_cast<v2i*>(q) = (v2i){c0, encode4<FMT, FAST>(widen<IN, 1>(w), s, inv)};
+  }
+}
+
+template <int G, int FMT, int IN>
+__global__ __launch_bounds__(G == 256 ? 1024 : 256) void quant_fp8_blocks(const void* __restrict__ xv,
                                                                           uint8_t* __restrict__ q,
                                                                           float* __restrict__ scales, int rows,
                                                                           int cols) {
   constexpr int NT = G == 256 ? 1024 : 256;
   constexpr float FMAX = FMT == 1 ? 57344.0f : 448.0f;
-  constexpr int ROW_V4 = G / 4;              // float4 per block row
-  constexpr int ROWS_PER_PASS = NT / ROW_V4;  // block rows covered by one pass
+  constexpr int EPL = InKind<IN>::kPerLoad;
+  constexpr int ROW_L = G / EPL;              // lanes per block row
+  constexpr int ROWS_PER_PASS = NT / ROW_L;   // block rows covered by one pass
   constexpr int PASSES = G / ROWS_PER_PASS;
+  static_assert(PASSES * ROWS_PER_PASS == G, "passes");
   __shared__ float red[NT / 64];
+  const char* x = static_cast<const char*>(xv);
 
   const int ncb = cols / G;
   const int rb = blockIdx.x / ncb, cb = blockIdx.x % ncb;
   const int t = threadIdx.x;
-  const int rsub = t / ROW_V4, c4 = t % ROW_V4;
-  const int col = cb * G + c4 * 4;
+  const int rsub = t / ROW_L, cl = t % ROW_L;
+  const int col = cb * G + cl * EPL;
 
-  v4f v[PASSES];
+  v4u v[PASSES];
   float amax = 0.0f;
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int r = rb * G + p * ROWS_PER_PASS + rsub;
     if (r < rows) {
-      v[p] = *reinterpret_cast<const v4f*>(x + (int64_t)r * cols + col);
+      v[p] = *reinterpret_cast<const v4u*>(x + ((int64_t)r * cols + col) * InKind<IN>::kBytes);
     } else {
-      v[p] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      v[p] = (v4u){0u, 0u, 0u, 0u};
     }
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w))));
+    amax = fmaxf(amax, amax_load<IN>(v[p]));
   }
   // max is exact and order-free: over the wave, then across the waves
   amax = group_max<64>(amax);
@@ -161,29 +238,33 @@ __global__ __launch_bounds__(G == 256 ? 1024 : 256) void quant_fp8_blocks(const 
   for (int p = 0; p < PASSES; ++p) {
     const int r = rb * G + p * ROWS_PER_PASS + rsub;
     if (r < rows) {
-      const int packed = fast ? encode4<FMT, true>(v[p], scale, inv) : encode4<FMT, false>(v[p], scale, inv);
-      *reinterpret_cast<int*>(q + (int64_t)r * cols + col) = packed;
+      uint8_t* dst = q + (int64_t)r * cols + col;
+      if (fast) encode_store<FMT, IN, true>(v[p], scale, inv, dst);
+      else encode_store<FMT, IN, false>(v[p], scale, inv, dst);
     }
   }
 }
 
 // 1 x g blocks (one factor per row and g-wide column segment; the per-row A
 // factors of the template article's per-channel choice, §3.4): the same rule
-// per segment. G/4 lanes own a segment, four elements each, so one load
-// instruction of a wave covers 256 / G segments, 256 consecutive floats when a
-// row has that many; amax is a butterfly over the segment's lanes. Each wave
-// takes U such groups, all loads issued before any is used, so a thread has
-// U x 16 bytes in flight. Segments are numbered row-major
-// (row * cols/G + column block), which is also the factor's index in the
-// [rows][cols/G] scale tensor; the host keeps their count below 2^31.
-template <int G, int FMT, int U>
-__global__ __launch_bounds__(256) void quant_fp8_rows(const float* __restrict__ x, uint8_t* __restrict__ q,
+// per segment. A lane loads 16 bytes (four FP32 or eight 16-bit elements), so
+// g / 4 or g / 8 lanes own a segment and one load instruction of a wave
+// covers 1 KB of consecutive input when a row has that much; amax is a
+// butterfly over the segment's lanes. Each wave takes U such groups, all
+// loads issued before any is used, so a thread has U x 16 bytes in flight.
+// Segments are numbered row-major (row * cols/G + column block), which is
+// also the factor's index in the [rows][cols/G] scale tensor; the host keeps
+// their count below 2^31.
+template <int G, int FMT, int IN, int U>
+__global__ __launch_bounds__(256) void quant_fp8_rows(const void* __restrict__ xv, uint8_t* __restrict__ q,
                                                       float* __restrict__ scales, unsigned nseg, int cols) {
   constexpr float FMAX = FMT == 1 ? 57344.0f : 448.0f;
-  constexpr int LPS = G / 4;        // lanes per segment
+  constexpr int EPL = InKind<IN>::kPerLoad;
+  constexpr int LPS = G / EPL;      // lanes per segment
   constexpr int SPW = 64 / LPS;     // segments per wave-wide load
+  const char* x = static_cast<const char*>(xv);
   const int lane = threadIdx.x & 63;
-  const int c4 = lane % LPS;
+  const int cl = lane % LPS;
   const unsigned ncb = (unsigned)(cols / G);
   // unsigned: the last workgroup's segments may pass 2^31 - 1 (and are not live)
   const unsigned wseg = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (unsigned)(SPW * U);  // the wave's first segment
@@ -191,7 +272,7 @@ __global__ __launch_bounds__(256) void quant_fp8_rows(const float* __restrict__ 
   // (row, column block) of the wave's first segment from one division; the
   // lane's segments follow it by at most SPW * U - 1, a few row wraps at most
   const unsigned wrow = wseg / ncb, wcb = wseg - wrow * ncb;
-  v4f v[U];
+  v4u v[U];
   int64_t off[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -203,22 +284,20 @@ __global__ __launch_bounds__(256) void quant_fp8_rows(const float* __restrict__ 
       cb -= k * ncb;
     }
     // whole segments are live or not, so each reduction stays inside live lanes
-    off[u] = seg < nseg ? (int64_t)row * cols + cb * G + c4 * 4 : 0;
-    v[u] = seg < nseg ? *reinterpret_cast<const v4f*>(x + off[u]) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    off[u] = seg < nseg ? (int64_t)row * cols + cb * G + cl * EPL : 0;
+    v[u] = seg < nseg ? *reinterpret_cast<const v4u*>(x + off[u] * InKind<IN>::kBytes) : (v4u){0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const unsigned seg = seg0 + (unsigned)(u * SPW);
-    const float amax =
-        group_max<LPS>(fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
+    const float amax = group_max<LPS>(amax_load<IN>(v[u]));
     if (seg >= nseg) continue;
     const float scale = block_scale(amax, FMAX);
-    if (c4 == 0) scales[seg] = scale;
+    if (cl == 0) scales[seg] = scale;
     // the segment's lanes agree on scale, so a divergent choice splits
     // whole segments
-    const int packed = recip_ok(scale) ? encode4<FMT, true>(v[u], scale, 1.0f / scale)
-                                       : encode4<FMT, false>(v[u], scale, 0.0f);
-    *reinterpret_cast<int*>(q + off[u]) = packed;
+    if (recip_ok(scale)) encode_store<FMT, IN, true>(v[u], scale, 1.0f / scale, q + off[u]);
+    else encode_store<FMT, IN, false>(v[u], scale, 0.0f, q + off[u]);
   }
 }
 
@@ -228,60 +307,86 @@ __global__ __launch_bounds__(256) void quant_fp8_rows(const float* __restrict__ 
 // runs: A of 8192^3 65.7 -> 63.8 us, B of the decode shape 31.6 -> 31.1 us,
 // A of the prefill shape unchanged; four per CU was as good on 8192^3 and
 // slower elsewhere, two per CU 10-15% slower.
-template <int G, int FMT>
+template <int G, int FMT, int IN>
 static hipError_t launch_rows_g(const QuantArgs& p, hipStream_t stream) {
   constexpr int U = 8;
   const int64_t nseg = p.rows * (p.cols / G);
-  const int64_t per_wg = 4 * (256 / G) * U;  // segments per workgroup of four waves
-  hipLaunchKernelGGL((quant_fp8_rows<G, FMT, U>), dim3((unsigned)((nseg + per_wg - 1) / per_wg)), dim3(256),
+  const int64_t per_wg = 4 * (64 / (G / InKind<IN>::kPerLoad)) * U;  // segments per workgroup of four waves
+  hipLaunchKernelGGL((quant_fp8_rows<G, FMT, IN, U>), dim3((unsigned)((nseg + per_wg - 1) / per_wg)), dim3(256),
                      32u * 1024u, stream, p.x, p.q, p.scales, (unsigned)nseg, (int)p.cols);
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, int IN>
 static hipError_t launch_rows_f(const QuantArgs& p, hipStream_t stream) {
   switch (p.gran) {
-    case 64: return launch_rows_g<64, FMT>(p, stream);
-    case 128: return launch_rows_g<128, FMT>(p, stream);
-    case 256: return launch_rows_g<256, FMT>(p, stream);
+    case 64: return launch_rows_g<64, FMT, IN>(p, stream);
+    case 128: return launch_rows_g<128, FMT, IN>(p, stream);
+    case 256: return launch_rows_g<256, FMT, IN>(p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int IN>
+static hipError_t launch_rows_i(const QuantArgs& p, hipStream_t stream) {
+  return p.fmt == 1 ? launch_rows_f<1, IN>(p, stream) : launch_rows_f<0, IN>(p, stream);
 }
 
 hipError_t launch_quant_rows(const QuantArgs& p, hipStream_t stream) {
-  return p.fmt == 1 ? launch_rows_f<1>(p, stream) : launch_rows_f<0>(p, stream);
-}
-
-// With at least four blocks per CU, the launch reserves 64 KB of LDS that
-// the kernel does not use, so that two workgroups share a CU instead of
-// five. Fewer blocks in flight at once stagger the workgroups: one block's
-// stores overlap the next blocks' loads instead of every CU loading, then
-// dividing, then storing together. Interleaved runs: B of the decode shape
-// (1792 blocks) 30.7 -> 29.6 us, A of 8192^3 (4096 blocks) 61.0 -> 59.9 us;
-// B of the prefill shape (896 blocks) was 2% slower this way (1.75 rounds of
-// two per CU) and keeps five. g = 256 runs 1024-thread workgroups, two per
-// CU already.
-template <int G, int FMT>
-static hipError_t launch_g(const QuantArgs& p, hipStream_t stream) {
-  const int64_t nblocks = ((p.rows + G - 1) / G) * (p.cols / G);
-  const unsigned lds = G != 256 && nblocks >= 4 * 256 ? 64u * 1024u : 0u;
-  hipLaunchKernelGGL((quant_fp8_blocks<G, FMT>), dim3((unsigned)nblocks), dim3(G == 256 ? 1024 : 256), lds, stream,
-                     p.x, p.q, p.scales, (int)p.rows, (int)p.cols);
-  return hipGetLastError();
-}
-
-template <int FMT>
-static hipError_t launch_f(const QuantArgs& p, hipStream_t stream) {
-  switch (p.gran) {
-    case 64: return launch_g<64, FMT>(p, stream);
-    case 128: return launch_g<128, FMT>(p, stream);
-    case 256: return launch_g<256, FMT>(p, stream);
+  switch (p.in) {
+    case 0: return launch_rows_i<0>(p, stream);
+    case 1: return launch_rows_i<1>(p, stream);
+    case 2: return launch_rows_i<2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+// For FP32 blocks of g = 128 (64 KB of input each) and at least four blocks
+// per CU, the launch reserves 64 KB of LDS that the kernel does not use, so
+// that two workgroups share a CU instead of five. Fewer blocks in flight at
+// once stagger the workgroups: one block's stores overlap the next blocks'
+// loads instead of every CU loading, then dividing, then storing together.
+// Interleaved runs: B of the decode shape (1792 blocks) 30.7 -> 29.6 us, A of
+// 8192^3 (4096 blocks) 61.0 -> 59.9 us; B of the prefill shape (896 blocks)
+// was 2% slower this way (1.75 rounds of two per CU) and keeps five.
+// Smaller blocks need every workgroup the registers allow, since two of them
+// per CU hold too few bytes in flight: without the reservation FP32 g = 64
+// ran 1.7-1.9x faster (B of the long-K shape 119.6 -> 64.5 us, A of 8192^3
+// at g = 64 122.9 -> 65.7 us) and 16-bit g = 128 blocks (32 KB) 7-9% faster
+// (A of 8192^3 in BF16 42.8 -> 39.4 us), 16-bit g = 64 1.5x (A of the long-K
+// shape 33.8 -> 22.3 us); a 32 KB reservation (five per CU) fell in between.
+// g = 256 runs 1024-thread workgroups, two per CU already.
+template <int G, int FMT, int IN>
+static hipError_t launch_g(const QuantArgs& p, hipStream_t stream) {
+  const int64_t nblocks = ((p.rows + G - 1) / G) * (p.cols / G);
+  const unsigned lds = IN == 0 && G == 128 && nblocks >= 4 * 256 ? 64u * 1024u : 0u;
+  hipLaunchKernelGGL((quant_fp8_blocks<G, FMT, IN>), dim3((unsigned)nblocks), dim3(G == 256 ? 1024 : 256), lds,
+                     stream, p.x, p.q, p.scales, (int)p.rows, (int)p.cols);
+  return hipGetLastError();
+}
+
+template <int FMT, int IN>
+static hipError_t launch_f(const QuantArgs& p, hipStream_t stream) {
+  switch (p.gran) {
+    case 64: return launch_g<64, FMT, IN>(p, stream);
+    case 128: return launch_g<128, FMT, IN>(p, stream);
+    case 256: return launch_g<256, FMT, IN>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int IN>
+static hipError_t launch_i(const QuantArgs& p, hipStream_t stream) {
+  return p.fmt == 1 ? launch_f<1, IN>(p, stream) : launch_f<0, IN>(p, stream);
+}
+
 hipError_t launch_quant(const QuantArgs& p, hipStream_t stream) {
-  return p.fmt == 1 ? launch_f<1>(p, stream) : launch_f<0>(p, stream);
+  switch (p.in) {
+    case 0: return launch_i<0>(p, stream);
+    case 1: return launch_i<1>(p, stream);
+    case 2: return launch_i<2>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace dg

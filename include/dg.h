@@ -58,10 +58,11 @@ extern "C" {
 #define DG_ELAUNCH (-4)      /* a HIP call failed (not recoverable); dg_strerror() gives its text */
 #define DG_ESCRATCH (-5)     /* dg_gemm_fp8_noalloc: the plan needs more than its fixed scratch; nothing launched */
 
-/* Version of this header and library: 2.0.0 (dg_tile_info gained
+/* Version of this header and library: 2.1.0 (2.0.0: dg_tile_info gained
  * workspace_bytes; dg_gemm_fp8_ws and dg_query_tile_ws were added; no call
- * but dg_gemm_fp8_ws splits K over workgroups). */
-#define DG_VERSION 200
+ * but dg_gemm_fp8_ws splits K over workgroups. 2.1.0: the quantisers take
+ * BF16 and FP16 input through the _typed calls). */
+#define DG_VERSION 210
 
 /* Largest accepted dimension, 2^24 - 256: a 256-row tile of K bytes per row
  * (256 * K) then stays below 2^32 bytes, the reach of a buffer descriptor,
@@ -101,6 +102,11 @@ int dg_gemm_fp8_nt(const void* a, const void* b, const float* sa, const float* s
  * m/4 * 2^-14, largest finite 57344, exponent field 31 = inf/NaN. */
 #define DG_FMT_E4M3 0
 #define DG_FMT_E5M2 1
+
+/* Element types of the quantisers' input (dg_quantize_fp8_*_typed). */
+#define DG_IN_F32 0
+#define DG_IN_BF16 1
+#define DG_IN_F16 2
 
 /*
  * dg_gemm_fp8_nt_fmt - dg_gemm_fp8_nt with each operand's format given:
@@ -336,6 +342,31 @@ int dg_quantize_fp8_blocks(const float* x, int64_t rows, int64_t cols, int gran,
  */
 int dg_quantize_fp8_rows(const float* x, int64_t rows, int64_t cols, int gran, int fmt, void* q,
                          float* scales, void* stream);
+
+/*
+ * dg_quantize_fp8_blocks_typed, dg_quantize_fp8_rows_typed - the two
+ * quantisers above on FP32, BF16 or FP16 input: the weights and activations
+ * to quantise arrive in FP16 or BF16 (DeepGEMM实战 §4.4), and reading them as
+ * they are moves half the bytes of an FP32 copy.
+ *
+ *   x        [rows][cols] row-major elements of kind in_type, 16-byte aligned:
+ *            DG_IN_F32 (float), DG_IN_BF16 (bfloat16 bit patterns: the high
+ *            half of an FP32 pattern) or DG_IN_F16 (IEEE binary16).
+ *   in_type  DG_IN_F32, DG_IN_BF16 or DG_IN_F16; anything else is DG_EINVAL.
+ *   q        codes out, [rows][cols] row-major; 4-byte aligned for FP32
+ *            input, 8-byte aligned for 16-bit input (DG_EALIGN otherwise).
+ *   scales   as dg_quantize_fp8_blocks (g x g) or dg_quantize_fp8_rows (1 x g).
+ *
+ * Each element is widened exactly to FP32 and the rule is then the FP32 one,
+ * so a 16-bit matrix and its FP32 copy give identical codes and factors.
+ * Inputs must be finite. Other arguments, status codes and asynchrony as
+ * dg_quantize_fp8_blocks; with DG_IN_F32 each call is that call (blocks) or
+ * dg_quantize_fp8_rows (rows).
+ */
+int dg_quantize_fp8_blocks_typed(const void* x, int in_type, int64_t rows, int64_t cols, int gran, int fmt, void* q,
+                                 float* scales, void* stream);
+int dg_quantize_fp8_rows_typed(const void* x, int in_type, int64_t rows, int64_t cols, int gran, int fmt, void* q,
+                               float* scales, void* stream);
 
 /* Text for a status code (for DG_ELAUNCH: the last HIP error on this
  * thread), so a caller can log which class of failure (the pitfalls article

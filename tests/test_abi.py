@@ -375,6 +375,40 @@ def test_quantize_overlaps(dg, x, q, s):
     assert dg.lib.dg_quantize_fp8_blocks(x, 64, 256, 128, 0, q, s, None) == dg.DG_EINVAL
     assert dg.lib.dg_quantize_fp8_rows(x, 64, 256, 128, 0, q, s, None) == dg.DG_EINVAL
 
+@pytest.mark.parametrize("in_type", [3, -1, 7])
+def test_quantize_typed_rejects_unknown_input_kind(dg, in_type):
+    for fn in (dg.lib.dg_quantize_fp8_blocks_typed, dg.lib.dg_quantize_fp8_rows_typed):
+        assert fn(A, in_type, 64, 256, 128, 0, B, SA, None) == dg.DG_EINVAL
+
+
+@pytest.mark.parametrize("fmt,g,cols", [(2, 128, 256), (1, 96, 192), (0, 256, 384), (0, 128, 0)])
+@pytest.mark.parametrize("in_type", [0, 1, 2])
+def test_quantize_typed_einval(dg, in_type, fmt, g, cols):
+    for fn in (dg.lib.dg_quantize_fp8_blocks_typed, dg.lib.dg_quantize_fp8_rows_typed):
+        assert fn(A, in_type, 64, cols, g, fmt, B, SA, None) == dg.DG_EINVAL
+
+
+def test_quantize_typed_alignment(dg):
+    # x 16-byte aligned always; q 8-byte aligned for 16-bit input (a lane
+    # writes eight codes), 4-byte for FP32
+    for fn in (dg.lib.dg_quantize_fp8_blocks_typed, dg.lib.dg_quantize_fp8_rows_typed):
+        for in_type in (1, 2):
+            assert fn(A, in_type, 64, 256, 128, 0, B + 4, SA, None) == dg.DG_EALIGN
+            assert fn(A + 8, in_type, 64, 256, 128, 0, B, SA, None) == dg.DG_EALIGN
+        assert fn(A + 8, 0, 64, 256, 128, 0, B, SA, None) == dg.DG_EALIGN
+        # FP32 input with q 4-byte aligned passes every argument check; what
+        # follows is the device check (no GPU here) or a launch
+        assert fn(A, 0, 64, 256, 128, 0, B + 4, SA, None) not in (dg.DG_EALIGN, dg.DG_EINVAL)
+
+
+@pytest.mark.parametrize("in_type,q_off,overlaps", [(1, 0x7F00, True), (1, 0x8000, False), (2, 0x7FF8, True),
+                                                    (2, 0x8000, False), (0, 0x8000, True), (0, 0x10000, False)])
+def test_quantize_typed_overlap_counts_element_bytes(dg, in_type, q_off, overlaps):
+    # x [64][256] is 32 KB of 16-bit elements, 64 KB of FP32; q is 16 KB
+    rc = dg.lib.dg_quantize_fp8_blocks_typed(A, in_type, 64, 256, 128, 0, A + q_off, SB, None)
+    assert (rc == dg.DG_EINVAL) == overlaps
+
+
 def test_quantize_scale_count_cap(dg):
     """More than 2^31 - 1 scale factors is rejected before any device work.
     rows = 2^24 - 256 with 129 segments per row is 2,164,227,840 factors, and
