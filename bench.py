@@ -82,10 +82,10 @@ DEFAULT_WORKLOAD = 4      # large square M=N=K=8192, g=128: the largest shape, M
 # workload runs (KERNEL_SOURCES) as they were when the counters were taken. A
 # different hash means the kernel changed since: traffic is null.
 TRAFFIC = {
-    "square8192": {"src": "22b88ed090c013cb", "bytes": 940600418},
-    "prefill_m4096_n7168_k2048": {"src": "22b88ed090c013cb", "bytes": 151255113},
-    "longk_m2000_n4000_k16384_g64": {"src": "22b88ed090c013cb", "bytes": 278791727},
-    "decode_m64_n4096_k7168": {"src": "2668ba32ebd577fb", "bytes": 33667236},
+    "square8192": {"src": "bb28682c6310a4e5", "bytes": 940560677},
+    "prefill_m4096_n7168_k2048": {"src": "bb28682c6310a4e5", "bytes": 151255113},
+    "longk_m2000_n4000_k16384_g64": {"src": "bb28682c6310a4e5", "bytes": 278791791},
+    "decode_m64_n4096_k7168": {"src": "86e89fe55db16f3c", "bytes": 33667236},
 }
 
 # Sources that make up each workload's kernel: its class's device code, the
