@@ -135,3 +135,32 @@ def test_fp32_through_the_typed_call():
     torch.cuda.synchronize()
     rq, rs = oracle.quantize_blocks_fmt(x, 128, 1)
     assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f16"])
+@pytest.mark.parametrize("g", [64, 128])
+def test_16bit_operands_quantised_then_multiplied(kind, g):
+    """The use the quantiser exists for: 16-bit activations (per-row factors)
+    and weights (g x g blocks) quantised on the GPU, then the GEMM; against the
+    oracle's 16-bit quantisers and its reference GEMM on the same bits."""
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+    from tests._common import within_tolerance
+
+    M, N, K = 300, 520, 8 * g
+    a16, abits = _as16(synth.make_a(3, M=M, K=K), kind)
+    b16, bbits = _as16(synth.make_b(3, N=N, K=K), kind)
+    say("quantise16 then gemm %s g=%d %dx%dx%d" % (kind, g, M, N, K))
+    a8, sa = dg.dg_quantize_fp8_rows_typed(a16, gran=g)
+    b8, sb = dg.dg_quantize_fp8_blocks_typed(b16, gran=g)
+    out = dg.dg_gemm_fp8_nt_ex(a8, b8, sa, sb, gran=g, sa_rows=1)
+    torch.cuda.synchronize()
+    ra8, rsa = oracle.quantize_rows_16(abits, KINDS[kind], g)
+    rb8, rsb = oracle.quantize_blocks_16(bbits, KINDS[kind], g)
+    assert np.array_equal(a8.cpu().numpy(), ra8) and np.array_equal(b8.cpu().numpy(), rb8)
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), rsa.view(np.uint32))
+    assert np.array_equal(sb.cpu().numpy().view(np.uint32), rsb.view(np.uint32))
+    ref = oracle.gemm_ref_rowa(ra8, rb8, rsa, rsb, g)
+    ok, _ = within_tolerance(out.float().cpu().numpy(), ref)
+    assert ok.all(), "%d outputs outside the bar" % int((~ok).sum())
