@@ -492,7 +492,7 @@ def main():
     ap.add_argument("--sa-rows", type=int, default=None, choices=(1,),
                     help="1: per-row A factors (1 x g blocks) instead of g x g blocks")
     ap.add_argument("--quant", default=None, choices=("a", "b"),
-                    help="time the GPU quantiser on the workload's FP32 A or B instead of the GEMM (g x g "
+                    help="time the GPU quantiser on the workload's A or B instead of the GEMM (g x g "
                          "blocks, or 1 x g with --sa-rows 1; format from the first letter pair of --fmt)")
     ap.add_argument("--quant-in", default="f32", choices=tuple(QUANT_IN),
                     help="with --quant: the operand's element type as the quantiser reads it")
