@@ -420,6 +420,9 @@ def test_quantize_scale_count_cap(dg):
     assert 4 * rows * rows < (1 << 52)
     assert dg.lib.dg_quantize_fp8_rows(x, rows, 129 * g, g, 0, q, s, None) == dg.DG_EINVAL
     assert dg.lib.dg_quantize_fp8_blocks(x, rows, rows, g, 0, q, s, None) == dg.DG_EINVAL
+    for in_type in (0, 1, 2):
+        assert dg.lib.dg_quantize_fp8_rows_typed(x, in_type, rows, 129 * g, g, 0, q, s, None) == dg.DG_EINVAL
+        assert dg.lib.dg_quantize_fp8_blocks_typed(x, in_type, rows, rows, g, 0, q, s, None) == dg.DG_EINVAL
 
 
 def test_noalloc_scratch_limit(dg):
