@@ -152,6 +152,17 @@ void quant_rejects() {
   expect(dg_quantize_fp8_blocks(x, 64, 128, 128, 0, shift((void*)x, 64), s, nullptr), DG_EINVAL, "q overlaps x");
   // 2^31 or more scale factors
   expect(dg_quantize_fp8_rows(x, DG_MAX_DIM, DG_MAX_DIM - 128, 64, 0, q, s, nullptr), DG_EINVAL, "too many factors");
+  // the typed calls: input kind, the 8-byte q alignment of 16-bit input, the
+  // overlap rule on 2-byte elements
+  expect(dg_quantize_fp8_blocks_typed(x, 3, 64, 128, 128, 0, q, s, nullptr), DG_EINVAL, "typed kind 3");
+  expect(dg_quantize_fp8_rows_typed(x, -1, 64, 128, 128, 0, q, s, nullptr), DG_EINVAL, "typed kind -1");
+  expect(dg_quantize_fp8_rows_typed(x, DG_IN_BF16, 64, 128, 128, 0, shift(q, 4), s, nullptr), DG_EALIGN,
+         "typed bf16 q misaligned");
+  expect(dg_quantize_fp8_blocks_typed(shift((void*)x, 8), DG_IN_F16, 64, 128, 128, 0, q, s, nullptr), DG_EALIGN,
+         "typed f16 x misaligned");
+  expect(dg_quantize_fp8_blocks_typed(x, DG_IN_BF16, 64, 128, 128, 0, shift((void*)x, 8192), s, nullptr),
+         DG_EINVAL, "typed q overlaps bf16 x");
+  expect(dg_quantize_fp8_blocks_typed(x, DG_IN_BF16, 64, 192, 128, 0, q, s, nullptr), DG_EINVAL, "typed cols % g");
 }
 
 void status_texts() {
