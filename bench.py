@@ -394,6 +394,81 @@ def quant_leg(c: int, operand: str, steps: int, warmup: int, sets: int | None, g
     return ms, sets, L, rows, cols, nblocks
 
 
+def pipeline_leg(c: int, steps: int, warmup: int, sets: int | None, g: int):
+    """Workload c as a layer runs it (DeepGEMM实战 §4.4: weights quantised offline, activations online): per
+    step, A in BF16 quantised on the GPU with 1 x g factors, then the GEMM against B quantised once beforehand.
+    Times the pipeline, the quantiser alone and the GEMM alone, each as replays of its own graph."""
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    w = synth.WORKLOADS[c]
+    M, N, K = w["M"], w["N"], w["K"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    a16 = torch.from_numpy(synth.make_a(c)).to(dev).to(torch.bfloat16)
+    xb = torch.from_numpy(synth.make_b(c)).to(dev)
+    b8, sb = dg.dg_quantize_fp8_blocks(xb, gran=g)  # the weights, quantised once (untimed)
+    del xb
+    set_bytes = 2 * M * K + M * K + 4 * M * (K // g) + b8.numel() + 4 * sb.numel() + 2 * M * N
+    if sets is None:
+        sets = max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes) + 1))
+    bufs = []
+    for i in range(sets):
+        bufs.append((a16 if i == 0 else a16.clone(), torch.empty((M, K), dtype=torch.uint8, device=dev),
+                     torch.empty((M, K // g), dtype=torch.float32, device=dev), b8 if i == 0 else b8.clone(),
+                     sb if i == 0 else sb.clone(), torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    stream = torch.cuda.current_stream(dev)
+
+    def quant(i, st):
+        x = bufs[i % sets]
+        dg.dg_quantize_fp8_rows_typed(x[0], gran=g, q=x[1], scales=x[2], stream=st)
+
+    def gemm(i, st):
+        x = bufs[i % sets]
+        dg.dg_gemm_fp8_nt_ex(x[1], x[3], x[2], x[4], out=x[5], gran=g, sa_rows=1, stream=st)
+
+    def both(i, st):
+        quant(i, st)
+        gemm(i, st)
+
+    for i in range(max(1, warmup)):
+        both(i, stream)
+    torch.cuda.synchronize(dev)
+    eager = bufs[0][5].clone()
+    L = max(d for d in range(1, min(steps, 100) + 1) if steps % d == 0)
+
+    def timed(fn):
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(L):
+                    fn(i, cap)
+        torch.cuda.synchronize(dev)
+        graph.replay()  # untimed: uploads the graph
+        torch.cuda.synchronize(dev)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps // L):
+            graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize(dev)
+        return start.elapsed_time(end) / steps
+
+    for x in bufs:
+        x[5].zero_()
+    ms_pipe = timed(both)
+    for i in range(min(sets, L)):
+        if not torch.equal(bufs[i][5].view(torch.int16), eager.view(torch.int16)):
+            raise SystemExit("graph replay output differs from the eager pipeline's")
+    ms_quant = timed(quant)
+    ms_gemm = timed(gemm)
+    return ms_pipe, ms_quant, ms_gemm, sets, L
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -496,6 +571,9 @@ def main():
                          "blocks, or 1 x g with --sa-rows 1; format from the first letter pair of --fmt)")
     ap.add_argument("--quant-in", default="f32", choices=tuple(QUANT_IN),
                     help="with --quant: the operand's element type as the quantiser reads it")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="time the workload as a layer runs it: A in BF16 quantised per row (1 x g) on the GPU, "
+                         "then the GEMM against B quantised beforehand; reports the quantiser's share")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes three times (calibrates the HBM "
                          "byte counters of a profiler run) and exit")
@@ -529,6 +607,33 @@ def main():
     if w["K"] % g:
         raise SystemExit("--gran %d does not divide K = %d" % (g, w["K"]))
     fa, fb = FORMATS[args.fmt]
+    if args.pipeline:
+        flops, gemm_bytes = algorithmic(w, g, 1)
+        M_, K_ = w["M"], w["K"]
+        # the quantiser reads A in BF16 and writes its codes and factors, which the GEMM reads back
+        pipe_bytes = gemm_bytes + 2.0 * M_ * K_ + M_ * K_ + 4.0 * M_ * (K_ // g)
+        ms, mq, mg, sets, glen = pipeline_leg(c, args.steps, args.warmup, args.sets, g)
+        tflops = flops / (ms * 1e-3) / 1e12
+        if bound_of(w) == "mfma":
+            roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": None}
+        else:
+            gbs = pipe_bytes / (ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+        print(json.dumps({
+            "metric": "FP8 block-scaled GEMM TFLOPS with the activation quantised on the GPU in each step (1 GPU)",
+            "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8_e4m3", "data": "synthetic",
+            "config": {"workload": w["name"], "M": w["M"], "N": w["N"], "K": w["K"], "gran": g,
+                       "a_input": "bf16, quantised per step with 1x%d factors" % g,
+                       "b_input": "e4m3 with %dx%d factors, quantised before the timed steps" % (g, g),
+                       "input_sets": sets, "quant_us": round(mq * 1e3, 3), "gemm_us": round(mg * 1e3, 3),
+                       "quant_share": round(mq / ms, 4),
+                       "launch": "hipGraph of %d quantise + GEMM pairs, replayed %d times" % (glen, args.steps // glen)},
+            "roofline": roof, "cpu_baseline": None}), flush=True)
+        return
     if args.quant:
         fmt = fa if args.quant == "a" else fb
         ms, sets, glen, rows, cols, nblocks = quant_leg(c, args.quant, args.steps, args.warmup, args.sets, g, fmt,
