@@ -307,14 +307,31 @@ __global__ __launch_bounds__(256) void quant_fp8_rows(const void* __restrict__ x
 // runs: A of 8192^3 65.7 -> 63.8 us, B of the decode shape 31.6 -> 31.1 us,
 // A of the prefill shape unchanged; four per CU was as good on 8192^3 and
 // slower elsewhere, two per CU 10-15% slower.
-template <int G, int FMT, int IN>
-static hipError_t launch_rows_g(const QuantArgs& p, hipStream_t stream) {
-  constexpr int U = 8;
-  const int64_t nseg = p.rows * (p.cols / G);
+template <int G, int FMT, int IN, int U>
+static hipError_t launch_rows_u(const QuantArgs& p, hipStream_t stream, int64_t nseg) {
   const int64_t per_wg = 4 * (64 / (G / InKind<IN>::kPerLoad)) * U;  // segments per workgroup of four waves
   hipLaunchKernelGGL((quant_fp8_rows<G, FMT, IN, U>), dim3((unsigned)((nseg + per_wg - 1) / per_wg)), dim3(256),
                      32u * 1024u, stream, p.x, p.q, p.scales, (unsigned)nseg, (int)p.cols);
   return hipGetLastError();
+}
+
+// Loads per lane: the most of 8, 4, 2 and 1 that still give at least 2048
+// workgroups (eight per CU), else 1. Large operands keep eight loads in
+// flight per lane; a small activation is spread over the whole chip instead
+// of a few CUs. Interleaved runs, per-row factors at g = 128: A of the decode
+// shape (64 x 7168, 28 workgroups at eight loads) 5.15 -> 2.52 us in FP32 and
+// 5.15 -> 2.42 us in BF16 at one load; A of the prefill shape in BF16 (4096 x
+// 2048) 10.1 -> 8.4 us at two (9.3 at one or four); A of 8192^3 in BF16 best
+// at eight or four (44.3 us; two 46.4, one 56.5).
+template <int G, int FMT, int IN>
+static hipError_t launch_rows_g(const QuantArgs& p, hipStream_t stream) {
+  const int64_t nseg = p.rows * (p.cols / G);
+  constexpr int64_t per_load = 4 * (64 / (G / InKind<IN>::kPerLoad));  // segments per workgroup and load
+  constexpr int64_t kMinGroups = 2048;
+  if (nseg >= kMinGroups * per_load * 8) return launch_rows_u<G, FMT, IN, 8>(p, stream, nseg);
+  if (nseg >= kMinGroups * per_load * 4) return launch_rows_u<G, FMT, IN, 4>(p, stream, nseg);
+  if (nseg >= kMinGroups * per_load * 2) return launch_rows_u<G, FMT, IN, 2>(p, stream, nseg);
+  return launch_rows_u<G, FMT, IN, 1>(p, stream, nseg);
 }
 
 template <int FMT, int IN>

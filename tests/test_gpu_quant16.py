@@ -164,3 +164,29 @@ def test_16bit_operands_quantised_then_multiplied(kind, g):
     ref = oracle.gemm_ref_rowa(ra8, rb8, rsa, rsb, g)
     ok, _ = within_tolerance(out.float().cpu().numpy(), ref)
     assert ok.all(), "%d outputs outside the bar" % int((~ok).sum())
+
+
+# The per-row quantiser takes 8, 4, 2 or 1 loads per lane by the number of
+# 1 x g segments (the most that still give 2048 workgroups). These shapes land
+# on each choice at g = 128 for FP32 (32 segments per workgroup and load) and
+# for 16-bit input (64), and just below a boundary.
+@pytest.mark.parametrize("kind,rows,cols", [
+    ("f32", 4096, 8192), ("f32", 2048, 8192), ("f32", 1024, 8192), ("f32", 1023, 8192), ("f32", 64, 7168),
+    ("bf16", 4096, 8192), ("bf16", 2048, 8192), ("bf16", 2047, 8192), ("bf16", 1024, 8192), ("bf16", 64, 7168),
+    ("f16", 1100, 7680)])
+def test_rows_each_unroll_bitwise(kind, rows, cols):
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    g = 128
+    x = synth.normal(5600 + rows, (rows, cols))
+    if kind == "f32":
+        say("quantise rows unroll f32 %dx%d" % (rows, cols))
+        q, s = dg.dg_quantize_fp8_rows(torch.from_numpy(x).to("cuda:0"), gran=g)
+        torch.cuda.synchronize()
+        rq, rs = oracle.quantize_rows_fmt(x, g, 0)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32)), "scales differ"
+        assert np.array_equal(q.cpu().numpy(), rq), "codes differ"
+    else:
+        _check(x, g, 0, kind, rows_kind=True, label="unroll")
