@@ -20,11 +20,12 @@
 // BF16, DeepGEMM实战 §4.4) are widened exactly to FP32 as they are used; the
 // rule is then the FP32 one, on the same values.
 //
-// One workgroup per block, 256 threads (1024 for g = 256). The block (64 KB
-// of FP32 for g = 128) stays in registers, as loaded, between the amax pass
-// and the encode pass, so x is read from HBM once: the kernel is bound by HBM
-// bandwidth (4 or 2 bytes in, 1 byte out per element). Every load is 16
-// bytes: four FP32 or eight 16-bit elements per lane.
+// One workgroup per block, 256 threads (1024 for g = 256, and for a launch of
+// at most 256 blocks). The block (64 KB of FP32 for g = 128) stays in
+// registers, as loaded, between the amax pass and the encode pass, so x is
+// read from HBM once: the kernel is bound by HBM bandwidth (4 or 2 bytes in,
+// 1 byte out per element). Every load is 16 bytes: four FP32 or eight 16-bit
+// elements per lane.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -189,12 +190,14 @@ __device__ __forceinline__ void encode_store(v4u w, float s, float inv, uint8_t*
   }
 }
 
-template <int G, int FMT, int IN>
-__global__ __launch_bounds__(G == 256 ? 1024 : 256) void quant_fp8_blocks(const void* __restrict__ xv,
+// NT threads per block: 256, or 1024 (at most one lane per 16 bytes of the
+// block) when the blocks are few enough that each CU holds at most one; g =
+// 256 always takes 1024.
+template <int G, int FMT, int IN, int NT>
+__global__ __launch_bounds__(NT) void quant_fp8_blocks(const void* __restrict__ xv,
                                                                           uint8_t* __restrict__ q,
                                                                           float* __restrict__ scales, int rows,
                                                                           int cols) {
-  constexpr int NT = G == 256 ? 1024 : 256;
   constexpr float FMAX = FMT == 1 ? 57344.0f : 448.0f;
   constexpr int EPL = InKind<IN>::kPerLoad;
   constexpr int ROW_L = G / EPL;              // lanes per block row
@@ -373,13 +376,30 @@ hipError_t launch_quant_rows(const QuantArgs& p, hipStream_t stream) {
 // (A of 8192^3 in BF16 42.8 -> 39.4 us), 16-bit g = 64 1.5x (A of the long-K
 // shape 33.8 -> 22.3 us); a 32 KB reservation (five per CU) fell in between.
 // g = 256 runs 1024-thread workgroups, two per CU already.
+template <int G, int FMT, int IN, int NT>
+static hipError_t launch_gt(const QuantArgs& p, hipStream_t stream, int64_t nblocks, unsigned lds) {
+  hipLaunchKernelGGL((quant_fp8_blocks<G, FMT, IN, NT>), dim3((unsigned)nblocks), dim3(NT), lds, stream, p.x, p.q,
+                     p.scales, (int)p.rows, (int)p.cols);
+  return hipGetLastError();
+}
+
+// With at most 256 blocks (one per CU) a block's workgroup has the CU to
+// itself, and up to 1024 threads take a quarter of the passes of 256 over it.
+// Interleaved runs, A of the decode shape (64 x 7168): g = 64 in FP32 (112
+// blocks) 4.05 -> 3.01 us, g = 128 in BF16 3.28 -> 3.14 us, but g = 128 in
+// FP32 3.67 -> 3.84 us (its 64-row blocks leave half of 1024 lanes idle);
+// A of the 256^3 shape (4 blocks) 4.43 -> 4.21 us.
 template <int G, int FMT, int IN>
 static hipError_t launch_g(const QuantArgs& p, hipStream_t stream) {
   const int64_t nblocks = ((p.rows + G - 1) / G) * (p.cols / G);
-  const unsigned lds = IN == 0 && G == 128 && nblocks >= 4 * 256 ? 64u * 1024u : 0u;
-  hipLaunchKernelGGL((quant_fp8_blocks<G, FMT, IN>), dim3((unsigned)nblocks), dim3(G == 256 ? 1024 : 256), lds,
-                     stream, p.x, p.q, p.scales, (int)p.rows, (int)p.cols);
-  return hipGetLastError();
+  if constexpr (G == 256) {
+    return launch_gt<G, FMT, IN, 1024>(p, stream, nblocks, 0u);
+  } else {
+    constexpr int kLanes = (G / InKind<IN>::kPerLoad) * G;  // 16-byte pieces of a block
+    if (nblocks <= 256) return launch_gt<G, FMT, IN, kLanes < 1024 ? kLanes : 1024>(p, stream, nblocks, 0u);
+    const unsigned lds = IN == 0 && G == 128 && nblocks >= 4 * 256 ? 64u * 1024u : 0u;
+    return launch_gt<G, FMT, IN, 256>(p, stream, nblocks, lds);
+  }
 }
 
 template <int FMT, int IN>
