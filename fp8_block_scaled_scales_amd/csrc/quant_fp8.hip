@@ -1,9 +1,10 @@
 // Block quantiser FP32, BF16 or FP16 -> FP8 (E4M3FN or E5M2) with one FP32
-// scale per g x g block, g = 64, 128 or 256, for gfx950. It produces the GEMM's inputs: the
-// pages place quantisation outside the GEMM, say that activations must be
-// quantised online and that the granularity must equal the GEMM's
-// (DeepGEMM实战 §4.4), that one factor per block maps the block into FP8 range
-// (§2.2) by dividing (§5.2), and name E4M3 and E5M2 as the formats (§2.2).
+// scale per g x g block (or 1 x g segment), g = 64, 128 or 256, for gfx950.
+// It produces the GEMM's inputs: the pages place quantisation outside the
+// GEMM, say that activations must be quantised online and that the
+// granularity must equal the GEMM's (DeepGEMM实战 §4.4), that one factor per
+// block maps the block into FP8 range (§2.2) by dividing (§5.2), and name E4M3
+// and E5M2 as the formats (§2.2).
 //
 // Per block: amax = max |x| over the elements present (edge blocks past the
 // last row are partial), scale = amax / fmax (FP32, correctly rounded; 1.0
@@ -190,14 +191,12 @@ __device__ __forceinline__ void encode_store(v4u w, float s, float inv, uint8_t*
   }
 }
 
-// NT threads per block: 256, or 1024 (at most one lane per 16 bytes of the
-// block) when the blocks are few enough that each CU holds at most one; g =
+// NT threads per block: 256, or up to 1024 (no more than the block's 16-byte
+// pieces) when the blocks are few enough that each CU holds at most one; g =
 // 256 always takes 1024.
 template <int G, int FMT, int IN, int NT>
-__global__ __launch_bounds__(NT) void quant_fp8_blocks(const void* __restrict__ xv,
-                                                                          uint8_t* __restrict__ q,
-                                                                          float* __restrict__ scales, int rows,
-                                                                          int cols) {
+__global__ __launch_bounds__(NT) void quant_fp8_blocks(const void* __restrict__ xv, uint8_t* __restrict__ q,
+                                                       float* __restrict__ scales, int rows, int cols) {
   constexpr float FMAX = FMT == 1 ? 57344.0f : 448.0f;
   constexpr int EPL = InKind<IN>::kPerLoad;
   constexpr int ROW_L = G / EPL;              // lanes per block row
