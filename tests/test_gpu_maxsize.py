@@ -160,11 +160,13 @@ def _max_m_or_n(pool, M, N, K, g, big_m, layout):
     say("max %s layout=%d: max|err|/rms = %.3g" % ("M" if big_m else "N", layout, np.max(np.abs(got - ref)) / rms))
 
 
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
 @pytest.mark.parametrize("rows_max", [False, True])
 @pytest.mark.parametrize("per_row", [False, True])
-def test_max_quantizer(rows_max, per_row):
-    # block (g x g) and row (1 x g) quantisers at rows or cols = DG_MAX_DIM:
-    # sampled blocks bitwise against the oracle's quantiser on those blocks
+def test_max_quantizer(rows_max, per_row, kind):
+    # block (g x g) and row (1 x g) quantisers at rows or cols = DG_MAX_DIM, on
+    # FP32 or (through the typed calls) BF16 input: sampled blocks bitwise
+    # against the oracle's quantiser on those blocks
     import torch
 
     import fp8_block_scaled_scales_amd as dg
@@ -173,21 +175,32 @@ def test_max_quantizer(rows_max, per_row):
     rows, cols = (MAX_DIM, 256) if rows_max else (64, MAX_DIM)
     gen = torch.Generator(device="cuda:0").manual_seed(77 + rows_max + 2 * per_row)
     x = torch.randn((rows, cols), generator=gen, device="cuda:0", dtype=torch.float32)
-    say("max quantiser: rows=%d cols=%d per_row=%d" % (rows, cols, per_row))
-    q, s = (dg.dg_quantize_fp8_rows if per_row else dg.dg_quantize_fp8_blocks)(x, gran=g)
+    if kind == "bf16":
+        x = x.to(torch.bfloat16)
+        fn = dg.dg_quantize_fp8_rows_typed if per_row else dg.dg_quantize_fp8_blocks_typed
+    else:
+        fn = dg.dg_quantize_fp8_rows if per_row else dg.dg_quantize_fp8_blocks
+    say("max quantiser: rows=%d cols=%d per_row=%d %s" % (rows, cols, per_row, kind))
+    q, s = fn(x, gran=g)
     torch.cuda.synchronize()
     nrb, ncb = rows // g, cols // g
     blocks = [(0, 0), (nrb - 1, ncb - 1), (nrb // 2, ncb // 3), (nrb - 1, 0), (0, ncb - 1)]
     for rb, cb in blocks:
-        xb = x[rb * g:(rb + 1) * g, cb * g:(cb + 1) * g].cpu().numpy()
+        xt = x[rb * g:(rb + 1) * g, cb * g:(cb + 1) * g].contiguous().cpu()
         qb = q[rb * g:(rb + 1) * g, cb * g:(cb + 1) * g].cpu().numpy()
+        if kind == "bf16":
+            bits = xt.view(torch.int16).numpy().view(np.uint16)
+            ref = oracle.quantize_rows_16 if per_row else oracle.quantize_blocks_16
+            want_q, want_s = ref(bits, oracle.IN_BF16, g, 0)
+        elif per_row:
+            want_q, want_s = oracle.quantize_rows_fmt(xt.numpy(), g)
+        else:
+            want_q, want_s = oracle.quantize_blocks_fmt(xt.numpy(), g, 0)
         if per_row:
-            want_q, want_s = oracle.quantize_rows_fmt(xb, g)
             got_s = s[rb * g:(rb + 1) * g, cb].cpu().numpy()[:, None]
         else:
-            want_q, want_s = oracle.quantize_blocks_fmt(xb, g, 0)
             got_s = s[rb, cb].cpu().numpy().reshape(1, 1)
         assert np.array_equal(qb, want_q), (rb, cb)
-        assert np.array_equal(got_s.view(np.uint32), np.asarray(want_s, np.float32).view(np.uint32)), (rb, cb)
+        assert np.array_equal(got_s.view(np.uint32), np.asarray(want_s, np.float32).reshape(got_s.shape).view(np.uint32)), (rb, cb)
     del x, q, s
     torch.cuda.empty_cache()
