@@ -190,3 +190,35 @@ def test_rows_each_unroll_bitwise(kind, rows, cols):
         assert np.array_equal(q.cpu().numpy(), rq), "codes differ"
     else:
         _check(x, g, 0, kind, rows_kind=True, label="unroll")
+
+
+def test_quantisers_on_concurrent_streams():
+    """Quantiser calls of every input kind and both block shapes on three
+    streams at once, repeated: each result equals the same call made alone
+    (the quantisers keep no state between calls)."""
+    import torch
+
+    import fp8_block_scaled_scales_amd as dg
+
+    g = 128
+    xs = [torch.from_numpy(synth.normal(5700 + i, (1500 + 37 * i, 2048))).to("cuda:0") for i in range(3)]
+    xs[1] = xs[1].to(torch.bfloat16)
+    xs[2] = xs[2].to(torch.float16)
+    calls = [(dg.dg_quantize_fp8_blocks_typed, xs[0], 0), (dg.dg_quantize_fp8_rows_typed, xs[1], 1),
+             (dg.dg_quantize_fp8_blocks_typed, xs[2], 0)]
+    say("quantisers on three streams")
+    alone = []
+    for fn, x, fmt in calls:
+        q, s = fn(x, gran=g, fmt=fmt)
+        torch.cuda.synchronize()
+        alone.append((q.clone(), s.clone()))
+    streams = [torch.cuda.Stream() for _ in calls]
+    for _ in range(4):
+        outs = []
+        for (fn, x, fmt), st in zip(calls, streams):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                outs.append(fn(x, gran=g, fmt=fmt, stream=st))
+        torch.cuda.synchronize()
+        for (q, s), (q0, s0) in zip(outs, alone):
+            assert torch.equal(q, q0) and torch.equal(s.view(torch.int32), s0.view(torch.int32))
