@@ -21,8 +21,8 @@
 // BF16, DeepGEMM实战 §4.4) are widened exactly to FP32 as they are used; the
 // rule is then the FP32 one, on the same values.
 //
-// One workgroup per block, 256 threads (1024 for g = 256, and for a launch of
-// at most 256 blocks). The block (64 KB of FP32 for g = 128) stays in
+// One workgroup per block, 256 or 512 threads by block size (1024 for g =
+// 256, and for a launch of at most 256 blocks). The block (64 KB of FP32 for g = 128) stays in
 // registers, as loaded, between the amax pass and the encode pass, so x is
 // read from HBM once: the kernel is bound by HBM bandwidth (4 or 2 bytes in,
 // 1 byte out per element). Every load is 16 bytes: four FP32 or eight 16-bit
@@ -191,9 +191,9 @@ __device__ __forceinline__ void encode_store(v4u w, float s, float inv, uint8_t*
   }
 }
 
-// NT threads per block: 256, or up to 1024 (no more than the block's 16-byte
-// pieces) when the blocks are few enough that each CU holds at most one; g =
-// 256 always takes 1024.
+// NT threads per block: 256 or 512 by block size (launch_g), or up to 1024
+// (no more than the block's 16-byte pieces) when the blocks are few enough
+// that each CU holds at most one; g = 256 always takes 1024.
 template <int G, int FMT, int IN, int NT>
 __global__ __launch_bounds__(NT) void quant_fp8_blocks(const void* __restrict__ xv, uint8_t* __restrict__ q,
                                                        float* __restrict__ scales, int rows, int cols) {
@@ -396,8 +396,19 @@ static hipError_t launch_g(const QuantArgs& p, hipStream_t stream) {
   } else {
     constexpr int kLanes = (G / InKind<IN>::kPerLoad) * G;  // 16-byte pieces of a block
     if (nblocks <= 256) return launch_gt<G, FMT, IN, kLanes < 1024 ? kLanes : 1024>(p, stream, nblocks, 0u);
-    const unsigned lds = IN == 0 && G == 128 && nblocks >= 4 * 256 ? 64u * 1024u : 0u;
-    return launch_gt<G, FMT, IN, 256>(p, stream, nblocks, lds);
+    // Blocks of 16 or 32 KB (FP32 at g = 64, 16-bit input at g = 128) take
+    // 512 threads, two or four loads per lane: interleaved runs, A of the
+    // long-K shape in FP32 35.2 -> 31.5 us, its B 63.7 -> 60.0 us, A of 8192^3
+    // in BF16 40.4 -> 39.2 us, B of the prefill shape in BF16 13.9 -> 12.8 us.
+    // 8 KB blocks (16-bit, g = 64) keep 256, one load per lane being too few
+    // (A of the long-K shape in BF16 22.6 -> 26.6 us at 512); FP32 at g = 128
+    // keeps 256 and the reservation below.
+    if constexpr ((IN == 0 && G == 64) || (IN != 0 && G == 128)) {
+      return launch_gt<G, FMT, IN, 512>(p, stream, nblocks, 0u);
+    } else {
+      const unsigned lds = IN == 0 && G == 128 && nblocks >= 4 * 256 ? 64u * 1024u : 0u;
+      return launch_gt<G, FMT, IN, 256>(p, stream, nblocks, lds);
+    }
   }
 }
 
