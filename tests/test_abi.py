@@ -218,7 +218,8 @@ def test_python_binding_checks_layout_shapes(dg):
 
 def test_format_codes_match_header(dg):
     text = open(HEADER).read()
-    for name in ("DG_FMT_E4M3", "DG_FMT_E5M2", "DG_ACT_NONE", "DG_ACT_RELU", "DG_ACT_GELU"):
+    for name in ("DG_FMT_E4M3", "DG_FMT_E5M2", "DG_ACT_NONE", "DG_ACT_RELU", "DG_ACT_GELU", "DG_IN_F32", "DG_IN_BF16",
+                 "DG_IN_F16"):
         m = re.search(r"#define %s (\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(dg, name), name
 
